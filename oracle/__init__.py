@@ -1,0 +1,157 @@
+"""fp64 CPU oracle for grouped-query attention (ctypes front end of ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library
+and its binding) never does, and this package never imports the product.
+
+Every function takes bf16 inputs as numpy uint16 bit patterns (the layouts of
+``gqa_workloads.generate``) and returns float64 results.  The arithmetic lives
+in ``oracle.c``; the header of that file states the definitions and cites the
+passages they follow.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, invariants, special cases and a brute-force check built on
+library routines) and by the planted-mistake checks in
+``tests/test_oracle_mutants.py``.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(source=SOURCE, output=LIBRARY, extra_flags=()):
+    """Compile ``oracle.c`` with gcc into a shared library; returns its path."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, source, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+def _bind(lib):
+    u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+    ci, cd, cl = ctypes.c_int, ctypes.c_double, ctypes.c_long
+    lib.oracle_decode.argtypes = [u16p, u16p, u16p, ctypes.c_void_p, f64p, f64p,
+                                  ci, ci, ci, ci, ci, cd, ci]
+    lib.oracle_decode.restype = ci
+    lib.oracle_prefill_causal_rows.argtypes = [u16p, u16p, u16p, f64p, f64p,
+                                               ci, ci, ci, ci, ci, cd, i32p, cl, ci]
+    lib.oracle_prefill_causal_rows.restype = ci
+    lib.oracle_decode_partial.argtypes = [u16p, u16p, u16p, f64p, f64p, f64p,
+                                          ci, ci, ci, ci, ci, cd, ci, ci, ci]
+    lib.oracle_decode_partial.restype = ci
+    lib.oracle_merge_states.argtypes = [f64p, f64p, f64p, cl, ci, ci, f64p, f64p]
+    lib.oracle_merge_states.restype = ci
+    return lib
+
+
+def load(path=None):
+    """Load the oracle library (building it first if it is missing)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _lib = _bind(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def default_threads():
+    return len(os.sched_getaffinity(0))
+
+
+def _u16(a):
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def decode(q, k, v, seqlens=None, tau=None, nthreads=0, lib=None):
+    """Attention of one query token per (sequence, query head) over its cached keys.
+
+    q [B, H_q, d]; k, v [B, S_max, H_kv, d] (uint16 bf16 bits); seqlens int32 [B] or None.
+    ``tau`` defaults to 1/sqrt(d).  Returns (o [B, H_q, d], lse [B, H_q]) in float64.
+    """
+    lib = lib or load()
+    B, H_q, d = q.shape
+    _, S_max, H_kv, _ = k.shape
+    tau = 1.0 / np.sqrt(d) if tau is None else float(tau)
+    o = np.zeros((B, H_q, d), dtype=np.float64)
+    lse = np.zeros((B, H_q), dtype=np.float64)
+    sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
+    rc = lib.oracle_decode(_u16(q), _u16(k), _u16(v),
+                           None if sl is None else sl.ctypes.data_as(ctypes.c_void_p),
+                           o, lse, B, H_q, H_kv, d, S_max, tau, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_decode rejected its arguments (code {rc})")
+    return o, lse
+
+
+def prefill_causal_rows(q, k, v, rows, tau=None, nthreads=0, lib=None):
+    """Causal attention (key j visible to query i iff j <= i) on selected rows.
+
+    q [B, S, H_q, d]; k, v [B, S, H_kv, d]; rows int array [n, 3] of (b, h, i).
+    Returns (o [n, d], lse [n]) in float64.
+    """
+    lib = lib or load()
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    tau = 1.0 / np.sqrt(d) if tau is None else float(tau)
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 3)
+    n = rows.shape[0]
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_prefill_causal_rows(_u16(q), _u16(k), _u16(v), o, lse, B, S, H_q, H_kv, d,
+                                        tau, rows, n, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_causal_rows rejected its arguments (code {rc})")
+    return o, lse
+
+
+def prefill_causal(q, k, v, tau=None, nthreads=0, lib=None):
+    """Causal prefill on every row: returns (o [B, S, H_q, d], lse [B, H_q, S])."""
+    B, S, H_q, d = q.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H_q), np.arange(S), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
+    o, lse = prefill_causal_rows(q, k, v, rows, tau=tau, nthreads=nthreads, lib=lib)
+    o = o.reshape(B, H_q, S, d).transpose(0, 2, 1, 3).copy()
+    return o, lse.reshape(B, H_q, S)
+
+
+def decode_partial(q, k, v, j0, j1, tau=None, nthreads=0, lib=None):
+    """Partial state (m, l, O unnormalised) of every decode row over keys [j0, j1)."""
+    lib = lib or load()
+    B, H_q, d = q.shape
+    _, S_max, H_kv, _ = k.shape
+    tau = 1.0 / np.sqrt(d) if tau is None else float(tau)
+    m = np.zeros((B, H_q), dtype=np.float64)
+    l = np.zeros((B, H_q), dtype=np.float64)
+    o = np.zeros((B, H_q, d), dtype=np.float64)
+    rc = lib.oracle_decode_partial(_u16(q), _u16(k), _u16(v), m, l, o, B, H_q, H_kv, d, S_max,
+                                   tau, int(j0), int(j1), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_decode_partial rejected its arguments (code {rc})")
+    return m, l, o
+
+
+def merge_states(m, l, o, lib=None):
+    """Merge partial states: m, l [R, P]; o [R, P, d] -> (o [R, d], lse [R])."""
+    lib = lib or load()
+    m = np.ascontiguousarray(m, dtype=np.float64)
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    R, P = m.shape
+    d = o.shape[-1]
+    o_out = np.zeros((R, d), dtype=np.float64)
+    lse = np.zeros(R, dtype=np.float64)
+    lib.oracle_merge_states(m, l, o, R, P, d, o_out, lse)
+    return o_out, lse

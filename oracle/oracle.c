@@ -1,0 +1,308 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file.  Its users are the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark.  It shares no source, header, table or
+ * helper with the HIP library.
+ *
+ * What it computes is the plain definition of attention, not the tiled
+ * algorithm (FlashAttention reaches the same result with the same FLOP:
+ * "Attention Kernel lineage" (V07), section 4):
+ *
+ *   for every query row i of head h, with KV head g = floor(h / G), G = H_q/H_kv
+ *   ("Attention Kernel lineage", section 14, group formula):
+ *     s_j  = tau * sum_c q[i][c] * k_g[j][c]       for every visible key j
+ *     m    = max_j s_j                             (safe softmax pass 1,
+ *     l    = sum_j exp(s_j - m)                     pass 2,
+ *     p_j  = exp(s_j - m) / l                       pass 3; section 2 step 1)
+ *     o[c] = sum_j p_j * v_g[j][c]                 (section 1, O = PV)
+ *     lse  = m + ln l                              (section 2, LSE kept per row)
+ *
+ * Visible keys: decode (one query token) sees keys [0, seqlen); the decode
+ * step is a pure read of the cache with no mask but the sequence end (ADR-0060
+ * "AHBM GQA Fused Attention", sections 0.5.1 and 5.2).  Causal prefill row i
+ * sees keys j <= i (V07 section 12, causal definition).
+ *
+ * All bf16 inputs are widened exactly to double; every product and sum is in
+ * double.  A row with no visible key gives o = 0 and lse = -inf (the identity
+ * state (-inf, 0, 0) of the merge, V07 section 3).
+ *
+ * The partial-state and merge functions restate V07 section 3 (partial
+ * definition over a key subset and the combination formula) and section 17
+ * (second stage of split-K decode): they let the tests check that merging the
+ * states of any partition of the keys gives the unsplit result.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* Exact widening of a bfloat16 bit pattern (the high half of an IEEE single). */
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* One query row against n key/value rows.
+ * krow(j) = k + j*kv_stride, vrow(j) = v + j*kv_stride, each d bf16 values.
+ * s is caller scratch of n doubles; o receives d doubles. */
+static void attend_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       size_t kv_stride, int n, int d, double tau,
+                       double *s, double *qd, double *o, double *lse)
+{
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    if (n <= 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[c]);
+
+    /* the whole score row, materialised */
+    for (int j = 0; j < n; ++j) {
+        const uint16_t *kj = k + (size_t)j * kv_stride;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += qd[c] * bf16_to_double(kj[c]);
+        s[j] = tau * dot;
+    }
+    /* pass 1: row maximum */
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    /* pass 2: denominator */
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) l += exp(s[j] - m);
+    /* pass 3: probabilities, then the weighted sum of V */
+    for (int j = 0; j < n; ++j) {
+        double p = exp(s[j] - m) / l;
+        const uint16_t *vj = v + (size_t)j * kv_stride;
+        for (int c = 0; c < d; ++c) o[c] += p * bf16_to_double(vj[c]);
+    }
+    *lse = m + log(l);
+}
+
+/* ------------------------------------------------------------------------- */
+/* A tiny thread pool over row indices: worker t takes rows t, t+T, t+2T, ... */
+
+typedef void (*row_fn)(void *ctx, long row, double *s, double *qd);
+
+struct pool_arg {
+    row_fn fn;
+    void *ctx;
+    long nrows;
+    int tid, nthreads;
+    int scratch_n, d;
+};
+
+static void *pool_worker(void *p)
+{
+    struct pool_arg *a = (struct pool_arg *)p;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(a->scratch_n > 0 ? a->scratch_n : 1));
+    double *qd = (double *)malloc(sizeof(double) * (size_t)a->d);
+    if (s && qd)
+        for (long r = a->tid; r < a->nrows; r += a->nthreads) a->fn(a->ctx, r, s, qd);
+    free(s);
+    free(qd);
+    return NULL;
+}
+
+static int resolve_threads(int nthreads)
+{
+    if (nthreads > 0) return nthreads;
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static int run_rows(row_fn fn, void *ctx, long nrows, int nthreads, int scratch_n, int d)
+{
+    nthreads = resolve_threads(nthreads);
+    if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    struct pool_arg *args = (struct pool_arg *)malloc(sizeof(struct pool_arg) * (size_t)nthreads);
+    if (!th || !args) {
+        free(th);
+        free(args);
+        return -1;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        args[t] = (struct pool_arg){fn, ctx, nrows, t, nthreads, scratch_n, d};
+        if (t > 0) pthread_create(&th[t], NULL, pool_worker, &args[t]);
+    }
+    pool_worker(&args[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(th);
+    free(args);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Decode: q [B, H_q, d]; k, v [B, S_max, H_kv, d]; seqlens [B] or NULL.
+ * o [B, H_q, d] (double), lse [B, H_q] (double, natural log). */
+
+struct decode_ctx {
+    const uint16_t *q, *k, *v;
+    const int32_t *seqlens;
+    double *o, *lse;
+    int B, H_q, H_kv, d, S_max;
+    double tau;
+};
+
+static void decode_row(void *p, long r, double *s, double *qd)
+{
+    struct decode_ctx *c = (struct decode_ctx *)p;
+    int b = (int)(r / c->H_q), h = (int)(r % c->H_q);
+    int G = c->H_q / c->H_kv;
+    int g = h / G;
+    int n = c->seqlens ? c->seqlens[b] : c->S_max;
+    const uint16_t *k0 = c->k + ((size_t)b * c->S_max * c->H_kv + g) * c->d;
+    const uint16_t *v0 = c->v + ((size_t)b * c->S_max * c->H_kv + g) * c->d;
+    attend_row(c->q + (size_t)r * c->d, k0, v0, (size_t)c->H_kv * c->d, n, c->d, c->tau, s, qd,
+               c->o + (size_t)r * c->d, c->lse + r);
+}
+
+int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens,
+                  double *o, double *lse, int B, int H_q, int H_kv, int d, int S_max,
+                  double tau, int nthreads)
+{
+    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
+    if (seqlens)
+        for (int b = 0; b < B; ++b)
+            if (seqlens[b] < 0 || seqlens[b] > S_max) return -2;
+    struct decode_ctx c = {q, k, v, seqlens, o, lse, B, H_q, H_kv, d, S_max, tau};
+    return run_rows(decode_row, &c, (long)B * H_q, nthreads, S_max, d);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Causal prefill on selected rows.
+ * q [B, S, H_q, d]; k, v [B, S, H_kv, d]; rows: nrows triples (b, h, i).
+ * o [nrows, d] (double), lse [nrows] (double). */
+
+struct prefill_ctx {
+    const uint16_t *q, *k, *v;
+    const int32_t *rows;
+    double *o, *lse;
+    int B, S, H_q, H_kv, d;
+    double tau;
+};
+
+static void prefill_row(void *p, long r, double *s, double *qd)
+{
+    struct prefill_ctx *c = (struct prefill_ctx *)p;
+    int b = c->rows[3 * r], h = c->rows[3 * r + 1], i = c->rows[3 * r + 2];
+    int G = c->H_q / c->H_kv;
+    int g = h / G;
+    const uint16_t *qrow = c->q + (((size_t)b * c->S + i) * c->H_q + h) * c->d;
+    const uint16_t *k0 = c->k + ((size_t)b * c->S * c->H_kv + g) * c->d;
+    const uint16_t *v0 = c->v + ((size_t)b * c->S * c->H_kv + g) * c->d;
+    /* causal: keys 0..i inclusive */
+    attend_row(qrow, k0, v0, (size_t)c->H_kv * c->d, i + 1, c->d, c->tau, s, qd,
+               c->o + (size_t)r * c->d, c->lse + r);
+}
+
+int oracle_prefill_causal_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               double *o, double *lse, int B, int S, int H_q, int H_kv, int d,
+                               double tau, const int32_t *rows, long nrows, int nthreads)
+{
+    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
+    for (long r = 0; r < nrows; ++r) {
+        int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H_q || i < 0 || i >= S) return -2;
+    }
+    struct prefill_ctx c = {q, k, v, rows, o, lse, B, S, H_q, H_kv, d, tau};
+    return run_rows(prefill_row, &c, nrows, nthreads, S, d);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Partial state of a decode row over keys [j0, j1) (V07 section 3, partial definition):
+ *   m = max s_j,  l = sum exp(s_j - m),  O = sum exp(s_j - m) * v_j   (O not divided by l)
+ * The empty range gives the identity (-inf, 0, 0).
+ * m, l [B, H_q]; o [B, H_q, d]. */
+
+struct partial_ctx {
+    const uint16_t *q, *k, *v;
+    double *m, *l, *o;
+    int B, H_q, H_kv, d, S_max, j0, j1;
+    double tau;
+};
+
+static void partial_row(void *p, long r, double *s, double *qd)
+{
+    struct partial_ctx *c = (struct partial_ctx *)p;
+    int b = (int)(r / c->H_q), h = (int)(r % c->H_q);
+    int g = h / (c->H_q / c->H_kv);
+    int n = c->j1 - c->j0;
+    double *o = c->o + (size_t)r * c->d;
+    for (int x = 0; x < c->d; ++x) o[x] = 0.0;
+    if (n <= 0) {
+        c->m[r] = -INFINITY;
+        c->l[r] = 0.0;
+        return;
+    }
+    size_t stride = (size_t)c->H_kv * c->d;
+    const uint16_t *k0 = c->k + (((size_t)b * c->S_max + c->j0) * c->H_kv + g) * c->d;
+    const uint16_t *v0 = c->v + (((size_t)b * c->S_max + c->j0) * c->H_kv + g) * c->d;
+    const uint16_t *qr = c->q + (size_t)r * c->d;
+    for (int x = 0; x < c->d; ++x) qd[x] = bf16_to_double(qr[x]);
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int x = 0; x < c->d; ++x) dot += qd[x] * bf16_to_double(k0[j * stride + x]);
+        s[j] = c->tau * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) {
+        double e = exp(s[j] - m);
+        l += e;
+        for (int x = 0; x < c->d; ++x) o[x] += e * bf16_to_double(v0[j * stride + x]);
+    }
+    c->m[r] = m;
+    c->l[r] = l;
+}
+
+int oracle_decode_partial(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          double *m, double *l, double *o, int B, int H_q, int H_kv, int d,
+                          int S_max, double tau, int j0, int j1, int nthreads)
+{
+    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
+    if (j0 < 0 || j1 > S_max || j0 > j1) return -2;
+    struct partial_ctx c = {q, k, v, m, l, o, B, H_q, H_kv, d, S_max, j0, j1, tau};
+    return run_rows(partial_row, &c, (long)B * H_q, nthreads, S_max, d);
+}
+
+/* Merge of P partial states per row (V07 section 3 combination formula, applied
+ * over all partials at once as in the second stage of split-K decode, section 17):
+ *   M = max_p m_p,  a_p = exp(m_p - M),  L = sum a_p l_p,
+ *   O = (sum a_p O_p) / L,  lse = M + ln L.
+ * A partial with m_p = -inf contributes a_p = 0; all partials empty gives O = 0, lse = -inf.
+ * m, l [R, P]; o [R, P, d]; o_out [R, d]; lse_out [R]. */
+int oracle_merge_states(const double *m, const double *l, const double *o, long R, int P, int d,
+                        double *o_out, double *lse_out)
+{
+    for (long r = 0; r < R; ++r) {
+        const double *mr = m + r * P, *lr = l + r * P, *orow = o + r * (long)P * d;
+        double *out = o_out + r * d;
+        for (int x = 0; x < d; ++x) out[x] = 0.0;
+        double M = -INFINITY;
+        for (int p = 0; p < P; ++p)
+            if (mr[p] > M) M = mr[p];
+        if (M == -INFINITY) {
+            lse_out[r] = -INFINITY;
+            continue;
+        }
+        double L = 0.0;
+        for (int p = 0; p < P; ++p) {
+            double a = exp(mr[p] - M);
+            L += a * lr[p];
+            for (int x = 0; x < d; ++x) out[x] += a * orow[(long)p * d + x];
+        }
+        for (int x = 0; x < d; ++x) out[x] /= L;
+        lse_out[r] = M + log(L);
+    }
+    return 0;
+}

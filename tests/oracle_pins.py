@@ -1,0 +1,321 @@
+"""Pins for the fp64 oracle: checks against what the definitions and the pages fix.
+
+Each pin is a function ``pin_*(lib)`` that raises AssertionError when the
+oracle library ``lib`` disagrees with a closed form, an invariant, a special
+case, or a brute-force evaluation built on library routines (scipy's softmax
+and logsumexp, ``math.fsum``).  ``test_oracle_pins.py`` runs them on the real
+oracle; ``test_oracle_mutants.py`` runs them on copies of ``oracle.c`` with a
+planted mistake and requires that some pin fails for every such mistake.
+"""
+import math
+
+import numpy as np
+from scipy.special import logsumexp, softmax
+
+import oracle
+from gqa_workloads.generate import bf16_bits_from_f32, decode_inputs, f32_from_bf16_bits, \
+    prefill_inputs
+
+BF16_ONE = 0x3F80
+
+
+def _f64(bits):
+    return f32_from_bf16_bits(bits).astype(np.float64)
+
+
+def _fsum_dot(a, b):
+    return math.fsum(float(x) * float(y) for x, y in zip(a, b))
+
+
+def _brute_row(qrow, K, V, tau):
+    """Library-routine evaluation of one attention row (exact dot products via fsum)."""
+    s = np.array([tau * _fsum_dot(qrow, K[j]) for j in range(K.shape[0])])
+    p = softmax(s)
+    o = np.array([math.fsum(p[j] * V[j, c] for j in range(K.shape[0])) for c in range(V.shape[1])])
+    return o, float(logsumexp(s))
+
+
+def _rel_close(a, b, rtol, atol=0.0):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    assert np.all(np.isfinite(a) == np.isfinite(b)), "finiteness differs"
+    fin = np.isfinite(b)
+    err = np.abs(a[fin] - b[fin])
+    bound = atol + rtol * np.maximum(np.abs(b[fin]), 1e-300)
+    assert np.all(err <= bound), f"max err {err.max() if err.size else 0} (rtol {rtol})"
+    assert np.array_equal(a[~fin], b[~fin]), "non-finite values differ"
+
+
+# ---------------------------------------------------------------------------
+# Softmax normalisation (V07 section 2, safe softmax): with V = identity rows the
+# output row IS the probability vector, so it must be non-negative and sum to 1.
+
+def pin_softmax_rows_sum_to_one(lib):
+    rng = np.random.default_rng(7)
+    B, H_q, H_kv, d, S = 2, 4, 2, 32, 20
+    q = bf16_bits_from_f32(rng.standard_normal((B, H_q, d)).astype(np.float32) * 2)
+    k = bf16_bits_from_f32(rng.standard_normal((B, S, H_kv, d)).astype(np.float32))
+    v = np.zeros((B, S, H_kv, d), dtype=np.uint16)
+    for j in range(S):
+        v[:, j, :, j] = BF16_ONE
+    o, _ = oracle.decode(q, k, v, lib=lib)
+    assert np.all(o >= 0.0)
+    assert np.all(o[..., S:] == 0.0)
+    assert np.max(np.abs(o.sum(axis=-1) - 1.0)) <= 1e-12
+    # the probabilities must also be the softmax of the score row (brute force)
+    for b in range(B):
+        for h in range(H_q):
+            g = h // (H_q // H_kv)
+            s = np.array([_fsum_dot(_f64(q[b, h]), _f64(k[b, j, g])) for j in range(S)])
+            p = softmax(s / math.sqrt(d))
+            _rel_close(o[b, h, :S], p, 1e-12, 1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny inputs, decode and causal prefill.
+
+def pin_brute_force_decode(lib):
+    inp = decode_inputs(2, 4, 2, 8, ragged=(1, 13), seed=11)
+    q, k, v, sl = inp["q"], inp["k"], inp["v"], inp["seqlens"]
+    o, lse = oracle.decode(q, k, v, sl, lib=lib)
+    tau = 1.0 / math.sqrt(8)
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            n = int(sl[b])
+            ob, lb = _brute_row(_f64(q[b, h]), _f64(k[b, :n, g]), _f64(v[b, :n, g]), tau)
+            _rel_close(o[b, h], ob, 1e-12, 1e-14)
+            assert abs(lse[b, h] - lb) <= 1e-13 * max(1.0, abs(lb))
+
+
+def pin_brute_force_prefill(lib):
+    B, S, H_q, H_kv, d = 1, 9, 4, 2, 16
+    inp = prefill_inputs(B, S, H_q, H_kv, d, seed=12)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = oracle.prefill_causal(q, k, v, lib=lib)
+    tau = 1.0 / math.sqrt(d)
+    for h in range(H_q):
+        g = h // (H_q // H_kv)
+        for i in range(S):
+            ob, lb = _brute_row(_f64(q[0, i, h]), _f64(k[0, :i + 1, g]), _f64(v[0, :i + 1, g]), tau)
+            _rel_close(o[0, i, h], ob, 1e-12, 1e-14)
+            assert abs(lse[0, h, i] - lb) <= 1e-13 * max(1.0, abs(lb))
+
+
+# ---------------------------------------------------------------------------
+# Merge associativity (V07 section 3): the merged states of ANY partition of the
+# keys -- uneven, singleton and empty chunks included -- equal the unsplit result.
+
+def pin_split_merge_equals_unsplit(lib):
+    inp = decode_inputs(1, 8, 2, 32, S_max=96, seed=13)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o_full, lse_full = oracle.decode(q, k, v, lib=lib)
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        ncut = rng.integers(1, 9)
+        cuts = np.sort(rng.integers(0, 97, size=ncut))
+        bounds = [0, *cuts.tolist(), 96]
+        if trial == 0:
+            bounds = [0, 0, 1, 1, 50, 96, 96]          # empty, singleton, empty, ..., empty
+        parts = [oracle.decode_partial(q, k, v, a, b, lib=lib) for a, b in zip(bounds, bounds[1:])]
+        m = np.stack([p[0].reshape(-1) for p in parts], axis=1)
+        l = np.stack([p[1].reshape(-1) for p in parts], axis=1)
+        ob = np.stack([p[2].reshape(-1, 32) for p in parts], axis=1)
+        if trial % 2:
+            perm = rng.permutation(m.shape[1])        # commutativity: any order of partials
+            m, l, ob = m[:, perm], l[:, perm], ob[:, perm]
+        o_m, lse_m = oracle.merge_states(m, l, ob, lib=lib)
+        _rel_close(o_m, o_full.reshape(-1, 32), 1e-12, 1e-14)
+        _rel_close(lse_m, lse_full.reshape(-1), 1e-13)
+
+
+def pin_merge_identity_and_empty(lib):
+    inp = decode_inputs(1, 4, 1, 16, S_max=10, seed=14)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    m, l, o = oracle.decode_partial(q, k, v, 0, 10, lib=lib)
+    me, le, oe = oracle.decode_partial(q, k, v, 4, 4, lib=lib)
+    assert np.all(me == -np.inf) and np.all(le == 0.0) and np.all(oe == 0.0)
+    # merging with the identity state (-inf, 0, 0) leaves the result unchanged, exactly
+    o1, lse1 = oracle.merge_states(m.reshape(-1, 1), l.reshape(-1, 1), o.reshape(-1, 1, 16), lib=lib)
+    o2, lse2 = oracle.merge_states(np.stack([m.reshape(-1), me.reshape(-1)], 1),
+                                   np.stack([l.reshape(-1), le.reshape(-1)], 1),
+                                   np.stack([o.reshape(-1, 16), oe.reshape(-1, 16)], 1), lib=lib)
+    assert np.array_equal(o1, o2) and np.array_equal(lse1, lse2)
+    # a single state normalises to O/l and lse = m + ln l
+    _rel_close(o1, (o / l[..., None]).reshape(-1, 16), 1e-15, 1e-300)
+    _rel_close(lse1, (m + np.log(l)).reshape(-1), 1e-15)
+    # all partials empty -> O = 0, lse = -inf
+    o3, lse3 = oracle.merge_states(np.full((2, 3), -np.inf), np.zeros((2, 3)),
+                                   np.zeros((2, 3, 16)), lib=lib)
+    assert np.all(o3 == 0.0) and np.all(lse3 == -np.inf)
+    # decode with the full state equals the normalised partial
+    o_full, lse_full = oracle.decode(q, k, v, lib=lib)
+    _rel_close(o1, o_full.reshape(-1, 16), 1e-13, 1e-15)
+    _rel_close(lse1, lse_full.reshape(-1), 1e-14)
+
+
+# ---------------------------------------------------------------------------
+# GQA head map (V07 section 14): query head h reads KV head floor(h / G).  G = 1
+# is plain multi-head attention, so GQA must equal MHA on K/V repeated G times
+# per head (the materialised broadcast of ADR-0061, rejected for the kernels
+# but a valid definition to test against).
+
+def pin_gqa_equals_mha_on_repeated_kv(lib):
+    inp = decode_inputs(2, 8, 2, 16, S_max=24, seed=15)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o_g, lse_g = oracle.decode(q, k, v, lib=lib)
+    k_rep = np.repeat(k, 4, axis=2)
+    v_rep = np.repeat(v, 4, axis=2)
+    o_m, lse_m = oracle.decode(q, k_rep, v_rep, lib=lib)
+    assert np.array_equal(o_g, o_m) and np.array_equal(lse_g, lse_m)
+    # the modulo map (h mod H_kv) is a different function on these inputs
+    o_t, _ = oracle.decode(q, np.tile(k, (1, 1, 4, 1)), np.tile(v, (1, 1, 4, 1)), lib=lib)
+    assert not np.allclose(o_t, o_g)
+    # same for causal prefill
+    pin = prefill_inputs(1, 12, 8, 2, 16, seed=16)
+    o_pg, l_pg = oracle.prefill_causal(pin["q"], pin["k"], pin["v"], lib=lib)
+    o_pm, l_pm = oracle.prefill_causal(pin["q"], np.repeat(pin["k"], 4, axis=2),
+                                       np.repeat(pin["v"], 4, axis=2), lib=lib)
+    assert np.array_equal(o_pg, o_pm) and np.array_equal(l_pg, l_pm)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms derived from the definition.
+
+def pin_identical_keys_give_mean_of_v(lib):
+    rng = np.random.default_rng(17)
+    B, H_q, H_kv, d, S = 1, 4, 2, 32, 37
+    q = bf16_bits_from_f32(rng.standard_normal((B, H_q, d)).astype(np.float32))
+    krow = bf16_bits_from_f32(rng.standard_normal((H_kv, d)).astype(np.float32))
+    k = np.broadcast_to(krow, (B, S, H_kv, d)).copy()
+    v = bf16_bits_from_f32(rng.standard_normal((B, S, H_kv, d)).astype(np.float32))
+    o, lse = oracle.decode(q, k, v, lib=lib)
+    for h in range(H_q):
+        g = h // 2
+        mean = np.array([math.fsum(_f64(v[0, :, g, c])) / S for c in range(d)])
+        _rel_close(o[0, h], mean, 1e-13, 1e-15)
+        s = _fsum_dot(_f64(q[0, h]), _f64(krow[g])) / math.sqrt(d)
+        assert abs(lse[0, h] - (s + math.log(S))) <= 1e-13 * max(1.0, abs(s) + math.log(S))
+
+
+def pin_zero_scale_gives_mean_and_log_n(lib):
+    inp = decode_inputs(1, 4, 2, 16, S_max=29, seed=18)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], tau=0.0, lib=lib)
+    v = _f64(inp["v"])
+    for h in range(4):
+        mean = v[0, :, h // 2].mean(axis=0)
+        _rel_close(o[0, h], mean, 1e-13, 1e-15)
+        assert abs(lse[0, h] - math.log(29)) <= 1e-14
+
+
+def pin_single_key(lib):
+    inp = decode_inputs(1, 4, 2, 32, S_max=5, seed=19)
+    sl = np.array([1], dtype=np.int32)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], sl, lib=lib)
+    for h in range(4):
+        g = h // 2
+        assert np.array_equal(o[0, h], _f64(inp["v"][0, 0, g]))
+        s = _fsum_dot(_f64(inp["q"][0, h]), _f64(inp["k"][0, 0, g])) / math.sqrt(32)
+        assert abs(lse[0, h] - s) <= 1e-14 * max(1.0, abs(s))
+
+
+def pin_two_keys_sigmoid(lib):
+    inp = decode_inputs(1, 2, 1, 16, S_max=2, seed=20)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], lib=lib)
+    q, k, v = _f64(inp["q"]), _f64(inp["k"]), _f64(inp["v"])
+    for h in range(2):
+        s0 = _fsum_dot(q[0, h], k[0, 0, 0]) / 4.0
+        s1 = _fsum_dot(q[0, h], k[0, 1, 0]) / 4.0
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        _rel_close(o[0, h], w0 * v[0, 0, 0] + w1 * v[0, 1, 0], 1e-13, 1e-15)
+        assert abs(lse[0, h] - np.logaddexp(s0, s1)) <= 1e-14 * max(1.0, abs(lse[0, h]))
+
+
+def pin_safe_softmax_survives_huge_logits(lib):
+    """V07 section 2: the unshifted exponential overflows (fp32 beyond x > 88, fp64
+    beyond ~709); the max-shifted form stays finite.  With logits thousands apart the
+    softmax is one-hot on the largest score, so O is that key's V row exactly and
+    LSE is that score."""
+    d, S = 32, 6
+    q = bf16_bits_from_f32(np.full((1, 1, d), 64.0, dtype=np.float32))
+    levels = np.array([1.0, -2.0, 4.0, 3.0, -4.0, 0.5], dtype=np.float32)
+    k = bf16_bits_from_f32(np.broadcast_to(levels[:, None], (S, d)).reshape(1, S, 1, d).copy())
+    v = bf16_bits_from_f32(
+        np.random.default_rng(26).standard_normal((1, S, 1, d)).astype(np.float32))
+    o, lse = oracle.decode(q, k, v, lib=lib)
+    s = 64.0 * levels.astype(np.float64) * d / math.sqrt(d)      # exact: spread > 1000
+    j = int(np.argmax(s))
+    assert np.array_equal(o[0, 0], _f64(v[0, j, 0]))
+    assert abs(lse[0, 0] - s[j]) <= 1e-12 * abs(s[j])
+
+
+def pin_empty_sequence(lib):
+    inp = decode_inputs(2, 4, 2, 16, S_max=6, seed=21)
+    sl = np.array([0, 6], dtype=np.int32)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], sl, lib=lib)
+    assert np.all(o[0] == 0.0) and np.all(lse[0] == -np.inf)
+    assert np.all(np.isfinite(o[1])) and np.all(np.isfinite(lse[1]))
+
+
+def pin_ragged_tail_never_read(lib):
+    inp = decode_inputs(3, 4, 2, 16, ragged=(3, 17), seed=22, nan_fill=True)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], lib=lib)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    # truncating each sequence's cache to its own length gives the same rows
+    for b in range(3):
+        n = int(inp["seqlens"][b])
+        ob, lb = oracle.decode(inp["q"][b:b + 1], inp["k"][b:b + 1, :n].copy(),
+                               inp["v"][b:b + 1, :n].copy(), lib=lib)
+        assert np.array_equal(ob[0], o[b]) and np.array_equal(lb[0], lse[b])
+
+
+def pin_key_permutation_invariance(lib):
+    inp = decode_inputs(1, 4, 2, 32, S_max=40, seed=23)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], lib=lib)
+    perm = np.random.default_rng(3).permutation(40)
+    o_p, lse_p = oracle.decode(inp["q"], inp["k"][:, perm].copy(), inp["v"][:, perm].copy(),
+                               lib=lib)
+    _rel_close(o_p, o, 1e-13, 1e-15)
+    _rel_close(lse_p, lse, 1e-14)
+    # but permuting only V changes the result (K and V must stay paired)
+    o_v, _ = oracle.decode(inp["q"], inp["k"], inp["v"][:, perm].copy(), lib=lib)
+    assert not np.allclose(o_v, o)
+
+
+# ---------------------------------------------------------------------------
+# Causal prefill (V07 section 12): row i sees keys 0..i, the diagonal included.
+
+def pin_causal_row0_and_bounds(lib):
+    B, S, H_q, H_kv, d = 1, 16, 4, 2, 32
+    inp = prefill_inputs(B, S, H_q, H_kv, d, seed=24)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = oracle.prefill_causal(q, k, v, lib=lib)
+    for h in range(H_q):
+        g = h // 2
+        assert np.array_equal(o[0, 0, h], _f64(v[0, 0, g]))          # row 0: O = v_0 exactly
+        s00 = _fsum_dot(_f64(q[0, 0, h]), _f64(k[0, 0, g])) / math.sqrt(d)
+        assert abs(lse[0, h, 0] - s00) <= 1e-14 * max(1.0, abs(s00))
+    # the future never matters: change keys/values after row 7, rows 0..7 unchanged
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 8:] = bf16_bits_from_f32(np.full(k2[:, 8:].shape, 3.0, dtype=np.float32))
+    v2[:, 8:] = bf16_bits_from_f32(np.full(v2[:, 8:].shape, -5.0, dtype=np.float32))
+    o2, lse2 = oracle.prefill_causal(q, k2, v2, lib=lib)
+    assert np.array_equal(o2[:, :8], o[:, :8]) and np.array_equal(lse2[..., :8], lse[..., :8])
+    # ...but the diagonal key does: row 8 changes
+    assert not np.allclose(o2[:, 8], o[:, 8])
+
+
+def pin_prefill_row_equals_decode(lib):
+    B, S, H_q, H_kv, d = 1, 13, 4, 2, 16
+    inp = prefill_inputs(B, S, H_q, H_kv, d, seed=25)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    rows = np.array([[0, h, i] for h in range(H_q) for i in (0, 5, 12)], dtype=np.int32)
+    o, lse = oracle.prefill_causal_rows(q, k, v, rows, lib=lib)
+    for r, (_, h, i) in enumerate(rows):
+        od, ld = oracle.decode(q[:, i].copy(), k, v, np.array([i + 1], dtype=np.int32), lib=lib)
+        assert np.array_equal(o[r], od[0, h]) and lse[r] == ld[0, h]
+
+
+PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
