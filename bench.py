@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA attention hot path on one MI355X.
+
+One step is one pass over both entry points of the library on synthetic bf16
+N(0,1) inputs at Llama3-70B head shapes (H_q=64, H_kv=8, G=8, d=128):
+  1. split-KV decode of one token against a 32768-token cache in 32 chunks
+     (decode_split kernel, then the lse_merge kernel), and
+  2. causal prefill of an 8192-token prompt (prefill_causal kernel).
+Inputs are resident in HBM before the timed region.  The decode reads one of
+``--kv-copies`` distinct copies of the cache per step (4 x 128 MiB by default),
+so its K/V bytes come from HBM and not from the 256 MB last-level cache.
+
+Timing: ``--warmup`` untimed steps, then ``--steps`` steps bracketed by a device
+synchronisation; HIP events on the launch stream bracket each kernel, giving
+the per-kernel durations that the roofline figures use.
+
+Reported (one JSON line):
+  value        decode K/V bytes read per second (GB/s): 128 MiB per decode call
+               divided by the call's GPU time (decode_split + lse_merge, events);
+  ms_per_step  wall time of one whole step (decode + prefill) over the timed loop;
+  roofline     decode_split, HBM-bound: K/V bytes / its mean duration vs 8 TB/s;
+  roofline_prefill  prefill_causal, MFMA-bound: 4*S^2*d*H_q/2 FLOP / its mean
+               duration vs the 2.5 PFLOP/s bf16 dense peak;
+  cpu_baseline the fp64 CPU oracle on the same decode workload (rank 0 only).
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gqa_attention_amd as g  # noqa: E402
+from gqa_workloads import LLAMA_DECODE, LLAMA_PREFILL  # noqa: E402
+from gqa_workloads import accounting as acc  # noqa: E402
+from gqa_workloads.generate import for_config  # noqa: E402
+
+METRIC = "decode KV GB/s (% HBM peak) at Llama3-70B GQA; causal prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def upload(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(seconds):
+    """The fp64 oracle on the decode workload, repeated to fill about ``seconds``."""
+    import oracle
+    inp = for_config(LLAMA_DECODE)
+    threads = oracle.default_threads()
+    kv = acc.decode_kv_bytes([LLAMA_DECODE.S_kv], LLAMA_DECODE.H_kv, LLAMA_DECODE.d)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(inp["q"], inp["k"], inp["v"], nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": kv * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"full decode workload (B=1, H_q=64, H_kv=8, d=128, S_kv=32768) "
+                      f"repeated {reps}x in {el:.1f} s, fp64, {threads} threads",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kv-copies", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+
+    dc, pc = LLAMA_DECODE, LLAMA_PREFILL
+    dinp = for_config(dc)
+    q_d = upload(dinp["q"])
+    k0, v0 = upload(dinp["k"]), upload(dinp["v"])
+    kv_copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.kv_copies - 1)]
+    del dinp
+    ws = g.decode_workspace(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
+    o_d = torch.empty((dc.B, dc.H_q, dc.d), dtype=torch.bfloat16, device="cuda")
+    lse_d = torch.empty((dc.B, dc.H_q), dtype=torch.float32, device="cuda")
+
+    pinp = for_config(pc)
+    q_p, k_p, v_p = upload(pinp["q"]), upload(pinp["k"]), upload(pinp["v"])
+    del pinp
+    o_p = torch.empty_like(q_p)
+    lse_p = torch.empty((pc.B, pc.H_q, pc.S), dtype=torch.float32, device="cuda")
+
+    def step(i, ev=None):
+        k, v = kv_copies[i % len(kv_copies)]
+        if ev:
+            ev[0].record()
+        g.decode_partials(q_d, k, v, None, ws, num_splits=dc.num_splits)
+        if ev:
+            ev[1].record()
+        g.decode_combine(None, ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
+                         num_splits=dc.num_splits)
+        if ev:
+            ev[2].record()
+        g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
+        if ev:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                   for e in events])
+    split_ms, merge_ms, prefill_ms = ms.mean(axis=0)
+    decode_ms = split_ms + merge_ms
+
+    kv_bytes = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
+    flop = acc.prefill_causal_flop(pc.B, pc.S, pc.H_q, pc.d)
+    decode_gbs = kv_bytes / (decode_ms * 1e-3) / 1e9
+    split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+    prefill_tflops = flop / (prefill_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(decode_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama3-70B GQA attention: decode B=1 S_kv=32768 (32 splits) + "
+                        "causal prefill B=1 S=8192",
+            "H_q": 64, "H_kv": 8, "d": 128,
+            "decode": {"B": dc.B, "S_kv": dc.S_kv, "num_splits": dc.num_splits,
+                       "kv_copies": len(kv_copies)},
+            "prefill": {"B": pc.B, "S": pc.S},
+        },
+        "decode": {
+            "kv_bytes": kv_bytes,
+            "gbs": round(decode_gbs, 1),
+            "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(dc.B / (decode_ms * 1e-3), 1),
+            "split_us": round(split_ms * 1e3, 2),
+            "merge_us": round(merge_ms * 1e3, 2),
+        },
+        "prefill": {
+            "flop": flop,
+            "tflops": round(prefill_tflops, 1),
+            "frac_bf16_peak": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
+            "ms": round(prefill_ms, 4),
+        },
+        "roofline": {"kernel": "decode_split", "bound": "hbm", "achieved": round(split_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline_prefill": {"kernel": "prefill_causal", "bound": "mfma",
+                             "achieved": round(prefill_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
+                             "traffic": None},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+"""gqa_attention_amd -- grouped-query fused attention for MI355X (gfx950).
+
+A thin ctypes binding of ``libgqa_attn.so`` (C ABI in ``include/gqa_attn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor dtypes/shapes, allocates outputs and the decode workspace
+with torch, and passes raw device pointers plus torch's current HIP stream.
+There is no fallback: if the library is missing the calls raise.
+
+Entry points (names follow the C ABI):
+  decode(q, k_cache, v_cache, seqlens=None, ...)      -> (o, lse)
+  decode_partials(...) / decode_combine(...)           the two stages of decode
+  lse_merge(part_m2, part_l, part_o, split_counts)     -> (o, lse)
+  prefill_causal(q, k, v, ...)                         -> (o, lse)
+"""
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libgqa_attn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gqa_attn.h")
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status, name, detail):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+def load_library(path=LIBRARY):
+    """Load libgqa_attn.so and declare its C signatures (no GPU call is made)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m gqa_attention_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    ci, cf, cs = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.gqa_status_string.argtypes = [ci]
+    L.gqa_status_string.restype = ctypes.c_char_p
+    L.gqa_last_error.argtypes = []
+    L.gqa_last_error.restype = ctypes.c_char_p
+    L.gqa_version.argtypes = []
+    L.gqa_version.restype = ctypes.c_char_p
+    L.gqa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
+                                  ctypes.POINTER(cs)]
+    L.gqa_decode_plan.restype = ci
+    L.gqa_attn_decode.argtypes = [vp, vp, vp, i32p, vp, f32p, ci, ci, ci, ci, ci, cf, ci, vp, cs, vp]
+    L.gqa_attn_decode.restype = ci
+    L.gqa_decode_partials.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci, ci, cf, ci, vp, cs, vp]
+    L.gqa_decode_partials.restype = ci
+    L.gqa_decode_combine.argtypes = [i32p, vp, f32p, ci, ci, ci, ci, ci, ci, vp, cs, vp]
+    L.gqa_decode_combine.restype = ci
+    L.gqa_lse_merge.argtypes = [f32p, f32p, f32p, i32p, ci, vp, f32p, ci, ci, ci, vp]
+    L.gqa_lse_merge.restype = ci
+    L.gqa_attn_prefill_causal.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, cf, vp]
+    L.gqa_attn_prefill_causal.restype = ci
+    if path == LIBRARY:
+        _lib = L
+    return L
+
+
+def header_functions(header=HEADER):
+    """Names of the functions ``include/gqa_attn.h`` declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def _check(rc):
+    if rc != 0:
+        L = load_library()
+        raise GQAError(rc, L.gqa_status_string(rc).decode(), L.gqa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scale(d, softmax_scale):
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def decode_plan(B, H_q, H_kv, d, S_max, num_splits=0):
+    """(splits, chunk, workspace_bytes) of a decode launch."""
+    L = load_library()
+    P, chunk, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check(L.gqa_decode_plan(B, H_q, H_kv, d, S_max, num_splits, ctypes.byref(P),
+                             ctypes.byref(chunk), ctypes.byref(ws)))
+    return P.value, chunk.value, ws.value
+
+
+def decode_workspace(B, H_q, H_kv, d, S_max, num_splits=0, device="cuda"):
+    """A workspace tensor sized for a decode launch."""
+    _, _, ws = decode_plan(B, H_q, H_kv, d, S_max, num_splits)
+    return torch.empty(ws, dtype=torch.uint8, device=device)
+
+
+def _decode_shapes(q, k_cache, v_cache, seqlens):
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, H_q, d = q.shape
+    Bk, S_max, H_kv, dk = k_cache.shape
+    if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, "
+                         f"v {tuple(v_cache.shape)}")
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, 1)
+        if seqlens.shape[0] != B:
+            raise ValueError("seqlens must have B entries")
+    return B, H_q, H_kv, d, S_max
+
+
+def decode(q, k_cache, v_cache, seqlens=None, softmax_scale=None, num_splits=0, out=None,
+           lse=None, workspace=None):
+    """Split-KV GQA decode: q [B,H_q,d], caches [B,S_max,H_kv,d] bf16 -> (o [B,H_q,d], lse [B,H_q])."""
+    B, H_q, H_kv, d, S_max = _decode_shapes(q, k_cache, v_cache, seqlens)
+    if workspace is None:
+        workspace = decode_workspace(B, H_q, H_kv, d, S_max, num_splits, q.device)
+    o = torch.empty((B, H_q, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, H_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(load_library().gqa_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(l), B, H_q, H_kv, d,
+        S_max, _scale(d, softmax_scale), num_splits, _ptr(workspace), workspace.numel(),
+        _stream(q.device)))
+    return o, l
+
+
+def decode_partials(q, k_cache, v_cache, seqlens, workspace, softmax_scale=None, num_splits=0):
+    """Stage 1 of decode: fill ``workspace`` with the partial (m2, l, O) of every chunk."""
+    B, H_q, H_kv, d, S_max = _decode_shapes(q, k_cache, v_cache, seqlens)
+    _check(load_library().gqa_decode_partials(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), B, H_q, H_kv, d, S_max,
+        _scale(d, softmax_scale), num_splits, _ptr(workspace), workspace.numel(),
+        _stream(q.device)))
+
+
+def decode_combine(seqlens, workspace, out, lse, H_kv, S_max, num_splits=0):
+    """Stage 2 of decode: merge the workspace's partials into ``out`` and ``lse``."""
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    B, H_q, d = out.shape
+    _check(load_library().gqa_decode_combine(
+        _ptr(seqlens), _ptr(out), _ptr(lse), B, H_q, H_kv, d, S_max, num_splits, _ptr(workspace),
+        workspace.numel(), _stream(out.device)))
+
+
+def workspace_views(workspace, B, H_q, H_kv, d, S_max, num_splits=0):
+    """(m2 [B,H_q,P], l [B,H_q,P], o [B,H_q,P,d]) float32 views of a decode workspace."""
+    P, _, _ = decode_plan(B, H_q, H_kv, d, S_max, num_splits)
+    rows = B * H_q * P
+    a256 = lambda n: (n + 255) // 256 * 256
+    off_l = a256(rows * 4)
+    off_o = off_l + a256(rows * 4)
+    f = workspace.view(torch.uint8)
+    m2 = f[:rows * 4].view(torch.float32).view(B, H_q, P)
+    l = f[off_l:off_l + rows * 4].view(torch.float32).view(B, H_q, P)
+    o = f[off_o:off_o + rows * d * 4].view(torch.float32).view(B, H_q, P, d)
+    return m2, l, o
+
+
+def lse_merge(part_m2, part_l, part_o, split_counts=None, out=None, lse=None):
+    """Merge partial states: m2, l [B,H_q,P] fp32 (m2 in log2 units), o [B,H_q,P,d] fp32."""
+    _need(part_m2, "part_m2", torch.float32, 3)
+    _need(part_l, "part_l", torch.float32, 3)
+    _need(part_o, "part_o", torch.float32, 4)
+    B, H_q, P, d = part_o.shape
+    if tuple(part_m2.shape) != (B, H_q, P) or tuple(part_l.shape) != (B, H_q, P):
+        raise ValueError("partial shapes disagree")
+    if split_counts is not None:
+        _need(split_counts, "split_counts", torch.int32, 1)
+    o = torch.empty((B, H_q, d), dtype=torch.bfloat16, device=part_o.device) if out is None else out
+    l = torch.empty((B, H_q), dtype=torch.float32, device=part_o.device) if lse is None else lse
+    _check(load_library().gqa_lse_merge(_ptr(part_m2), _ptr(part_l), _ptr(part_o),
+                                        _ptr(split_counts), P, _ptr(o), _ptr(l), B, H_q, d,
+                                        _stream(part_o.device)))
+    return o, l
+
+
+def prefill_causal(q, k, v, softmax_scale=None, out=None, lse=None):
+    """Causal GQA prefill: q [B,S,H_q,d], k/v [B,S,H_kv,d] bf16 -> (o [B,S,H_q,d], lse [B,H_q,S])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, S, H_q, d = q.shape
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    H_kv = k.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H_q, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(load_library().gqa_attn_prefill_causal(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, S, H_q, H_kv, d,
+        _scale(d, softmax_scale), _stream(q.device)))
+    return o, l

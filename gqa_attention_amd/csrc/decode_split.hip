@@ -1,0 +1,276 @@
+// decode_split.hip -- stage 1 of split-KV decode on gfx950.
+//
+// One workgroup per (chunk p, KV head, sequence b) sweeps the chunk's keys with
+// an online softmax and writes the chunk's partial state (m2, l, O) for every
+// query head of the group ("Attention Kernel lineage" (V07), section 17: split-K
+// partial kernel; section 2: running (m, l, O) update; ADR-0060 "AHBM GQA Fused
+// Attention", section 3: per-tile op sequence of the decode sweep).
+//
+// GQA M-fold (ADR-0060 TL;DR and section 5.2; V07 section 14): the G query heads
+// of a KV head share every K/V tile, so each K/V byte is read from HBM once.
+// On the matrix cores the product is formed transposed, S^T = K . Q^T, so keys
+// are the 16 rows of the MFMA and the (up to 16) query heads its columns: the
+// K fragment of a lane is 4 x 16 contiguous bytes of one key row and goes from
+// HBM straight into the A operand registers, and each lane ends up owning one
+// head's scores, so the softmax row statistics need only two cross-lane steps.
+//
+// The P.V product is formed as O^T = V^T . P^T: P^T is exactly the S^T registers
+// after the softmax (no data movement), and V^T fragments (8 keys of one d
+// column per lane) are gathered from a per-wave LDS copy of the V tile.
+//
+// The 8 waves of a workgroup take interleaved 32-key tiles of the chunk (the
+// K-split of V07 section 7/8) with the next tile's loads in flight while the
+// current one is computed (ADR-0060 TL;DR, software pipelining), then merge
+// their states through LDS (V07 section 8, K-split reduction).
+//
+// Scores are kept in log2 units: s2 = (q.k) * tau * log2(e), folded into one
+// fp32 multiplier applied to the fp32 accumulator (V07 section 2, exp2 trick).
+#include "gqa_device.h"
+#include "gqa_launch.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kTile = 32;  // keys per wave iteration = two 16-key MFMA row tiles
+constexpr int kWaves = 8;
+
+template <int D>
+struct DecodeTraits {
+    static constexpr int KS = D / 32;           // 32-deep k-steps of Q.K^T
+    static constexpr int LPR = D / 8;           // lanes per V row (16 B each)
+    static constexpr int RPI = 64 / LPR;        // V rows per wave load
+    static constexpr int NVI = kTile / RPI;     // V loads per lane per tile
+    static constexpr int NDT = D / 16;          // 16-wide d tiles of O^T
+    static constexpr int VPITCH = D + 4;        // staged V row pitch (bf16): 8-byte pad
+};
+
+template <int D>
+struct TileRegs {
+    u32x4 k[2][DecodeTraits<D>::KS];
+    u32x4 v[DecodeTraits<D>::NVI];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kbase,
+                                          const uint16_t *vbase, size_t kv_row, int key0,
+                                          int last_key, int lane) {
+    using T = DecodeTraits<D>;
+    const int row16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        int key = min(key0 + t * 16 + row16, last_key);
+        const uint16_t *p = kbase + (size_t)key * kv_row + grp * (D / 4);
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) r.k[t][ks] = load16(p + ks * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < T::NVI; ++i) {
+        int key = min(key0 + i * T::RPI + lane / T::LPR, last_key);
+        r.v[i] = load16(vbase + (size_t)key * kv_row + (lane % T::LPR) * 8);
+    }
+}
+
+template <int D>
+struct WaveState {
+    float m;                          // running max, log2 units (this lane's head)
+    float l;                          // running denominator
+    f32x4 o[DecodeTraits<D>::NDT];    // O^T tiles: d = 16*dt + 4*grp + r, head = lane%16
+};
+
+template <int D>
+__device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D> &r,
+                                             const bf16x8 (&qf)[DecodeTraits<D>::KS],
+                                             uint16_t *vs, int key0, int key_end,
+                                             float scale_log2, int lane) {
+    using T = DecodeTraits<D>;
+    const int row16 = lane & 15, grp = lane >> 4;
+
+    // S^T = K . Q^T for keys key0..key0+31 (two 16-row tiles)
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) s[t] = mfma16(as_bf16x8(r.k[t][ks]), qf[ks], s[t]);
+    }
+
+    // stage the V tile (row-major, padded) for the transposed P.V operand
+#pragma unroll
+    for (int i = 0; i < T::NVI; ++i) {
+        uint16_t *dst = vs + (i * T::RPI + lane / T::LPR) * T::VPITCH + (lane % T::LPR) * 8;
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{r.v[i][0], r.v[i][1]};
+        *reinterpret_cast<u32x2 *>(dst + 4) = u32x2{r.v[i][2], r.v[i][3]};
+    }
+
+    // scale to log2 units; keys past the chunk/sequence end are masked
+    float s2[8];
+    float mx = neg_inf();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int key = key0 + t * 16 + grp * 4 + i;
+            float x = key < key_end ? s[t][i] * scale_log2 : neg_inf();
+            s2[t * 4 + i] = x;
+            mx = fmaxf(mx, x);
+        }
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = exp2_fast(st.m - m_new);
+
+    float psum = 0.f;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = exp2_fast(s2[j] - m_new);
+        psum += p[j];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+
+    // P^T as the B operand: slot j of lane group grp is key (j/4)*16 + 4*grp + j%4
+    u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                pack_bf16x2(p[6], p[7])};
+    const bf16x8 pf = as_bf16x8(pw);
+
+    __builtin_amdgcn_wave_barrier();
+    // O^T = alpha * O^T + V^T . P^T; V^T fragment: row d = 16*dt + row16, the same 8 keys
+#pragma unroll
+    for (int dt = 0; dt < T::NDT; ++dt) {
+        const uint16_t *col = vs + dt * 16 + row16;
+        uint32_t w[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint16_t *c0 = col + (h * 16 + grp * 4) * T::VPITCH;
+            w[2 * h] = (uint32_t)c0[0] | ((uint32_t)c0[T::VPITCH] << 16);
+            w[2 * h + 1] = (uint32_t)c0[2 * T::VPITCH] | ((uint32_t)c0[3 * T::VPITCH] << 16);
+        }
+        const bf16x8 vf = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        st.o[dt] *= alpha;
+        st.o[dt] = mfma16(vf, pf, st.o[dt]);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitArgs a, int n_hg) {
+    using T = DecodeTraits<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * kTile * T::VPITCH];
+
+    const int p = blockIdx.x;
+    const int hk = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
+    const int b = blockIdx.z;
+    const int G = a.H_q / a.H_kv;
+    const int Sb = a.seqlens ? min(max(a.seqlens[b], 0), a.S_max) : a.S_max;
+    const int s0 = p * a.chunk;
+    if (s0 >= Sb) return;  // the whole workgroup leaves: this chunk is past the sequence end
+    const int s1 = min(s0 + a.chunk, Sb);
+    const int h0 = hk * G + hg * 16;
+    const int nh = min(16, G - hg * 16);
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row16 = lane & 15, grp = lane >> 4;
+
+    // Q^T fragments (B operand): column = query head h0 + row16, k-slots = d
+    bf16x8 qf[T::KS];
+    {
+        const uint16_t *qrow =
+            a.q + ((size_t)b * a.H_q + h0 + min(row16, nh - 1)) * D + grp * (D / 4);
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) {
+            u32x4 x = load16(qrow + ks * 8);
+            if (row16 >= nh) x = u32x4{0u, 0u, 0u, 0u};
+            qf[ks] = as_bf16x8(x);
+        }
+    }
+
+    const size_t kv_row = (size_t)a.H_kv * D;
+    const size_t head_off = ((size_t)b * a.S_max * a.H_kv + hk) * D;
+    const uint16_t *kbase = a.k + head_off;
+    const uint16_t *vbase = a.v + head_off;
+    uint16_t *vs = smem + w * kTile * T::VPITCH;
+
+    WaveState<D> st;
+    st.m = neg_inf();
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (s1 - s0 + kTile - 1) / kTile;
+    const int last_key = s1 - 1;
+    TileRegs<D> ra, rb;
+    int t = w;
+    if (t < ntiles) load_tile<D>(ra, kbase, vbase, kv_row, s0 + t * kTile, last_key, lane);
+    while (t < ntiles) {
+        const int t1 = t + kWaves;
+        if (t1 < ntiles) load_tile<D>(rb, kbase, vbase, kv_row, s0 + t1 * kTile, last_key, lane);
+        compute_tile<D>(st, ra, qf, vs, s0 + t * kTile, s1, a.scale_log2, lane);
+        if (t1 >= ntiles) break;
+        const int t2 = t1 + kWaves;
+        if (t2 < ntiles) load_tile<D>(ra, kbase, vbase, kv_row, s0 + t2 * kTile, last_key, lane);
+        compute_tile<D>(st, rb, qf, vs, s0 + t1 * kTile, s1, a.scale_log2, lane);
+        t = t2;
+    }
+
+    // merge the waves' states through LDS (reusing the V staging area):
+    // red[w][head][0..D) = O^T column, [D] = m, [D+1] = l
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);
+    constexpr int RS = D + 2;
+    float *mine = red + (w * 16 + row16) * RS;
+#pragma unroll
+    for (int dt = 0; dt < T::NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[dt * 16 + grp * 4 + i] = st.o[dt][i];
+    if (grp == 0) {
+        mine[D] = st.m;
+        mine[D + 1] = st.l;
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * 64) {
+        const int h = idx / D, d = idx % D;
+        float M = neg_inf();
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * 16 + h) * RS + D]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float *rw = red + (ww * 16 + h) * RS;
+            const float al = exp2_fast(rw[D] - M);  // empty wave: 2^-inf = 0
+            L += al * rw[D + 1];
+            O += al * rw[d];
+        }
+        const size_t row = ((size_t)b * a.H_q + h0 + h) * a.P + p;
+        a.part_o[row * D + d] = O;
+        if (d == 0) {
+            a.part_m2[row] = M;
+            a.part_l[row] = L;
+        }
+    }
+}
+
+template <int D>
+hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
+    const int G = a.H_q / a.H_kv;
+    const int n_hg = (G + 15) / 16;
+    dim3 grid(a.P, a.H_kv * n_hg, a.B);
+    hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, n_hg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_split(const DecodeSplitArgs &a, hipStream_t stream) {
+    switch (a.d) {
+    case 32: return launch<32>(a, stream);
+    case 64: return launch<64>(a, stream);
+    case 128: return launch<128>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gqa

@@ -1,0 +1,330 @@
+// gqa_attn_api.cpp -- the C ABI of libgqa_attn.so: argument checks, split-KV
+// planning, workspace layout and kernel launches.  Every check runs on the
+// host before the first launch, so a call with bad arguments returns an error
+// code without touching the GPU.  Nothing here allocates or synchronises.
+#include "../../include/gqa_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "gqa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return GQA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+constexpr int kMaxSplits = 65535;
+constexpr int kGridYZ = 65535;
+constexpr int kSplitAlign = 32;       // chunk lengths are multiples of the kernel's key tile
+constexpr int kAutoMinChunk = 256;
+constexpr int kAutoTargetGroups = 512; // two workgroups per compute unit on a 256-CU part
+constexpr float kLog2e = 1.44269504088896340736f;
+
+bool decode_head_size_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+struct Plan {
+    int P, chunk;
+    size_t off_l, off_o, bytes;
+};
+
+int check_heads(int B, int H_q, int H_kv) {
+    if (B <= 0 || H_q <= 0 || H_kv <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "B=%d, H_q=%d, H_kv=%d must all be positive", B, H_q, H_kv);
+    if (H_q % H_kv != 0)
+        return fail(GQA_ERR_BAD_SHAPE, "H_kv=%d does not divide H_q=%d", H_kv, H_q);
+    return GQA_OK;
+}
+
+int make_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *pl) {
+    int rc = check_heads(B, H_q, H_kv);
+    if (rc) return rc;
+    if (!decode_head_size_ok(d))
+        return fail(GQA_ERR_UNSUPPORTED, "decode head size d=%d (supported: 32, 64, 128)", d);
+    if (S_max <= 0) return fail(GQA_ERR_BAD_SHAPE, "S_max=%d must be positive", S_max);
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return fail(GQA_ERR_SPLITS, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
+    const int G = H_q / H_kv;
+    const long n_hg = (G + 15) / 16;
+    if ((long)H_kv * n_hg > kGridYZ || B > kGridYZ)
+        return fail(GQA_ERR_BAD_SHAPE, "B=%d or H_kv*ceil(G/16)=%ld exceeds %d", B,
+                    (long)H_kv * n_hg, kGridYZ);
+    long chunk;
+    if (num_splits > 0) {
+        chunk = ((long)S_max + num_splits - 1) / num_splits;
+    } else {
+        long groups = (long)B * H_kv * n_hg;
+        long want = (kAutoTargetGroups + groups - 1) / groups;
+        chunk = ((long)S_max + want - 1) / want;
+        long floor_chunk = S_max < kAutoMinChunk ? S_max : kAutoMinChunk;
+        if (chunk < floor_chunk) chunk = floor_chunk;
+    }
+    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    long P = ((long)S_max + chunk - 1) / chunk;
+    pl->P = (int)P;
+    pl->chunk = (int)chunk;
+    const size_t rows = (size_t)B * H_q * (size_t)P;
+    pl->off_l = align256(rows * sizeof(float));
+    pl->off_o = pl->off_l + align256(rows * sizeof(float));
+    pl->bytes = pl->off_o + align256(rows * (size_t)d * sizeof(float));
+    return GQA_OK;
+}
+
+int check_scale(float scale) {
+    if (!std::isfinite(scale) || scale < 0.f)
+        return fail(GQA_ERR_SCALE, "softmax_scale=%g must be finite and >= 0", (double)scale);
+    return GQA_OK;
+}
+
+int check_workspace(const void *ws, size_t bytes, const Plan &pl) {
+    if (!ws) return fail(GQA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.bytes);
+    if (!aligned(ws, 256)) return fail(GQA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (bytes < pl.bytes)
+        return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, pl.bytes);
+    return GQA_OK;
+}
+
+int check_bf16(const void *p, const char *name) {
+    if (!p) return fail(GQA_ERR_NULL_POINTER, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(GQA_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+    return GQA_OK;
+}
+
+int check_f32(const void *p, const char *name) {
+    if (!p) return fail(GQA_ERR_NULL_POINTER, "%s is NULL", name);
+    if (!aligned(p, 4)) return fail(GQA_ERR_ALIGNMENT, "%s is not 4-byte aligned", name);
+    return GQA_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(GQA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return GQA_OK;
+}
+
+int decode_common_checks(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                         float scale) {
+    int rc;
+    if ((rc = check_bf16(q, "q")) || (rc = check_bf16(k, "k_cache")) ||
+        (rc = check_bf16(v, "v_cache")))
+        return rc;
+    if (seqlens && !aligned(seqlens, 4)) return fail(GQA_ERR_ALIGNMENT, "seqlens misaligned");
+    return check_scale(scale);
+}
+
+gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
+                                const int32_t *seqlens, int B, int H_q, int H_kv, int d, int S_max,
+                                float scale, const Plan &pl, void *ws) {
+    char *base = static_cast<char *>(ws);
+    gqa::DecodeSplitArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.seqlens = seqlens;
+    a.part_m2 = reinterpret_cast<float *>(base);
+    a.part_l = reinterpret_cast<float *>(base + pl.off_l);
+    a.part_o = reinterpret_cast<float *>(base + pl.off_o);
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.d = d;
+    a.S_max = S_max;
+    a.chunk = pl.chunk;
+    a.P = pl.P;
+    a.scale_log2 = scale * kLog2e;
+    return a;
+}
+
+gqa::MergeArgs combine_args(const int32_t *seqlens, void *o, float *lse, int B, int H_q, int d,
+                            int S_max, const Plan &pl, const void *ws) {
+    const char *base = static_cast<const char *>(ws);
+    gqa::MergeArgs m;
+    m.part_m2 = reinterpret_cast<const float *>(base);
+    m.part_l = reinterpret_cast<const float *>(base + pl.off_l);
+    m.part_o = reinterpret_cast<const float *>(base + pl.off_o);
+    m.counts = seqlens;
+    m.counts_are_lengths = 1;
+    m.chunk = pl.chunk;
+    m.S_max = S_max;
+    m.P = pl.P;
+    m.o = static_cast<uint16_t *>(o);
+    m.lse = lse;
+    m.B = B;
+    m.H_q = H_q;
+    m.d = d;
+    return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gqa_status_string(int status) {
+    switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_NULL_POINTER: return "GQA_ERR_NULL_POINTER";
+    case GQA_ERR_BAD_SHAPE: return "GQA_ERR_BAD_SHAPE";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_SPLITS: return "GQA_ERR_SPLITS";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+    case GQA_ERR_ALIGNMENT: return "GQA_ERR_ALIGNMENT";
+    case GQA_ERR_SCALE: return "GQA_ERR_SCALE";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP";
+    default: return "GQA_ERR_UNKNOWN";
+    }
+}
+
+const char *gqa_last_error(void) { return g_err; }
+
+const char *gqa_version(void) { return "gqa_attn 0.1.0 (gfx950)"; }
+
+int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, int *splits_out,
+                    int *chunk_out, size_t *workspace_bytes_out) {
+    Plan pl;
+    int rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl);
+    if (rc) return rc;
+    if (splits_out) *splits_out = pl.P;
+    if (chunk_out) *chunk_out = pl.chunk;
+    if (workspace_bytes_out) *workspace_bytes_out = pl.bytes;
+    return ok();
+}
+
+int gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seqlens, int B, int H_q, int H_kv, int d, int S_max,
+                        float softmax_scale, int num_splits, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = decode_common_checks(q, k_cache, v_cache, seqlens, softmax_scale))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
+    auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
+                        workspace);
+    if ((rc = hip_status(gqa::launch_decode_split(a, static_cast<hipStream_t>(stream)),
+                         "decode_split")))
+        return rc;
+    return ok();
+}
+
+int gqa_decode_combine(const int32_t *seqlens, void *o, float *lse, int B, int H_q, int H_kv,
+                       int d, int S_max, int num_splits, const void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
+    if (seqlens && !aligned(seqlens, 4)) return fail(GQA_ERR_ALIGNMENT, "seqlens misaligned");
+    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
+    auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
+    if ((rc = hip_status(gqa::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "lse_merge")))
+        return rc;
+    return ok();
+}
+
+int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *seqlens, void *o, float *lse, int B, int H_q, int H_kv, int d,
+                    int S_max, float softmax_scale, int num_splits, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = decode_common_checks(q, k_cache, v_cache, seqlens, softmax_scale))) return rc;
+    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
+                        workspace);
+    if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split"))) return rc;
+    auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
+    if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
+    return ok();
+}
+
+int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o,
+                  const int32_t *split_counts, int max_splits, void *o, float *lse, int B, int H_q,
+                  int d, void *stream) {
+    int rc;
+    if (B <= 0 || H_q <= 0) return fail(GQA_ERR_BAD_SHAPE, "B=%d, H_q=%d must be positive", B, H_q);
+    if (B > kGridYZ) return fail(GQA_ERR_BAD_SHAPE, "B=%d exceeds %d", B, kGridYZ);
+    if (!decode_head_size_ok(d))
+        return fail(GQA_ERR_UNSUPPORTED, "merge head size d=%d (supported: 32, 64, 128)", d);
+    if (max_splits <= 0 || max_splits > kMaxSplits)
+        return fail(GQA_ERR_SPLITS, "max_splits=%d outside [1, %d]", max_splits, kMaxSplits);
+    if ((rc = check_f32(part_m2, "part_m2")) || (rc = check_f32(part_l, "part_l")) ||
+        (rc = check_f32(part_o, "part_o")) || (rc = check_bf16(o, "o")) ||
+        (rc = check_f32(lse, "lse")))
+        return rc;
+    if (split_counts && !aligned(split_counts, 4))
+        return fail(GQA_ERR_ALIGNMENT, "split_counts misaligned");
+    gqa::MergeArgs m;
+    m.part_m2 = part_m2;
+    m.part_l = part_l;
+    m.part_o = part_o;
+    m.counts = split_counts;
+    m.counts_are_lengths = 0;
+    m.chunk = 1;
+    m.S_max = 0;
+    m.P = max_splits;
+    m.o = static_cast<uint16_t *>(o);
+    m.lse = lse;
+    m.B = B;
+    m.H_q = H_q;
+    m.d = d;
+    if ((rc = hip_status(gqa::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "lse_merge")))
+        return rc;
+    return ok();
+}
+
+int gqa_attn_prefill_causal(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int S, int H_q, int H_kv, int d, float softmax_scale,
+                            void *stream) {
+    int rc;
+    if ((rc = check_heads(B, H_q, H_kv))) return rc;
+    if (S <= 0) return fail(GQA_ERR_BAD_SHAPE, "S=%d must be positive", S);
+    if (d != 128) return fail(GQA_ERR_UNSUPPORTED, "prefill head size d=%d (supported: 128)", d);
+    const long n_qb = (S + 127) / 128;
+    if (n_qb * (long)B * H_q > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*H_q*ceil(S/128) exceeds the grid limit");
+    if ((rc = check_bf16(q, "q")) || (rc = check_bf16(k, "k")) || (rc = check_bf16(v, "v")) ||
+        (rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse")))
+        return rc;
+    if ((rc = check_scale(softmax_scale))) return rc;
+    gqa::PrefillArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = B;
+    a.S = S;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.d = d;
+    a.scale_log2 = softmax_scale * kLog2e;
+    if ((rc = hip_status(gqa::launch_prefill_causal(a, static_cast<hipStream_t>(stream)),
+                         "prefill_causal")))
+        return rc;
+    return ok();
+}
+
+}  // extern "C"

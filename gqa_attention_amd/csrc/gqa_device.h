@@ -1,0 +1,65 @@
+// gqa_device.h -- device-side types and helpers shared by the gfx950 kernels.
+//
+// Vector types follow the operand shapes of the CDNA4 bf16 matrix-core
+// instructions used here:
+//   v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C/D 16x16 fp32.  Each lane holds
+//     8 bf16 of A (row lane%16, k-slots 8*(lane/16)..+7), 8 bf16 of B (column
+//     lane%16, the same k-slots) and 4 fp32 of D (rows 4*(lane/16)..+3, column
+//     lane%16).
+//   v_mfma_f32_32x32x16_bf16: A 32x16, B 16x32, C/D 32x32 fp32.  Each lane holds
+//     8 bf16 of A (row lane%32, k-slots 8*(lane/32)..+7), 8 of B (column
+//     lane%32, same k-slots) and 16 fp32 of D (rows 8*(r/4) + 4*(lane/32) + r%4
+//     for r = 0..15, column lane%32).
+// Since A and B use the same lane/slot -> k assignment, any permutation of the
+// reduction index that is applied to both operands leaves the product
+// unchanged; the kernels use that freedom to make every lane's slots
+// contiguous in memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit; 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 -> two bf16 (round to nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask));
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+}  // namespace gqa

@@ -1,0 +1,46 @@
+// gqa_launch.h -- host-side launchers of the gfx950 kernels (internal to the library).
+//
+// Every launcher trusts its arguments: the C ABI layer validates shapes,
+// pointers and sizes before calling any of these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct DecodeSplitArgs {
+    const uint16_t *q, *k, *v;  // bf16 bit patterns
+    const int32_t *seqlens;     // [B] or nullptr
+    float *part_m2, *part_l, *part_o;
+    int B, H_q, H_kv, d, S_max;
+    int chunk;                  // keys per split
+    int P;                      // splits of the longest sequence (workspace split dim)
+    float scale_log2;           // softmax_scale * log2(e)
+};
+
+struct MergeArgs {
+    const float *part_m2, *part_l, *part_o;
+    const int32_t *counts;      // [B] or nullptr
+    int counts_are_lengths;     // 1: counts are sequence lengths, split count = ceil(len/chunk)
+    int chunk, S_max;           // used when counts_are_lengths
+    int P;                      // split dim of the partial arrays
+    uint16_t *o;                // bf16 out [B, H_q, d]
+    float *lse;                 // [B, H_q]
+    int B, H_q, d;
+};
+
+struct PrefillArgs {
+    const uint16_t *q, *k, *v;
+    uint16_t *o;
+    float *lse;
+    int B, S, H_q, H_kv, d;
+    float scale_log2;
+};
+
+hipError_t launch_decode_split(const DecodeSplitArgs &a, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream);
+hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace gqa

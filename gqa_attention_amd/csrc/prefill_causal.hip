@@ -1,0 +1,253 @@
+// prefill_causal.hip -- causal GQA prefill (T_q = S_kv = S) on gfx950.
+//
+// FlashAttention-2 forward ("Attention Kernel lineage" (V07), sections 7-8):
+// each workgroup owns one block of 128 query rows of one query head for its
+// whole life, keeps the rows' (m, l, O) state in registers, and streams 64-key
+// K/V tiles through LDS; the division by l is deferred to the end, and the
+// score matrix is never written (section 4).  Causal block classification
+// (section 12): a tile wholly above the diagonal is never loaded, a tile wholly
+// below needs no mask, and only tiles crossing the diagonal are masked
+// element-wise with a select.  The classification is also applied per wave
+// (32 rows), so a wave skips tiles that are in its own future.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16): scores are formed
+// transposed, S^T = K . Q^T, so each lane owns one query row (lane % 32) and
+// holds 32 of that row's 64 scores; the row max and sum need one cross-lane
+// step.  P.V is formed as O^T = V^T . P^T, whose B operand is exactly the
+// softmax output registers, and whose accumulator keeps one query row per lane,
+// so the rescale by alpha is a per-lane scalar.  Q (B operand) stays in
+// registers; the K fragments are 16-byte LDS reads; V^T fragments (8 keys of
+// one d column) are gathered from the row-major V tile.
+//
+// Scores are kept in log2 units (s2 = acc * tau * log2(e), one fp32 multiply
+// folded into the exponent's FMA; V07 section 2, exp2 trick).
+//
+// Grid: one workgroup per (q-block, sequence, query head), heaviest q-blocks
+// first (V07 section 12, causal-aware scheduling).  Consecutive workgroups are
+// dispatched round-robin over the 8 XCDs; the index is remapped so that the G
+// query heads sharing one KV head and q-block run back to back on one XCD and
+// hit its L2 for the shared K/V tiles (V07 section 14: K/V loaded once, reused
+// by the group).
+#include "gqa_device.h"
+#include "gqa_launch.h"
+
+namespace gqa {
+namespace {
+
+constexpr int D = 128;
+constexpr int kBr = 128;          // query rows per workgroup
+constexpr int kBc = 64;           // keys per tile
+constexpr int kWaves = 4;         // 32 query rows per wave
+constexpr int kThreads = kWaves * 64;
+constexpr int kPitch = D + 8;     // LDS row pitch in bf16 (272 B: 16-byte aligned rows)
+constexpr int kLoads = kBc * D * 2 / 16 / kThreads;   // 16-byte loads per thread per tensor
+constexpr int kXcds = 8;
+
+static_assert(kLoads == 4, "tile staging assumes 4 loads per thread");
+
+struct Stage {
+    u32x4 k[kLoads];
+    u32x4 v[kLoads];
+};
+
+__device__ __forceinline__ void load_stage(Stage &st, const uint16_t *kbase, const uint16_t *vbase,
+                                           size_t kv_row, int k0, int S) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int key = min(k0 + i * 16 + t / 16, S - 1);
+        const size_t off = (size_t)key * kv_row + (t % 16) * 8;
+        st.k[i] = load16(kbase + off);
+        st.v[i] = load16(vbase + off);
+    }
+}
+
+__device__ __forceinline__ void store_stage(const Stage &st, uint16_t *ks, uint16_t *vs) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int off = (i * 16 + t / 16) * kPitch + (t % 16) * 8;
+        *reinterpret_cast<u32x4 *>(ks + off) = st.k[i];
+        *reinterpret_cast<u32x4 *>(vs + off) = st.v[i];
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs a, int n_qb,
+                                                                     int remap) {
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kBc * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kBc * kPitch];
+
+    const int G = a.H_q / a.H_kv;
+    // ---- workgroup -> (q-block, b, h) ----
+    int wid = blockIdx.x;
+    if (remap) {
+        const int x = wid % kXcds, t = wid / kXcds;
+        const int j = t % G, u = (t / G) * kXcds + x;
+        wid = u * G + j;
+    }
+    const int j = wid % G;
+    int u = wid / G;
+    const int hk = u % a.H_kv;
+    u /= a.H_kv;
+    const int b = u % a.B;
+    const int qb = n_qb - 1 - u / a.B;  // heavy (long-prefix) blocks first
+    const int h = hk * G + j;
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r32 = lane & 31, hf = lane >> 5;
+    const int i0 = qb * kBr;
+    const int r0 = i0 + w * 32;            // this wave's first query row
+    const int row = r0 + r32;              // this lane's query row
+    const int last_row = min(i0 + kBr, a.S) - 1;
+    const int n_kb = last_row / kBc + 1;
+    const bool wave_rows = r0 < a.S;
+
+    const size_t kv_row = (size_t)a.H_kv * D;
+    const uint16_t *kbase = a.k + ((size_t)b * a.S * a.H_kv + hk) * D;
+    const uint16_t *vbase = a.v + ((size_t)b * a.S * a.H_kv + hk) * D;
+
+    // Q^T fragments: column = query row, k-slots (hf, j) <-> d = 64*hf + 8*ks + j
+    bf16x8 qf[8];
+    {
+        const uint16_t *qrow =
+            a.q + (((size_t)b * a.S + min(row, a.S - 1)) * a.H_q + h) * D + hf * 64;
+#pragma unroll
+        for (int k8 = 0; k8 < 8; ++k8) qf[k8] = as_bf16x8(load16(qrow + k8 * 8));
+    }
+
+    f32x16 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m = neg_inf(), l = 0.f;
+    const float c = a.scale_log2;
+
+    Stage stage;
+    load_stage(stage, kbase, vbase, kv_row, 0, a.S);
+
+    for (int kb = 0; kb < n_kb; ++kb) {
+        const int k0 = kb * kBc;
+        __syncthreads();
+        store_stage(stage, ks, vs);
+        __syncthreads();
+        if (kb + 1 < n_kb) load_stage(stage, kbase, vbase, kv_row, k0 + kBc, a.S);
+
+        if (!wave_rows || k0 > r0 + 31) continue;   // tile wholly in this wave's future
+        const bool diag = k0 + kBc - 1 > r0;         // some key may pass some row
+
+        // ---- S^T = K . Q^T : two 32-key sub-tiles ----
+        f32x16 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+            const uint16_t *krow = ks + (kt * 32 + r32) * kPitch + hf * 64;
+#pragma unroll
+            for (int k8 = 0; k8 < 8; ++k8) {
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(krow + k8 * 8));
+                s[kt] = mfma32(kf, qf[k8], s[kt]);
+            }
+        }
+
+        // ---- online softmax on this lane's row (32 of its 64 scores) ----
+        // element (kt, r) is key k0 + 32*kt + 8*(r/4) + 4*hf + r%4
+        float mx = neg_inf();
+        if (diag) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                    mx = fmaxf(mx, key <= row ? s[kt][r] : neg_inf());
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+        }
+        mx = wave_max_xor(mx, 32);
+        const float m_new = fmaxf(m, mx * c);
+        const float alpha = exp2_fast(m - m_new);
+        const float neg_m = -m_new;
+
+        float rs = 0.f;
+        float p[2][16];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float e = exp2_fast(fmaf(s[kt][r], c, neg_m));
+                if (diag) {
+                    const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                    e = key <= row ? e : 0.f;
+                }
+                p[kt][r] = e;
+                rs += e;
+            }
+        rs += __shfl_xor(rs, 32);
+        l = l * alpha + rs;
+        m = m_new;
+
+        // P^T as B operand, k-step kk (16 keys): slot j <-> S^T element r = 8*(kk%2) + j of
+        // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float *pp = &p[kk >> 1][(kk & 1) * 8];
+            pf[kk] = as_bf16x8(u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
+                                     pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])});
+        }
+
+        // ---- O^T = alpha * O^T + V^T . P^T ----
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint16_t *col = vs + (16 * kk + 4 * hf) * kPitch + dt * 32 + r32;
+                uint32_t wv[4];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint16_t *c0 = col + hh * 8 * kPitch;
+                    wv[2 * hh] = (uint32_t)c0[0] | ((uint32_t)c0[kPitch] << 16);
+                    wv[2 * hh + 1] = (uint32_t)c0[2 * kPitch] | ((uint32_t)c0[3 * kPitch] << 16);
+                }
+                o[dt] = mfma32(as_bf16x8(u32x4{wv[0], wv[1], wv[2], wv[3]}), pf[kk], o[dt]);
+            }
+        }
+    }
+
+    // ---- epilogue: O = O^T / l -> bf16, LSE = ln2 * (m + log2 l) ----
+    if (!wave_rows || row >= a.S) return;
+    const float inv = 1.f / l;
+    uint16_t *orow = a.o + (((size_t)b * a.S + row) * a.H_q + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int d = dt * 32 + rq * 8 + hf * 4;
+            const int r = rq * 4;
+            *reinterpret_cast<u32x2 *>(orow + d) =
+                u32x2{pack_bf16x2(o[dt][r] * inv, o[dt][r + 1] * inv),
+                      pack_bf16x2(o[dt][r + 2] * inv, o[dt][r + 3] * inv)};
+        }
+    if (hf == 0) a.lse[((size_t)b * a.H_q + h) * a.S + row] = kLn2 * (m + __builtin_log2f(l));
+}
+
+}  // namespace
+
+hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream) {
+    if (a.d != D) return hipErrorInvalidValue;
+    const int n_qb = (a.S + kBr - 1) / kBr;
+    const long units = (long)n_qb * a.B * a.H_kv;
+    const int remap = (units % kXcds) == 0;
+    const long blocks = units * (a.H_q / a.H_kv);
+    hipLaunchKernelGGL(prefill_causal_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
+                       n_qb, remap);
+    return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,193 @@
+/*
+ * gqa_attn.h -- C ABI of libgqa_attn.so: grouped-query fused attention on
+ * AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The library computes attention of post-RoPE queries against a read-only
+ * K/V cache, in the form the pages state it: the attention call sits between
+ * the QKV/RoPE/cache-append kernel upstream and the output projection
+ * downstream, reads Q, the K cache and the V cache, and writes O; it neither
+ * rotates nor writes the cache, and the score matrix S and probabilities P are
+ * never produced (ADR-0060 "AHBM GQA Fused Attention", section 0.5: position
+ * in the decoder layer, preconditions, launch inputs and outputs).  Query head
+ * h reads KV head floor(h / G), G = H_q / H_kv, and H_kv must divide H_q
+ * ("Attention Kernel lineage" (V07), section 14).
+ *
+ * Every call also returns the log-sum-exp of each query row's scores,
+ * LSE = m + ln(l) in natural-log units of the scaled logits (V07, section 2:
+ * LSE is kept per row instead of S).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major (last index fastest), no padding.
+ * - bf16 tensors are passed as `const void*` / `void*` device pointers to
+ *   IEEE bfloat16 values; they must be 16-byte aligned.  fp32 and int32
+ *   arrays must be 4-byte aligned; the decode workspace 256-byte aligned.
+ * - All device pointers are allocated and owned by the caller.  The library
+ *   never allocates, frees or synchronises; inputs are read-only; outputs are
+ *   fully overwritten.
+ * - `stream` is a hipStream_t (NULL = the default stream).  A call returns
+ *   after enqueueing its kernels; GQA_OK means the launches were accepted.
+ * - Errors are status codes; nothing aborts and no exception crosses the ABI.
+ *   All argument checks run on the host before any launch, so a bad shape
+ *   fails at the call.  gqa_last_error() gives a one-line explanation of the
+ *   most recent failure on the calling thread.
+ * - softmax_scale is tau in s = tau * q.k (normally 1/sqrt(d)); any finite
+ *   value >= 0 is accepted.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+    GQA_OK = 0,
+    GQA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+    GQA_ERR_BAD_SHAPE = 2,    /* a size is <= 0, H_kv does not divide H_q, or an index overflows */
+    GQA_ERR_UNSUPPORTED = 3,  /* head size (or group size) this build has no kernel for */
+    GQA_ERR_SPLITS = 4,       /* num_splits / max_splits out of range */
+    GQA_ERR_WORKSPACE = 5,    /* workspace missing, too small or misaligned */
+    GQA_ERR_ALIGNMENT = 6,    /* a tensor pointer is not aligned as stated above */
+    GQA_ERR_SCALE = 7,        /* softmax_scale is negative, NaN or infinite */
+    GQA_ERR_HIP = 8           /* the HIP runtime rejected a launch */
+} gqa_status_t;
+
+/* Name of a status code ("GQA_OK", ...); never NULL. */
+const char *gqa_status_string(int status);
+
+/* Explanation of the most recent failing call on this thread ("" if none). */
+const char *gqa_last_error(void);
+
+/* Library version string. */
+const char *gqa_version(void);
+
+/*
+ * Split-KV plan of a decode launch (V07, section 17, split-K decode: the key
+ * axis of every sequence is cut into partitions whose partial states a second
+ * stage merges).
+ *
+ * The keys of each sequence are cut into contiguous chunks of `chunk` keys
+ * (the last one ragged).  `chunk` is ceil(S_max / num_splits) rounded up to a
+ * multiple of 32, so a sequence of the longest length S_max gets
+ * ceil(S_max / chunk) <= num_splits chunks and a sequence of length S_b gets
+ * ceil(S_b / chunk).  num_splits = 0 lets the library choose (enough chunks to
+ * give the GPU at least two workgroups per compute unit, chunks of >= 256
+ * keys).
+ *
+ * Outputs (any may be NULL): *splits_out = chunks of the longest sequence
+ * (the workspace's split dimension P), *chunk_out = chunk, *workspace_bytes_out
+ * = bytes of decode workspace the launch needs.
+ *
+ * Supported: d in {32, 64, 128}; any G = H_q / H_kv (groups above 16 query
+ * heads run as several workgroups per KV head); 1 <= num_splits <= 65535.
+ */
+int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
+                    int *splits_out, int *chunk_out, size_t *workspace_bytes_out);
+
+/*
+ * gqa_attn_decode -- one query token per sequence against its KV cache.
+ *
+ * The G query heads of a KV head are folded into the rows of one matrix
+ * product so each K/V tile is read from HBM once for all of them (ADR-0060,
+ * TL;DR and section 5.2: M-fold; V07, section 14, GQA kernel layout).  Each
+ * (sequence, KV head, chunk) runs an online-softmax sweep over its chunk
+ * (V07, section 2: running (m, l, O) update; section 7: deferred division),
+ * then a separate merge kernel combines the partial states of the chunks
+ * (V07, section 3 merge formula; section 17, second stage of split-K decode).
+ * There is no causal mask: the query sees every cached key [0, seqlen)
+ * (ADR-0060, section 5.2).
+ *
+ *   q        [B, H_q, d]        bf16, device, read-only
+ *   k_cache  [B, S_max, H_kv, d] bf16, device, read-only (batch stride S_max*H_kv*d)
+ *   v_cache  [B, S_max, H_kv, d] bf16, device, read-only
+ *   seqlens  [B] int32, device, or NULL (= every sequence has S_max keys).
+ *            Rows at or past seqlens[b] are never read.  Values outside
+ *            [0, S_max] are clamped into it on the device; seqlens[b] = 0
+ *            gives O = 0 and LSE = -inf for that sequence.
+ *   o        [B, H_q, d]        bf16, device, written (RNE from fp32)
+ *   lse      [B, H_q]           fp32, device, written (natural log)
+ *   workspace / workspace_bytes: device scratch of at least the size
+ *            gqa_decode_plan reports for the same arguments (256-byte aligned).
+ *            Layout, P = splits: m2 [B][H_q][P] fp32 (running max, log2 units),
+ *            then l [B][H_q][P] fp32, then O [B][H_q][P][d] fp32 (unnormalised),
+ *            each region starting at a 256-byte boundary.
+ *
+ * Calls that share a workspace on overlapping streams race.
+ */
+int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *seqlens, void *o, float *lse,
+                    int B, int H_q, int H_kv, int d, int S_max,
+                    float softmax_scale, int num_splits,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two stages of gqa_attn_decode as separate calls, with the same
+ * arguments and workspace layout (V07, section 17: stage 1 writes the partial
+ * (m, l, O) of every partition, stage 2 merges them).  gqa_decode_partials
+ * runs the split-KV sweep and fills the workspace; gqa_decode_combine runs the
+ * merge kernel on it.  Calling them in this order on one stream is exactly
+ * gqa_attn_decode.
+ */
+int gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seqlens,
+                        int B, int H_q, int H_kv, int d, int S_max,
+                        float softmax_scale, int num_splits,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+int gqa_decode_combine(const int32_t *seqlens, void *o, float *lse,
+                       int B, int H_q, int H_kv, int d, int S_max, int num_splits,
+                       const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gqa_lse_merge -- merge caller-provided partial states (V07, section 3:
+ * M = max m_p, a_p = 2^(m_p - M), L = sum a_p l_p, O = sum a_p O_p / L;
+ * section 17, second stage).  Partial maxima are in log2 units of the scaled
+ * logits (m2 = m * log2(e)), so LSE = ln(2) * (M + log2(L)).  A partial with
+ * m2 = -inf is empty and contributes nothing; a row whose partials are all
+ * empty gets O = 0 and LSE = -inf.
+ *
+ *   part_m2  [B, H_q, max_splits] fp32, device, read-only
+ *   part_l   [B, H_q, max_splits] fp32, device, read-only (l >= 0)
+ *   part_o   [B, H_q, max_splits, d] fp32, device, read-only (unnormalised O)
+ *   split_counts [B] int32, device, or NULL: partials [0, split_counts[b]) of
+ *            sequence b are merged (clamped to [0, max_splits]); NULL = all.
+ *   o        [B, H_q, d] bf16, device, written
+ *   lse      [B, H_q]    fp32, device, written
+ *
+ * Supported: d in {32, 64, 128}; 1 <= max_splits <= 65535.
+ */
+int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o,
+                  const int32_t *split_counts, int max_splits,
+                  void *o, float *lse, int B, int H_q, int d, void *stream);
+
+/*
+ * gqa_attn_prefill_causal -- causal self-attention over a whole prompt
+ * (T_q = S_kv = S): query i sees keys j <= i (V07, section 12).
+ *
+ * FlashAttention-2 style: each workgroup keeps one block of query rows and its
+ * (m, l, O) state on chip and streams K/V tiles past it, with P.V fused and the
+ * score matrix never written (V07, sections 4, 7 and 8); tiles wholly above
+ * the diagonal are skipped and only diagonal tiles are masked (V07, section
+ * 12: block classification).
+ *
+ *   q   [B, S, H_q, d]  bf16, device, read-only
+ *   k   [B, S, H_kv, d] bf16, device, read-only
+ *   v   [B, S, H_kv, d] bf16, device, read-only
+ *   o   [B, S, H_q, d]  bf16, device, written (RNE from fp32)
+ *   lse [B, H_q, S]     fp32, device, written (natural log)
+ *
+ * Supported: d = 128.
+ */
+int gqa_attn_prefill_causal(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int S, int H_q, int H_kv, int d,
+                            float softmax_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,142 @@
+"""The C ABI on the CPU: symbols, plans and argument checks (no kernel is launched).
+
+Every call below fails validation on the host, before the library touches the
+GPU, so these run without one.  Pointers are fake but aligned addresses that
+are never dereferenced.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+import gqa_attention_amd as g
+
+OK, NULLP, SHAPE, UNSUP, SPLITS, WS, ALIGN, SCALE, HIP = range(9)
+A = ctypes.c_void_p(0x10000)          # aligned fake device address
+MIS = ctypes.c_void_p(0x10002)        # 2-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return g.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = g.header_functions()
+    assert {"gqa_attn_decode", "gqa_attn_prefill_causal", "gqa_lse_merge", "gqa_decode_plan",
+            "gqa_decode_partials", "gqa_decode_combine", "gqa_status_string",
+            "gqa_last_error", "gqa_version"} <= set(declared)
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for f in declared:
+        getattr(lib, f)
+
+
+def test_status_strings(lib):
+    names = [lib.gqa_status_string(i).decode() for i in range(9)]
+    assert names == ["GQA_OK", "GQA_ERR_NULL_POINTER", "GQA_ERR_BAD_SHAPE", "GQA_ERR_UNSUPPORTED",
+                     "GQA_ERR_SPLITS", "GQA_ERR_WORKSPACE", "GQA_ERR_ALIGNMENT", "GQA_ERR_SCALE",
+                     "GQA_ERR_HIP"]
+    assert lib.gqa_status_string(99).decode() == "GQA_ERR_UNKNOWN"
+    assert b"gfx950" in lib.gqa_version()
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 64, 8, 128, 32768, 32), (32, 1024)),        # Llama decode: 32 chunks of 1024 keys
+    ((1, 8, 2, 32, 512, 4), (4, 128)),               # tiny decode: 4 chunks of 128 keys
+    ((8, 64, 8, 128, 131072, 64), (64, 2048)),       # ragged decode bound: 2048-key chunks
+    ((8, 64, 8, 128, 131000, 64), (64, 2048)),       # chunk rounded up to a multiple of 32
+    ((1, 64, 8, 128, 100, 32), (4, 32)),               # chunk rounded up to the 32-key tile
+])
+def test_decode_plan(args, expect):
+    P, chunk, ws = g.decode_plan(*args)
+    assert (P, chunk) == expect
+    B, H_q, _, d, S_max, _ = args
+    rows = B * H_q * P
+    a256 = lambda n: (n + 255) // 256 * 256
+    assert ws == 2 * a256(rows * 4) + a256(rows * d * 4)
+    assert (P - 1) * chunk < S_max <= P * chunk
+
+
+def test_decode_plan_auto_fills_the_gpu():
+    P, chunk, _ = g.decode_plan(1, 64, 8, 128, 32768, 0)
+    assert 8 * P >= 512 and chunk >= 256 and chunk % 32 == 0
+    P, chunk, _ = g.decode_plan(1, 8, 2, 32, 100, 0)
+    assert chunk == 128 and P == 1                   # short sequence: one chunk
+
+
+def test_decode_plan_workspace_size_at_llama_shape():
+    # 32 splits x 64 heads x (m, l, 128-wide O) fp32 = 1,064,960 bytes of partials
+    _, _, ws = g.decode_plan(1, 64, 8, 128, 32768, 32)
+    assert ws == 32 * 64 * (128 + 2) * 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 64, 7, 128, 1024, 0), SHAPE),       # H_kv does not divide H_q
+    ((0, 64, 8, 128, 1024, 0), SHAPE),
+    ((1, 64, 8, 128, 0, 0), SHAPE),
+    ((1, 64, 8, 96, 1024, 0), UNSUP),        # head size without a kernel
+    ((1, 64, 8, 128, 1024, -1), SPLITS),
+    ((1, 64, 8, 128, 1024, 70000), SPLITS),
+])
+def test_decode_plan_rejects(lib, args, code):
+    rc = lib.gqa_decode_plan(*args, None, None, None)
+    assert rc == code
+    assert lib.gqa_last_error().decode() != ""
+
+
+def _decode(lib, q=A, k=A, v=A, seqlens=None, o=A, lse=A, B=1, H_q=8, H_kv=2, d=32, S=512,
+            scale=0.17, splits=4, ws=A, ws_bytes=1 << 30):
+    return lib.gqa_attn_decode(q, k, v, seqlens, o, lse, B, H_q, H_kv, d, S, scale, splits, ws,
+                               ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(k=None), NULLP), (dict(v=None), NULLP), (dict(o=None), NULLP),
+    (dict(lse=None), NULLP), (dict(ws=None), WS),
+    (dict(q=MIS), ALIGN), (dict(o=MIS), ALIGN), (dict(seqlens=ctypes.c_void_p(0x10001)), ALIGN),
+    (dict(ws=ctypes.c_void_p(0x10010)), WS),      # workspace not 256-byte aligned
+    (dict(ws_bytes=100), WS),
+    (dict(scale=-1.0), SCALE), (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE),
+    (dict(H_kv=3), SHAPE), (dict(d=16), UNSUP), (dict(splits=-2), SPLITS),
+])
+def test_decode_rejects_before_launch(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_stage_calls_reject_before_launch(lib):
+    assert lib.gqa_decode_partials(None, A, A, None, 1, 8, 2, 32, 512, 0.1, 4, A, 1 << 30,
+                                   None) == NULLP
+    assert lib.gqa_decode_combine(None, A, A, 1, 8, 2, 32, 512, 4, A, 10, None) == WS
+    assert lib.gqa_decode_combine(None, MIS, A, 1, 8, 2, 32, 512, 4, A, 1 << 30, None) == ALIGN
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m2=None), NULLP), (dict(o=MIS), ALIGN), (dict(P=0), SPLITS), (dict(P=70000), SPLITS),
+    (dict(d=48), UNSUP), (dict(B=0), SHAPE), (dict(counts=ctypes.c_void_p(0x10003)), ALIGN),
+])
+def test_lse_merge_rejects_before_launch(lib, kw, code):
+    a = dict(m2=A, l=A, po=A, counts=None, P=4, o=A, lse=A, B=1, H_q=8, d=32)
+    a.update(kw)
+    assert lib.gqa_lse_merge(a["m2"], a["l"], a["po"], a["counts"], a["P"], a["o"], a["lse"],
+                             a["B"], a["H_q"], a["d"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(lse=None), NULLP), (dict(k=MIS), ALIGN),
+    (dict(H_kv=5), SHAPE), (dict(S=0), SHAPE), (dict(d=64), UNSUP), (dict(scale=-0.5), SCALE),
+])
+def test_prefill_rejects_before_launch(lib, kw, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, B=1, S=256, H_q=8, H_kv=2, d=128, scale=0.088)
+    a.update(kw)
+    assert lib.gqa_attn_prefill_causal(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["S"],
+                                       a["H_q"], a["H_kv"], a["d"], a["scale"], None) == code
+
+
+def test_binding_raises_with_detail():
+    with pytest.raises(g.GQAError) as ei:
+        g.decode_plan(1, 64, 7, 128, 1024, 0)
+    assert ei.value.name == "GQA_ERR_BAD_SHAPE" and "divide" in ei.value.detail

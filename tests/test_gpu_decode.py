@@ -1,0 +1,173 @@
+"""Decode (split-KV sweep + LSE merge) against the fp64 oracle on the GPU."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_amd as g
+import oracle
+from gpu_util import say, to_gpu_bf16, to_gpu_i32
+from gqa_workloads import LLAMA_DECODE, LLAMA_RAGGED_DECODE, TINY_DECODE
+from gqa_workloads.generate import bf16_bits_from_f32, decode_inputs, for_config
+from parity import check, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(inp, num_splits, use_seqlens=True, scale=None):
+    q, k, v = (to_gpu_bf16(inp[x]) for x in ("q", "k", "v"))
+    sl = to_gpu_i32(inp["seqlens"]) if use_seqlens else None
+    o, lse = g.decode(q, k, v, sl, softmax_scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_decode(inp, use_seqlens=True, scale=None):
+    tau = None if scale is None else float(np.float32(scale))
+    return oracle.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"] if use_seqlens else None,
+                         tau=tau)
+
+
+@pytest.mark.parametrize("cfg", [TINY_DECODE, LLAMA_DECODE], ids=lambda c: c.name)
+def test_decode_config_full(cfg, gpu_available):
+    inp = for_config(cfg)
+    say(f"decode {cfg.name} splits={cfg.num_splits}")
+    o, lse = run_decode(inp, cfg.num_splits, use_seqlens=False)
+    o_ref, lse_ref = oracle_decode(inp, use_seqlens=False)
+    stats = check(to_f64(o), to_f64(lse), o_ref, lse_ref, cfg.name)
+    say(f"  {stats}")
+
+
+def test_decode_ragged_batch_full(gpu_available):
+    cfg = LLAMA_RAGGED_DECODE
+    inp = for_config(cfg, nan_fill=True)      # rows past each length hold NaN: never read
+    say(f"decode {cfg.name} seqlens={inp['seqlens'].tolist()}")
+    o, lse = run_decode(inp, cfg.num_splits)
+    o_ref, lse_ref = oracle_decode(inp)
+    stats = check(to_f64(o), to_f64(lse), o_ref, lse_ref, cfg.name)
+    say(f"  {stats}")
+
+
+CASES = [
+    # (B, H_q, H_kv, d, S_max or ragged, num_splits)
+    (1, 4, 4, 128, 1000, 8),            # G = 1: plain multi-head attention
+    (2, 8, 1, 64, 777, 5),              # MQA (one KV head), d = 64
+    (1, 16, 1, 128, 300, 3),            # G = 16 fills the head columns
+    (1, 32, 1, 32, 257, 2),             # G = 32: two head groups per KV head
+    (2, 24, 2, 128, 4100, 0),           # G = 12, library-chosen splits
+    (1, 8, 2, 128, 1, 1),               # a single cached key
+    (1, 8, 2, 32, 33, 1),               # one ragged tile past a full one
+    (3, 8, 2, 128, (1, 5000), 16),      # ragged lengths, tiny to long
+    (2, 64, 8, 128, 2048, 64),          # 32-key chunks: one tile per workgroup
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_decode_shapes(case, gpu_available):
+    B, H_q, H_kv, d, S, splits = case
+    ragged = S if isinstance(S, tuple) else None
+    inp = decode_inputs(B, H_q, H_kv, d, S_max=None if ragged else S, seed=100 + sum(case[:4]),
+                        ragged=ragged)
+    say(f"decode case {case}")
+    o, lse = run_decode(inp, splits)
+    o_ref, lse_ref = oracle_decode(inp)
+    check(to_f64(o), to_f64(lse), o_ref, lse_ref, str(case))
+
+
+def test_decode_empty_and_clamped_lengths(gpu_available):
+    inp = decode_inputs(4, 8, 2, 128, S_max=300, seed=7)
+    inp["seqlens"] = np.array([0, 300, 17, 300], dtype=np.int32)
+    say("decode with an empty sequence")
+    o, lse = run_decode(inp, 4)
+    o_ref, lse_ref = oracle_decode(inp)
+    check(to_f64(o), to_f64(lse), o_ref, lse_ref, "empty")
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    # lengths outside [0, S_max] are clamped on the device
+    sl = to_gpu_i32(np.array([-5, 10 ** 6, 17, 300], dtype=np.int32))
+    q, k, v = (to_gpu_bf16(inp[x]) for x in ("q", "k", "v"))
+    o2, lse2 = g.decode(q, k, v, sl, num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)
+
+
+def test_decode_identical_keys_give_mean_of_v(gpu_available):
+    rng = np.random.default_rng(3)
+    B, H_q, H_kv, d, S = 1, 8, 2, 128, 4096
+    inp = decode_inputs(B, H_q, H_kv, d, S_max=S, seed=8)
+    krow = bf16_bits_from_f32(rng.standard_normal((H_kv, d)).astype(np.float32))
+    inp["k"] = np.broadcast_to(krow, (B, S, H_kv, d)).copy()
+    say("decode identical keys")
+    o, lse = run_decode(inp, 16)
+    o_ref, lse_ref = oracle_decode(inp)
+    check(to_f64(o), to_f64(lse), o_ref, lse_ref, "identical keys")
+
+
+def test_decode_zero_scale_and_custom_scale(gpu_available):
+    inp = decode_inputs(1, 8, 2, 64, S_max=500, seed=9)
+    for scale in (0.0, 0.3):
+        say(f"decode scale={scale}")
+        o, lse = run_decode(inp, 4, scale=scale)
+        o_ref, lse_ref = oracle_decode(inp, scale=scale)
+        check(to_f64(o), to_f64(lse), o_ref, lse_ref, f"scale {scale}")
+        if scale == 0.0:     # every logit is 0: LSE = ln(number of keys)
+            assert np.max(np.abs(to_f64(lse) - math.log(500))) < 1e-5
+
+
+def test_decode_stages_equal_one_call_and_are_deterministic(gpu_available):
+    inp = decode_inputs(1, 64, 8, 128, S_max=8192, seed=10)
+    q, k, v = (to_gpu_bf16(inp[x]) for x in ("q", "k", "v"))
+    say("decode determinism and stage split")
+    o1, l1 = g.decode(q, k, v, None, num_splits=8)
+    o2, l2 = g.decode(q, k, v, None, num_splits=8)
+    ws = g.decode_workspace(1, 64, 8, 128, 8192, 8)
+    g.decode_partials(q, k, v, None, ws, num_splits=8)
+    o3 = torch.empty_like(o1)
+    l3 = torch.empty_like(l1)
+    g.decode_combine(None, ws, o3, l3, H_kv=8, S_max=8192, num_splits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # the workspace holds the per-chunk partial states: they match the oracle's
+    m2, lp, op = g.workspace_views(ws, 1, 64, 8, 128, 8192, 8)
+    chunk = 1024
+    for p in (0, 7):
+        m_ref, l_ref, o_ref = oracle.decode_partial(inp["q"], inp["k"], inp["v"], p * chunk,
+                                                    (p + 1) * chunk)
+        m_gpu = to_f64(m2[..., p]) * math.log(2.0)
+        shift = np.exp(m_gpu - m_ref)          # GPU state is relative to its own max
+        assert np.max(np.abs(m_gpu - m_ref)) < 1e-4
+        np.testing.assert_allclose(to_f64(lp[..., p]), l_ref / shift, rtol=5e-3)
+        got = to_f64(op[..., p, :])
+        want = o_ref / shift[..., None]
+        assert np.linalg.norm(got - want) / np.linalg.norm(want) < 5e-3
+
+
+def test_lse_merge_fuzz_against_oracle_merge(gpu_available):
+    rng = np.random.default_rng(11)
+    for trial, (B, H_q, P, d) in enumerate([(2, 8, 5, 128), (1, 4, 64, 32), (3, 2, 200, 64),
+                                            (1, 8, 1, 128)]):
+        m2 = (rng.standard_normal((B, H_q, P)) * 6).astype(np.float32)
+        l = rng.uniform(1.0, 50.0, (B, H_q, P)).astype(np.float32)
+        o = rng.standard_normal((B, H_q, P, d)).astype(np.float32) * l[..., None]
+        empty = rng.random((B, H_q, P)) < 0.2
+        empty[0, 0, :] = True                    # one row with no partial at all
+        m2[empty] = -np.inf
+        l[empty] = 0.0
+        o[empty] = 0.0
+        counts = rng.integers(0, P + 1, size=B).astype(np.int32)
+        say(f"lse_merge fuzz {trial} B={B} H_q={H_q} P={P} d={d}")
+        for use_counts in (False, True):
+            cnt = counts if use_counts else np.full(B, P, dtype=np.int32)
+            og, lg = g.lse_merge(torch.from_numpy(m2).cuda(), torch.from_numpy(l).cuda(),
+                                 torch.from_numpy(o).cuda(),
+                                 to_gpu_i32(counts) if use_counts else None)
+            torch.cuda.synchronize()
+            mask = np.arange(P)[None, :] < cnt[:, None]               # [B, P]
+            m_nat = np.where(mask[:, None, :], m2.astype(np.float64) * math.log(2.0), -np.inf)
+            l_in = np.where(mask[:, None, :], l, 0.0)
+            o_in = np.where(mask[:, None, :, None], o, 0.0)
+            o_ref, lse_ref = oracle.merge_states(m_nat.reshape(-1, P), l_in.reshape(-1, P),
+                                                 o_in.reshape(-1, P, d))
+            check(to_f64(og).reshape(-1, d), to_f64(lg).reshape(-1), o_ref, lse_ref,
+                  f"merge {trial} counts={use_counts}")

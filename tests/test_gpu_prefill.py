@@ -1,0 +1,119 @@
+"""Causal prefill against the fp64 oracle on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_amd as g
+import oracle
+from gpu_util import bf16_bits, say, to_gpu_bf16
+from gqa_workloads import LLAMA_LONG_PREFILL, LLAMA_PREFILL
+from gqa_workloads.generate import for_config, prefill_inputs
+from parity import check, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(inp, scale=None):
+    q, k, v = (to_gpu_bf16(inp[x]) for x in ("q", "k", "v"))
+    o, lse = g.prefill_causal(q, k, v, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse
+
+
+SMALL = [
+    # (B, S, H_q, H_kv)
+    (1, 256, 8, 2),       # two q-blocks, diagonal and off-diagonal tiles
+    (2, 200, 8, 2),       # ragged last q-block and key tile
+    (1, 1, 8, 2),         # a single token
+    (1, 63, 4, 4),        # G = 1 (MHA), shorter than one key tile
+    (1, 384, 8, 1),       # MQA, three q-blocks
+    (1, 520, 16, 2),      # G = 8 with the XCD remap active, ragged tail
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+def test_prefill_small_full(case, gpu_available):
+    B, S, H_q, H_kv = case
+    inp = prefill_inputs(B, S, H_q, H_kv, 128, seed=200 + S + H_q)
+    say(f"prefill small {case}")
+    _, _, v, o, lse = run_prefill(inp)
+    o_ref, lse_ref = oracle.prefill_causal(inp["q"], inp["k"], inp["v"])
+    check(to_f64(o), to_f64(lse), o_ref, lse_ref, str(case))
+    # row 0 attends to key 0 only: O is V_0 exactly, for every head
+    G = H_q // H_kv
+    o0 = bf16_bits(o[:, 0])                                    # [B, H_q, d]
+    v0 = np.repeat(inp["v"][:, 0], G, axis=1)                  # [B, H_q, d]
+    assert np.array_equal(o0, v0)
+
+
+def sample_rows(S, H_q, B, rng, n_random, extra_rows=()):
+    """A stratified set of (b, h, i): first and last rows, q-block edges, random rows."""
+    rows = set()
+    heads = sorted({0, H_q - 1, *rng.integers(0, H_q, size=6).tolist()})
+    edges = [i for qb in range(0, S, 1024) for i in (qb - 1, qb, qb + 63, qb + 64, qb + 127)
+             if 0 <= i < S]
+    fixed = list(range(0, 16)) + list(range(S - 16, S)) + edges + list(extra_rows)
+    for b in range(B):
+        for h in heads:
+            for i in fixed:
+                rows.add((b, h, int(i)))
+    for _ in range(n_random):
+        rows.add((int(rng.integers(0, B)), int(rng.integers(0, H_q)), int(rng.integers(0, S))))
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+def check_sampled(inp, o, lse, rows, what):
+    o_ref, lse_ref = oracle.prefill_causal_rows(inp["q"], inp["k"], inp["v"], rows)
+    b, h, i = (torch.from_numpy(rows[:, c].astype(np.int64)).to(o.device) for c in range(3))
+    o_all = o[b, i, h]                                         # o is [B, S, H_q, d]
+    l_all = lse[b, h, i]                                       # lse is [B, H_q, S]
+    return check(to_f64(o_all), to_f64(l_all), o_ref, lse_ref, what)
+
+
+def test_prefill_llama_s8192_sampled(gpu_available):
+    cfg = LLAMA_PREFILL
+    inp = for_config(cfg)
+    say(f"prefill {cfg.name}")
+    q, k, v, o, lse = run_prefill(inp)
+    rows = sample_rows(cfg.S, cfg.H_q, cfg.B, np.random.default_rng(41), 256)
+    stats = check_sampled(inp, o, lse, rows, cfg.name)
+    say(f"  {len(rows)} rows: {stats}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    # deterministic: a second run is bitwise identical
+    o2, lse2 = g.prefill_causal(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_prefill_long_outliers_sampled(gpu_available):
+    cfg = LLAMA_LONG_PREFILL
+    inp = for_config(cfg)
+    say(f"prefill {cfg.name}")
+    q, k, v, o, lse = run_prefill(inp)
+    # rows right at and after outlier keys stress the online rescale
+    mask = inp["outlier_mask"][0, :, 0]
+    outlier_rows = np.flatnonzero(mask)
+    rng = np.random.default_rng(42)
+    pick = rng.choice(outlier_rows, size=24, replace=False)
+    extra = np.concatenate([pick, np.minimum(pick + 1, cfg.S - 1)])
+    rows = sample_rows(cfg.S, cfg.H_q, cfg.B, rng, 128, extra_rows=extra)
+    stats = check_sampled(inp, o, lse, rows, cfg.name)
+    say(f"  {len(rows)} rows: {stats}")
+    # properties at full size: finite, and LSE_i >= s_ii (the diagonal term is one of the sum's)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    G = cfg.H_q // cfg.H_kv
+    for h in (0, 17, 63):
+        qi = q[0, :, h].float()
+        ki = k[0, :, h // G].float()
+        s_diag = (qi * ki).sum(-1) * (1.0 / np.sqrt(cfg.d))
+        assert torch.all(lse[0, h] >= s_diag - 1e-3)
+
+
+def test_prefill_custom_scale(gpu_available):
+    inp = prefill_inputs(1, 300, 8, 2, 128, seed=5)
+    for scale in (0.0, 0.05):
+        say(f"prefill scale={scale}")
+        _, _, _, o, lse = run_prefill(inp, scale=scale)
+        o_ref, lse_ref = oracle.prefill_causal(inp["q"], inp["k"], inp["v"],
+                                               tau=float(np.float32(scale)))
+        check(to_f64(o), to_f64(lse), o_ref, lse_ref, f"scale {scale}")
