@@ -44,6 +44,7 @@ from gqa_workloads.generate import for_config  # noqa: E402
 METRIC = "decode KV GB/s (% HBM peak) at Llama3-70B GQA; causal prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many bytes
 
 
 def upload(bits):
@@ -77,6 +78,9 @@ def main():
     ap.add_argument("--kv-copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 512 MiB device copy (torch copy_), whose "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the kernels' HBM traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -118,6 +122,14 @@ def main():
         g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
         if ev:
             ev[3].record()
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)

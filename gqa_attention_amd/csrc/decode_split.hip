@@ -16,7 +16,8 @@
 //
 // The P.V product is formed as O^T = V^T . P^T: P^T is exactly the S^T registers
 // after the softmax (no data movement), and V^T fragments (8 keys of one d
-// column per lane) are gathered from a per-wave LDS copy of the V tile.
+// column per lane) come from a per-wave LDS copy of the V tile through the LDS
+// transpose read.
 //
 // The 8 waves of a workgroup take interleaved 32-key tiles of the chunk (the
 // K-split of V07 section 7/8) with the next tile's loads in flight while the
@@ -41,7 +42,8 @@ struct DecodeTraits {
     static constexpr int RPI = 64 / LPR;        // V rows per wave load
     static constexpr int NVI = kTile / RPI;     // V loads per lane per tile
     static constexpr int NDT = D / 16;          // 16-wide d tiles of O^T
-    static constexpr int VPITCH = D + 4;        // staged V row pitch (bf16): 8-byte pad
+    static constexpr int VPITCH = D + 16;       // staged V row pitch (bf16): 16-B aligned,
+                                                // 4 consecutive rows on disjoint banks
 };
 
 template <int D>
@@ -98,8 +100,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D>
 #pragma unroll
     for (int i = 0; i < T::NVI; ++i) {
         uint16_t *dst = vs + (i * T::RPI + lane / T::LPR) * T::VPITCH + (lane % T::LPR) * 8;
-        *reinterpret_cast<u32x2 *>(dst) = u32x2{r.v[i][0], r.v[i][1]};
-        *reinterpret_cast<u32x2 *>(dst + 4) = u32x2{r.v[i][2], r.v[i][3]};
+        *reinterpret_cast<u32x4 *>(dst) = r.v[i];
     }
 
     // scale to log2 units; keys past the chunk/sequence end are masked
@@ -137,18 +138,15 @@ __device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D>
     const bf16x8 pf = as_bf16x8(pw);
 
     __builtin_amdgcn_wave_barrier();
-    // O^T = alpha * O^T + V^T . P^T; V^T fragment: row d = 16*dt + row16, the same 8 keys
+    // O^T = alpha * O^T + V^T . P^T.  V^T fragment of lane (row16, grp): column d = 16*dt +
+    // row16, keys 4*grp + 0..3 and 16 + 4*grp + 0..3, via two LDS transpose reads whose
+    // lanes point at row 4*grp + row16/4, columns 16*dt + 4*(row16%4).
+    const uint16_t *vrow = vs + (4 * grp + (row16 >> 2)) * T::VPITCH + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) {
-        const uint16_t *col = vs + dt * 16 + row16;
-        uint32_t w[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint16_t *c0 = col + (h * 16 + grp * 4) * T::VPITCH;
-            w[2 * h] = (uint32_t)c0[0] | ((uint32_t)c0[T::VPITCH] << 16);
-            w[2 * h + 1] = (uint32_t)c0[2 * T::VPITCH] | ((uint32_t)c0[3 * T::VPITCH] << 16);
-        }
-        const bf16x8 vf = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        const u32x2 lo = lds_read_tr16(vrow + dt * 16);
+        const u32x2 hi = lds_read_tr16(vrow + 16 * T::VPITCH + dt * 16);
+        const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         st.o[dt] *= alpha;
         st.o[dt] = mfma16(vf, pf, st.o[dt]);
     }
@@ -199,20 +197,31 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // This wave's tiles are w, w + kWaves, ...; tile i starts at key0(i).  The loop is
+    // written so that every compute is preceded, on its own path, by an unconditional
+    // prefetch of the next tile (or by nothing, for the last tile): the load counter then
+    // only has to drain the current tile's loads, never the prefetch.
     const int ntiles = (s1 - s0 + kTile - 1) / kTile;
+    const int n_w = w < ntiles ? (ntiles - 1 - w) / kWaves + 1 : 0;
     const int last_key = s1 - 1;
+    auto key0 = [&](int i) { return s0 + (w + i * kWaves) * kTile; };
     TileRegs<D> ra, rb;
-    int t = w;
-    if (t < ntiles) load_tile<D>(ra, kbase, vbase, kv_row, s0 + t * kTile, last_key, lane);
-    while (t < ntiles) {
-        const int t1 = t + kWaves;
-        if (t1 < ntiles) load_tile<D>(rb, kbase, vbase, kv_row, s0 + t1 * kTile, last_key, lane);
-        compute_tile<D>(st, ra, qf, vs, s0 + t * kTile, s1, a.scale_log2, lane);
-        if (t1 >= ntiles) break;
-        const int t2 = t1 + kWaves;
-        if (t2 < ntiles) load_tile<D>(ra, kbase, vbase, kv_row, s0 + t2 * kTile, last_key, lane);
-        compute_tile<D>(st, rb, qf, vs, s0 + t1 * kTile, s1, a.scale_log2, lane);
-        t = t2;
+    if (n_w > 0) {
+        load_tile<D>(ra, kbase, vbase, kv_row, key0(0), last_key, lane);
+        for (int i = 0;; i += 2) {
+            if (i + 1 >= n_w) {
+                compute_tile<D>(st, ra, qf, vs, key0(i), s1, a.scale_log2, lane);
+                break;
+            }
+            load_tile<D>(rb, kbase, vbase, kv_row, key0(i + 1), last_key, lane);
+            compute_tile<D>(st, ra, qf, vs, key0(i), s1, a.scale_log2, lane);
+            if (i + 2 >= n_w) {
+                compute_tile<D>(st, rb, qf, vs, key0(i + 1), s1, a.scale_log2, lane);
+                break;
+            }
+            load_tile<D>(ra, kbase, vbase, kv_row, key0(i + 2), last_key, lane);
+            compute_tile<D>(st, rb, qf, vs, key0(i + 1), s1, a.scale_log2, lane);
+        }
     }
 
     // merge the waves' states through LDS (reusing the V staging area):

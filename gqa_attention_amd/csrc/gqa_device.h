@@ -29,6 +29,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -54,6 +55,18 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 x = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// receives 16-bit element (i % 4) of the 8-byte chunks addressed by lanes
+// 4e + i/4, e = 0..3 (layout checked on the device).  So if lane j of a group
+// points at row k0 + j/4, columns n0 + 4*(j%4) of a row-major 16-bit tile, lane i
+// receives rows k0..k0+3 of column n0 + i: four consecutive reduction-index values
+// of one output column, as a matrix-core operand wants them.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

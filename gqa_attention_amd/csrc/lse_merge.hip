@@ -11,31 +11,25 @@
 // m2 = -inf is empty (a_p = 0); a row with no non-empty partial gets O = 0 and
 // LSE = -inf (the identity state of the merge, V07 section 3).
 //
-// One wavefront per (b, h): lanes share the partial loop for M and L with a
-// butterfly reduction, then each lane accumulates D/64 output columns.  The
-// merge order is fixed, so results are run-to-run deterministic.
+// Four waves per (b, h): wave w folds the partials p = w, w+4, ... into a running
+// (M, L, O) with the same online update (every load is independent of the running
+// state, so a wave's loads are all in flight at once), then the four wave states are
+// merged through LDS.  The order is fixed, so results are run-to-run deterministic.
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
 namespace gqa {
 namespace {
 
-__device__ __forceinline__ float wave_reduce_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
-}
-
-__device__ __forceinline__ float wave_reduce_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
+constexpr int kMergeWaves = 4;
+constexpr int kBatch = 8;      // partials per wave per memory round trip
 
 template <int D>
-__global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
     constexpr int EPL = (D + 63) / 64;  // output columns per lane
-    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    __shared__ float red[kMergeWaves][D + 2];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
     int n = a.P;
     if (a.counts) {
@@ -52,43 +46,79 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
     const float *lp = a.part_l + row * a.P;
     const float *op = a.part_o + row * a.P * D;
 
-    float M = neg_inf();
-    for (int p = lane; p < n; p += 64) M = fmaxf(M, m2[p]);
-    M = wave_reduce_max(M);
-
+    // running state of this wave (uniform M and L; O spread over lanes)
+    float M = neg_inf(), L = 0.f;
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    float L = 0.f;
-    if (M != neg_inf()) {
-        for (int p = lane; p < n; p += 64) L += exp2_fast(m2[p] - M) * lp[p];
-        L = wave_reduce_sum(L);
-#pragma unroll 8
-        for (int p = 0; p < n; ++p) {
-            const float al = exp2_fast(m2[p] - M);
+    // Batches of kBatch partials: all loads of a batch are issued (clamped indices,
+    // unconditional) before any is used, so one memory round trip serves the batch.
+    for (int base = w; base < n; base += kMergeWaves * kBatch) {
+        float mv[kBatch], lv[kBatch], ov[kBatch][EPL];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int p = min(base + j * kMergeWaves, n - 1);
+            mv[j] = m2[p];
+            lv[j] = lp[p];
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 const int d = lane + 64 * e;
-                if (d < D) acc[e] += al * op[(size_t)p * D + d];
+                ov[j][e] = d < D ? op[(size_t)p * D + d] : 0.f;
             }
         }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const float mp = mv[j];
+            // past the end, or an empty partial: the state is unchanged
+            const bool use = (base + j * kMergeWaves < n) && (mp != neg_inf());
+            const float m_new = fmaxf(M, mp);
+            const float a_old = exp2_fast(M - m_new);  // 2^-inf = 0 while the state is empty
+            const float a_p = exp2_fast(mp - m_new);
+            L = use ? L * a_old + a_p * lv[j] : L;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = use ? acc[e] * a_old + a_p * ov[j][e] : acc[e];
+            M = use ? m_new : M;
+        }
     }
-    const bool empty = (M == neg_inf());
-    const float inv = empty ? 0.f : 1.f / L;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int d = lane + 64 * e;
+        if (d < D) red[w][d] = acc[e];
+    }
+    if (lane == 0) {
+        red[w][D] = M;
+        red[w][D + 1] = L;
+    }
+    __syncthreads();
+    if (w != 0) return;
+
+    float Mt = neg_inf();
+#pragma unroll
+    for (int ww = 0; ww < kMergeWaves; ++ww) Mt = fmaxf(Mt, red[ww][D]);
+    const bool empty = (Mt == neg_inf());
+    float al[kMergeWaves], Lt = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kMergeWaves; ++ww) {
+        al[ww] = empty ? 0.f : exp2_fast(red[ww][D] - Mt);
+        Lt += al[ww] * red[ww][D + 1];
+    }
+    const float inv = empty ? 0.f : 1.f / Lt;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
         const int d = lane + 64 * e;
         if (d < D) {
-            const uint32_t packed = pack_bf16x2(acc[e] * inv, 0.f);
-            a.o[row * D + d] = (uint16_t)(packed & 0xFFFFu);
+            float o = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kMergeWaves; ++ww) o += al[ww] * red[ww][d];
+            a.o[row * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
         }
     }
-    if (lane == 0) a.lse[row] = empty ? neg_inf() : kLn2 * (M + __builtin_log2f(L));
+    if (lane == 0) a.lse[row] = empty ? neg_inf() : kLn2 * (Mt + __builtin_log2f(Lt));
 }
 
 template <int D>
 hipError_t launch(const MergeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q, a.B), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q, a.B), dim3(kMergeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

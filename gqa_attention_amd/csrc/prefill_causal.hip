@@ -17,7 +17,7 @@
 // softmax output registers, and whose accumulator keeps one query row per lane,
 // so the rescale by alpha is a per-lane scalar.  Q (B operand) stays in
 // registers; the K fragments are 16-byte LDS reads; V^T fragments (8 keys of
-// one d column) are gathered from the row-major V tile.
+// one d column) come from the row-major V tile through the LDS transpose read.
 //
 // Scores are kept in log2 units (s2 = acc * tau * log2(e), one fp32 multiply
 // folded into the exponent's FMA; V07 section 2, exp2 trick).
@@ -39,7 +39,8 @@ constexpr int kBr = 128;          // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
 constexpr int kWaves = 4;         // 32 query rows per wave
 constexpr int kThreads = kWaves * 64;
-constexpr int kPitch = D + 8;     // LDS row pitch in bf16 (272 B: 16-byte aligned rows)
+constexpr int kPitch = D + 8;     // K tile row pitch in bf16 (272 B): conflict-free 16-byte reads
+constexpr int kVPitch = D + 16;   // V tile row pitch in bf16 (288 B): conflict-free transpose reads
 constexpr int kLoads = kBc * D * 2 / 16 / kThreads;   // 16-byte loads per thread per tensor
 constexpr int kXcds = 8;
 
@@ -66,16 +67,16 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint16_t *ks, uint1
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-        const int off = (i * 16 + t / 16) * kPitch + (t % 16) * 8;
-        *reinterpret_cast<u32x4 *>(ks + off) = st.k[i];
-        *reinterpret_cast<u32x4 *>(vs + off) = st.v[i];
+        const int row = i * 16 + t / 16, col = (t % 16) * 8;
+        *reinterpret_cast<u32x4 *>(ks + row * kPitch + col) = st.k[i];
+        *reinterpret_cast<u32x4 *>(vs + row * kVPitch + col) = st.v[i];
     }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs a, int n_qb,
                                                                      int remap) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[kBc * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kBc * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kBc * kVPitch];
 
     const int G = a.H_q / a.H_kv;
     // ---- workgroup -> (q-block, b, h) ----
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r32 = lane & 31, hf = lane >> 5;
+    const int v_row = 4 * hf + ((lane & 15) >> 2);          // transpose-read row offset
+    const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int i0 = qb * kBr;
     const int r0 = i0 + w * 32;            // this wave's first query row
     const int row = r0 + r32;              // this lane's query row
@@ -207,15 +210,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
             for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const uint16_t *col = vs + (16 * kk + 4 * hf) * kPitch + dt * 32 + r32;
-                uint32_t wv[4];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint16_t *c0 = col + hh * 8 * kPitch;
-                    wv[2 * hh] = (uint32_t)c0[0] | ((uint32_t)c0[kPitch] << 16);
-                    wv[2 * hh + 1] = (uint32_t)c0[2 * kPitch] | ((uint32_t)c0[3 * kPitch] << 16);
-                }
-                o[dt] = mfma32(as_bf16x8(u32x4{wv[0], wv[1], wv[2], wv[3]}), pf[kk], o[dt]);
+                // lanes of each 16-lane group point at rows 16kk + 4hf + (lane%16)/4 (+8 for
+                // the second half), columns 32dt + 16((lane/16)%2) + 4(lane%4): the transpose
+                // read hands lane l the 4 keys of its slot run at column 32dt + lane%32
+                const uint16_t *vp = vs + (16 * kk + v_row) * kVPitch + dt * 32 + v_col;
+                const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * kVPitch);
+                const u32x4 wv = {lo[0], lo[1], hi[0], hi[1]};
+                o[dt] = mfma32(as_bf16x8(wv), pf[kk], o[dt]);
             }
         }
     }
