@@ -43,6 +43,7 @@ constexpr int kPitch = D + 8;     // K tile row pitch in bf16 (272 B): conflict-
 constexpr int kVPitch = D + 16;   // V tile row pitch in bf16 (288 B): conflict-free transpose reads
 constexpr int kLoads = kBc * D * 2 / 16 / kThreads;   // 16-byte loads per thread per tensor
 constexpr int kXcds = 8;
+constexpr float kSlack = 8.f;     // lazy-rescale slack, log2 units: P <= 2^8 between rescales
 
 static_assert(kLoads == 4, "tile staging assumes 4 loads per thread");
 
@@ -73,10 +74,110 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint16_t *ks, uint1
     }
 }
 
+// One 64-key tile for this wave's 32 query rows: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
+__device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *vs,
+                                            const bf16x8 (&qf)[8], f32x16 (&o)[4], float &m,
+                                            float &l, int k0, int row, int r0, float c, int r32,
+                                            int hf, int v_row, int v_col) {
+    const bool diag = k0 + kBc - 1 > r0;         // some key may pass some row
+    // ---- S^T = K . Q^T : two 32-key sub-tiles ----
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+        const uint16_t *krow = ks + (kt * 32 + r32) * kPitch + hf * 64;
+#pragma unroll
+        for (int k8 = 0; k8 < 8; ++k8) {
+            const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(krow + k8 * 8));
+            s[kt] = mfma32(kf, qf[k8], s[kt]);
+        }
+    }
+
+    // ---- online softmax on this lane's row (32 of its 64 scores) ----
+    // element (kt, r) is key k0 + 32*kt + 8*(r/4) + 4*hf + r%4
+    float mx = neg_inf();
+    if (diag) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                mx = fmaxf(mx, key <= row ? s[kt][r] : neg_inf());
+            }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    }
+    mx = wave_max_xor(mx, 32);
+    // Lazy rescale: the running max m moves only when this tile's max passes it by more
+    // than kSlack (log2 units); otherwise p = 2^(s2 - m) <= 2^kSlack and O and l keep
+    // their scale.  A common shift cancels in O / l (V07 section 3, shift insertion), so
+    // the result is the same; the slack only bounds P and spares the O rescale in almost
+    // every tile.  The first tile always moves m (m = -inf).
+    const float m_tile = mx * c;
+    const bool grow = m_tile > m + kSlack;
+    if (__any(grow)) {
+        const float m_new = grow ? m_tile : m;
+        const float alpha = exp2_fast(m - m_new);     // 0 on the first tile, 1 where !grow
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m = m_new;
+    }
+    const float neg_m = -m;
+
+    float rs = 0.f;
+    float p[2][16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float e = exp2_fast(fmaf(s[kt][r], c, neg_m));
+            if (diag) {
+                const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                e = key <= row ? e : 0.f;
+            }
+            p[kt][r] = e;
+            rs += e;
+        }
+    rs += __shfl_xor(rs, 32);
+    l += rs;
+
+    // P^T as B operand, k-step kk (16 keys): slot j <-> S^T element r = 8*(kk%2) + j of
+    // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const float *pp = &p[kk >> 1][(kk & 1) * 8];
+        pf[kk] = as_bf16x8(u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
+                                 pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])});
+    }
+
+    // ---- O^T += V^T . P^T ----
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            // lanes of each 16-lane group point at rows 16kk + 4hf + (lane%16)/4 (+8 for
+            // the second half), columns 32dt + 16((lane/16)%2) + 4(lane%4): the transpose
+            // read hands lane l the 4 keys of its slot run at column 32dt + lane%32
+            const uint16_t *vp = vs + (16 * kk + v_row) * kVPitch + dt * 32 + v_col;
+            const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * kVPitch);
+            const u32x4 wv = {lo[0], lo[1], hi[0], hi[1]};
+            o[dt] = mfma32(as_bf16x8(wv), pf[kk], o[dt]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs a, int n_qb,
                                                                      int remap) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kBc * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kBc * kVPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kBc * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t vs_buf[2][kBc * kVPitch];
 
     const int G = a.H_q / a.H_kv;
     // ---- workgroup -> (q-block, b, h) ----
@@ -126,101 +227,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
     float m = neg_inf(), l = 0.f;
     const float c = a.scale_log2;
 
+    // K/V tiles go through two LDS buffers: tile kb+1 is stored while tile kb is being
+    // computed from the other buffer, and the loads of tile kb+2 are in flight meanwhile,
+    // so one barrier per tile separates the writers of a buffer from its readers.
     Stage stage;
     load_stage(stage, kbase, vbase, kv_row, 0, a.S);
+    store_stage(stage, ks_buf[0], vs_buf[0]);
+    if (n_kb > 1) load_stage(stage, kbase, vbase, kv_row, kBc, a.S);
+    __syncthreads();
 
     for (int kb = 0; kb < n_kb; ++kb) {
         const int k0 = kb * kBc;
+        const uint16_t *ks = ks_buf[kb & 1];
+        const uint16_t *vs = vs_buf[kb & 1];
+        if (wave_rows && k0 <= r0 + 31) {   // else: tile wholly in this wave's future
+            attend_tile(ks, vs, qf, o, m, l, k0, row, r0, c, r32, hf, v_row, v_col);
+        }
+        if (kb + 1 < n_kb) {
+            store_stage(stage, ks_buf[(kb + 1) & 1], vs_buf[(kb + 1) & 1]);
+            if (kb + 2 < n_kb) load_stage(stage, kbase, vbase, kv_row, k0 + 2 * kBc, a.S);
+        }
         __syncthreads();
-        store_stage(stage, ks, vs);
-        __syncthreads();
-        if (kb + 1 < n_kb) load_stage(stage, kbase, vbase, kv_row, k0 + kBc, a.S);
-
-        if (!wave_rows || k0 > r0 + 31) continue;   // tile wholly in this wave's future
-        const bool diag = k0 + kBc - 1 > r0;         // some key may pass some row
-
-        // ---- S^T = K . Q^T : two 32-key sub-tiles ----
-        f32x16 s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-            const uint16_t *krow = ks + (kt * 32 + r32) * kPitch + hf * 64;
-#pragma unroll
-            for (int k8 = 0; k8 < 8; ++k8) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(krow + k8 * 8));
-                s[kt] = mfma32(kf, qf[k8], s[kt]);
-            }
-        }
-
-        // ---- online softmax on this lane's row (32 of its 64 scores) ----
-        // element (kt, r) is key k0 + 32*kt + 8*(r/4) + 4*hf + r%4
-        float mx = neg_inf();
-        if (diag) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                    mx = fmaxf(mx, key <= row ? s[kt][r] : neg_inf());
-                }
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        }
-        mx = wave_max_xor(mx, 32);
-        const float m_new = fmaxf(m, mx * c);
-        const float alpha = exp2_fast(m - m_new);
-        const float neg_m = -m_new;
-
-        float rs = 0.f;
-        float p[2][16];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float e = exp2_fast(fmaf(s[kt][r], c, neg_m));
-                if (diag) {
-                    const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                    e = key <= row ? e : 0.f;
-                }
-                p[kt][r] = e;
-                rs += e;
-            }
-        rs += __shfl_xor(rs, 32);
-        l = l * alpha + rs;
-        m = m_new;
-
-        // P^T as B operand, k-step kk (16 keys): slot j <-> S^T element r = 8*(kk%2) + j of
-        // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const float *pp = &p[kk >> 1][(kk & 1) * 8];
-            pf[kk] = as_bf16x8(u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
-                                     pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])});
-        }
-
-        // ---- O^T = alpha * O^T + V^T . P^T ----
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                // lanes of each 16-lane group point at rows 16kk + 4hf + (lane%16)/4 (+8 for
-                // the second half), columns 32dt + 16((lane/16)%2) + 4(lane%4): the transpose
-                // read hands lane l the 4 keys of its slot run at column 32dt + lane%32
-                const uint16_t *vp = vs + (16 * kk + v_row) * kVPitch + dt * 32 + v_col;
-                const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * kVPitch);
-                const u32x4 wv = {lo[0], lo[1], hi[0], hi[1]};
-                o[dt] = mfma32(as_bf16x8(wv), pf[kk], o[dt]);
-            }
-        }
     }
-
     // ---- epilogue: O = O^T / l -> bf16, LSE = ln2 * (m + log2 l) ----
     if (!wave_rows || row >= a.S) return;
     const float inv = 1.f / l;
