@@ -57,6 +57,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2 against (1, 1)).  The kernels
+// sum the softmax denominator from the same bf16-rounded P that enters the P.V matrix
+// product, so the output is an exact convex combination of the weights actually used.
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
 // receives 16-bit element (i % 4) of the 8-byte chunks addressed by lanes
 // 4e + i/4, e = 0..3 (layout checked on the device).  So if lane j of a group

@@ -75,11 +75,13 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint16_t *ks, uint1
 }
 
 // One 64-key tile for this wave's 32 query rows: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
+// DIAG: the tile crosses the diagonal for some row of the wave, so keys j > i are masked;
+// a compile-time flag keeps the mask code out of the (far more common) unmasked tiles.
+template <bool DIAG>
 __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *vs,
                                             const bf16x8 (&qf)[8], f32x16 (&o)[4], float &m,
                                             float &l, int k0, int row, int r0, float c, int r32,
                                             int hf, int v_row, int v_col) {
-    const bool diag = k0 + kBc - 1 > r0;         // some key may pass some row
     // ---- S^T = K . Q^T : two 32-key sub-tiles ----
     f32x16 s[2];
 #pragma unroll
@@ -97,7 +99,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
     // ---- online softmax on this lane's row (32 of its 64 scores) ----
     // element (kt, r) is key k0 + 32*kt + 8*(r/4) + 4*hf + r%4
     float mx = neg_inf();
-    if (diag) {
+    if constexpr (DIAG) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -131,32 +133,35 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
     }
     const float neg_m = -m;
 
-    float rs = 0.f;
     float p[2][16];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float e = exp2_fast(fmaf(s[kt][r], c, neg_m));
-            if (diag) {
+            if constexpr (DIAG) {
                 const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
                 e = key <= row ? e : 0.f;
             }
             p[kt][r] = e;
-            rs += e;
         }
-    rs += __shfl_xor(rs, 32);
-    l += rs;
 
     // P^T as B operand, k-step kk (16 keys): slot j <-> S^T element r = 8*(kk%2) + j of
-    // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4
+    // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4.  The row sum is taken from
+    // these rounded values.
     bf16x8 pf[4];
+    float rs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const float *pp = &p[kk >> 1][(kk & 1) * 8];
-        pf[kk] = as_bf16x8(u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
-                                 pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])});
+        const u32x4 w = {pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
+                         pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs = add_bf16_pair(w[i], rs);
+        pf[kk] = as_bf16x8(w);
     }
+    rs += __shfl_xor(rs, 32);
+    l += rs;
 
     // ---- O^T += V^T . P^T ----
 #pragma unroll
@@ -241,7 +246,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
         const uint16_t *ks = ks_buf[kb & 1];
         const uint16_t *vs = vs_buf[kb & 1];
         if (wave_rows && k0 <= r0 + 31) {   // else: tile wholly in this wave's future
-            attend_tile(ks, vs, qf, o, m, l, k0, row, r0, c, r32, hf, v_row, v_col);
+            if (k0 + kBc - 1 > r0)           // crosses this wave's diagonal
+                attend_tile<true>(ks, vs, qf, o, m, l, k0, row, r0, c, r32, hf, v_row, v_col);
+            else
+                attend_tile<false>(ks, vs, qf, o, m, l, k0, row, r0, c, r32, hf, v_row, v_col);
         }
         if (kb + 1 < n_kb) {
             store_stage(stage, ks_buf[(kb + 1) & 1], vs_buf[(kb + 1) & 1]);
