@@ -120,18 +120,18 @@ __device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D>
     const float m_new = fmaxf(st.m, mx);
     const float alpha = exp2_fast(st.m - m_new);
 
+    float psum = 0.f;
     float p[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(s2[j] - m_new);
+    for (int j = 0; j < 8; ++j) {
+        p[j] = exp2_fast(s2[j] - m_new);
+        psum += p[j];
+    }
 
-    // P^T as the B operand: slot j of lane group grp is key (j/4)*16 + 4*grp + j%4.
-    // The row sum is taken from these rounded values.
+    // P^T as the B operand: slot j of lane group grp is key (j/4)*16 + 4*grp + j%4
     const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7])};
     const bf16x8 pf = as_bf16x8(pw);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) psum = add_bf16_pair(pw[i], psum);
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     st.l = st.l * alpha + psum;

@@ -80,7 +80,7 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint16_t *ks, uint1
 template <bool DIAG>
 __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *vs,
                                             const bf16x8 (&qf)[8], f32x16 (&o)[4], float &m,
-                                            float &l, int k0, int row, int r0, float c, int r32,
+                                            float &l, float &lw, int k0, int row, int r0, float c, int r32,
                                             int hf, int v_row, int v_col) {
     // ---- S^T = K . Q^T : two 32-key sub-tiles ----
     f32x16 s[2];
@@ -125,6 +125,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
         const float m_new = grow ? m_tile : m;
         const float alpha = exp2_fast(m - m_new);     // 0 on the first tile, 1 where !grow
         l *= alpha;
+        lw *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -147,21 +148,26 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
         }
 
     // P^T as B operand, k-step kk (16 keys): slot j <-> S^T element r = 8*(kk%2) + j of
-    // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4.  The row sum is taken from
-    // these rounded values.
+    // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4.  Two row sums: l of the fp32
+    // P gives the LSE; lw of the bf16-rounded P (the weights the matrix product uses)
+    // normalises O, so O is an exact convex combination of those weights.
     bf16x8 pf[4];
-    float rs = 0.f;
+    float rs = 0.f, rw = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const float *pp = &p[kk >> 1][(kk & 1) * 8];
         const u32x4 w = {pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
                          pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rs = add_bf16_pair(w[i], rs);
+        for (int i = 0; i < 8; ++i) rs += pp[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rw = add_bf16_pair(w[i], rw);
         pf[kk] = as_bf16x8(w);
     }
     rs += __shfl_xor(rs, 32);
+    rw += __shfl_xor(rw, 32);
     l += rs;
+    lw += rw;
 
     // ---- O^T += V^T . P^T ----
 #pragma unroll
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m = neg_inf(), l = 0.f;
+    float m = neg_inf(), l = 0.f, lw = 0.f;
     const float c = a.scale_log2;
 
     // K/V tiles go through two LDS buffers: tile kb+1 is stored while tile kb is being
@@ -247,9 +253,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
         const uint16_t *vs = vs_buf[kb & 1];
         if (wave_rows && k0 <= r0 + 31) {   // else: tile wholly in this wave's future
             if (k0 + kBc - 1 > r0)           // crosses this wave's diagonal
-                attend_tile<true>(ks, vs, qf, o, m, l, k0, row, r0, c, r32, hf, v_row, v_col);
+                attend_tile<true>(ks, vs, qf, o, m, l, lw, k0, row, r0, c, r32, hf, v_row, v_col);
             else
-                attend_tile<false>(ks, vs, qf, o, m, l, k0, row, r0, c, r32, hf, v_row, v_col);
+                attend_tile<false>(ks, vs, qf, o, m, l, lw, k0, row, r0, c, r32, hf, v_row, v_col);
         }
         if (kb + 1 < n_kb) {
             store_stage(stage, ks_buf[(kb + 1) & 1], vs_buf[(kb + 1) & 1]);
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
     }
     // ---- epilogue: O = O^T / l -> bf16, LSE = ln2 * (m + log2 l) ----
     if (!wave_rows || row >= a.S) return;
-    const float inv = 1.f / l;
+    const float inv = 1.f / lw;
     uint16_t *orow = a.o + (((size_t)b * a.S + row) * a.H_q + h) * D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
