@@ -53,7 +53,7 @@ def load_library(path=LIBRARY):
     L.gqa_version.argtypes = []
     L.gqa_version.restype = ctypes.c_char_p
     L.gqa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
-                                  ctypes.POINTER(cs)]
+                                  ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(cs)]
     L.gqa_decode_plan.restype = ci
     L.gqa_attn_decode.argtypes = [vp, vp, vp, i32p, vp, f32p, ci, ci, ci, ci, ci, cf, ci, vp, cs, vp]
     L.gqa_attn_decode.restype = ci
@@ -108,17 +108,22 @@ def _scale(d, softmax_scale):
 
 
 def decode_plan(B, H_q, H_kv, d, S_max, num_splits=0):
-    """(splits, chunk, workspace_bytes) of a decode launch."""
+    """Split plan of a decode launch as a dict: chunks, chunk_keys, slabs (per chunk),
+    slab_keys, states (partial states per row = chunks * slabs) and workspace_bytes."""
     L = load_library()
-    P, chunk, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    P, chunk, slabs, slab = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    ws = ctypes.c_size_t()
     _check(L.gqa_decode_plan(B, H_q, H_kv, d, S_max, num_splits, ctypes.byref(P),
-                             ctypes.byref(chunk), ctypes.byref(ws)))
-    return P.value, chunk.value, ws.value
+                             ctypes.byref(chunk), ctypes.byref(slabs), ctypes.byref(slab),
+                             ctypes.byref(ws)))
+    return {"chunks": P.value, "chunk_keys": chunk.value, "slabs": slabs.value,
+            "slab_keys": slab.value, "states": P.value * slabs.value,
+            "workspace_bytes": ws.value}
 
 
 def decode_workspace(B, H_q, H_kv, d, S_max, num_splits=0, device="cuda"):
     """A workspace tensor sized for a decode launch."""
-    _, _, ws = decode_plan(B, H_q, H_kv, d, S_max, num_splits)
+    ws = decode_plan(B, H_q, H_kv, d, S_max, num_splits)["workspace_bytes"]
     return torch.empty(ws, dtype=torch.uint8, device=device)
 
 
@@ -173,16 +178,17 @@ def decode_combine(seqlens, workspace, out, lse, H_kv, S_max, num_splits=0):
 
 
 def workspace_views(workspace, B, H_q, H_kv, d, S_max, num_splits=0):
-    """(m2 [B,H_q,P], l [B,H_q,P], o [B,H_q,P,d]) float32 views of a decode workspace."""
-    P, _, _ = decode_plan(B, H_q, H_kv, d, S_max, num_splits)
-    rows = B * H_q * P
+    """(m2 [B,H_q,N], l [B,H_q,N], o [B,H_q,N,d]) float32 views of a decode workspace,
+    N = chunks * slabs, state index chunk * slabs + slab."""
+    N = decode_plan(B, H_q, H_kv, d, S_max, num_splits)["states"]
+    rows = B * H_q * N
     a256 = lambda n: (n + 255) // 256 * 256
     off_l = a256(rows * 4)
     off_o = off_l + a256(rows * 4)
     f = workspace.view(torch.uint8)
-    m2 = f[:rows * 4].view(torch.float32).view(B, H_q, P)
-    l = f[off_l:off_l + rows * 4].view(torch.float32).view(B, H_q, P)
-    o = f[off_o:off_o + rows * d * 4].view(torch.float32).view(B, H_q, P, d)
+    m2 = f[:rows * 4].view(torch.float32).view(B, H_q, N)
+    l = f[off_l:off_l + rows * 4].view(torch.float32).view(B, H_q, N)
+    o = f[off_o:off_o + rows * d * 4].view(torch.float32).view(B, H_q, N, d)
     return m2, l, o
 
 

@@ -1,8 +1,9 @@
 // decode_split.hip -- stage 1 of split-KV decode on gfx950.
 //
-// One workgroup per (chunk p, KV head, sequence b) sweeps the chunk's keys with
-// an online softmax and writes the chunk's partial state (m2, l, O) for every
-// query head of the group ("Attention Kernel lineage" (V07), section 17: split-K
+// The keys of a sequence are cut into chunks and every chunk into slabs.  One
+// workgroup per (slab, group of up to 8 KV heads, sequence b) sweeps the slab's
+// keys with an online softmax and writes the slab's partial state (m2, l, O) for
+// every query head of those KV heads ("Attention Kernel lineage" (V07), section 17: split-K
 // partial kernel; section 2: running (m, l, O) update; ADR-0060 "AHBM GQA Fused
 // Attention", section 3: per-tile op sequence of the decode sweep).
 //
@@ -19,10 +20,14 @@
 // column per lane) come from a per-wave LDS copy of the V tile through the LDS
 // transpose read.
 //
-// The 8 waves of a workgroup take interleaved 32-key tiles of the chunk (the
-// K-split of V07 section 7/8) with the next tile's loads in flight while the
-// current one is computed (ADR-0060 TL;DR, software pipelining), then merge
-// their states through LDS (V07 section 8, K-split reduction).
+// The 8 waves of a workgroup are spread over its KV heads, so at any moment the
+// workgroup streams whole [kv head][d] runs of consecutive cache rows (a probe on
+// MI355X read this pattern at ~6 TB/s against ~4.9 TB/s when each workgroup
+// owned one head's 256-byte slices of a longer key range).  The waves of one head
+// take interleaved 32-key tiles (the K-split of V07 section 7/8) with the next
+// tile's loads in flight while the current one is computed (ADR-0060 TL;DR,
+// software pipelining); with one wave per head the state is written straight
+// from registers, otherwise the waves merge through LDS (V07 section 8).
 //
 // Scores are kept in log2 units: s2 = (q.k) * tau * log2(e), folded into one
 // fp32 multiplier applied to the fp32 accumulator (V07 section 2, exp2 trick).
@@ -158,19 +163,36 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     using T = DecodeTraits<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * kTile * T::VPITCH];
 
-    const int p = blockIdx.x;
-    const int hk = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
+    const int p = blockIdx.x / a.slabs, sl = blockIdx.x % a.slabs;
+    const int hgrp = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
     const int b = blockIdx.z;
     const int G = a.H_q / a.H_kv;
     const int Sb = a.seqlens ? min(max(a.seqlens[b], 0), a.S_max) : a.S_max;
-    const int s0 = p * a.chunk;
-    if (s0 >= Sb) return;  // the whole workgroup leaves: this chunk is past the sequence end
-    const int s1 = min(s0 + a.chunk, Sb);
-    const int h0 = hk * G + hg * 16;
-    const int nh = min(16, G - hg * 16);
+    const int c0 = p * a.chunk;
+    if (c0 >= Sb) return;  // the whole chunk is past the sequence end: its states are never read
+    const int c1 = min(c0 + a.chunk, Sb);
+    const int s0 = c0 + sl * a.slab;
+    const int s1 = min(s0 + a.slab, c1);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int row16 = lane & 15, grp = lane >> 4;
+    // wave w sweeps KV head hw of this workgroup's group; the wph waves of one head take
+    // interleaved 32-key tiles of the slab (phase = first tile)
+    const int wph = kWaves / a.hpw;
+    const int hw = w % a.hpw, phase = w / a.hpw;
+    const int hk = hgrp * a.hpw + hw;
+    const int h0 = hk * G + hg * 16;
+    const int nh = min(16, G - hg * 16);
+    const size_t n_states = (size_t)a.P * a.slabs;
+    const size_t state0 = ((size_t)b * a.H_q + h0) * n_states + (size_t)p * a.slabs + sl;
+
+    if (s0 >= s1) {  // a slab past the end of a live chunk: mark its states empty
+        if (phase == 0 && lane < nh) {
+            a.part_m2[state0 + lane * n_states] = neg_inf();
+            a.part_l[state0 + lane * n_states] = 0.f;
+        }
+        return;
+    }
 
     // Q^T fragments (B operand): column = query head h0 + row16, k-slots = d
     bf16x8 qf[T::KS];
@@ -197,14 +219,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // This wave's tiles are w, w + kWaves, ...; tile i starts at key0(i).  The loop is
+    // This wave's tiles are phase, phase + wph, ...; tile i starts at key0(i).  The loop is
     // written so that every compute is preceded, on its own path, by an unconditional
     // prefetch of the next tile (or by nothing, for the last tile): the load counter then
     // only has to drain the current tile's loads, never the prefetch.
     const int ntiles = (s1 - s0 + kTile - 1) / kTile;
-    const int n_w = w < ntiles ? (ntiles - 1 - w) / kWaves + 1 : 0;
+    const int n_w = phase < ntiles ? (ntiles - 1 - phase) / wph + 1 : 0;
     const int last_key = s1 - 1;
-    auto key0 = [&](int i) { return s0 + (w + i * kWaves) * kTile; };
+    auto key0 = [&](int i) { return s0 + (phase + i * wph) * kTile; };
     TileRegs<D> ra, rb;
     if (n_w > 0) {
         load_tile<D>(ra, kbase, vbase, kv_row, key0(0), last_key, lane);
@@ -224,7 +246,22 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         }
     }
 
-    // merge the waves' states through LDS (reusing the V staging area):
+    if (wph == 1) {
+        // one wave per head: its registers hold the slab's whole state
+        if (row16 < nh) {
+            const size_t row = state0 + row16 * n_states;
+            float *orow = a.part_o + row * D + grp * 4;
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt) *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[dt];
+            if (grp == 0) {
+                a.part_m2[row] = st.m;
+                a.part_l[row] = st.l;
+            }
+        }
+        return;
+    }
+
+    // several waves per head: merge their states through LDS (reusing the V staging area):
     // red[w][head][0..D) = O^T column, [D] = m, [D+1] = l
     __syncthreads();
     float *red = reinterpret_cast<float *>(smem);
@@ -240,20 +277,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * 64) {
-        const int h = idx / D, d = idx % D;
+    for (int idx = threadIdx.x; idx < a.hpw * nh * D; idx += kWaves * 64) {
+        const int hw2 = idx / (nh * D), h = (idx / D) % nh, d = idx % D;
         float M = neg_inf();
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * 16 + h) * RS + D]);
+        for (int ph = 0; ph < wph; ++ph) M = fmaxf(M, red[((hw2 + a.hpw * ph) * 16 + h) * RS + D]);
         float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float *rw = red + (ww * 16 + h) * RS;
-            const float al = exp2_fast(rw[D] - M);  // empty wave: 2^-inf = 0
+        for (int ph = 0; ph < wph; ++ph) {
+            const float *rw = red + ((hw2 + a.hpw * ph) * 16 + h) * RS;
+            const float al = exp2_fast(rw[D] - M);  // a wave without tiles: 2^-inf = 0
             L += al * rw[D + 1];
             O += al * rw[d];
         }
-        const size_t row = ((size_t)b * a.H_q + h0 + h) * a.P + p;
+        const int hk2 = hgrp * a.hpw + hw2;
+        const size_t row = ((size_t)b * a.H_q + hk2 * G + hg * 16 + h) * n_states +
+                           (size_t)p * a.slabs + sl;
         a.part_o[row * D + d] = O;
         if (d == 0) {
             a.part_m2[row] = M;
@@ -266,7 +303,7 @@ template <int D>
 hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 15) / 16;
-    dim3 grid(a.P, a.H_kv * n_hg, a.B);
+    dim3 grid(a.P * a.slabs, (a.H_kv / a.hpw) * n_hg, a.B);
     hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, n_hg);
     return hipGetLastError();
 }

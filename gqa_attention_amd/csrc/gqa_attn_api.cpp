@@ -37,16 +37,20 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 constexpr int kMaxSplits = 65535;
 constexpr int kGridYZ = 65535;
 constexpr int kSplitAlign = 32;       // chunk lengths are multiples of the kernel's key tile
-constexpr int kAutoMinChunk = 256;
-constexpr int kAutoTargetGroups = 512; // two workgroups per compute unit on a 256-CU part
+constexpr int kAutoChunk = 1024;       // num_splits = 0: chunks of 1024 keys
 constexpr float kLog2e = 1.44269504088896340736f;
 
 bool decode_head_size_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
 struct Plan {
-    int P, chunk;
+    int P, chunk;       // chunks of the longest sequence, keys per chunk
+    int slab, slabs;    // keys per slab, slabs per chunk
+    int hpw;            // KV heads swept together by one workgroup
     size_t off_l, off_o, bytes;
 };
+
+constexpr int kDecodeWaves = 8;        // waves per decode workgroup
+constexpr int kSlabTilesPerWave = 4;   // 32-key tiles per wave in a full slab
 
 int check_heads(int B, int H_q, int H_kv) {
     if (B <= 0 || H_q <= 0 || H_kv <= 0)
@@ -70,20 +74,28 @@ int make_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *
         return fail(GQA_ERR_BAD_SHAPE, "B=%d or H_kv*ceil(G/16)=%ld exceeds %d", B,
                     (long)H_kv * n_hg, kGridYZ);
     long chunk;
-    if (num_splits > 0) {
+    if (num_splits > 0)
         chunk = ((long)S_max + num_splits - 1) / num_splits;
-    } else {
-        long groups = (long)B * H_kv * n_hg;
-        long want = (kAutoTargetGroups + groups - 1) / groups;
-        chunk = ((long)S_max + want - 1) / want;
-        long floor_chunk = S_max < kAutoMinChunk ? S_max : kAutoMinChunk;
-        if (chunk < floor_chunk) chunk = floor_chunk;
-    }
+    else
+        chunk = S_max < kAutoChunk ? S_max : kAutoChunk;
     chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
     long P = ((long)S_max + chunk - 1) / chunk;
+    // KV heads per workgroup: the largest power of two <= 8 that divides H_kv; the
+    // workgroup's 8 waves are spread evenly over them
+    int hpw = 8;
+    while (H_kv % hpw) hpw /= 2;
+    const long wph = kDecodeWaves / hpw;
+    long slab = 32L * kSlabTilesPerWave * wph;
+    if (slab > chunk) slab = chunk;
+    const long slabs = (chunk + slab - 1) / slab;
+    if (P * slabs > 0x7FFFFFFFL)
+        return fail(GQA_ERR_SPLITS, "too many chunk slabs (%ld)", P * slabs);
     pl->P = (int)P;
     pl->chunk = (int)chunk;
-    const size_t rows = (size_t)B * H_q * (size_t)P;
+    pl->slab = (int)slab;
+    pl->slabs = (int)slabs;
+    pl->hpw = hpw;
+    const size_t rows = (size_t)B * H_q * (size_t)P * (size_t)slabs;
     pl->off_l = align256(rows * sizeof(float));
     pl->off_o = pl->off_l + align256(rows * sizeof(float));
     pl->bytes = pl->off_o + align256(rows * (size_t)d * sizeof(float));
@@ -151,6 +163,9 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.S_max = S_max;
     a.chunk = pl.chunk;
     a.P = pl.P;
+    a.slab = pl.slab;
+    a.slabs = pl.slabs;
+    a.hpw = pl.hpw;
     a.scale_log2 = scale * kLog2e;
     return a;
 }
@@ -165,8 +180,9 @@ gqa::MergeArgs combine_args(const int32_t *seqlens, void *o, float *lse, int B, 
     m.counts = seqlens;
     m.counts_are_lengths = 1;
     m.chunk = pl.chunk;
+    m.slabs = pl.slabs;
     m.S_max = S_max;
-    m.P = pl.P;
+    m.P = pl.P * pl.slabs;
     m.o = static_cast<uint16_t *>(o);
     m.lse = lse;
     m.B = B;
@@ -198,13 +214,16 @@ const char *gqa_last_error(void) { return g_err; }
 
 const char *gqa_version(void) { return "gqa_attn 0.1.0 (gfx950)"; }
 
-int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, int *splits_out,
-                    int *chunk_out, size_t *workspace_bytes_out) {
+int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, int *chunks_out,
+                    int *chunk_keys_out, int *slabs_out, int *slab_keys_out,
+                    size_t *workspace_bytes_out) {
     Plan pl;
     int rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl);
     if (rc) return rc;
-    if (splits_out) *splits_out = pl.P;
-    if (chunk_out) *chunk_out = pl.chunk;
+    if (chunks_out) *chunks_out = pl.P;
+    if (chunk_keys_out) *chunk_keys_out = pl.chunk;
+    if (slabs_out) *slabs_out = pl.slabs;
+    if (slab_keys_out) *slab_keys_out = pl.slab;
     if (workspace_bytes_out) *workspace_bytes_out = pl.bytes;
     return ok();
 }
@@ -283,6 +302,7 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
     m.counts = split_counts;
     m.counts_are_lengths = 0;
     m.chunk = 1;
+    m.slabs = 1;
     m.S_max = 0;
     m.P = max_splits;
     m.o = static_cast<uint16_t *>(o);

@@ -10,22 +10,27 @@
 
 namespace gqa {
 
+// Split-KV plan: the keys of a sequence are cut into chunks of `chunk` keys (P chunks for
+// the longest sequence) and every chunk into `slabs` slabs of `slab` keys (the last ragged).
+// One workgroup sweeps one slab for `hpw` KV heads at once, so it reads whole runs of the
+// cache's [token][kv head][d] rows; each (query head, chunk, slab) gets one partial state.
 struct DecodeSplitArgs {
     const uint16_t *q, *k, *v;  // bf16 bit patterns
     const int32_t *seqlens;     // [B] or nullptr
     float *part_m2, *part_l, *part_o;
     int B, H_q, H_kv, d, S_max;
-    int chunk;                  // keys per split
-    int P;                      // splits of the longest sequence (workspace split dim)
+    int chunk, P;               // keys per chunk, chunks of the longest sequence
+    int slab, slabs;            // keys per slab, slabs per chunk
+    int hpw;                    // KV heads per workgroup (divides H_kv and the wave count)
     float scale_log2;           // softmax_scale * log2(e)
 };
 
 struct MergeArgs {
     const float *part_m2, *part_l, *part_o;
     const int32_t *counts;      // [B] or nullptr
-    int counts_are_lengths;     // 1: counts are sequence lengths, split count = ceil(len/chunk)
-    int chunk, S_max;           // used when counts_are_lengths
-    int P;                      // split dim of the partial arrays
+    int counts_are_lengths;     // 1: counts are sequence lengths, states = ceil(len/chunk)*slabs
+    int chunk, slabs, S_max;    // used when counts_are_lengths
+    int P;                      // state dim of the partial arrays
     uint16_t *o;                // bf16 out [B, H_q, d]
     float *lse;                 // [B, H_q]
     int B, H_q, d;

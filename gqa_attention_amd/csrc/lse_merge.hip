@@ -11,18 +11,19 @@
 // m2 = -inf is empty (a_p = 0); a row with no non-empty partial gets O = 0 and
 // LSE = -inf (the identity state of the merge, V07 section 3).
 //
-// Four waves per (b, h): wave w folds the partials p = w, w+4, ... into a running
-// (M, L, O) with the same online update (every load is independent of the running
-// state, so a wave's loads are all in flight at once), then the four wave states are
-// merged through LDS.  The order is fixed, so results are run-to-run deterministic.
+// Sixteen waves per (b, h): wave w folds the partials p = w, w+16, ... into a running
+// (M, L, O) with the same online update, in batches whose loads are all issued before
+// any is used (one memory round trip per 256 partials of a row), then the sixteen wave
+// states are merged through LDS.  The order is fixed, so results are run-to-run
+// deterministic.
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
 namespace gqa {
 namespace {
 
-constexpr int kMergeWaves = 4;
-constexpr int kBatch = 8;      // partials per wave per memory round trip
+constexpr int kMergeWaves = 16;
+constexpr int kBatch = 16;     // partials per wave per memory round trip
 
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
         int c = a.counts[b];
         if (a.counts_are_lengths) {
             c = min(max(c, 0), a.S_max);
-            n = (c + a.chunk - 1) / a.chunk;
+            n = (c + a.chunk - 1) / a.chunk * a.slabs;
         } else {
             n = min(max(c, 0), a.P);
         }

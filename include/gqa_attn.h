@@ -68,25 +68,31 @@ const char *gqa_version(void);
 /*
  * Split-KV plan of a decode launch (V07, section 17, split-K decode: the key
  * axis of every sequence is cut into partitions whose partial states a second
- * stage merges).
+ * stage merges; ADR-0060, section 4: the partial states are combined in two
+ * levels).
  *
- * The keys of each sequence are cut into contiguous chunks of `chunk` keys
- * (the last one ragged).  `chunk` is ceil(S_max / num_splits) rounded up to a
- * multiple of 32, so a sequence of the longest length S_max gets
- * ceil(S_max / chunk) <= num_splits chunks and a sequence of length S_b gets
- * ceil(S_b / chunk).  num_splits = 0 lets the library choose (enough chunks to
- * give the GPU at least two workgroups per compute unit, chunks of >= 256
- * keys).
+ * The keys of each sequence are cut into contiguous chunks of `chunk_keys`
+ * keys, and every chunk into `slabs` contiguous slabs of `slab_keys` keys (the
+ * last chunk and the last slab of a chunk may be ragged).  chunk_keys is
+ * ceil(S_max / num_splits) rounded up to a multiple of 32, so a sequence of the
+ * longest length S_max gets `chunks` = ceil(S_max / chunk_keys) <= num_splits
+ * chunks and a sequence of length S_b gets ceil(S_b / chunk_keys).
+ * num_splits = 0 lets the library choose (chunks of 1024 keys).  One workgroup
+ * sweeps one slab for up to 8 KV heads at once (slab_keys is 128 keys per wave
+ * of each head, at most a chunk), so it streams whole runs of consecutive cache
+ * rows; every (query head, chunk, slab) gets one partial state, and the merge
+ * combines all of a row's states (the merge is associative: V07, section 3).
  *
- * Outputs (any may be NULL): *splits_out = chunks of the longest sequence
- * (the workspace's split dimension P), *chunk_out = chunk, *workspace_bytes_out
- * = bytes of decode workspace the launch needs.
+ * Outputs (any may be NULL): *chunks_out, *chunk_keys_out, *slabs_out (slabs
+ * per chunk), *slab_keys_out, *workspace_bytes_out (decode workspace the
+ * launch needs).
  *
  * Supported: d in {32, 64, 128}; any G = H_q / H_kv (groups above 16 query
- * heads run as several workgroups per KV head); 1 <= num_splits <= 65535.
+ * heads run as several workgroups per KV head); 0 <= num_splits <= 65535.
  */
 int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
-                    int *splits_out, int *chunk_out, size_t *workspace_bytes_out);
+                    int *chunks_out, int *chunk_keys_out, int *slabs_out, int *slab_keys_out,
+                    size_t *workspace_bytes_out);
 
 /*
  * gqa_attn_decode -- one query token per sequence against its KV cache.
@@ -94,10 +100,11 @@ int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
  * The G query heads of a KV head are folded into the rows of one matrix
  * product so each K/V tile is read from HBM once for all of them (ADR-0060,
  * TL;DR and section 5.2: M-fold; V07, section 14, GQA kernel layout).  Each
- * (sequence, KV head, chunk) runs an online-softmax sweep over its chunk
+ * slab of the split plan (see gqa_decode_plan) runs an online-softmax sweep
  * (V07, section 2: running (m, l, O) update; section 7: deferred division),
- * then a separate merge kernel combines the partial states of the chunks
- * (V07, section 3 merge formula; section 17, second stage of split-K decode).
+ * then a separate merge kernel combines the partial states of all slabs of all
+ * chunks (V07, section 3 merge formula; section 17, second stage of split-K
+ * decode).
  * There is no causal mask: the query sees every cached key [0, seqlen)
  * (ADR-0060, section 5.2).
  *
@@ -112,9 +119,12 @@ int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
  *   lse      [B, H_q]           fp32, device, written (natural log)
  *   workspace / workspace_bytes: device scratch of at least the size
  *            gqa_decode_plan reports for the same arguments (256-byte aligned).
- *            Layout, P = splits: m2 [B][H_q][P] fp32 (running max, log2 units),
- *            then l [B][H_q][P] fp32, then O [B][H_q][P][d] fp32 (unnormalised),
- *            each region starting at a 256-byte boundary.
+ *            Layout, with N = chunks * slabs partial states per row, state index
+ *            (chunk * slabs + slab): m2 [B][H_q][N] fp32 (running max, log2 units),
+ *            then l [B][H_q][N] fp32, then O [B][H_q][N][d] fp32 (unnormalised),
+ *            each region starting at a 256-byte boundary.  States of chunks past a
+ *            sequence's end are not written; a slab past the end inside a live chunk
+ *            gets m2 = -inf.
  *
  * Calls that share a workspace on overlapping streams race.
  */

@@ -45,33 +45,38 @@ def test_status_strings(lib):
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((1, 64, 8, 128, 32768, 32), (32, 1024)),        # Llama decode: 32 chunks of 1024 keys
-    ((1, 8, 2, 32, 512, 4), (4, 128)),               # tiny decode: 4 chunks of 128 keys
-    ((8, 64, 8, 128, 131072, 64), (64, 2048)),       # ragged decode bound: 2048-key chunks
-    ((8, 64, 8, 128, 131000, 64), (64, 2048)),       # chunk rounded up to a multiple of 32
-    ((1, 64, 8, 128, 100, 32), (4, 32)),               # chunk rounded up to the 32-key tile
+    # (B, H_q, H_kv, d, S_max, num_splits) -> (chunks, chunk_keys, slabs, slab_keys)
+    ((1, 64, 8, 128, 32768, 32), (32, 1024, 8, 128)),   # Llama decode: 32 chunks of 1024 keys
+    ((1, 8, 2, 32, 512, 4), (4, 128, 1, 128)),          # tiny decode: 4 chunks of 128 keys
+    ((8, 64, 8, 128, 131072, 64), (64, 2048, 16, 128)),  # ragged decode bound: 2048-key chunks
+    ((8, 64, 8, 128, 131000, 64), (64, 2048, 16, 128)),  # chunk rounded up to a multiple of 32
+    ((1, 64, 8, 128, 100, 32), (4, 32, 1, 32)),          # chunk rounded up to the 32-key tile
+    ((1, 8, 1, 128, 5000, 2), (2, 2528, 3, 1024)),       # one KV head: 8 waves, 1024-key slabs
+    ((1, 24, 6, 64, 1000, 1), (1, 1024, 2, 512)),        # 6 KV heads: 2 per workgroup
 ])
 def test_decode_plan(args, expect):
-    P, chunk, ws = g.decode_plan(*args)
-    assert (P, chunk) == expect
+    plan = g.decode_plan(*args)
+    assert (plan["chunks"], plan["chunk_keys"], plan["slabs"], plan["slab_keys"]) == expect
     B, H_q, _, d, S_max, _ = args
-    rows = B * H_q * P
+    rows = B * H_q * plan["states"]
     a256 = lambda n: (n + 255) // 256 * 256
-    assert ws == 2 * a256(rows * 4) + a256(rows * d * 4)
+    assert plan["workspace_bytes"] == 2 * a256(rows * 4) + a256(rows * d * 4)
+    P, chunk = plan["chunks"], plan["chunk_keys"]
     assert (P - 1) * chunk < S_max <= P * chunk
+    assert (plan["slabs"] - 1) * plan["slab_keys"] < chunk <= plan["slabs"] * plan["slab_keys"]
 
 
-def test_decode_plan_auto_fills_the_gpu():
-    P, chunk, _ = g.decode_plan(1, 64, 8, 128, 32768, 0)
-    assert 8 * P >= 512 and chunk >= 256 and chunk % 32 == 0
-    P, chunk, _ = g.decode_plan(1, 8, 2, 32, 100, 0)
-    assert chunk == 128 and P == 1                   # short sequence: one chunk
+def test_decode_plan_auto_uses_1024_key_chunks():
+    plan = g.decode_plan(1, 64, 8, 128, 32768, 0)
+    assert plan["chunk_keys"] == 1024 and plan["chunks"] == 32
+    plan = g.decode_plan(1, 8, 2, 32, 100, 0)
+    assert plan["chunk_keys"] == 128 and plan["chunks"] == 1     # short sequence: one chunk
 
 
 def test_decode_plan_workspace_size_at_llama_shape():
-    # 32 splits x 64 heads x (m, l, 128-wide O) fp32 = 1,064,960 bytes of partials
-    _, _, ws = g.decode_plan(1, 64, 8, 128, 32768, 32)
-    assert ws == 32 * 64 * (128 + 2) * 4
+    # 32 chunks x 8 slabs x 64 heads x (m, l, 128-wide O) fp32 partial states
+    plan = g.decode_plan(1, 64, 8, 128, 32768, 32)
+    assert plan["workspace_bytes"] == 32 * 8 * 64 * (128 + 2) * 4
 
 
 @pytest.mark.parametrize("args,code", [
@@ -83,7 +88,7 @@ def test_decode_plan_workspace_size_at_llama_shape():
     ((1, 64, 8, 128, 1024, 70000), SPLITS),
 ])
 def test_decode_plan_rejects(lib, args, code):
-    rc = lib.gqa_decode_plan(*args, None, None, None)
+    rc = lib.gqa_decode_plan(*args, None, None, None, None, None)
     assert rc == code
     assert lib.gqa_last_error().decode() != ""
 

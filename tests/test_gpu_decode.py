@@ -128,17 +128,20 @@ def test_decode_stages_equal_one_call_and_are_deterministic(gpu_available):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
-    # the workspace holds the per-chunk partial states: they match the oracle's
+    # the workspace holds one partial state per (chunk, slab): they match the oracle's
+    plan = g.decode_plan(1, 64, 8, 128, 8192, 8)
     m2, lp, op = g.workspace_views(ws, 1, 64, 8, 128, 8192, 8)
-    chunk = 1024
-    for p in (0, 7):
-        m_ref, l_ref, o_ref = oracle.decode_partial(inp["q"], inp["k"], inp["v"], p * chunk,
-                                                    (p + 1) * chunk)
-        m_gpu = to_f64(m2[..., p]) * math.log(2.0)
+    chunk, slabs, slab = plan["chunk_keys"], plan["slabs"], plan["slab_keys"]
+    for p, sl in ((0, 0), (3, slabs - 1), (7, 2)):
+        j0 = p * chunk + sl * slab
+        j1 = min(j0 + slab, (p + 1) * chunk)
+        m_ref, l_ref, o_ref = oracle.decode_partial(inp["q"], inp["k"], inp["v"], j0, j1)
+        n = p * slabs + sl
+        m_gpu = to_f64(m2[..., n]) * math.log(2.0)
         shift = np.exp(m_gpu - m_ref)          # GPU state is relative to its own max
         assert np.max(np.abs(m_gpu - m_ref)) < 1e-4
-        np.testing.assert_allclose(to_f64(lp[..., p]), l_ref / shift, rtol=5e-3)
-        got = to_f64(op[..., p, :])
+        np.testing.assert_allclose(to_f64(lp[..., n]), l_ref / shift, rtol=5e-3)
+        got = to_f64(op[..., n, :])
         want = o_ref / shift[..., None]
         assert np.linalg.norm(got - want) / np.linalg.norm(want) < 5e-3
 
