@@ -77,10 +77,16 @@ __device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kbase,
     }
 }
 
+// Lazy-rescale slack in log2 units: the shared running max moves only when a score
+// passes it by more than this, so P <= 2^kSlack in between (exact: a common shift
+// cancels in O / l, V07 section 3).
+constexpr float kSlack = 8.f;
+
 template <int D>
 struct WaveState {
-    float m;                          // running max, log2 units (this lane's head)
-    float l;                          // running denominator
+    float m;                          // running max shared by the 4 lanes of a head (log2 units)
+    float l;                          // this lane's share of the denominator (fp32 P)
+    float lw;                         // the same from the bf16-rounded P that enters P.V
     f32x4 o[DecodeTraits<D>::NDT];    // O^T tiles: d = 16*dt + 4*grp + r, head = lane%16
 };
 
@@ -108,7 +114,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D>
         *reinterpret_cast<u32x4 *>(dst) = r.v[i];
     }
 
-    // scale to log2 units; keys past the chunk/sequence end are masked
+    // scale to log2 units; keys past the slab/sequence end are masked
     float s2[8];
     float mx = neg_inf();
 #pragma unroll
@@ -120,42 +126,60 @@ __device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D>
             s2[t * 4 + i] = x;
             mx = fmaxf(mx, x);
         }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = exp2_fast(st.m - m_new);
+    // Each lane holds 8 of a head's 32 scores.  Only when one of them passes the shared
+    // max by the slack (always on the first tile, where m = -inf) do the head's 4 lanes
+    // agree on a new max and rescale; otherwise no cross-lane step is needed.
+    if (__any(mx > st.m + kSlack)) {
+        mx = wave_max_xor(mx, 16);
+        mx = wave_max_xor(mx, 32);
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = exp2_fast(st.m - m_new);   // 0 on the first tile
+        st.l *= alpha;
+        st.lw *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] *= alpha;
+        st.m = m_new;
+    }
 
-    float psum = 0.f;
     float p[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        p[j] = exp2_fast(s2[j] - m_new);
-        psum += p[j];
+        p[j] = exp2_fast(s2[j] - st.m);
+        st.l += p[j];
     }
-
     // P^T as the B operand: slot j of lane group grp is key (j/4)*16 + 4*grp + j%4
     const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7])};
     const bf16x8 pf = as_bf16x8(pw);
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.lw = add_bf16_pair(pw[i], st.lw);
 
     __builtin_amdgcn_wave_barrier();
-    // O^T = alpha * O^T + V^T . P^T.  V^T fragment of lane (row16, grp): column d = 16*dt +
-    // row16, keys 4*grp + 0..3 and 16 + 4*grp + 0..3, via two LDS transpose reads whose
-    // lanes point at row 4*grp + row16/4, columns 16*dt + 4*(row16%4).
+    // O^T += V^T . P^T.  V^T fragment of lane (row16, grp): column d = 16*dt + row16,
+    // keys 4*grp + 0..3 and 16 + 4*grp + 0..3, via two LDS transpose reads whose lanes
+    // point at row 4*grp + row16/4, columns 16*dt + 4*(row16%4).
     const uint16_t *vrow = vs + (4 * grp + (row16 >> 2)) * T::VPITCH + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) {
         const u32x2 lo = lds_read_tr16(vrow + dt * 16);
         const u32x2 hi = lds_read_tr16(vrow + 16 * T::VPITCH + dt * 16);
         const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        st.o[dt] *= alpha;
         st.o[dt] = mfma16(vf, pf, st.o[dt]);
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// End of a wave's sweep: add up the head's four lane shares of l and lw, and scale O^T
+// by l / lw so that O / l is the convex combination of V with the rounded weights.
+template <int D>
+__device__ __forceinline__ void finish_state(WaveState<D> &st) {
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    st.lw += __shfl_xor(st.lw, 16);
+    st.lw += __shfl_xor(st.lw, 32);
+    const float f = st.lw > 0.f ? st.l / st.lw : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DecodeTraits<D>::NDT; ++dt) st.o[dt] *= f;
 }
 
 template <int D>
@@ -216,6 +240,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     WaveState<D> st;
     st.m = neg_inf();
     st.l = 0.f;
+    st.lw = 0.f;
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -245,6 +270,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
             compute_tile<D>(st, rb, qf, vs, key0(i + 1), s1, a.scale_log2, lane);
         }
     }
+
+    finish_state<D>(st);
 
     if (wph == 1) {
         // one wave per head: its registers hold the slab's whole state

@@ -293,6 +293,7 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
         (rc = check_f32(part_o, "part_o")) || (rc = check_bf16(o, "o")) ||
         (rc = check_f32(lse, "lse")))
         return rc;
+    if (!aligned(part_o, 16)) return fail(GQA_ERR_ALIGNMENT, "part_o is not 16-byte aligned");
     if (split_counts && !aligned(split_counts, 4))
         return fail(GQA_ERR_ALIGNMENT, "split_counts misaligned");
     gqa::MergeArgs m;

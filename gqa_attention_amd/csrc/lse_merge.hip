@@ -11,11 +11,12 @@
 // m2 = -inf is empty (a_p = 0); a row with no non-empty partial gets O = 0 and
 // LSE = -inf (the identity state of the merge, V07 section 3).
 //
-// Sixteen waves per (b, h): wave w folds the partials p = w, w+16, ... into a running
-// (M, L, O) with the same online update, in batches whose loads are all issued before
-// any is used (one memory round trip per 256 partials of a row), then the sixteen wave
-// states are merged through LDS.  The order is fixed, so results are run-to-run
-// deterministic.
+// Sixteen waves per (b, h), split into 32 half-waves: half-wave i folds the partials
+// p = i, i+32, ... into a running (M, L, O) with the same online update, its 32 lanes
+// each holding D/32 consecutive columns (16-byte loads at d = 128).  A batch's loads are
+// all issued before any is used, so one memory round trip serves 256 partials of a row.
+// The 32 half-wave states are then merged through LDS.  The order is fixed, so results
+// are run-to-run deterministic.
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -23,14 +24,39 @@ namespace gqa {
 namespace {
 
 constexpr int kMergeWaves = 16;
-constexpr int kBatch = 16;     // partials per wave per memory round trip
+constexpr int kHalves = 2 * kMergeWaves;
+constexpr int kBatch = 8;      // partials per half-wave per memory round trip
+
+template <int N>
+struct FloatVec {
+    float v[N];
+};
+
+template <int N>
+__device__ __forceinline__ FloatVec<N> load_floats(const float *p) {
+    FloatVec<N> r;
+    if constexpr (N == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i] = x[i];
+    } else if constexpr (N == 2) {
+        const f32x2 x = *reinterpret_cast<const f32x2 *>(p);
+        r.v[0] = x[0];
+        r.v[1] = x[1];
+    } else {
+        r.v[0] = *p;
+    }
+    return r;
+}
 
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
-    constexpr int EPL = (D + 63) / 64;  // output columns per lane
-    __shared__ float red[kMergeWaves][D + 2];
+    constexpr int DPL = D / 32;           // columns per lane of a half-wave
+    constexpr int EPL = (D + 63) / 64;    // columns per lane in the final combine
+    __shared__ float red[kHalves][D + 2];
     const int h = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = 2 * w + (lane >> 5), hl = lane & 31;
 
     int n = a.P;
     if (a.counts) {
@@ -45,63 +71,54 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
     const size_t row = (size_t)b * a.H_q + h;
     const float *m2 = a.part_m2 + row * a.P;
     const float *lp = a.part_l + row * a.P;
-    const float *op = a.part_o + row * a.P * D;
+    const float *op = a.part_o + row * a.P * D + hl * DPL;
 
-    // running state of this wave (uniform M and L; O spread over lanes)
     float M = neg_inf(), L = 0.f;
-    float acc[EPL];
+    float acc[DPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    // Batches of kBatch partials: all loads of a batch are issued (clamped indices,
-    // unconditional) before any is used, so one memory round trip serves the batch.
-    for (int base = w; base < n; base += kMergeWaves * kBatch) {
-        float mv[kBatch], lv[kBatch], ov[kBatch][EPL];
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+    for (int base = half; base < n; base += kHalves * kBatch) {
+        float mv[kBatch], lv[kBatch];
+        FloatVec<DPL> ov[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int p = min(base + j * kMergeWaves, n - 1);
+            const int p = min(base + j * kHalves, n - 1);   // clamped: loads stay in range
             mv[j] = m2[p];
             lv[j] = lp[p];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const int d = lane + 64 * e;
-                ov[j][e] = d < D ? op[(size_t)p * D + d] : 0.f;
-            }
+            ov[j] = load_floats<DPL>(op + (size_t)p * D);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const float mp = mv[j];
             // past the end, or an empty partial: the state is unchanged
-            const bool use = (base + j * kMergeWaves < n) && (mp != neg_inf());
+            const bool use = (base + j * kHalves < n) && (mp != neg_inf());
             const float m_new = fmaxf(M, mp);
             const float a_old = exp2_fast(M - m_new);  // 2^-inf = 0 while the state is empty
             const float a_p = exp2_fast(mp - m_new);
             L = use ? L * a_old + a_p * lv[j] : L;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = use ? acc[e] * a_old + a_p * ov[j][e] : acc[e];
+            for (int e = 0; e < DPL; ++e) acc[e] = use ? acc[e] * a_old + a_p * ov[j].v[e] : acc[e];
             M = use ? m_new : M;
         }
     }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int d = lane + 64 * e;
-        if (d < D) red[w][d] = acc[e];
-    }
-    if (lane == 0) {
-        red[w][D] = M;
-        red[w][D + 1] = L;
+    for (int e = 0; e < DPL; ++e) red[half][hl * DPL + e] = acc[e];
+    if (hl == 0) {
+        red[half][D] = M;
+        red[half][D + 1] = L;
     }
     __syncthreads();
     if (w != 0) return;
 
     float Mt = neg_inf();
 #pragma unroll
-    for (int ww = 0; ww < kMergeWaves; ++ww) Mt = fmaxf(Mt, red[ww][D]);
+    for (int i = 0; i < kHalves; ++i) Mt = fmaxf(Mt, red[i][D]);
     const bool empty = (Mt == neg_inf());
-    float al[kMergeWaves], Lt = 0.f;
+    float al[kHalves], Lt = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kMergeWaves; ++ww) {
-        al[ww] = empty ? 0.f : exp2_fast(red[ww][D] - Mt);
-        Lt += al[ww] * red[ww][D + 1];
+    for (int i = 0; i < kHalves; ++i) {
+        al[i] = empty ? 0.f : exp2_fast(red[i][D] - Mt);
+        Lt += al[i] * red[i][D + 1];
     }
     const float inv = empty ? 0.f : 1.f / Lt;
 #pragma unroll
@@ -110,7 +127,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
         if (d < D) {
             float o = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < kMergeWaves; ++ww) o += al[ww] * red[ww][d];
+            for (int i = 0; i < kHalves; ++i) o += al[i] * red[i][d];
             a.o[row * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
         }
     }

@@ -113,17 +113,16 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     }
-    mx = wave_max_xor(mx, 32);
-    // Lazy rescale: the running max m moves only when this tile's max passes it by more
-    // than kSlack (log2 units); otherwise p = 2^(s2 - m) <= 2^kSlack and O and l keep
-    // their scale.  A common shift cancels in O / l (V07 section 3, shift insertion), so
-    // the result is the same; the slack only bounds P and spares the O rescale in almost
-    // every tile.  The first tile always moves m (m = -inf).
-    const float m_tile = mx * c;
-    const bool grow = m_tile > m + kSlack;
-    if (__any(grow)) {
-        const float m_new = grow ? m_tile : m;
-        const float alpha = exp2_fast(m - m_new);     // 0 on the first tile, 1 where !grow
+    // Lazy rescale: the running max m (shared by the row's two lanes) moves only when a
+    // score passes it by more than kSlack (log2 units); otherwise p = 2^(s2 - m) <= 2^kSlack
+    // and O and l keep their scale, and no cross-lane step is needed.  A common shift
+    // cancels in O / l (V07 section 3, shift insertion), so the result is the same; the
+    // slack only bounds P and spares the O rescale in almost every tile.  The first tile
+    // always moves m (m = -inf).
+    if (__any(mx * c > m + kSlack)) {
+        mx = wave_max_xor(mx, 32);
+        const float m_new = fmaxf(m, mx * c);
+        const float alpha = exp2_fast(m - m_new);     // 0 on the first tile
         l *= alpha;
         lw *= alpha;
 #pragma unroll
@@ -164,9 +163,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
         for (int i = 0; i < 4; ++i) rw = add_bf16_pair(w[i], rw);
         pf[kk] = as_bf16x8(w);
     }
-    rs += __shfl_xor(rs, 32);
-    rw += __shfl_xor(rw, 32);
-    l += rs;
+    l += rs;       // this lane's half of the row; the halves are added at the end
     lw += rw;
 
     // ---- O^T += V^T . P^T ----
@@ -264,6 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
         __syncthreads();
     }
     // ---- epilogue: O = O^T / l -> bf16, LSE = ln2 * (m + log2 l) ----
+    l += __shfl_xor(l, 32);
+    lw += __shfl_xor(lw, 32);
     if (!wave_rows || row >= a.S) return;
     const float inv = 1.f / lw;
     uint16_t *orow = a.o + (((size_t)b * a.S + row) * a.H_q + h) * D;

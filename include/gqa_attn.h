@@ -162,7 +162,8 @@ int gqa_decode_combine(const int32_t *seqlens, void *o, float *lse,
  *
  *   part_m2  [B, H_q, max_splits] fp32, device, read-only
  *   part_l   [B, H_q, max_splits] fp32, device, read-only (l >= 0)
- *   part_o   [B, H_q, max_splits, d] fp32, device, read-only (unnormalised O)
+ *   part_o   [B, H_q, max_splits, d] fp32, device, read-only (unnormalised O),
+ *            16-byte aligned
  *   split_counts [B] int32, device, or NULL: partials [0, split_counts[b]) of
  *            sequence b are merged (clamped to [0, max_splits]); NULL = all.
  *   o        [B, H_q, d] bf16, device, written

@@ -121,6 +121,7 @@ def test_stage_calls_reject_before_launch(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(m2=None), NULLP), (dict(o=MIS), ALIGN), (dict(P=0), SPLITS), (dict(P=70000), SPLITS),
+    (dict(po=ctypes.c_void_p(0x10004)), ALIGN),
     (dict(d=48), UNSUP), (dict(B=0), SHAPE), (dict(counts=ctypes.c_void_p(0x10003)), ALIGN),
 ])
 def test_lse_merge_rejects_before_launch(lib, kw, code):
