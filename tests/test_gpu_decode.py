@@ -137,9 +137,11 @@ def test_decode_stages_equal_one_call_and_are_deterministic(gpu_available):
         j1 = min(j0 + slab, (p + 1) * chunk)
         m_ref, l_ref, o_ref = oracle.decode_partial(inp["q"], inp["k"], inp["v"], j0, j1)
         n = p * slabs + sl
+        # a state is defined up to a common shift: the kernel's stored max may trail the
+        # slab's true max by up to 2^8 in log2 units; l and O are relative to it
         m_gpu = to_f64(m2[..., n]) * math.log(2.0)
-        shift = np.exp(m_gpu - m_ref)          # GPU state is relative to its own max
-        assert np.max(np.abs(m_gpu - m_ref)) < 1e-4
+        assert np.all(m_gpu <= m_ref + 1e-4) and np.all(m_gpu >= m_ref - 8 * math.log(2.0) - 1e-4)
+        shift = np.exp(m_gpu - m_ref)
         np.testing.assert_allclose(to_f64(lp[..., n]), l_ref / shift, rtol=5e-3)
         got = to_f64(op[..., n, :])
         want = o_ref / shift[..., None]
