@@ -10,13 +10,17 @@ Inputs are resident in HBM before the timed region.  The decode reads one of
 ``--kv-copies`` distinct copies of the cache per step (4 x 128 MiB by default),
 so its K/V bytes come from HBM and not from the 256 MB last-level cache.
 
-Timing: ``--warmup`` untimed steps, then ``--steps`` steps bracketed by a device
-synchronisation; HIP events on the launch stream bracket each kernel, giving
-the per-kernel durations that the roofline figures use.
+Timing: ``--warmup`` untimed eager steps; then each measured loop (``--steps``
+back-to-back calls, the decode cycling over the cache copies) is captured in a
+HIP graph, replayed once untimed, and replayed once between two HIP events on
+the launch stream: time per call = elapsed / steps, free of host launch cost.
+The timed region (decode loop, then prefill loop) is bracketed by device
+synchronisations; two more loops time decode_split and lse_merge alone for the
+per-kernel roofline figures.
 
 Reported (one JSON line):
   value        decode K/V bytes read per second (GB/s): 128 MiB per decode call
-               divided by the call's GPU time (decode_split + lse_merge, events);
+               divided by the time per call (decode_split + lse_merge);
   ms_per_step  wall time of one whole step (decode + prefill) over the timed loop;
   roofline     decode_split, HBM-bound: K/V bytes / its mean duration vs 8 TB/s;
   roofline_prefill  prefill_causal, MFMA-bound: 4*S^2*d*H_q/2 FLOP / its mean
@@ -108,20 +112,22 @@ def main():
     o_p = torch.empty_like(q_p)
     lse_p = torch.empty((pc.B, pc.H_q, pc.S), dtype=torch.float32, device="cuda")
 
-    def step(i, ev=None):
+    def decode_call(i):
         k, v = kv_copies[i % len(kv_copies)]
-        if ev:
-            ev[0].record()
         g.decode_partials(q_d, k, v, None, ws, num_splits=dc.num_splits)
-        if ev:
-            ev[1].record()
         g.decode_combine(None, ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
                          num_splits=dc.num_splits)
-        if ev:
-            ev[2].record()
+
+    def split_call(i):
+        k, v = kv_copies[i % len(kv_copies)]
+        g.decode_partials(q_d, k, v, None, ws, num_splits=dc.num_splits)
+
+    def merge_call(i):
+        g.decode_combine(None, ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
+                         num_splits=dc.num_splits)
+
+    def prefill_call(i):
         g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
-        if ev:
-            ev[3].record()
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -131,21 +137,46 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # warm-up: eager calls of every kernel
     for i in range(args.warmup):
-        step(i)
+        decode_call(i)
+        prefill_call(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    def capture(fn, n):
+        """A HIP graph of n back-to-back calls fn(0..n-1) on the capture stream."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()            # one untimed replay
+        torch.cuda.synchronize()
+        return graph
+
+    K = args.steps
+    graphs = {name: capture(fn, K) for name, fn in
+              (("decode", decode_call), ("prefill", prefill_call), ("split", split_call),
+               ("merge", merge_call))}
+
+    def replay_ms(name):
+        """Mean time per call of one replay, from events on the launch stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graphs[name].replay()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    # the timed region: K whole-hot-path steps, run as K decodes then K prefills
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
+    decode_ms = replay_ms("decode")
+    prefill_ms = replay_ms("prefill")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                   for e in events])
-    split_ms, merge_ms, prefill_ms = ms.mean(axis=0)
-    decode_ms = split_ms + merge_ms
+    # per-kernel durations for the roofline figures (same launch stream, back to back)
+    split_ms = replay_ms("split")
+    merge_ms = replay_ms("merge")
 
     kv_bytes = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
     flop = acc.prefill_causal_flop(pc.B, pc.S, pc.H_q, pc.d)
