@@ -40,7 +40,7 @@ constexpr int kBc = 64;           // keys per tile
 constexpr int kWaves = 4;         // 32 query rows per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kPitch = D + 8;     // K tile row pitch in bf16 (272 B): conflict-free 16-byte reads
-constexpr int kVPitch = D + 16;   // V tile row pitch in bf16 (288 B): conflict-free transpose reads
+constexpr int kVPitch = D + 32;   // V tile row pitch in bf16 (288 B): conflict-free transpose reads
 constexpr int kLoads = kBc * D * 2 / 16 / kThreads;   // 16-byte loads per thread per tensor
 constexpr int kXcds = 8;
 constexpr float kSlack = 8.f;     // lazy-rescale slack, log2 units: P <= 2^8 between rescales
@@ -83,6 +83,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
                                             float &l, float &lw, int k0, int row, int r0, float c, int r32,
                                             int hf, int v_row, int v_col) {
     // ---- S^T = K . Q^T : two 32-key sub-tiles ----
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -96,6 +97,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
         }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- online softmax on this lane's row (32 of its 64 scores) ----
     // element (kt, r) is key k0 + 32*kt + 8*(r/4) + 4*hf + r%4
     float mx = neg_inf();
@@ -167,6 +169,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
     lw += rw;
 
     // ---- O^T += V^T . P^T ----
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -180,6 +183,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
             o[dt] = mfma32(as_bf16x8(wv), pf[kk], o[dt]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs a, int n_qb,
