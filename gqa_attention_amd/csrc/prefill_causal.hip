@@ -52,15 +52,27 @@ struct Stage {
     u32x4 v[kLoads];
 };
 
+// row_off[i] = (16i + t/16) * kv_row + 8(t%16) is fixed per thread; only the tile base
+// moves.  Keys past the sequence end (ragged last tile) are clamped to the last key.
 __device__ __forceinline__ void load_stage(Stage &st, const uint16_t *kbase, const uint16_t *vbase,
-                                           size_t kv_row, int k0, int S) {
-    const int t = threadIdx.x;
+                                           size_t kv_row, const uint32_t (&row_off)[kLoads],
+                                           int k0, int S) {
+    if (k0 + kBc <= S) {
+        const size_t tb = (size_t)k0 * kv_row;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int key = min(k0 + i * 16 + t / 16, S - 1);
-        const size_t off = (size_t)key * kv_row + (t % 16) * 8;
-        st.k[i] = load16(kbase + off);
-        st.v[i] = load16(vbase + off);
+        for (int i = 0; i < kLoads; ++i) {
+            st.k[i] = load16(kbase + tb + row_off[i]);
+            st.v[i] = load16(vbase + tb + row_off[i]);
+        }
+    } else {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int key = min(k0 + i * 16 + t / 16, S - 1);
+            const size_t off = (size_t)key * kv_row + (t % 16) * 8;
+            st.k[i] = load16(kbase + off);
+            st.v[i] = load16(vbase + off);
+        }
     }
 }
 
@@ -242,10 +254,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
     // K/V tiles go through two LDS buffers: tile kb+1 is stored while tile kb is being
     // computed from the other buffer, and the loads of tile kb+2 are in flight meanwhile,
     // so one barrier per tile separates the writers of a buffer from its readers.
+    uint32_t row_off[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+        row_off[i] = (uint32_t)((i * 16 + threadIdx.x / 16) * kv_row + (threadIdx.x % 16) * 8);
     Stage stage;
-    load_stage(stage, kbase, vbase, kv_row, 0, a.S);
+    load_stage(stage, kbase, vbase, kv_row, row_off, 0, a.S);
     store_stage(stage, ks_buf[0], vs_buf[0]);
-    if (n_kb > 1) load_stage(stage, kbase, vbase, kv_row, kBc, a.S);
+    if (n_kb > 1) load_stage(stage, kbase, vbase, kv_row, row_off, kBc, a.S);
     __syncthreads();
 
     for (int kb = 0; kb < n_kb; ++kb) {
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
         }
         if (kb + 1 < n_kb) {
             store_stage(stage, ks_buf[(kb + 1) & 1], vs_buf[(kb + 1) & 1]);
-            if (kb + 2 < n_kb) load_stage(stage, kbase, vbase, kv_row, k0 + 2 * kBc, a.S);
+            if (kb + 2 < n_kb) load_stage(stage, kbase, vbase, kv_row, row_off, k0 + 2 * kBc, a.S);
         }
         __syncthreads();
     }
