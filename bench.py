@@ -50,6 +50,32 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many bytes
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE at this workload
+# (fetch counter x 2.00, write x 1.00, both factors from the plain-copy calibration),
+# keyed by a digest of the kernel's sources: a kernel edited since its counters were
+# taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
+MEASURED_TRAFFIC = {
+    "decode_split": ("8da4c10e9057bd54", 146_646_682),
+    "lse_merge": ("7545ad904d1f4ad9", 8_630_739),
+    "prefill_causal": ("2fd4a609aa138e99", 416_799_900),
+}
+
+
+def kernel_digest(kernel):
+    """sha256 (first 16 hex digits) of a kernel's source and the two shared headers."""
+    import hashlib
+    csrc = os.path.join(ROOT, "gqa_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (kernel + ".hip", "gqa_device.h", "gqa_launch.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    digest, nbytes = MEASURED_TRAFFIC[kernel]
+    return nbytes if kernel_digest(kernel) == digest else None
+
 
 def upload(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
@@ -212,6 +238,7 @@ def main():
             "tokens_per_s": round(dc.B / (decode_ms * 1e-3), 1),
             "split_us": round(split_ms * 1e3, 2),
             "merge_us": round(merge_ms * 1e3, 2),
+            "merge_traffic": measured_traffic("lse_merge"),
         },
         "prefill": {
             "flop": flop,
@@ -221,11 +248,12 @@ def main():
         },
         "roofline": {"kernel": "decode_split", "bound": "hbm", "achieved": round(split_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_split")},
         "roofline_prefill": {"kernel": "prefill_causal", "bound": "mfma",
                              "achieved": round(prefill_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
-                             "traffic": None},
+                             "traffic": measured_traffic("prefill_causal")},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }

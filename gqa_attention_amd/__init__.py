@@ -179,16 +179,17 @@ def decode_combine(seqlens, workspace, out, lse, H_kv, S_max, num_splits=0):
 
 def workspace_views(workspace, B, H_q, H_kv, d, S_max, num_splits=0):
     """(m2 [B,H_q,N], l [B,H_q,N], o [B,H_q,N,d]) float32 views of a decode workspace,
-    N = chunks * slabs, state index chunk * slabs + slab."""
+    N = chunks * slabs, state index chunk * slabs + slab.  The workspace stores the states
+    state-major ([B][N][H_q], O [B][N][H_q][d]); the views are permuted to head-major."""
     N = decode_plan(B, H_q, H_kv, d, S_max, num_splits)["states"]
     rows = B * H_q * N
     a256 = lambda n: (n + 255) // 256 * 256
     off_l = a256(rows * 4)
     off_o = off_l + a256(rows * 4)
     f = workspace.view(torch.uint8)
-    m2 = f[:rows * 4].view(torch.float32).view(B, H_q, N)
-    l = f[off_l:off_l + rows * 4].view(torch.float32).view(B, H_q, N)
-    o = f[off_o:off_o + rows * d * 4].view(torch.float32).view(B, H_q, N, d)
+    m2 = f[:rows * 4].view(torch.float32).view(B, N, H_q).permute(0, 2, 1)
+    l = f[off_l:off_l + rows * 4].view(torch.float32).view(B, N, H_q).permute(0, 2, 1)
+    o = f[off_o:off_o + rows * d * 4].view(torch.float32).view(B, N, H_q, d).permute(0, 2, 1, 3)
     return m2, l, o
 
 

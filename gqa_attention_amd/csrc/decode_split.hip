@@ -37,7 +37,8 @@
 namespace gqa {
 namespace {
 
-constexpr int kTile = 32;  // keys per wave iteration = two 16-key MFMA row tiles
+constexpr int kTile = 16;   // keys per tile: one 16-row matrix-core tile
+constexpr int kDepth = 2;   // tiles in flight per wave
 constexpr int kWaves = 8;
 
 template <int D>
@@ -53,28 +54,32 @@ struct DecodeTraits {
 
 template <int D>
 struct TileRegs {
-    u32x4 k[2][DecodeTraits<D>::KS];
+    u32x4 k[DecodeTraits<D>::KS];
     u32x4 v[DecodeTraits<D>::NVI];
 };
 
+// Per-lane byte offsets of a tile's loads from the tile's first key row (loop invariant).
+template <int D>
+struct TileOffsets {
+    uint32_t k;                               // K: row lane%16, d-slots from 8*(lane/16)*KS
+    uint32_t v[DecodeTraits<D>::NVI];         // V: row i*RPI + lane/LPR, 16 B at lane%LPR
+};
+
+// Load the tile of keys key0..key0+15 of one KV head (kbase/vbase: that head's slice of
+// key row 0).  Rows at or past key_end read as zeros and cost no memory traffic, so a
+// tile that lies wholly past the end may be "loaded" unconditionally.
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kbase,
                                           const uint16_t *vbase, size_t kv_row, int key0,
-                                          int last_key, int lane) {
+                                          int key_end, const TileOffsets<D> &off) {
     using T = DecodeTraits<D>;
-    const int row16 = lane & 15, grp = lane >> 4;
+    const uint32_t bytes = (uint32_t)max(key_end - key0, 0) * (uint32_t)kv_row * 2u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)key0 * kv_row, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)key0 * kv_row, bytes);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        int key = min(key0 + t * 16 + row16, last_key);
-        const uint16_t *p = kbase + (size_t)key * kv_row + grp * (D / 4);
+    for (int ks = 0; ks < T::KS; ++ks) r.k[ks] = buffer_load16(rk, off.k, ks * 16);
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) r.k[t][ks] = load16(p + ks * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < T::NVI; ++i) {
-        int key = min(key0 + i * T::RPI + lane / T::LPR, last_key);
-        r.v[i] = load16(vbase + (size_t)key * kv_row + (lane % T::LPR) * 8);
-    }
+    for (int i = 0; i < T::NVI; ++i) r.v[i] = buffer_load16(rv, off.v[i], 0);
 }
 
 // Lazy-rescale slack in log2 units: the shared running max moves only when a score
@@ -90,43 +95,42 @@ struct WaveState {
     f32x4 o[DecodeTraits<D>::NDT];    // O^T tiles: d = 16*dt + 4*grp + r, head = lane%16
 };
 
+// First half of a tile: S^T = K . Q^T (rows: keys key0 + 4*(lane/16) + r, column: head
+// lane%16) and the V tile staged row-major in the wave's LDS area.  After it the tile's
+// registers are free for the next prefetch.
 template <int D>
-__device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D> &r,
-                                             const bf16x8 (&qf)[DecodeTraits<D>::KS],
-                                             uint16_t *vs, int key0, int key_end,
-                                             float scale_log2, int lane) {
+__device__ __forceinline__ f32x4 score_tile(const TileRegs<D> &r,
+                                            const bf16x8 (&qf)[DecodeTraits<D>::KS],
+                                            uint16_t *vs, int lane) {
     using T = DecodeTraits<D>;
-    const int row16 = lane & 15, grp = lane >> 4;
-
-    // S^T = K . Q^T for keys key0..key0+31 (two 16-row tiles)
-    f32x4 s[2];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) s[t] = mfma16(as_bf16x8(r.k[t][ks]), qf[ks], s[t]);
-    }
-
-    // stage the V tile (row-major, padded) for the transposed P.V operand
+    for (int ks = 0; ks < T::KS; ++ks) s = mfma16(as_bf16x8(r.k[ks]), qf[ks], s);
 #pragma unroll
     for (int i = 0; i < T::NVI; ++i) {
         uint16_t *dst = vs + (i * T::RPI + lane / T::LPR) * T::VPITCH + (lane % T::LPR) * 8;
         *reinterpret_cast<u32x4 *>(dst) = r.v[i];
     }
+    return s;
+}
+
+// Second half: online softmax of the tile's scores and O^T += V^T . P^T.
+template <int D>
+__device__ __forceinline__ void softmax_pv(WaveState<D> &st, f32x4 s, const uint16_t *vs,
+                                           int key0, int key_end, float scale_log2, int lane) {
+    using T = DecodeTraits<D>;
+    const int row16 = lane & 15, grp = lane >> 4;
 
     // scale to log2 units; keys past the slab/sequence end are masked
-    float s2[8];
+    float s2[4];
     float mx = neg_inf();
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int key = key0 + t * 16 + grp * 4 + i;
-            float x = key < key_end ? s[t][i] * scale_log2 : neg_inf();
-            s2[t * 4 + i] = x;
-            mx = fmaxf(mx, x);
-        }
-    // Each lane holds 8 of a head's 32 scores.  Only when one of them passes the shared
+    for (int i = 0; i < 4; ++i) {
+        const float x = key0 + grp * 4 + i < key_end ? s[i] * scale_log2 : neg_inf();
+        s2[i] = x;
+        mx = fmaxf(mx, x);
+    }
+    // Each lane holds 4 of a head's 16 scores.  Only when one of them passes the shared
     // max by the slack (always on the first tile, where m = -inf) do the head's 4 lanes
     // agree on a new max and rescale; otherwise no cross-lane step is needed.
     if (__any(mx > st.m + kSlack)) {
@@ -141,30 +145,27 @@ __device__ __forceinline__ void compute_tile(WaveState<D> &st, const TileRegs<D>
         st.m = m_new;
     }
 
-    float p[8];
+    float p[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
         p[j] = exp2_fast(s2[j] - st.m);
         st.l += p[j];
     }
-    // P^T as the B operand: slot j of lane group grp is key (j/4)*16 + 4*grp + j%4
-    const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-    const bf16x8 pf = as_bf16x8(pw);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.lw = add_bf16_pair(pw[i], st.lw);
+    // P^T as the B operand of the 16x16x16 product: keys 4*grp + j, head lane%16
+    const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    const s16x4 pf = __builtin_bit_cast(s16x4, pw);
+    st.lw = add_bf16_pair(pw[0], st.lw);
+    st.lw = add_bf16_pair(pw[1], st.lw);
 
     __builtin_amdgcn_wave_barrier();
     // O^T += V^T . P^T.  V^T fragment of lane (row16, grp): column d = 16*dt + row16,
-    // keys 4*grp + 0..3 and 16 + 4*grp + 0..3, via two LDS transpose reads whose lanes
-    // point at row 4*grp + row16/4, columns 16*dt + 4*(row16%4).
+    // keys 4*grp + 0..3, via one LDS transpose read whose lanes point at row
+    // 4*grp + row16/4, columns 16*dt + 4*(row16%4).
     const uint16_t *vrow = vs + (4 * grp + (row16 >> 2)) * T::VPITCH + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) {
-        const u32x2 lo = lds_read_tr16(vrow + dt * 16);
-        const u32x2 hi = lds_read_tr16(vrow + 16 * T::VPITCH + dt * 16);
-        const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        st.o[dt] = mfma16(vf, pf, st.o[dt]);
+        const s16x4 vf = __builtin_bit_cast(s16x4, lds_read_tr16(vrow + dt * 16));
+        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, st.o[dt], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -185,7 +186,11 @@ __device__ __forceinline__ void finish_state(WaveState<D> &st) {
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitArgs a, int n_hg) {
     using T = DecodeTraits<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * kTile * T::VPITCH];
+    // V staging during the sweep, then (several waves per head) the cross-wave merge
+    constexpr int kStageBytes = kWaves * kTile * T::VPITCH * 2;
+    constexpr int kMergeBytes = kWaves * 16 * (D + 2) * 4;
+    __shared__ __attribute__((aligned(16)))
+    uint16_t smem[(kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes) / 2];
 
     const int p = blockIdx.x / a.slabs, sl = blockIdx.x % a.slabs;
     const int hgrp = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
@@ -198,37 +203,35 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     const int s0 = c0 + sl * a.slab;
     const int s1 = min(s0 + a.slab, c1);
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row16 = lane & 15, grp = lane >> 4;
     // wave w sweeps KV head hw of this workgroup's group; the wph waves of one head take
-    // interleaved 32-key tiles of the slab (phase = first tile)
+    // interleaved 16-key tiles of the slab (phase = first tile)
     const int wph = kWaves / a.hpw;
     const int hw = w % a.hpw, phase = w / a.hpw;
     const int hk = hgrp * a.hpw + hw;
     const int h0 = hk * G + hg * 16;
     const int nh = min(16, G - hg * 16);
+    // this slab's states: [b][state][H_q], state = p * slabs + sl
     const size_t n_states = (size_t)a.P * a.slabs;
-    const size_t state0 = ((size_t)b * a.H_q + h0) * n_states + (size_t)p * a.slabs + sl;
+    const size_t srow = ((size_t)b * n_states + (size_t)p * a.slabs + sl) * a.H_q;
 
     if (s0 >= s1) {  // a slab past the end of a live chunk: mark its states empty
         if (phase == 0 && lane < nh) {
-            a.part_m2[state0 + lane * n_states] = neg_inf();
-            a.part_l[state0 + lane * n_states] = 0.f;
+            a.part_m2[srow + h0 + lane] = neg_inf();
+            a.part_l[srow + h0 + lane] = 0.f;
         }
         return;
     }
 
-    // Q^T fragments (B operand): column = query head h0 + row16, k-slots = d
+    // Q^T fragments (B operand): column = query head h0 + row16, k-slots = d.  Columns past
+    // the group's last head repeat that head; their results are never stored.
     bf16x8 qf[T::KS];
     {
         const uint16_t *qrow =
             a.q + ((size_t)b * a.H_q + h0 + min(row16, nh - 1)) * D + grp * (D / 4);
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-            u32x4 x = load16(qrow + ks * 8);
-            if (row16 >= nh) x = u32x4{0u, 0u, 0u, 0u};
-            qf[ks] = as_bf16x8(x);
-        }
+        for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 8));
     }
 
     const size_t kv_row = (size_t)a.H_kv * D;
@@ -244,31 +247,44 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // This wave's tiles are phase, phase + wph, ...; tile i starts at key0(i).  The loop is
-    // written so that every compute is preceded, on its own path, by an unconditional
-    // prefetch of the next tile (or by nothing, for the last tile): the load counter then
-    // only has to drain the current tile's loads, never the prefetch.
+    // This wave's tiles are phase, phase + wph, ...; tile t starts at key0(t).  kDepth tiles
+    // are in flight in a ring of register sets: as soon as tile t's scores are formed and
+    // its V is staged, tile t + kDepth is loaded into the freed set, before the softmax and
+    // P.V of tile t.  Tiles past the end read zeros without touching memory, so every
+    // iteration issues the same loads and the load counter only drains the oldest tile.
     const int ntiles = (s1 - s0 + kTile - 1) / kTile;
     const int n_w = phase < ntiles ? (ntiles - 1 - phase) / wph + 1 : 0;
-    const int last_key = s1 - 1;
-    auto key0 = [&](int i) { return s0 + (phase + i * wph) * kTile; };
-    TileRegs<D> ra, rb;
-    if (n_w > 0) {
-        load_tile<D>(ra, kbase, vbase, kv_row, key0(0), last_key, lane);
-        for (int i = 0;; i += 2) {
-            if (i + 1 >= n_w) {
-                compute_tile<D>(st, ra, qf, vs, key0(i), s1, a.scale_log2, lane);
-                break;
-            }
-            load_tile<D>(rb, kbase, vbase, kv_row, key0(i + 1), last_key, lane);
-            compute_tile<D>(st, ra, qf, vs, key0(i), s1, a.scale_log2, lane);
-            if (i + 2 >= n_w) {
-                compute_tile<D>(st, rb, qf, vs, key0(i + 1), s1, a.scale_log2, lane);
-                break;
-            }
-            load_tile<D>(ra, kbase, vbase, kv_row, key0(i + 2), last_key, lane);
-            compute_tile<D>(st, rb, qf, vs, key0(i + 1), s1, a.scale_log2, lane);
+    TileOffsets<D> toff;
+    toff.k = (uint32_t)((row16 * kv_row + grp * (D / 4)) * 2);
+#pragma unroll
+    for (int i = 0; i < T::NVI; ++i)
+        toff.v[i] = (uint32_t)(((i * T::RPI + lane / T::LPR) * kv_row + (lane % T::LPR) * 8) * 2);
+    auto key0 = [&](int t) { return s0 + (phase + t * wph) * kTile; };
+    TileRegs<D> ring[kDepth];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+        load_tile<D>(ring[j], kbase, vbase, kv_row, key0(j), s1, toff);
+        __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: oldest tile first
+    }
+    // whole rounds of kDepth tiles (no exit inside a round, so every pass through the loop
+    // has the same loads outstanding), then the last n_w % kDepth tiles with no new loads
+    const int n_full = n_w - n_w % kDepth;
+    int t = 0;
+    for (; t < n_full; t += kDepth) {
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) {
+            const f32x4 sc = score_tile<D>(ring[j], qf, vs, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile<D>(ring[j], kbase, vbase, kv_row, key0(t + j + kDepth), s1, toff);
+            softmax_pv<D>(st, sc, vs, key0(t + j), s1, a.scale_log2, lane);
         }
+    }
+#pragma unroll
+    for (int j = 0; j < kDepth - 1; ++j) {
+        if (t + j >= n_w) break;
+        const f32x4 sc = score_tile<D>(ring[j], qf, vs, lane);
+        softmax_pv<D>(st, sc, vs, key0(t + j), s1, a.scale_log2, lane);
     }
 
     finish_state<D>(st);
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     if (wph == 1) {
         // one wave per head: its registers hold the slab's whole state
         if (row16 < nh) {
-            const size_t row = state0 + row16 * n_states;
+            const size_t row = srow + h0 + row16;
             float *orow = a.part_o + row * D + grp * 4;
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt) *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[dt];
@@ -316,8 +332,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
             O += al * rw[d];
         }
         const int hk2 = hgrp * a.hpw + hw2;
-        const size_t row = ((size_t)b * a.H_q + hk2 * G + hg * 16 + h) * n_states +
-                           (size_t)p * a.slabs + sl;
+        const size_t row = srow + hk2 * G + hg * 16 + h;
         a.part_o[row * D + d] = O;
         if (d == 0) {
             a.part_m2[row] = M;

@@ -183,6 +183,9 @@ gqa::MergeArgs combine_args(const int32_t *seqlens, void *o, float *lse, int B, 
     m.slabs = pl.slabs;
     m.S_max = S_max;
     m.P = pl.P * pl.slabs;
+    m.batch_stride = (long)m.P * H_q;   // workspace: [B][state][H_q]
+    m.head_stride = 1;
+    m.state_stride = H_q;
     m.o = static_cast<uint16_t *>(o);
     m.lse = lse;
     m.B = B;
@@ -306,6 +309,9 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
     m.slabs = 1;
     m.S_max = 0;
     m.P = max_splits;
+    m.batch_stride = (long)H_q * max_splits;   // caller's partials: [B][H_q][P]
+    m.head_stride = max_splits;
+    m.state_stride = 1;
     m.o = static_cast<uint16_t *>(o);
     m.lse = lse;
     m.B = B;

@@ -38,6 +38,19 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Buffer resource over [base, base + bytes) for raw (unstrided) buffer loads: a load at a
+// byte offset >= bytes returns zeros and touches no memory.  Word 3 is the gfx9-family
+// default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes at byte offset voff + imm of a buffer (imm a compile-time constant < 4096).
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int imm) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff + imm, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -13,7 +13,9 @@ namespace gqa {
 // Split-KV plan: the keys of a sequence are cut into chunks of `chunk` keys (P chunks for
 // the longest sequence) and every chunk into `slabs` slabs of `slab` keys (the last ragged).
 // One workgroup sweeps one slab for `hpw` KV heads at once, so it reads whole runs of the
-// cache's [token][kv head][d] rows; each (query head, chunk, slab) gets one partial state.
+// cache's [token][kv head][d] rows; each (query head, chunk, slab) gets one partial state,
+// stored state-major: [B][chunk * slabs + slab][H_q] (O: [..][d]), so the states a
+// workgroup writes are contiguous.
 struct DecodeSplitArgs {
     const uint16_t *q, *k, *v;  // bf16 bit patterns
     const int32_t *seqlens;     // [B] or nullptr
@@ -25,12 +27,15 @@ struct DecodeSplitArgs {
     float scale_log2;           // softmax_scale * log2(e)
 };
 
+// Partial state (b, h, p) sits at index b*batch_stride + h*head_stride + p*state_stride of
+// the m2 and l arrays, and at d times that index in the O array.
 struct MergeArgs {
     const float *part_m2, *part_l, *part_o;
     const int32_t *counts;      // [B] or nullptr
     int counts_are_lengths;     // 1: counts are sequence lengths, states = ceil(len/chunk)*slabs
     int chunk, slabs, S_max;    // used when counts_are_lengths
-    int P;                      // state dim of the partial arrays
+    int P;                      // states per row when counts is nullptr (and the upper bound)
+    long batch_stride, head_stride, state_stride;
     uint16_t *o;                // bf16 out [B, H_q, d]
     float *lse;                 // [B, H_q]
     int B, H_q, d;

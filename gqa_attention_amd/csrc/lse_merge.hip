@@ -15,8 +15,8 @@
 // p = i, i+32, ... into a running (M, L, O) with the same online update, its 32 lanes
 // each holding D/32 consecutive columns (16-byte loads at d = 128).  A batch's loads are
 // all issued before any is used, so one memory round trip serves 256 partials of a row.
-// The 32 half-wave states are then merged through LDS.  The order is fixed, so results
-// are run-to-run deterministic.
+// The 32 half-wave states are then merged through LDS, one output column per thread.
+// The order is fixed, so results are run-to-run deterministic.
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -52,7 +52,6 @@ __device__ __forceinline__ FloatVec<N> load_floats(const float *p) {
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
     constexpr int DPL = D / 32;           // columns per lane of a half-wave
-    constexpr int EPL = (D + 63) / 64;    // columns per lane in the final combine
     __shared__ float red[kHalves][D + 2];
     const int h = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -69,9 +68,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
         }
     }
     const size_t row = (size_t)b * a.H_q + h;
-    const float *m2 = a.part_m2 + row * a.P;
-    const float *lp = a.part_l + row * a.P;
-    const float *op = a.part_o + row * a.P * D + hl * DPL;
+    const size_t row0 = (size_t)b * a.batch_stride + (size_t)h * a.head_stride;
+    const size_t ss = a.state_stride;
+    const float *m2 = a.part_m2 + row0;
+    const float *lp = a.part_l + row0;
+    const float *op = a.part_o + row0 * D + hl * DPL;
 
     float M = neg_inf(), L = 0.f;
     float acc[DPL];
@@ -83,9 +84,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int p = min(base + j * kHalves, n - 1);   // clamped: loads stay in range
-            mv[j] = m2[p];
-            lv[j] = lp[p];
-            ov[j] = load_floats<DPL>(op + (size_t)p * D);
+            mv[j] = m2[p * ss];
+            lv[j] = lp[p * ss];
+            ov[j] = load_floats<DPL>(op + (size_t)p * ss * D);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
@@ -108,30 +109,24 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
         red[half][D + 1] = L;
     }
     __syncthreads();
-    if (w != 0) return;
 
+    // combine the 32 half-wave states: one output column per thread
+    if (threadIdx.x >= D) return;
+    const int d = threadIdx.x;
     float Mt = neg_inf();
 #pragma unroll
     for (int i = 0; i < kHalves; ++i) Mt = fmaxf(Mt, red[i][D]);
     const bool empty = (Mt == neg_inf());
-    float al[kHalves], Lt = 0.f;
+    float Lt = 0.f, o = 0.f;
 #pragma unroll
     for (int i = 0; i < kHalves; ++i) {
-        al[i] = empty ? 0.f : exp2_fast(red[i][D] - Mt);
-        Lt += al[i] * red[i][D + 1];
+        const float al = empty ? 0.f : exp2_fast(red[i][D] - Mt);
+        Lt += al * red[i][D + 1];
+        o += al * red[i][d];
     }
     const float inv = empty ? 0.f : 1.f / Lt;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int d = lane + 64 * e;
-        if (d < D) {
-            float o = 0.f;
-#pragma unroll
-            for (int i = 0; i < kHalves; ++i) o += al[i] * red[i][d];
-            a.o[row * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
-        }
-    }
-    if (lane == 0) a.lse[row] = empty ? neg_inf() : kLn2 * (Mt + __builtin_log2f(Lt));
+    a.o[row * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
+    if (d == 0) a.lse[row] = empty ? neg_inf() : kLn2 * (Mt + __builtin_log2f(Lt));
 }
 
 template <int D>

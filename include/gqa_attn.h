@@ -120,11 +120,12 @@ int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
  *   workspace / workspace_bytes: device scratch of at least the size
  *            gqa_decode_plan reports for the same arguments (256-byte aligned).
  *            Layout, with N = chunks * slabs partial states per row, state index
- *            (chunk * slabs + slab): m2 [B][H_q][N] fp32 (running max, log2 units),
- *            then l [B][H_q][N] fp32, then O [B][H_q][N][d] fp32 (unnormalised),
- *            each region starting at a 256-byte boundary.  States of chunks past a
- *            sequence's end are not written; a slab past the end inside a live chunk
- *            gets m2 = -inf.
+ *            n = chunk * slabs + slab, stored state-major so that the states one
+ *            workgroup writes are contiguous: m2 [B][N][H_q] fp32 (running max, log2
+ *            units), then l [B][N][H_q] fp32, then O [B][N][H_q][d] fp32
+ *            (unnormalised), each region starting at a 256-byte boundary.  States of
+ *            chunks past a sequence's end are not written; a slab past the end inside
+ *            a live chunk gets m2 = -inf (its O is not written).
  *
  * Calls that share a workspace on overlapping streams race.
  */
