@@ -1,23 +1,34 @@
 // prefill_causal.hip -- causal GQA prefill (T_q = S_kv = S) on gfx950.
 //
 // FlashAttention-2 forward ("Attention Kernel lineage" (V07), sections 7-8):
-// each workgroup owns one block of 128 query rows of one query head for its
-// whole life, keeps the rows' (m, l, O) state in registers, and streams 64-key
-// K/V tiles through LDS; the division by l is deferred to the end, and the
-// score matrix is never written (section 4).  Causal block classification
-// (section 12): a tile wholly above the diagonal is never loaded, a tile wholly
-// below needs no mask, and only tiles crossing the diagonal are masked
-// element-wise with a select.  The classification is also applied per wave
-// (32 rows), so a wave skips tiles that are in its own future.
+// each workgroup owns one block of 256 query rows of one query head for its
+// whole life (8 waves of 32 rows, one workgroup per CU), keeps the rows'
+// (m, l, O) state in registers, and streams 64-key K/V tiles through LDS; the
+// division by l is deferred to the end, and the score matrix is never written
+// (section 4).  Causal block classification (section 12): a tile wholly above
+// the diagonal is never loaded, and only keys crossing the diagonal are masked.
+// The classification is applied per wave in 32-key steps: a wave stops after the
+// step holding its own diagonal, and only that step's scores are masked (to -inf,
+// when they are formed one step earlier), so every step runs the same code.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16): scores are formed
 // transposed, S^T = K . Q^T, so each lane owns one query row (lane % 32) and
-// holds 32 of that row's 64 scores; the row max and sum need one cross-lane
-// step.  P.V is formed as O^T = V^T . P^T, whose B operand is exactly the
-// softmax output registers, and whose accumulator keeps one query row per lane,
-// so the rescale by alpha is a per-lane scalar.  Q (B operand) stays in
-// registers; the K fragments are 16-byte LDS reads; V^T fragments (8 keys of
-// one d column) come from the row-major V tile through the LDS transpose read.
+// holds 16 of that row's 32 scores of a step; the row max and sum need one
+// cross-lane step.  P.V is formed as O^T = V^T . P^T, whose B operand is exactly
+// the softmax output registers, and whose accumulator keeps one query row per
+// lane, so the rescale by alpha is a per-lane scalar.  Q (B operand) stays in
+// registers; the K fragments are 16-byte LDS reads; V^T fragments (8 keys of one
+// d column) come from the row-major V tile through the LDS transpose read.
+//
+// Software pipeline inside each wave (32-key steps): the matrix cores form the
+// scores of step u+1 while the vector units run the softmax of step u, and the
+// row maximum of step u+1 is taken while step u's P.V runs (V07 section 10
+// overlaps the same two phases across warpgroups).  K/V tiles travel from HBM
+// straight into LDS (buffer loads with an LDS destination: no staging
+// registers; rows past the sequence end read as zeros) through rings of four K
+// and three V tile buffers, issued a tile ahead of the tile that waits for them.
+// Rows are stored with their 16-byte chunks XOR-permuted so that the fragment
+// reads of both products are bank-conflict free without padding.
 //
 // Scores are kept in log2 units (s2 = acc * tau * log2(e), one fp32 multiply
 // folded into the exponent's FMA; V07 section 2, exp2 trick).
@@ -35,108 +46,108 @@ namespace gqa {
 namespace {
 
 constexpr int D = 128;
-constexpr int kBr = 128;          // query rows per workgroup
-constexpr int kBc = 64;           // keys per tile
-constexpr int kWaves = 4;         // 32 query rows per wave
+constexpr int kBr = 256;          // query rows per workgroup
+constexpr int kBc = 64;           // keys per LDS tile
+constexpr int kHalf = 32;         // keys per pipeline step (half a tile)
+constexpr int kWaves = 8;         // 32 query rows per wave, two waves per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kPitch = D + 8;     // K tile row pitch in bf16 (272 B): conflict-free 16-byte reads
-constexpr int kVPitch = D + 32;   // V tile row pitch in bf16 (288 B): conflict-free transpose reads
-constexpr int kLoads = kBc * D * 2 / 16 / kThreads;   // 16-byte loads per thread per tensor
+constexpr int kRowBytes = D * 2;                  // one key row of one head: 256 B
+constexpr int kTileBytes = kBc * kRowBytes;       // 16 KiB
+constexpr int kNK = 4;                            // LDS: a ring of four K tile buffers
+constexpr int kNV = 3;                            // and a ring of three V tile buffers
+constexpr int kKBuf = 0;
+constexpr int kVBuf = kNK * kTileBytes;
+constexpr int kLdsBytes = (kNK + kNV) * kTileBytes;   // 112 KiB: one workgroup per CU
+constexpr int kDmaPerTile = 2;                    // DMA instructions per wave, tile and tensor
 constexpr int kXcds = 8;
 constexpr float kSlack = 8.f;     // lazy-rescale slack, log2 units: P <= 2^8 between rescales
 
-static_assert(kLoads == 4, "tile staging assumes 4 loads per thread");
+typedef __attribute__((address_space(3))) void lds_void;
 
-struct Stage {
-    u32x4 k[kLoads];
-    u32x4 v[kLoads];
+// LDS row layouts (16-byte chunk c of row r lives at chunk position c ^ f(r)):
+//   K: f(r) = r % 16   -- the QK fragment read has 16 consecutive rows read the same
+//                         chunk in one pass, which then fall on 16 distinct positions;
+//   V: f(r) = 4 (r % 4) -- a transpose read covers 4 consecutive rows x 4 chunks of one
+//                         64-byte column group, which then fill all 16 positions.
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
+
+// Issue the DMA of one 64-row K or V tile (keys k0..k0+63) into the LDS buffer at byte
+// offset dst.  Wave w writes rows 32i + 4w .. +3 (i = 0, 1); its lane l lands at row
+// 32i + 4w + l/16, chunk position l%16, and fetches the chunk the layout puts there
+// (voff: that chunk's byte offset from key row 32i).  Each 32-row group gets its own
+// buffer range, ending at the sequence end, so rows past it arrive as zeros (a tile
+// wholly past the end costs no memory traffic and just zero-fills its buffer).
+__device__ __forceinline__ void dma_tile(uint8_t *lds, int dst, const uint16_t *gbase,
+                                         size_t kv_row, int k0, int S, uint32_t voff, int w) {
+    const uint32_t row_bytes = (uint32_t)kv_row * 2u;
+    const bool full = k0 + kBc <= S;   // every tile but the last ones
+#pragma unroll
+    for (int i = 0; i < kDmaPerTile; ++i) {
+        const int r0 = k0 + 32 * i;
+        uint32_t bytes = 32u * row_bytes;
+        if (!full) {
+            const int rows = S - r0;
+            bytes = rows <= 0 ? 0u : rows >= 32 ? bytes : (uint32_t)rows * row_bytes;
+        }
+        // (uniform; readfirstlane keeps the resource in scalar registers)
+        bytes = __builtin_amdgcn_readfirstlane(bytes);
+        const uint64_t base = (uint64_t)(gbase + (size_t)r0 * kv_row);
+        // buffer resource: base, stride 0, range `bytes`, gfx9 data format word
+        const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
+        const uint32_t lds_dst = (uint32_t)(uintptr_t)(lds + dst + (32 * i + 4 * w) * kRowBytes);
+        // Issued as assembly so that the compiler does not add a wait for this DMA before
+        // every later LDS read: the tile loop's own waits and barriers order the buffers.
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_dst))
+                     : "memory");
+    }
+}
+
+// Per-lane LDS byte offsets of the fragment reads, fixed for the kernel's life.
+struct FragAddr {
+    uint32_t k[8];   // K: row r32, chunk hf*8 + k8, from a half tile's first row
+    uint32_t v[4];   // V: transpose-read start for d tile dt (add 16 rows per k-step)
 };
 
-// row_off[i] = (16i + t/16) * kv_row + 8(t%16) is fixed per thread; only the tile base
-// moves.  Keys past the sequence end (ragged last tile) are clamped to the last key.
-__device__ __forceinline__ void load_stage(Stage &st, const uint16_t *kbase, const uint16_t *vbase,
-                                           size_t kv_row, const uint32_t (&row_off)[kLoads],
-                                           int k0, int S) {
-    if (k0 + kBc <= S) {
-        const size_t tb = (size_t)k0 * kv_row;
+// S^T = K . Q^T for 32 keys whose K rows start at LDS byte offset kh.
+__device__ __forceinline__ void qk_half(f32x16 &s, const uint8_t *kh, const FragAddr &fa,
+                                        const bf16x8 (&qf)[8]) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            st.k[i] = load16(kbase + tb + row_off[i]);
-            st.v[i] = load16(vbase + tb + row_off[i]);
-        }
-    } else {
-        const int t = threadIdx.x;
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int key = min(k0 + i * 16 + t / 16, S - 1);
-            const size_t off = (size_t)key * kv_row + (t % 16) * 8;
-            st.k[i] = load16(kbase + off);
-            st.v[i] = load16(vbase + off);
-        }
+    for (int k8 = 0; k8 < 8; ++k8) {
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(kh + fa.k[k8]));
+        s = mfma32(kf, qf[k8], s);
     }
 }
 
-__device__ __forceinline__ void store_stage(const Stage &st, uint16_t *ks, uint16_t *vs) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int row = i * 16 + t / 16, col = (t % 16) * 8;
-        *reinterpret_cast<u32x4 *>(ks + row * kPitch + col) = st.k[i];
-        *reinterpret_cast<u32x4 *>(vs + row * kVPitch + col) = st.v[i];
-    }
+// Element r of a lane's 16 scores of a half is key k0 + 8*(r/4) + 4*hf + r%4.
+__device__ __forceinline__ int score_key(int k0, int r, int hf) {
+    return k0 + (r >> 2) * 8 + hf * 4 + (r & 3);
 }
 
-// One 64-key tile for this wave's 32 query rows: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
-// DIAG: the tile crosses the diagonal for some row of the wave, so keys j > i are masked;
-// a compile-time flag keeps the mask code out of the (far more common) unmasked tiles.
-template <bool DIAG>
-__device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *vs,
-                                            const bf16x8 (&qf)[8], f32x16 (&o)[4], float &m,
-                                            float &l, float &lw, int k0, int row, int r0, float c, int r32,
-                                            int hf, int v_row, int v_col) {
-    // ---- S^T = K . Q^T : two 32-key sub-tiles ----
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-        const uint16_t *krow = ks + (kt * 32 + r32) * kPitch + hf * 64;
-#pragma unroll
-        for (int k8 = 0; k8 < 8; ++k8) {
-            const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(krow + k8 * 8));
-            s[kt] = mfma32(kf, qf[k8], s[kt]);
-        }
-    }
-
-    __builtin_amdgcn_s_setprio(0);
-    // ---- online softmax on this lane's row (32 of its 64 scores) ----
-    // element (kt, r) is key k0 + 32*kt + 8*(r/4) + 4*hf + r%4
+// Row maximum of a lane's 16 raw scores (masked keys hold -inf).
+__device__ __forceinline__ float half_max(const f32x16 &s) {
     float mx = neg_inf();
-    if constexpr (DIAG) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                mx = fmaxf(mx, key <= row ? s[kt][r] : neg_inf());
-            }
-    } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    }
-    // Lazy rescale: the running max m (shared by the row's two lanes) moves only when a
-    // score passes it by more than kSlack (log2 units); otherwise p = 2^(s2 - m) <= 2^kSlack
-    // and O and l keep their scale, and no cross-lane step is needed.  A common shift
-    // cancels in O / l (V07 section 3, shift insertion), so the result is the same; the
-    // slack only bounds P and spares the O rescale in almost every tile.  The first tile
-    // always moves m (m = -inf).
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return mx;
+}
+
+// Lazy rescale: the running max m (shared by the row's two lanes) moves only when a
+// score passes it by more than kSlack (log2 units); otherwise p = 2^(s2 - m) <= 2^kSlack,
+// O and l keep their scale, and no cross-lane step is needed.  A common shift cancels in
+// O / l (V07 section 3, shift insertion), so the result is the same; the slack only
+// bounds P and spares the O rescale in almost every step.  The first step always moves m
+// (m = -inf).  mx is the step's raw row max from this lane's half of the row.
+__device__ __forceinline__ void update_max(float mx, float c, float &m, float &l, float &lw,
+                                           f32x16 (&o)[4]) {
     if (__any(mx * c > m + kSlack)) {
         mx = wave_max_xor(mx, 32);
         const float m_new = fmaxf(m, mx * c);
-        const float alpha = exp2_fast(m - m_new);     // 0 on the first tile
+        const float alpha = exp2_fast(m - m_new);     // 0 on the first step
         l *= alpha;
         lw *= alpha;
 #pragma unroll
@@ -145,63 +156,139 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
             for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         m = m_new;
     }
+}
+
+// P = 2^(s * c - m) as the B operand of P.V (a masked score, -inf, gives 0).  k-step kk
+// (16 keys): slot j <-> element r = 8*kk + j, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4.  Two
+// row sums: l of the fp32 P gives the LSE; lw of the bf16-rounded P (the weights the
+// matrix product uses) normalises O, so O is an exact convex combination of them.
+__device__ __forceinline__ void softmax_half(const f32x16 &s, float m, float c,
+                                             bf16x8 (&pf)[2], float &l, float &lw) {
     const float neg_m = -m;
-
-    float p[2][16];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float e = exp2_fast(fmaf(s[kt][r], c, neg_m));
-            if constexpr (DIAG) {
-                const int key = k0 + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                e = key <= row ? e : 0.f;
-            }
-            p[kt][r] = e;
-        }
-
-    // P^T as B operand, k-step kk (16 keys): slot j <-> S^T element r = 8*(kk%2) + j of
-    // sub-tile kk/2, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4.  Two row sums: l of the fp32
-    // P gives the LSE; lw of the bf16-rounded P (the weights the matrix product uses)
-    // normalises O, so O is an exact convex combination of those weights.
-    bf16x8 pf[4];
     float rs = 0.f, rw = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const float *pp = &p[kk >> 1][(kk & 1) * 8];
-        const u32x4 w = {pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
-                         pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7])};
+    for (int kk = 0; kk < 2; ++kk) {
+        float p[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rs += pp[i];
+        for (int j = 0; j < 8; ++j) {
+            p[j] = exp2_fast(fmaf(s[kk * 8 + j], c, neg_m));
+            rs += p[j];
+        }
+        const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
 #pragma unroll
         for (int i = 0; i < 4; ++i) rw = add_bf16_pair(w[i], rw);
         pf[kk] = as_bf16x8(w);
     }
     l += rs;       // this lane's half of the row; the halves are added at the end
     lw += rw;
+}
 
-    // ---- O^T += V^T . P^T ----
-    __builtin_amdgcn_s_setprio(1);
+// O^T += V^T . P^T over 32 keys whose V rows start at LDS byte offset vh.  Each transpose
+// read hands lane l the 4 keys of its slot run at column 32*dt + l%32; two of them make
+// one 8-key operand.
+__device__ __forceinline__ void pv_half(f32x16 (&o)[4], const uint8_t *vh, const uint32_t (&va)[4],
+                                        const bf16x8 (&pf)[2]) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            // lanes of each 16-lane group point at rows 16kk + 4hf + (lane%16)/4 (+8 for
-            // the second half), columns 32dt + 16((lane/16)%2) + 4(lane%4): the transpose
-            // read hands lane l the 4 keys of its slot run at column 32dt + lane%32
-            const uint16_t *vp = vs + (16 * kk + v_row) * kVPitch + dt * 32 + v_col;
-            const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * kVPitch);
+        for (int kk = 0; kk < 2; ++kk) {
+            const uint8_t *vp = vh + va[dt] + kk * 16 * kRowBytes;
+            const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp));
+            const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp + 8 * kRowBytes));
             const u32x4 wv = {lo[0], lo[1], hi[0], hi[1]};
             o[dt] = mfma32(as_bf16x8(wv), pf[kk], o[dt]);
         }
     }
-    __builtin_amdgcn_s_setprio(0);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs a, int n_qb,
+struct WaveCtx {
+    uint8_t *lds;
+    const uint16_t *kbase, *vbase;
+    size_t kv_row;
+    int S, n_kb, n_sub, w, row, hf;
+    float c;
+    uint32_t koff, voff;   // DMA: this lane's byte offset within its 32-row group
+    FragAddr fa;
+};
+
+struct RowState {
+    f32x16 o[4];
+    float m, l, lw, mx;   // mx: raw row max of the next step's scores
+};
+
+// Scores of keys past the lane's row become -inf (their P is then exactly 0).
+__device__ __forceinline__ void mask_half(f32x16 &s, int k0, int row, int hf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = score_key(k0, r, hf) <= row ? s[r] : neg_inf();
+}
+
+// Pipeline step u (keys 32u .. 32u+31) of one wave, whose steps run 0 .. n_sub-1; the
+// last step holds the wave's diagonal, and its scores were masked when they were formed.
+// The step runs its softmax while the matrix cores form the scores of step u+1 (K rows
+// at kn), then its P.V (V rows at vh) while the row max of step u+1 is taken.  Every step
+// runs the same code, the last one included (its scores for a step u+1 are not used).
+__device__ __forceinline__ void half_step(const WaveCtx &x, int u, const f32x16 &s, f32x16 &sn,
+                                          const uint8_t *kn, const uint8_t *vh,
+                                          const uint32_t (&va)[4], const bf16x8 (&qf)[8],
+                                          RowState &st) {
+    if (u >= x.n_sub) return;
+    update_max(st.mx, x.c, st.m, st.l, st.lw, st.o);
+    bf16x8 pf[2];
+    softmax_half(s, st.m, x.c, pf, st.l, st.lw);
+    qk_half(sn, kn, x.fa, qf);
+    pv_half(st.o, vh, va, pf);
+    if (u + 2 == x.n_sub) mask_half(sn, (u + 1) * kHalf, x.row, x.hf);
+    st.mx = half_max(sn);
+    // issue order: each score product with one K fragment read and a share of the
+    // softmax, then each P.V product with its two V reads and a share of the rest
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix core
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // vector ALU
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+}
+
+// One LDS tile kb (KI = kb % 4 names its K buffer; V buffers rotate mod 3 at run time).
+// Start the DMA of K(kb+3) into the K buffer that K(kb-1) has left, run the first
+// pipeline step of tile kb, start the DMA of V(kb+2) into the V buffer V(kb-1) has left
+// (issuing the two apart measured slightly faster than back to back), run the second
+// step (which forms the scores of tile kb+1's first half); then wait for the DMA issued
+// one tile earlier (the data of tile kb+1 and of K(kb+2)) and meet the other waves.
+// Every buffer written here is read two barriers later, and every buffer read here is
+// refilled only after the next barrier.  The DMA is issued on every tile (past the end
+// it only zero-fills a free buffer), so each wave has exactly 2 * kDmaPerTile of them
+// per tile.
+template <int KI>
+__device__ __forceinline__ void tile_step(const WaveCtx &x, int kb, f32x16 &sa, f32x16 &sb,
+                                          const bf16x8 (&qf)[8], RowState &st) {
+    constexpr int kCur = kKBuf + KI * kTileBytes;
+    constexpr int kNext = kKBuf + ((KI + 1) % kNK) * kTileBytes;
+    constexpr int kFree = kKBuf + ((KI + 3) % kNK) * kTileBytes;
+    const int vcur = kVBuf + (kb % kNV) * kTileBytes;
+    dma_tile(x.lds, kFree, x.kbase, x.kv_row, (kb + 3) * kBc, x.S, x.koff, x.w);
+    uint32_t va[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) va[dt] = x.fa.v[dt] + (uint32_t)vcur;
+    half_step(x, 2 * kb, sa, sb, x.lds + kCur + kHalf * kRowBytes, x.lds, va, qf, st);
+    dma_tile(x.lds, kVBuf + ((kb + 2) % kNV) * kTileBytes, x.vbase, x.kv_row, (kb + 2) * kBc,
+             x.S, x.voff, x.w);
+    half_step(x, 2 * kb + 1, sb, sa, x.lds + kNext, x.lds + kHalf * kRowBytes, va, qf, st);
+    // vmcnt(2 * kDmaPerTile): only this tile's DMA may still be in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerTile));
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs a, int n_qb,
                                                                      int remap) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kBc * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t vs_buf[2][kBc * kVPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int G = a.H_q / a.H_kv;
     // ---- workgroup -> (q-block, b, h) ----
@@ -219,20 +306,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
     const int qb = n_qb - 1 - u / a.B;  // heavy (long-prefix) blocks first
     const int h = hk * G + j;
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r32 = lane & 31, hf = lane >> 5;
-    const int v_row = 4 * hf + ((lane & 15) >> 2);          // transpose-read row offset
-    const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int i0 = qb * kBr;
     const int r0 = i0 + w * 32;            // this wave's first query row
     const int row = r0 + r32;              // this lane's query row
     const int last_row = min(i0 + kBr, a.S) - 1;
-    const int n_kb = last_row / kBc + 1;
-    const bool wave_rows = r0 < a.S;
 
-    const size_t kv_row = (size_t)a.H_kv * D;
-    const uint16_t *kbase = a.k + ((size_t)b * a.S * a.H_kv + hk) * D;
-    const uint16_t *vbase = a.v + ((size_t)b * a.S * a.H_kv + hk) * D;
+    WaveCtx x;
+    x.lds = smem;
+    x.kv_row = (size_t)a.H_kv * D;
+    x.kbase = a.k + ((size_t)b * a.S * a.H_kv + hk) * D;
+    x.vbase = a.v + ((size_t)b * a.S * a.H_kv + hk) * D;
+    x.S = a.S;
+    x.n_kb = last_row / kBc + 1;
+    // 32-key steps this wave needs: keys [0, r0 + 32), the last step on its diagonal
+    x.n_sub = r0 < a.S ? r0 / kHalf + 1 : 0;
+    x.w = w;
+    x.row = row;
+    x.hf = hf;
+    // tau * log2(e); a zero scale is replaced by a tiny one so that a masked score
+    // (-inf) still scales to -inf: s * 1e-30 is far below fp32 resolution of the result
+    x.c = fmaxf(a.scale_log2, 1e-30f);
+    {
+        const int lr = 4 * w + lane / 16;   // DMA row within each 32-row group
+        const uint32_t rowb = (uint32_t)(lr * x.kv_row * 2);
+        x.koff = rowb + 16u * (uint32_t)((lane & 15) ^ k_swz(lr));
+        x.voff = rowb + 16u * (uint32_t)((lane & 15) ^ v_swz(lr));
+#pragma unroll
+        for (int k8 = 0; k8 < 8; ++k8)
+            x.fa.k[k8] = (uint32_t)(r32 * kRowBytes + 16 * ((hf * 8 + k8) ^ k_swz(r32)));
+        const int vr = 4 * hf + ((lane & 15) >> 2);             // transpose-read row
+        const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within 64 B
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            x.fa.v[dt] = (uint32_t)(vr * kRowBytes + 16 * ((4 * dt + cc) ^ v_swz(vr)) +
+                                    8 * (lane & 1));
+    }
 
     // Q^T fragments: column = query row, k-slots (hf, j) <-> d = 64*hf + 8*ks + j
     bf16x8 qf[8];
@@ -243,47 +354,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
         for (int k8 = 0; k8 < 8; ++k8) qf[k8] = as_bf16x8(load16(qrow + k8 * 8));
     }
 
-    f32x16 o[4];
+    RowState st;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m = neg_inf(), l = 0.f, lw = 0.f;
-    const float c = a.scale_log2;
+        for (int r = 0; r < 16; ++r) st.o[dt][r] = 0.f;
+    st.m = neg_inf();
+    st.l = 0.f;
+    st.lw = 0.f;
+    st.mx = neg_inf();
+    f32x16 sa, sb;
 
-    // K/V tiles go through two LDS buffers: tile kb+1 is stored while tile kb is being
-    // computed from the other buffer, and the loads of tile kb+2 are in flight meanwhile,
-    // so one barrier per tile separates the writers of a buffer from its readers.
-    uint32_t row_off[kLoads];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-        row_off[i] = (uint32_t)((i * 16 + threadIdx.x / 16) * kv_row + (threadIdx.x % 16) * 8);
-    Stage stage;
-    load_stage(stage, kbase, vbase, kv_row, row_off, 0, a.S);
-    store_stage(stage, ks_buf[0], vs_buf[0]);
-    if (n_kb > 1) load_stage(stage, kbase, vbase, kv_row, row_off, kBc, a.S);
+    // prologue: K(0..2) and V(0..1) into LDS, then the scores of the first step
+    for (int t = 0; t < 3; ++t)
+        dma_tile(smem, kKBuf + t * kTileBytes, x.kbase, x.kv_row, t * kBc, a.S, x.koff, w);
+    for (int t = 0; t < 2; ++t)
+        dma_tile(smem, kVBuf + t * kTileBytes, x.vbase, x.kv_row, t * kBc, a.S, x.voff, w);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    for (int kb = 0; kb < n_kb; ++kb) {
-        const int k0 = kb * kBc;
-        const uint16_t *ks = ks_buf[kb & 1];
-        const uint16_t *vs = vs_buf[kb & 1];
-        if (wave_rows && k0 <= r0 + 31) {   // else: tile wholly in this wave's future
-            if (k0 + kBc - 1 > r0)           // crosses this wave's diagonal
-                attend_tile<true>(ks, vs, qf, o, m, l, lw, k0, row, r0, c, r32, hf, v_row, v_col);
-            else
-                attend_tile<false>(ks, vs, qf, o, m, l, lw, k0, row, r0, c, r32, hf, v_row, v_col);
-        }
-        if (kb + 1 < n_kb) {
-            store_stage(stage, ks_buf[(kb + 1) & 1], vs_buf[(kb + 1) & 1]);
-            if (kb + 2 < n_kb) load_stage(stage, kbase, vbase, kv_row, row_off, k0 + 2 * kBc, a.S);
-        }
-        __syncthreads();
+    if (x.n_sub > 0) {
+        qk_half(sa, smem + kKBuf, x.fa, qf);
+        if (x.n_sub == 1) mask_half(sa, 0, row, hf);
+        st.mx = half_max(sa);
     }
-    // ---- epilogue: O = O^T / l -> bf16, LSE = ln2 * (m + log2 l) ----
-    l += __shfl_xor(l, 32);
-    lw += __shfl_xor(lw, 32);
-    if (!wave_rows || row >= a.S) return;
+
+    int kb = 0;
+    for (; kb + 3 < x.n_kb; kb += 4) {
+        tile_step<0>(x, kb, sa, sb, qf, st);
+        tile_step<1>(x, kb + 1, sa, sb, qf, st);
+        tile_step<2>(x, kb + 2, sa, sb, qf, st);
+        tile_step<3>(x, kb + 3, sa, sb, qf, st);
+    }
+    if (kb < x.n_kb) tile_step<0>(x, kb, sa, sb, qf, st);
+    if (kb + 1 < x.n_kb) tile_step<1>(x, kb + 1, sa, sb, qf, st);
+    if (kb + 2 < x.n_kb) tile_step<2>(x, kb + 2, sa, sb, qf, st);
+    __builtin_amdgcn_s_waitcnt(0);   // no DMA left in flight at exit
+
+    // ---- epilogue: O = O^T / lw -> bf16, LSE = ln2 * (m + log2 l) ----
+    const float l = st.l + __shfl_xor(st.l, 32);
+    const float lw = st.lw + __shfl_xor(st.lw, 32);
+    if (row >= a.S) return;
     const float inv = 1.f / lw;
     uint16_t *orow = a.o + (((size_t)b * a.S + row) * a.H_q + h) * D;
 #pragma unroll
@@ -293,10 +403,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_causal_kernel(PrefillArgs
             const int d = dt * 32 + rq * 8 + hf * 4;
             const int r = rq * 4;
             *reinterpret_cast<u32x2 *>(orow + d) =
-                u32x2{pack_bf16x2(o[dt][r] * inv, o[dt][r + 1] * inv),
-                      pack_bf16x2(o[dt][r + 2] * inv, o[dt][r + 3] * inv)};
+                u32x2{pack_bf16x2(st.o[dt][r] * inv, st.o[dt][r + 1] * inv),
+                      pack_bf16x2(st.o[dt][r + 2] * inv, st.o[dt][r + 3] * inv)};
         }
-    if (hf == 0) a.lse[((size_t)b * a.H_q + h) * a.S + row] = kLn2 * (m + __builtin_log2f(l));
+    if (hf == 0) a.lse[((size_t)b * a.H_q + h) * a.S + row] = kLn2 * (st.m + __builtin_log2f(l));
 }
 
 }  // namespace
