@@ -55,9 +55,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("8da4c10e9057bd54", 146_646_682),
-    "lse_merge": ("7545ad904d1f4ad9", 8_630_739),
-    "prefill_causal": ("2fd4a609aa138e99", 416_799_900),
+    "decode_split": ("243b6eb04cc08272", 143_295_866),
+    "lse_merge": ("b9c1048188cb8ec4", 9_540_201),
+    "prefill_causal": ("9817723fdbd09895", 421_950_158),
 }
 
 
