@@ -28,6 +28,8 @@ SMALL = [
     (1, 63, 4, 4),        # G = 1 (MHA), shorter than one key tile
     (1, 384, 8, 1),       # MQA, three q-blocks
     (1, 520, 16, 2),      # G = 8 with the XCD remap active, ragged tail
+    (2, 700, 16, 2),      # three 256-row q-blocks per head, ragged, B = 2 (remap active)
+    (1, 1000, 8, 8),      # MHA at four q-blocks with a ragged last key tile
 ]
 
 
@@ -50,7 +52,10 @@ def sample_rows(S, H_q, B, rng, n_random, extra_rows=()):
     """A stratified set of (b, h, i): first and last rows, q-block edges, random rows."""
     rows = set()
     heads = sorted({0, H_q - 1, *rng.integers(0, H_q, size=6).tolist()})
-    edges = [i for qb in range(0, S, 1024) for i in (qb - 1, qb, qb + 63, qb + 64, qb + 127)
+    # q-block (256 rows), key-tile (64) and pipeline-step (32) edges near every 1024th row
+    edges = [i for qb in range(0, S, 1024)
+             for i in (qb - 1, qb, qb + 31, qb + 32, qb + 63, qb + 64, qb + 127, qb + 128,
+                       qb + 255, qb + 256)
              if 0 <= i < S]
     fixed = list(range(0, 16)) + list(range(S - 16, S)) + edges + list(extra_rows)
     for b in range(B):
