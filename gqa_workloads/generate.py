@@ -11,13 +11,16 @@ tensor's values.
 
 Layouts (row-major, innermost last):
   decode  q [B, H_q, d];      k, v [B, S_max, H_kv, d];  seqlens int32 [B]
+  paged   q [B, H_q, d];      k_pool, v_pool [num_pages, page_size, H_kv, d];
+          block_table int32 [B, max_blocks];  seqlens int32 [B]
   prefill q [B, S, H_q, d];   k, v [B, S, H_kv, d]
+  chunk   q [B, T, H_q, d];   k, v [B, S_kv, H_kv, d]
 """
 import numpy as np
 
 BF16_QUIET_NAN = np.uint16(0x7FC0)
 
-_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_LEN, _STREAM_OUTLIER = range(5)
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_LEN, _STREAM_OUTLIER, _STREAM_PAGES = range(6)
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
@@ -37,8 +40,9 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
 
 
 def _streams(seed: int):
+    # child i of the seed sequence depends only on i, so adding streams shifts none
     return [np.random.Generator(np.random.PCG64(s))
-            for s in np.random.SeedSequence(seed).spawn(5)]
+            for s in np.random.SeedSequence(seed).spawn(6)]
 
 
 def _normal_bf16(rng, shape, chunk_rows: int = 1 << 22) -> np.ndarray:
@@ -62,7 +66,7 @@ def decode_inputs(B, H_q, H_kv, d, S_max=None, seed=0, ragged=None, nan_fill=Tru
     read them would produce NaN.  Without ``ragged`` every length is ``S_max``.
     Returns a dict with q, k, v (uint16 bf16 bits), seqlens (int32) and S_max.
     """
-    rq, rk, rv, rlen, _ = _streams(seed)
+    rq, rk, rv, rlen = _streams(seed)[:4]
     if ragged is not None:
         lo, hi = ragged
         seqlens = rlen.integers(lo, hi, endpoint=True, size=B).astype(np.int32)
@@ -85,6 +89,63 @@ def decode_inputs(B, H_q, H_kv, d, S_max=None, seed=0, ragged=None, nan_fill=Tru
     return {"q": q, "k": k, "v": v, "seqlens": seqlens, "S_max": S_max}
 
 
+def paged_decode_inputs(B, H_q, H_kv, d, page_size, S_max=None, seed=0, ragged=None,
+                        spare_pages=3, nan_fill=True):
+    """Inputs of one decode launch over a paged K/V cache.
+
+    Lengths, Q and the K/V rows of every sequence are the same values that
+    ``decode_inputs`` draws for the same arguments; the rows are then scattered
+    into pages of ``page_size`` tokens (token t of sequence b goes to row
+    t % page_size of page block_table[b, t // page_size]) placed at randomly
+    permuted positions of a pool that also holds ``spare_pages`` pages no table
+    references.  Pool rows that hold no token carry a bf16 NaN (``nan_fill``),
+    and table entries past a sequence's last block are -1, so a kernel that read
+    either would show it.  Returns q, k_pool, v_pool, block_table, seqlens,
+    page_size and S_max (= max_blocks * page_size, the table's key capacity).
+    """
+    rq, rk, rv, rlen = _streams(seed)[:4]
+    rpage = _streams(seed)[_STREAM_PAGES]
+    if ragged is not None:
+        lo, hi = ragged
+        seqlens = rlen.integers(lo, hi, endpoint=True, size=B).astype(np.int32)
+    else:
+        if S_max is None:
+            raise ValueError("S_max is required without ragged lengths")
+        seqlens = np.full(B, S_max, dtype=np.int32)
+    blocks = [-(-int(n) // page_size) for n in seqlens]
+    max_blocks = max(max(blocks), 1)
+    num_pages = sum(blocks) + spare_pages
+    order = rpage.permutation(num_pages).astype(np.int32)
+    fill = BF16_QUIET_NAN if nan_fill else np.uint16(0)
+    q = _normal_bf16(rq, (B, H_q, d))
+    k_pool = np.full((num_pages, page_size, H_kv, d), fill, dtype=np.uint16)
+    v_pool = np.full((num_pages, page_size, H_kv, d), fill, dtype=np.uint16)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    used = 0
+    for b in range(B):
+        n = int(seqlens[b])
+        kb = _normal_bf16(rk, (n, H_kv, d))
+        vb = _normal_bf16(rv, (n, H_kv, d))
+        for i in range(blocks[b]):
+            page = int(order[used])
+            used += 1
+            table[b, i] = page
+            rows = min(page_size, n - i * page_size)
+            k_pool[page, :rows] = kb[i * page_size:i * page_size + rows]
+            v_pool[page, :rows] = vb[i * page_size:i * page_size + rows]
+    return {"q": q, "k_pool": k_pool, "v_pool": v_pool, "block_table": table,
+            "seqlens": seqlens, "page_size": page_size, "S_max": max_blocks * page_size}
+
+
+def chunk_inputs(B, T, S_kv, H_q, H_kv, d, seed=0):
+    """Inputs of one chunked-prefill launch: T query rows against S_kv cached keys."""
+    rq, rk, rv = _streams(seed)[:3]
+    q = _normal_bf16(rq, (B, T, H_q, d))
+    k = _normal_bf16(rk, (B, S_kv, H_kv, d))
+    v = _normal_bf16(rv, (B, S_kv, H_kv, d))
+    return {"q": q, "k": k, "v": v}
+
+
 def prefill_inputs(B, S, H_q, H_kv, d, seed=0, outlier_frac=0.0, outlier_scale=1.0):
     """Inputs of one causal prefill launch.
 
@@ -94,7 +155,7 @@ def prefill_inputs(B, S, H_q, H_kv, d, seed=0, outlier_frac=0.0, outlier_scale=1
     values exact).  V is never scaled.  Returns q, k, v (uint16 bits) and the
     boolean outlier mask [B, S, H_kv].
     """
-    rq, rk, rv, _, rout = _streams(seed)
+    rq, rk, rv, _, rout = _streams(seed)[:5]
     q = _normal_bf16(rq, (B, S, H_q, d))
     k = _normal_bf16(rk, (B, S, H_kv, d))
     v = _normal_bf16(rv, (B, S, H_kv, d))

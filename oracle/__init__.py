@@ -47,6 +47,9 @@ def _bind(lib):
     lib.oracle_prefill_causal_rows.argtypes = [u16p, u16p, u16p, f64p, f64p,
                                                ci, ci, ci, ci, ci, cd, i32p, cl, ci]
     lib.oracle_prefill_causal_rows.restype = ci
+    lib.oracle_prefill_chunk_rows.argtypes = [u16p, u16p, u16p, f64p, f64p,
+                                              ci, ci, ci, ci, ci, ci, ci, cd, i32p, cl, ci]
+    lib.oracle_prefill_chunk_rows.restype = ci
     lib.oracle_decode_partial.argtypes = [u16p, u16p, u16p, f64p, f64p, f64p,
                                           ci, ci, ci, ci, ci, cd, ci, ci, ci]
     lib.oracle_decode_partial.restype = ci
@@ -125,6 +128,70 @@ def prefill_causal(q, k, v, tau=None, nthreads=0, lib=None):
     o, lse = prefill_causal_rows(q, k, v, rows, tau=tau, nthreads=nthreads, lib=lib)
     o = o.reshape(B, H_q, S, d).transpose(0, 2, 1, 3).copy()
     return o, lse.reshape(B, H_q, S)
+
+
+def prefill_chunk_rows(q, k, v, rows, q_start=None, tau=None, nthreads=0, lib=None):
+    """Causal attention of a chunk of T query rows against S_kv cached keys, on selected rows.
+
+    q [B, T, H_q, d]; k, v [B, S_kv, H_kv, d]; rows int array [n, 3] of (b, h, i).
+    Query row i is token q_start + i and sees keys j <= q_start + i; ``q_start``
+    defaults to S_kv - T (the chunk is the last T tokens: bottom-right alignment).
+    Returns (o [n, d], lse [n]) in float64.
+    """
+    lib = lib or load()
+    B, T, H_q, d = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    q_start = S_kv - T if q_start is None else int(q_start)
+    tau = 1.0 / np.sqrt(d) if tau is None else float(tau)
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 3)
+    n = rows.shape[0]
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_prefill_chunk_rows(_u16(q), _u16(k), _u16(v), o, lse, B, T, q_start, S_kv,
+                                       H_q, H_kv, d, tau, rows, n, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_chunk_rows rejected its arguments (code {rc})")
+    return o, lse
+
+
+def prefill_chunk(q, k, v, q_start=None, tau=None, nthreads=0, lib=None):
+    """Chunked causal prefill on every row: returns (o [B, T, H_q, d], lse [B, H_q, T])."""
+    B, T, H_q, d = q.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H_q), np.arange(T), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
+    o, lse = prefill_chunk_rows(q, k, v, rows, q_start=q_start, tau=tau, nthreads=nthreads,
+                                lib=lib)
+    o = o.reshape(B, H_q, T, d).transpose(0, 2, 1, 3).copy()
+    return o, lse.reshape(B, H_q, T)
+
+
+def gather_pages(pool, block_table, seqlens, page_size):
+    """The cache of every sequence in logical token order, read out of a paged pool.
+
+    pool [num_pages, page_size, H_kv, d]; block_table int32 [B, max_blocks];
+    seqlens int32 [B].  Token t of sequence b is row t % page_size of page
+    block_table[b, t // page_size] ("Attention Kernel lineage" (V07), section 16,
+    logical-token-to-page map).  Returns [B, max_blocks * page_size, H_kv, d]
+    with the rows past each sequence's length left zero.
+    """
+    B, max_blocks = block_table.shape
+    out = np.zeros((B, max_blocks * page_size) + pool.shape[2:], dtype=pool.dtype)
+    for b in range(B):
+        t = np.arange(int(seqlens[b]))
+        pages = block_table[b, t // page_size]
+        if np.any((pages < 0) | (pages >= pool.shape[0])):
+            raise ValueError(f"sequence {b}: a live block maps outside the pool")
+        out[b, :t.size] = pool[pages, t % page_size]
+    return out
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seqlens, page_size, tau=None, nthreads=0,
+                 lib=None):
+    """Decode over a paged K/V cache: gather each sequence's keys through its block
+    table (``gather_pages``), then the plain decode definition.  Returns (o, lse)."""
+    k = gather_pages(k_pool, block_table, seqlens, page_size)
+    v = gather_pages(v_pool, block_table, seqlens, page_size)
+    return decode(q, k, v, seqlens, tau=tau, nthreads=nthreads, lib=lib)
 
 
 def decode_partial(q, k, v, j0, j1, tau=None, nthreads=0, lib=None):

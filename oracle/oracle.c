@@ -22,7 +22,14 @@
  * Visible keys: decode (one query token) sees keys [0, seqlen); the decode
  * step is a pure read of the cache with no mask but the sequence end (ADR-0060
  * "AHBM GQA Fused Attention", sections 0.5.1 and 5.2).  Causal prefill row i
- * sees keys j <= i (V07 section 12, causal definition).
+ * sees keys j <= i (V07 section 12, causal definition).  A prefill chunk is
+ * T query rows that are the tokens q_start .. q_start + T - 1 of the sequence
+ * (ADR-0060 section 0.5.2: T_q is the chunk width, the launch carries the
+ * block's q_start and T_q; section 5.4: the query block [q_start, q_start + T)
+ * against the cached keys), so its row i sees keys j <= q_start + i.  Keys at
+ * or past q_start + T are never visible.  With the chunk at the end of the
+ * cache (q_start = S_kv - T) this is the bottom-right aligned causal mask;
+ * q_start = 0, T = S_kv is plain causal prefill.
  *
  * All bf16 inputs are widened exactly to double; every product and sum is in
  * double.  A row with no visible key gives o = 0 and lse = -inf (the identity
@@ -178,15 +185,16 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 }
 
 /* ------------------------------------------------------------------------- */
-/* Causal prefill on selected rows.
- * q [B, S, H_q, d]; k, v [B, S, H_kv, d]; rows: nrows triples (b, h, i).
+/* Causal prefill of a chunk, on selected rows.
+ * q [B, T, H_q, d]; k, v [B, S_kv, H_kv, d]; rows: nrows triples (b, h, i), 0 <= i < T;
+ * query row i is token q_start + i, and q_start + T <= S_kv.
  * o [nrows, d] (double), lse [nrows] (double). */
 
 struct prefill_ctx {
     const uint16_t *q, *k, *v;
     const int32_t *rows;
     double *o, *lse;
-    int B, S, H_q, H_kv, d;
+    int B, T, q_start, S_kv, H_q, H_kv, d;
     double tau;
 };
 
@@ -196,25 +204,37 @@ static void prefill_row(void *p, long r, double *s, double *qd)
     int b = c->rows[3 * r], h = c->rows[3 * r + 1], i = c->rows[3 * r + 2];
     int G = c->H_q / c->H_kv;
     int g = h / G;
-    const uint16_t *qrow = c->q + (((size_t)b * c->S + i) * c->H_q + h) * c->d;
-    const uint16_t *k0 = c->k + ((size_t)b * c->S * c->H_kv + g) * c->d;
-    const uint16_t *v0 = c->v + ((size_t)b * c->S * c->H_kv + g) * c->d;
-    /* causal: keys 0..i inclusive */
-    attend_row(qrow, k0, v0, (size_t)c->H_kv * c->d, i + 1, c->d, c->tau, s, qd,
+    const uint16_t *qrow = c->q + (((size_t)b * c->T + i) * c->H_q + h) * c->d;
+    const uint16_t *k0 = c->k + ((size_t)b * c->S_kv * c->H_kv + g) * c->d;
+    const uint16_t *v0 = c->v + ((size_t)b * c->S_kv * c->H_kv + g) * c->d;
+    /* row i is token q_start + i: causal, keys 0 .. q_start + i inclusive */
+    int pos = c->q_start + i;
+    attend_row(qrow, k0, v0, (size_t)c->H_kv * c->d, pos + 1, c->d, c->tau, s, qd,
                c->o + (size_t)r * c->d, c->lse + r);
 }
 
+int oracle_prefill_chunk_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              double *o, double *lse, int B, int T, int q_start, int S_kv,
+                              int H_q, int H_kv, int d, double tau, const int32_t *rows,
+                              long nrows, int nthreads)
+{
+    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
+    if (T <= 0 || q_start < 0 || q_start > S_kv - T) return -3;
+    for (long r = 0; r < nrows; ++r) {
+        int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H_q || i < 0 || i >= T) return -2;
+    }
+    struct prefill_ctx c = {q, k, v, rows, o, lse, B, T, q_start, S_kv, H_q, H_kv, d, tau};
+    return run_rows(prefill_row, &c, nrows, nthreads, S_kv, d);
+}
+
+/* Whole-prompt causal prefill: the chunk that is the whole sequence (q_start = 0, T = S). */
 int oracle_prefill_causal_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                double *o, double *lse, int B, int S, int H_q, int H_kv, int d,
                                double tau, const int32_t *rows, long nrows, int nthreads)
 {
-    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
-    for (long r = 0; r < nrows; ++r) {
-        int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
-        if (b < 0 || b >= B || h < 0 || h >= H_q || i < 0 || i >= S) return -2;
-    }
-    struct prefill_ctx c = {q, k, v, rows, o, lse, B, S, H_q, H_kv, d, tau};
-    return run_rows(prefill_row, &c, nrows, nthreads, S, d);
+    return oracle_prefill_chunk_rows(q, k, v, o, lse, B, S, 0, S, H_q, H_kv, d, tau, rows, nrows,
+                                     nthreads);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -7,14 +7,16 @@ and logsumexp, ``math.fsum``).  ``test_oracle_pins.py`` runs them on the real
 oracle; ``test_oracle_mutants.py`` runs them on copies of ``oracle.c`` with a
 planted mistake and requires that some pin fails for every such mistake.
 """
+import json
 import math
+import os
 
 import numpy as np
 from scipy.special import logsumexp, softmax
 
 import oracle
-from gqa_workloads.generate import bf16_bits_from_f32, decode_inputs, f32_from_bf16_bits, \
-    prefill_inputs
+from gqa_workloads.generate import bf16_bits_from_f32, chunk_inputs, decode_inputs, \
+    f32_from_bf16_bits, paged_decode_inputs, prefill_inputs
 
 BF16_ONE = 0x3F80
 
@@ -316,6 +318,134 @@ def pin_prefill_row_equals_decode(lib):
     for r, (_, h, i) in enumerate(rows):
         od, ld = oracle.decode(q[:, i].copy(), k, v, np.array([i + 1], dtype=np.int32), lib=lib)
         assert np.array_equal(o[r], od[0, h]) and lse[r] == ld[0, h]
+
+
+# ---------------------------------------------------------------------------
+# Chunked causal prefill (ADR-0060 sections 0.5.2 and 5.4: a query block of T_q
+# rows starting at q_start against the cached keys; V07 section 12: causal).
+
+def pin_chunk_whole_prompt_is_causal_prefill(lib):
+    inp = prefill_inputs(2, 11, 4, 2, 16, seed=27)
+    o, lse = oracle.prefill_causal(inp["q"], inp["k"], inp["v"], lib=lib)
+    oc, lc = oracle.prefill_chunk(inp["q"], inp["k"], inp["v"], q_start=0, lib=lib)
+    assert np.array_equal(o, oc) and np.array_equal(lse, lc)
+
+
+def pin_chunk_rows_are_rows_of_full_prefill(lib):
+    """Running a prompt's rows [q_start, q_start + T) as one chunk against the whole
+    cache gives exactly those rows of the whole-prompt causal prefill, wherever the
+    chunk sits; cache rows past the chunk's last token are never visible."""
+    B, S, H_q, H_kv, d = 2, 23, 4, 2, 16
+    inp = prefill_inputs(B, S, H_q, H_kv, d, seed=28)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = oracle.prefill_causal(q, k, v, lib=lib)
+    for q_start, T in ((0, 5), (7, 9), (15, 8), (22, 1)):
+        qc = q[:, q_start:q_start + T].copy()
+        # the cache past the chunk's end holds NaN: a read of it would show
+        kc, vc = k.copy(), v.copy()
+        kc[:, q_start + T:] = 0x7FC0
+        vc[:, q_start + T:] = 0x7FC0
+        oc, lc = oracle.prefill_chunk(qc, kc, vc, q_start=q_start, lib=lib)
+        assert np.array_equal(oc, o[:, q_start:q_start + T])
+        assert np.array_equal(lc, lse[..., q_start:q_start + T])
+        # the default alignment is bottom-right: the chunk is the cache's last T tokens
+        ob, lb = oracle.prefill_chunk(qc, k[:, :q_start + T].copy(), v[:, :q_start + T].copy(),
+                                      lib=lib)
+        assert np.array_equal(ob, oc) and np.array_equal(lb, lc)
+
+
+def pin_chunk_single_row_is_decode(lib):
+    B, S, H_q, H_kv, d = 2, 19, 8, 2, 32
+    inp = prefill_inputs(B, S, H_q, H_kv, d, seed=29)
+    q1 = inp["q"][:, -1:].copy()
+    oc, lc = oracle.prefill_chunk(q1, inp["k"], inp["v"], lib=lib)
+    od, ld = oracle.decode(q1[:, 0].copy(), inp["k"], inp["v"], lib=lib)
+    assert np.array_equal(oc[:, 0], od) and np.array_equal(lc[..., 0], ld)
+
+
+def pin_brute_force_chunk(lib):
+    B, T, S_kv, H_q, H_kv, d = 1, 4, 10, 4, 2, 8
+    inp = chunk_inputs(B, T, S_kv, H_q, H_kv, d, seed=30)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    for q_start in (6, 3):
+        o, lse = oracle.prefill_chunk(q, k, v, q_start=q_start, lib=lib)
+        for h in range(H_q):
+            g = h // 2
+            for i in range(T):
+                n = q_start + i + 1
+                ob, lb = _brute_row(_f64(q[0, i, h]), _f64(k[0, :n, g]), _f64(v[0, :n, g]),
+                                    1.0 / math.sqrt(d))
+                _rel_close(o[0, i, h], ob, 1e-12, 1e-14)
+                assert abs(lse[0, h, i] - lb) <= 1e-13 * max(1.0, abs(lb))
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache (V07 section 16: token t of a request is row t mod B_p of page
+# block_table[req][t div B_p]; section 17: the decode kernel reads through it).
+
+def pin_paged_equals_contiguous(lib):
+    """A paged cache holding the same token rows, in randomly permuted pages with
+    NaN in every unused slot and -1 past each table's last block, gives exactly the
+    contiguous result, for page sizes that do and do not divide the lengths."""
+    for page in (16, 32, 48):
+        a = decode_inputs(3, 8, 2, 32, ragged=(1, 90), seed=31)
+        p = paged_decode_inputs(3, 8, 2, 32, page, ragged=(1, 90), seed=31)
+        o, lse = oracle.decode(a["q"], a["k"], a["v"], a["seqlens"], lib=lib)
+        op, lp = oracle.decode_paged(p["q"], p["k_pool"], p["v_pool"], p["block_table"],
+                                     p["seqlens"], page, lib=lib)
+        assert np.array_equal(o, op) and np.array_equal(lse, lp)
+
+
+def pin_paged_identity_table(lib):
+    """Pages laid out in order (table[b][i] = b * blocks + i) are the contiguous cache."""
+    B, S, H_kv, d, page = 2, 64, 2, 16, 16
+    inp = decode_inputs(B, 4, H_kv, d, S_max=S, seed=32)
+    nb = S // page
+    pool_k = inp["k"].reshape(B * nb, page, H_kv, d)
+    pool_v = inp["v"].reshape(B * nb, page, H_kv, d)
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    sl = np.array([S, 37], dtype=np.int32)
+    o, lse = oracle.decode(inp["q"], inp["k"], inp["v"], sl, lib=lib)
+    op, lp = oracle.decode_paged(inp["q"], pool_k, pool_v, table, sl, page, lib=lib)
+    assert np.array_equal(o, op) and np.array_equal(lse, lp)
+
+
+def pin_paged_worked_example(lib):
+    """The block tables the pages draw: requests A and B share their first two pages,
+    so over those pages (and equal queries) they attend to the same keys; one token
+    further, A reads p5 and B reads p2.  Each request's keys are also its pages' rows
+    concatenated in table order."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "paged_block_table_example.json")))
+    page, H_kv, d = 4, 1, 16
+    rng = np.random.default_rng(33)
+    pool_k = bf16_bits_from_f32(rng.standard_normal((g["pool_pages"], page, H_kv, d),
+                                                    dtype=np.float32))
+    pool_v = bf16_bits_from_f32(rng.standard_normal((g["pool_pages"], page, H_kv, d),
+                                                    dtype=np.float32))
+    names = sorted(g["tables"])
+    width = max(len(t) for t in g["tables"].values())
+    table = np.full((len(names), width), -1, dtype=np.int32)
+    for r, n in enumerate(names):
+        table[r, :len(g["tables"][n])] = g["tables"][n]
+    q1 = bf16_bits_from_f32(rng.standard_normal((1, 2, d), dtype=np.float32))
+    q = np.repeat(q1, len(names), axis=0)
+    shared = g["shared_prefix_pages"] * page
+    a, b = names.index("A"), names.index("B")
+    sl = np.array([len(g["tables"][n]) * page for n in names], dtype=np.int32)
+    sl[a] = sl[b] = shared
+    o, lse = oracle.decode_paged(q, pool_k, pool_v, table, sl, page, lib=lib)
+    assert np.array_equal(o[a], o[b]) and np.array_equal(lse[a], lse[b])
+    sl[a] = sl[b] = shared + 1
+    o, lse = oracle.decode_paged(q, pool_k, pool_v, table, sl, page, lib=lib)
+    assert not np.allclose(o[a], o[b])
+    sl = np.array([len(g["tables"][n]) * page for n in names], dtype=np.int32)
+    o, lse = oracle.decode_paged(q, pool_k, pool_v, table, sl, page, lib=lib)
+    for r, n in enumerate(names):
+        kc = np.concatenate([pool_k[p] for p in g["tables"][n]])[None]
+        vc = np.concatenate([pool_v[p] for p in g["tables"][n]])[None]
+        oc, lc = oracle.decode(q[r:r + 1], kc, vc, lib=lib)
+        assert np.array_equal(oc[0], o[r]) and np.array_equal(lc[0], lse[r])
 
 
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

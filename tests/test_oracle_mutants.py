@@ -8,6 +8,7 @@ if none does, the pins do not constrain that part of the oracle.
 """
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -23,8 +24,13 @@ MUTANTS = {
     "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
     "scores_from_v": ("const uint16_t *kj = k + (size_t)j * kv_stride;",
                       "const uint16_t *kj = v + (size_t)j * kv_stride;"),
-    "causal_excludes_diagonal": ("i + 1, c->d, c->tau", "i, c->d, c->tau"),
-    "causal_one_extra_key": ("i + 1, c->d, c->tau", "(i + 2 < c->S ? i + 2 : c->S), c->d, c->tau"),
+    "causal_excludes_diagonal": ("pos + 1, c->d, c->tau", "pos, c->d, c->tau"),
+    "causal_one_extra_key": ("pos + 1, c->d, c->tau",
+                             "(pos + 2 < c->S_kv ? pos + 2 : c->S_kv), c->d, c->tau"),
+    "chunk_start_ignored": ("int pos = c->q_start + i;", "int pos = i;"),
+    "chunk_aligned_to_cache_end": ("int pos = c->q_start + i;", "int pos = c->S_kv - c->T + i;"),
+    "chunk_q_stride_from_keys": ("(((size_t)b * c->T + i) * c->H_q + h)",
+                                 "(((size_t)b * c->S_kv + i) * c->H_q + h)"),
     "kv_row_stride_wrong": ("attend_row(c->q + (size_t)r * c->d, k0, v0, (size_t)c->H_kv * c->d",
                             "attend_row(c->q + (size_t)r * c->d, k0, v0, (size_t)c->d"),
     "max_pass_min": ("        if (s[j] > m) m = s[j];\n    /* pass 2",
@@ -56,3 +62,36 @@ def test_planted_mistake_is_caught(name, tmp_path):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"no pin detects the planted mistake {name}"
+
+
+# Planted mistakes in the paged-cache gather (Python): the token-to-page map of
+# V07 section 16 with a swapped or shifted index must also fail a pin.
+def _gather_variant(kind):
+    def gather(pool, block_table, seqlens, page_size):
+        B, max_blocks = block_table.shape
+        out = np.zeros((B, max_blocks * page_size) + pool.shape[2:], dtype=pool.dtype)
+        for b in range(B):
+            t = np.arange(int(seqlens[b]))
+            if kind == "swapped":
+                blk, row = t % page_size % max_blocks, t // page_size % page_size
+            elif kind == "row_shift":
+                blk, row = t // page_size, (t + 1) % page_size
+            else:   # "table_of_first_sequence"
+                blk, row = t // page_size, t % page_size
+                out[b, :t.size] = pool[np.maximum(block_table[0, blk], 0), row]
+                continue
+            out[b, :t.size] = pool[np.maximum(block_table[b, blk], 0), row]
+        return out
+    return gather
+
+
+@pytest.mark.parametrize("kind", ["swapped", "row_shift", "table_of_first_sequence"])
+def test_planted_gather_mistake_is_caught(kind, monkeypatch, oracle_lib):
+    monkeypatch.setattr(oracle, "gather_pages", _gather_variant(kind))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(oracle_lib)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects the gather mistake {kind}"
