@@ -61,6 +61,9 @@ def load_library(path=LIBRARY):
     L.gqa_decode_partials.restype = ci
     L.gqa_decode_combine.argtypes = [i32p, vp, f32p, ci, ci, ci, ci, ci, ci, vp, cs, vp]
     L.gqa_decode_combine.restype = ci
+    L.gqa_attn_decode_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci, ci,
+                                        ci, cf, ci, vp, cs, vp]
+    L.gqa_attn_decode_paged.restype = ci
     L.gqa_lse_merge.argtypes = [f32p, f32p, f32p, i32p, ci, vp, f32p, ci, ci, ci, vp]
     L.gqa_lse_merge.restype = ci
     L.gqa_attn_prefill_causal.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, cf, vp]
@@ -155,6 +158,35 @@ def decode(q, k_cache, v_cache, seqlens=None, softmax_scale=None, num_splits=0, 
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(l), B, H_q, H_kv, d,
         S_max, _scale(d, softmax_scale), num_splits, _ptr(workspace), workspace.numel(),
         _stream(q.device)))
+    return o, l
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seqlens=None, softmax_scale=None, num_splits=0,
+                 out=None, lse=None, workspace=None):
+    """Split-KV GQA decode over a paged cache: q [B,H_q,d]; pools [num_pages,page,H_kv,d] bf16;
+    block_table [B,max_blocks] int32 -> (o [B,H_q,d], lse [B,H_q])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pool, "k_pool", torch.bfloat16, 4)
+    _need(v_pool, "v_pool", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    B, H_q, d = q.shape
+    num_pages, page, H_kv, dk = k_pool.shape
+    if dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, pools {tuple(k_pool.shape)} / "
+                         f"{tuple(v_pool.shape)}, block_table {tuple(block_table.shape)}")
+    max_blocks = block_table.shape[1]
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, 1)
+        if seqlens.shape[0] != B:
+            raise ValueError("seqlens must have B entries")
+    if workspace is None:
+        workspace = decode_workspace(B, H_q, H_kv, d, max_blocks * page, num_splits, q.device)
+    o = torch.empty((B, H_q, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, H_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(load_library().gqa_attn_decode_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seqlens), _ptr(o), _ptr(l),
+        B, H_q, H_kv, d, page, num_pages, max_blocks, _scale(d, softmax_scale), num_splits,
+        _ptr(workspace), workspace.numel(), _stream(q.device)))
     return o, l
 
 

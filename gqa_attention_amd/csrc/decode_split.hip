@@ -65,17 +65,16 @@ struct TileOffsets {
     uint32_t v[DecodeTraits<D>::NVI];         // V: row i*RPI + lane/LPR, 16 B at lane%LPR
 };
 
-// Load the tile of keys key0..key0+15 of one KV head (kbase/vbase: that head's slice of
-// key row 0).  Rows at or past key_end read as zeros and cost no memory traffic, so a
-// tile that lies wholly past the end may be "loaded" unconditionally.
+// Load a 16-key tile of one KV head whose first key row (that head's slice of it) sits at
+// kt / vt, with the following rows kv_row elements apart.  Only the first `bytes` bytes
+// from kt / vt are read; the rest of the tile reads as zeros and costs no memory traffic,
+// so a tile that lies wholly past the end (bytes = 0) may be "loaded" unconditionally.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kbase,
-                                          const uint16_t *vbase, size_t kv_row, int key0,
-                                          int key_end, const TileOffsets<D> &off) {
+__device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kt, const uint16_t *vt,
+                                          uint32_t bytes, const TileOffsets<D> &off) {
     using T = DecodeTraits<D>;
-    const uint32_t bytes = (uint32_t)max(key_end - key0, 0) * (uint32_t)kv_row * 2u;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)key0 * kv_row, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)key0 * kv_row, bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kt, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt, bytes);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) r.k[ks] = buffer_load16(rk, off.k, ks * 16);
 #pragma unroll
@@ -183,7 +182,15 @@ __device__ __forceinline__ void finish_state(WaveState<D> &st) {
     for (int dt = 0; dt < DecodeTraits<D>::NDT; ++dt) st.o[dt] *= f;
 }
 
-template <int D>
+// Paged: the cache is a pool of pages of a.page consecutive key rows ([page][row][H_kv][d]),
+// and key t of sequence b is row t % page of page block_table[b][t / page] (V07 section
+// 16, logical token to page map; section 17, the decode kernel reads through the table).
+// Chunks and slabs start at multiples of 32 keys and a page holds a multiple of 16, so a
+// 16-key tile never crosses a page: each tile is one table lookup plus the contiguous
+// read of the unpaged cache.  The lookups of a wave's tiles (at most 8 of them) are
+// loaded once, one per lane, before the sweep (the table is read when the workgroup
+// starts, as V07 section 17 describes), and each tile takes its entry with a lane read.
+template <int D, bool Paged>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitArgs a, int n_hg) {
     using T = DecodeTraits<D>;
     // V staging during the sweep, then (several waves per head) the cross-wave merge
@@ -235,7 +242,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     }
 
     const size_t kv_row = (size_t)a.H_kv * D;
-    const size_t head_off = ((size_t)b * a.S_max * a.H_kv + hk) * D;
+    // unpaged: this sequence's cache, head hk; paged: the pool, head hk
+    const size_t head_off = Paged ? (size_t)hk * D : ((size_t)b * a.S_max * a.H_kv + hk) * D;
     const uint16_t *kbase = a.k + head_off;
     const uint16_t *vbase = a.v + head_off;
     uint16_t *vs = smem + w * kTile * T::VPITCH;
@@ -260,11 +268,39 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     for (int i = 0; i < T::NVI; ++i)
         toff.v[i] = (uint32_t)(((i * T::RPI + lane / T::LPR) * kv_row + (lane % T::LPR) * 8) * 2);
     auto key0 = [&](int t) { return s0 + (phase + t * wph) * kTile; };
+    // Paged: lane t holds the pool row of this wave's tile t (-1: no tile, or a table
+    // entry outside the pool, which then reads as zeros instead of faulting).
+    int prow = -1;
+    if constexpr (Paged) {
+        if (lane < n_w) {
+            const int key = key0(lane);
+            const int pg = a.block_table[(size_t)b * a.max_blocks + key / a.page];
+            if ((unsigned)pg < (unsigned)a.num_pages) prow = pg * a.page + key % a.page;
+        }
+    }
+    // Tile t of this wave: the address of its first row (in kt, vt) and the bytes that
+    // hold live keys (rows at or past the slab end read as zeros).
+    // (All of it is uniform; readfirstlane keeps the buffer resources in scalar registers.)
+    auto issue = [&](TileRegs<D> &r, int t) {
+        const int k0 = key0(t);
+        if constexpr (Paged) {
+            const int pr = __builtin_amdgcn_readlane(prow, t & 63);
+            const uint32_t live = (uint32_t)min(max(s1 - k0, 0), kTile);
+            const size_t row = (size_t)max(pr, 0) * kv_row;
+            const uint32_t bytes = __builtin_amdgcn_readfirstlane(
+                pr >= 0 ? live * (uint32_t)kv_row * 2u : 0u);
+            load_tile<D>(r, kbase + row, vbase + row, bytes, toff);
+        } else {
+            const size_t row = (size_t)k0 * kv_row;
+            load_tile<D>(r, kbase + row, vbase + row,
+                         (uint32_t)max(s1 - k0, 0) * (uint32_t)kv_row * 2u, toff);
+        }
+    };
     TileRegs<D> ring[kDepth];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) {
-        load_tile<D>(ring[j], kbase, vbase, kv_row, key0(j), s1, toff);
+        issue(ring[j], j);
         __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: oldest tile first
     }
     // whole rounds of kDepth tiles (no exit inside a round, so every pass through the loop
@@ -276,7 +312,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         for (int j = 0; j < kDepth; ++j) {
             const f32x4 sc = score_tile<D>(ring[j], qf, vs, lane);
             __builtin_amdgcn_sched_barrier(0);
-            load_tile<D>(ring[j], kbase, vbase, kv_row, key0(t + j + kDepth), s1, toff);
+            issue(ring[j], t + j + kDepth);
             softmax_pv<D>(st, sc, vs, key0(t + j), s1, a.scale_log2, lane);
         }
     }
@@ -346,7 +382,12 @@ hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 15) / 16;
     dim3 grid(a.P * a.slabs, (a.H_kv / a.hpw) * n_hg, a.B);
-    hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, n_hg);
+    if (a.block_table)
+        hipLaunchKernelGGL((decode_split_kernel<D, true>), grid, dim3(kWaves * 64), 0, stream, a,
+                           n_hg);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, false>), grid, dim3(kWaves * 64), 0, stream, a,
+                           n_hg);
     return hipGetLastError();
 }
 

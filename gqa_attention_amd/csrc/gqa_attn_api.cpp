@@ -39,6 +39,8 @@ constexpr int kGridYZ = 65535;
 constexpr int kSplitAlign = 32;       // chunk lengths are multiples of the kernel's key tile
 constexpr int kAutoChunk = 1024;       // num_splits = 0: chunks of 1024 keys
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kPagedTile = 16;         // a page holds whole 16-key tiles of the decode sweep
+constexpr int kMaxPage = 1 << 16;
 
 bool decode_head_size_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
@@ -167,6 +169,10 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.slabs = pl.slabs;
     a.hpw = pl.hpw;
     a.scale_log2 = scale * kLog2e;
+    a.block_table = nullptr;
+    a.page = 0;
+    a.num_pages = 0;
+    a.max_blocks = 0;
     return a;
 }
 
@@ -277,6 +283,42 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
     auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
                         workspace);
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split"))) return rc;
+    auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
+    if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
+    return ok();
+}
+
+int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *block_table, const int32_t *seqlens, void *o, float *lse,
+                          int B, int H_q, int H_kv, int d, int page_size, int num_pages,
+                          int max_blocks, float softmax_scale, int num_splits, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (page_size < kPagedTile || page_size % kPagedTile != 0 || page_size > kMaxPage)
+        return fail(GQA_ERR_BAD_SHAPE, "page_size=%d must be a multiple of %d in [%d, %d]",
+                    page_size, kPagedTile, kPagedTile, kMaxPage);
+    if (num_pages <= 0 || max_blocks <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "num_pages=%d and max_blocks=%d must be positive",
+                    num_pages, max_blocks);
+    if ((long)num_pages * page_size > 0x7FFFFFFFL || (long)max_blocks * page_size > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE,
+                    "num_pages*page_size and max_blocks*page_size must fit in 31 bits");
+    const int S_max = max_blocks * page_size;
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = decode_common_checks(q, k_pool, v_pool, seqlens, softmax_scale))) return rc;
+    if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
+    if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
+    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto a = split_args(q, k_pool, v_pool, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
+                        workspace);
+    a.block_table = block_table;
+    a.page = page_size;
+    a.num_pages = num_pages;
+    a.max_blocks = max_blocks;
+    if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
     auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();

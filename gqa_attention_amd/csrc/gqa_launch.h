@@ -25,6 +25,11 @@ struct DecodeSplitArgs {
     int slab, slabs;            // keys per slab, slabs per chunk
     int hpw;                    // KV heads per workgroup (divides H_kv and the wave count)
     float scale_log2;           // softmax_scale * log2(e)
+    // Paged cache when block_table is not null: k and v are pools [num_pages][page][H_kv][d]
+    // and key t of sequence b is row t % page of page block_table[b * max_blocks + t / page]
+    // (page a multiple of 16; S_max = max_blocks * page).
+    const int32_t *block_table;
+    int page, num_pages, max_blocks;
 };
 
 // Partial state (b, h, p) sits at index b*batch_stride + h*head_stride + p*state_stride of

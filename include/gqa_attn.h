@@ -154,6 +154,46 @@ int gqa_decode_combine(const int32_t *seqlens, void *o, float *lse,
                        const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gqa_attn_decode_paged -- gqa_attn_decode over a paged KV cache.
+ *
+ * The cache lives in fixed-size pages of page_size tokens drawn from a pool,
+ * and each sequence lists its pages in a block table: token t of sequence b is
+ * row t % page_size of page block_table[b][t / page_size] ("Attention Kernel
+ * lineage" (V07), section 16: block pool, block table and the logical-token-to-
+ * page map; section 17: paged decode, split-K over the key axis with a second
+ * merge stage).  Everything else -- the M-fold of the G query heads, the split
+ * plan, the merge, the outputs -- is that of gqa_attn_decode, with
+ * S_max = max_blocks * page_size.
+ *
+ *   q           [B, H_q, d]                        bf16, device, read-only
+ *   k_pool      [num_pages, page_size, H_kv, d]    bf16, device, read-only
+ *   v_pool      [num_pages, page_size, H_kv, d]    bf16, device, read-only
+ *               (K and V are two pools with one page numbering; a page's K rows
+ *               and V rows sit at the same page index of each)
+ *   block_table [B, max_blocks] int32, device, read-only.  Only the entries of
+ *               blocks that hold live tokens (block < ceil(seqlens[b] / page_size))
+ *               are read; the rest may hold anything.  A live entry outside
+ *               [0, num_pages) is not dereferenced: its keys read as zeros (the
+ *               result for that sequence is then meaningless, but nothing faults).
+ *               Pages may be shared between sequences.
+ *   seqlens     [B] int32, device, or NULL (= max_blocks * page_size tokens each),
+ *               clamped to [0, max_blocks * page_size] on the device.
+ *   o, lse      as gqa_attn_decode.
+ *   page_size   tokens per page: a multiple of 16 in [16, 65536].
+ *   num_pages, max_blocks: pool size and table width; num_pages * page_size and
+ *               max_blocks * page_size must be below 2^31.
+ *   workspace   as gqa_attn_decode, sized by gqa_decode_plan with
+ *               S_max = max_blocks * page_size.
+ *
+ * Calls that share a workspace on overlapping streams race.
+ */
+int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *block_table, const int32_t *seqlens, void *o, float *lse,
+                          int B, int H_q, int H_kv, int d, int page_size, int num_pages,
+                          int max_blocks, float softmax_scale, int num_splits,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gqa_lse_merge -- merge caller-provided partial states (V07, section 3:
  * M = max m_p, a_p = 2^(m_p - M), L = sum a_p l_p, O = sum a_p O_p / L;
  * section 17, second stage).  Partial maxima are in log2 units of the scaled

@@ -23,7 +23,8 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     declared = g.header_functions()
-    assert {"gqa_attn_decode", "gqa_attn_prefill_causal", "gqa_lse_merge", "gqa_decode_plan",
+    assert {"gqa_attn_decode", "gqa_attn_decode_paged", "gqa_attn_prefill_causal",
+            "gqa_lse_merge", "gqa_decode_plan",
             "gqa_decode_partials", "gqa_decode_combine", "gqa_status_string",
             "gqa_last_error", "gqa_version"} <= set(declared)
     out = subprocess.run(["nm", "-D", "--defined-only", g.LIBRARY], capture_output=True,
@@ -117,6 +118,27 @@ def test_stage_calls_reject_before_launch(lib):
                                    None) == NULLP
     assert lib.gqa_decode_combine(None, A, A, 1, 8, 2, 32, 512, 4, A, 10, None) == WS
     assert lib.gqa_decode_combine(None, MIS, A, 1, 8, 2, 32, 512, 4, A, 1 << 30, None) == ALIGN
+
+
+def _paged(lib, q=A, kp=A, vp=A, tbl=A, seqlens=None, o=A, lse=A, B=1, H_q=8, H_kv=2, d=32,
+           page=16, num_pages=64, max_blocks=32, scale=0.17, splits=4, ws=A, ws_bytes=1 << 30):
+    return lib.gqa_attn_decode_paged(q, kp, vp, tbl, seqlens, o, lse, B, H_q, H_kv, d, page,
+                                     num_pages, max_blocks, scale, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tbl=None), NULLP), (dict(kp=None), NULLP), (dict(vp=MIS), ALIGN),
+    (dict(tbl=ctypes.c_void_p(0x10002)), ALIGN),
+    (dict(page=8), SHAPE), (dict(page=40), SHAPE), (dict(page=0), SHAPE),
+    (dict(page=1 << 17), SHAPE),
+    (dict(num_pages=0), SHAPE), (dict(max_blocks=0), SHAPE),
+    (dict(num_pages=1 << 27, page=32), SHAPE),     # num_pages * page_size overflows 31 bits
+    (dict(ws_bytes=100), WS), (dict(d=96), UNSUP), (dict(H_kv=3), SHAPE),
+    (dict(scale=float("nan")), SCALE),
+])
+def test_paged_decode_rejects_before_launch(lib, kw, code):
+    assert _paged(lib, **kw) == code
+    assert lib.gqa_last_error().decode() != ""
 
 
 @pytest.mark.parametrize("kw,code", [
