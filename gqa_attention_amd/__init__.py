@@ -68,6 +68,8 @@ def load_library(path=LIBRARY):
     L.gqa_lse_merge.restype = ci
     L.gqa_attn_prefill_causal.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, cf, vp]
     L.gqa_attn_prefill_causal.restype = ci
+    L.gqa_attn_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, ci, ci, cf, vp]
+    L.gqa_attn_prefill_chunk.restype = ci
     if path == LIBRARY:
         _lib = L
     return L
@@ -256,5 +258,28 @@ def prefill_causal(q, k, v, softmax_scale=None, out=None, lse=None):
     l = torch.empty((B, H_q, S), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(load_library().gqa_attn_prefill_causal(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, S, H_q, H_kv, d,
+        _scale(d, softmax_scale), _stream(q.device)))
+    return o, l
+
+
+def prefill_chunk(q, k_cache, v_cache, q_start=None, softmax_scale=None, out=None, lse=None):
+    """Causal prefill of a chunk: q [B,T_q,H_q,d] are tokens q_start .. q_start+T_q-1 of
+    sequences whose caches k/v [B,S_kv,H_kv,d] hold them; q_start defaults to S_kv - T_q
+    (the chunk is the cache's last T_q tokens).  -> (o [B,T_q,H_q,d], lse [B,H_q,T_q])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, T, H_q, d = q.shape
+    S_kv = k_cache.shape[1]
+    if (k_cache.shape[0] != B or k_cache.shape[3] != d or
+            tuple(v_cache.shape) != tuple(k_cache.shape)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, "
+                         f"v {tuple(v_cache.shape)}")
+    H_kv = k_cache.shape[2]
+    qs = S_kv - T if q_start is None else int(q_start)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H_q, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(load_library().gqa_attn_prefill_chunk(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l), B, T, qs, S_kv, H_q, H_kv, d,
         _scale(d, softmax_scale), _stream(q.device)))
     return o, l

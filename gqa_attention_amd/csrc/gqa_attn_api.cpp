@@ -200,6 +200,40 @@ gqa::MergeArgs combine_args(const int32_t *seqlens, void *o, float *lse, int B, 
     return m;
 }
 
+// Causal prefill of T query rows (tokens q_start .. q_start + T - 1) against a cache of
+// S rows per sequence; the callers have checked T > 0, S > 0 and 0 <= q_start <= S - T.
+int prefill(const void *q, const void *k, const void *v, void *o, float *lse, int B, int T,
+            int q_start, int S, int H_q, int H_kv, int d, float softmax_scale, void *stream) {
+    int rc;
+    if ((rc = check_heads(B, H_q, H_kv))) return rc;
+    if (d != 128) return fail(GQA_ERR_UNSUPPORTED, "prefill head size d=%d (supported: 128)", d);
+    const long n_qb = (T + 127) / 128;
+    if (n_qb * (long)B * H_q > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*H_q*ceil(T_q/128) exceeds the grid limit");
+    if ((rc = check_bf16(q, "q")) || (rc = check_bf16(k, "k")) || (rc = check_bf16(v, "v")) ||
+        (rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse")))
+        return rc;
+    if ((rc = check_scale(softmax_scale))) return rc;
+    gqa::PrefillArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = B;
+    a.S = S;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.d = d;
+    a.T = T;
+    a.q_start = q_start;
+    a.scale_log2 = softmax_scale * kLog2e;
+    if ((rc = hip_status(gqa::launch_prefill_causal(a, static_cast<hipStream_t>(stream)),
+                         "prefill_causal")))
+        return rc;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -367,33 +401,20 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
 int gqa_attn_prefill_causal(const void *q, const void *k, const void *v, void *o, float *lse,
                             int B, int S, int H_q, int H_kv, int d, float softmax_scale,
                             void *stream) {
-    int rc;
-    if ((rc = check_heads(B, H_q, H_kv))) return rc;
     if (S <= 0) return fail(GQA_ERR_BAD_SHAPE, "S=%d must be positive", S);
-    if (d != 128) return fail(GQA_ERR_UNSUPPORTED, "prefill head size d=%d (supported: 128)", d);
-    const long n_qb = (S + 127) / 128;
-    if (n_qb * (long)B * H_q > 0x7FFFFFFFL)
-        return fail(GQA_ERR_BAD_SHAPE, "B*H_q*ceil(S/128) exceeds the grid limit");
-    if ((rc = check_bf16(q, "q")) || (rc = check_bf16(k, "k")) || (rc = check_bf16(v, "v")) ||
-        (rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse")))
-        return rc;
-    if ((rc = check_scale(softmax_scale))) return rc;
-    gqa::PrefillArgs a;
-    a.q = static_cast<const uint16_t *>(q);
-    a.k = static_cast<const uint16_t *>(k);
-    a.v = static_cast<const uint16_t *>(v);
-    a.o = static_cast<uint16_t *>(o);
-    a.lse = lse;
-    a.B = B;
-    a.S = S;
-    a.H_q = H_q;
-    a.H_kv = H_kv;
-    a.d = d;
-    a.scale_log2 = softmax_scale * kLog2e;
-    if ((rc = hip_status(gqa::launch_prefill_causal(a, static_cast<hipStream_t>(stream)),
-                         "prefill_causal")))
-        return rc;
-    return ok();
+    return prefill(q, k, v, o, lse, B, S, 0, S, H_q, H_kv, d, softmax_scale, stream);
+}
+
+int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, void *o,
+                           float *lse, int B, int T_q, int q_start, int S_kv, int H_q, int H_kv,
+                           int d, float softmax_scale, void *stream) {
+    if (T_q <= 0 || S_kv <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "T_q=%d and S_kv=%d must be positive", T_q, S_kv);
+    if (q_start < 0 || q_start > S_kv - T_q)
+        return fail(GQA_ERR_BAD_SHAPE, "q_start=%d outside [0, S_kv - T_q] = [0, %d]", q_start,
+                    S_kv - T_q);
+    return prefill(q, k_cache, v_cache, o, lse, B, T_q, q_start, S_kv, H_q, H_kv, d,
+                   softmax_scale, stream);
 }
 
 }  // extern "C"

@@ -46,11 +46,15 @@ struct MergeArgs {
     int B, H_q, d;
 };
 
+// Causal prefill of T query rows per sequence, row i being token q_start + i (sees keys
+// j <= q_start + i), against a cache of S rows per sequence (q_start + T <= S).
+// q, o [B][T][H_q][d]; k, v [B][S][H_kv][d]; lse [B][H_q][T].  Whole prompt: T = S, q_start = 0.
 struct PrefillArgs {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     float *lse;
     int B, S, H_q, H_kv, d;
+    int T, q_start;
     float scale_log2;
 };
 

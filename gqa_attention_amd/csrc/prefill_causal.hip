@@ -1,4 +1,8 @@
-// prefill_causal.hip -- causal GQA prefill (T_q = S_kv = S) on gfx950.
+// prefill_causal.hip -- causal GQA prefill on gfx950: a whole prompt (T_q = S_kv), or a
+// chunk of T_q query rows that are the tokens q_start .. q_start + T_q - 1 of a sequence
+// whose keys are cached (ADR-0060 "AHBM GQA Fused Attention", section 0.5.2: the launch
+// carries the query block's q_start and T_q; section 5.4: the query block against the
+// KV tiles, past / future / partial).  Query row i sees keys j <= q_start + i.
 //
 // FlashAttention-2 forward ("Attention Kernel lineage" (V07), sections 7-8):
 // each workgroup owns one block of 256 query rows of one query head for its
@@ -206,7 +210,10 @@ struct WaveCtx {
     uint8_t *lds;
     const uint16_t *kbase, *vbase;
     size_t kv_row;
-    int S, n_kb, n_sub, w, row, hf;
+    int S;                    // keys that may be read: q_start + T (the rest read as zeros)
+    int n_kb, n_sub;          // LDS tiles of the workgroup, 32-key steps of this wave
+    int mask_from;            // first step holding a key past some row's diagonal
+    int w, row, hf;           // row: this lane's query position q_start + i
     float c;
     uint32_t koff, voff;   // DMA: this lane's byte offset within its 32-row group
     FragAddr fa;
@@ -217,14 +224,15 @@ struct RowState {
     float m, l, lw, mx;   // mx: raw row max of the next step's scores
 };
 
-// Scores of keys past the lane's row become -inf (their P is then exactly 0).
+// Scores of keys past the lane's query position become -inf (their P is then exactly 0).
 __device__ __forceinline__ void mask_half(f32x16 &s, int k0, int row, int hf) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = score_key(k0, r, hf) <= row ? s[r] : neg_inf();
 }
 
-// Pipeline step u (keys 32u .. 32u+31) of one wave, whose steps run 0 .. n_sub-1; the
-// last step holds the wave's diagonal, and its scores were masked when they were formed.
+// Pipeline step u (keys 32u .. 32u+31) of one wave, whose steps run 0 .. n_sub-1; steps
+// from mask_from on hold the wave's diagonal (the last one, or the last two when the
+// chunk start is not a multiple of 32), and their scores were masked when formed.
 // The step runs its softmax while the matrix cores form the scores of step u+1 (K rows
 // at kn), then its P.V (V rows at vh) while the row max of step u+1 is taken.  Every step
 // runs the same code, the last one included (its scores for a step u+1 are not used).
@@ -238,7 +246,8 @@ __device__ __forceinline__ void half_step(const WaveCtx &x, int u, const f32x16 
     softmax_half(s, st.m, x.c, pf, st.l, st.lw);
     qk_half(sn, kn, x.fa, qf);
     pv_half(st.o, vh, va, pf);
-    if (u + 2 == x.n_sub) mask_half(sn, (u + 1) * kHalf, x.row, x.hf);
+    // (masking the scores of step n_sub, which no step uses, is harmless)
+    if (u + 1 >= x.mask_from) mask_half(sn, (u + 1) * kHalf, x.row, x.hf);
     st.mx = half_max(sn);
     // issue order: each score product with one K fragment read and a share of the
     // softmax, then each P.V product with its two V reads and a share of the rest
@@ -312,19 +321,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     const int i0 = qb * kBr;
     const int r0 = i0 + w * 32;            // this wave's first query row
     const int row = r0 + r32;              // this lane's query row
-    const int last_row = min(i0 + kBr, a.S) - 1;
+    const int last_row = min(i0 + kBr, a.T) - 1;
+    const int qs = a.q_start;              // query row i is token qs + i
 
     WaveCtx x;
     x.lds = smem;
     x.kv_row = (size_t)a.H_kv * D;
     x.kbase = a.k + ((size_t)b * a.S * a.H_kv + hk) * D;
     x.vbase = a.v + ((size_t)b * a.S * a.H_kv + hk) * D;
-    x.S = a.S;
-    x.n_kb = last_row / kBc + 1;
-    // 32-key steps this wave needs: keys [0, r0 + 32), the last step on its diagonal
-    x.n_sub = r0 < a.S ? r0 / kHalf + 1 : 0;
+    // keys past the chunk's last token are never visible: they are not even read, so a
+    // cache row after it may hold anything (a zero row times a zero weight adds nothing)
+    x.S = qs + a.T;
+    x.n_kb = (qs + last_row) / kBc + 1;
+    // 32-key steps this wave needs: keys [0, qs + its last real row], the last on its
+    // diagonal; the steps that hold a key past the diagonal of its first row are masked
+    x.n_sub = r0 < a.T ? (qs + min(r0 + 31, a.T - 1)) / kHalf + 1 : 0;
+    x.mask_from = (qs + r0) / kHalf;
     x.w = w;
-    x.row = row;
+    x.row = qs + row;
     x.hf = hf;
     // tau * log2(e); a zero scale is replaced by a tiny one so that a masked score
     // (-inf) still scales to -inf: s * 1e-30 is far below fp32 resolution of the result
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     bf16x8 qf[8];
     {
         const uint16_t *qrow =
-            a.q + (((size_t)b * a.S + min(row, a.S - 1)) * a.H_q + h) * D + hf * 64;
+            a.q + (((size_t)b * a.T + min(row, a.T - 1)) * a.H_q + h) * D + hf * 64;
 #pragma unroll
         for (int k8 = 0; k8 < 8; ++k8) qf[k8] = as_bf16x8(load16(qrow + k8 * 8));
     }
@@ -367,14 +381,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
 
     // prologue: K(0..2) and V(0..1) into LDS, then the scores of the first step
     for (int t = 0; t < 3; ++t)
-        dma_tile(smem, kKBuf + t * kTileBytes, x.kbase, x.kv_row, t * kBc, a.S, x.koff, w);
+        dma_tile(smem, kKBuf + t * kTileBytes, x.kbase, x.kv_row, t * kBc, x.S, x.koff, w);
     for (int t = 0; t < 2; ++t)
-        dma_tile(smem, kVBuf + t * kTileBytes, x.vbase, x.kv_row, t * kBc, a.S, x.voff, w);
+        dma_tile(smem, kVBuf + t * kTileBytes, x.vbase, x.kv_row, t * kBc, x.S, x.voff, w);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (x.n_sub > 0) {
         qk_half(sa, smem + kKBuf, x.fa, qf);
-        if (x.n_sub == 1) mask_half(sa, 0, row, hf);
+        if (x.mask_from == 0) mask_half(sa, 0, x.row, hf);
         st.mx = half_max(sa);
     }
 
@@ -393,9 +407,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     // ---- epilogue: O = O^T / lw -> bf16, LSE = ln2 * (m + log2 l) ----
     const float l = st.l + __shfl_xor(st.l, 32);
     const float lw = st.lw + __shfl_xor(st.lw, 32);
-    if (row >= a.S) return;
+    if (row >= a.T) return;
     const float inv = 1.f / lw;
-    uint16_t *orow = a.o + (((size_t)b * a.S + row) * a.H_q + h) * D;
+    uint16_t *orow = a.o + (((size_t)b * a.T + row) * a.H_q + h) * D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -406,14 +420,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
                 u32x2{pack_bf16x2(st.o[dt][r] * inv, st.o[dt][r + 1] * inv),
                       pack_bf16x2(st.o[dt][r + 2] * inv, st.o[dt][r + 3] * inv)};
         }
-    if (hf == 0) a.lse[((size_t)b * a.H_q + h) * a.S + row] = kLn2 * (st.m + __builtin_log2f(l));
+    if (hf == 0) a.lse[((size_t)b * a.H_q + h) * a.T + row] = kLn2 * (st.m + __builtin_log2f(l));
 }
 
 }  // namespace
 
 hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream) {
     if (a.d != D) return hipErrorInvalidValue;
-    const int n_qb = (a.S + kBr - 1) / kBr;
+    const int n_qb = (a.T + kBr - 1) / kBr;
     const long units = (long)n_qb * a.B * a.H_kv;
     const int remap = (units % kXcds) == 0;
     const long blocks = units * (a.H_q / a.H_kv);

@@ -238,6 +238,30 @@ int gqa_attn_prefill_causal(const void *q, const void *k, const void *v, void *o
                             int B, int S, int H_q, int H_kv, int d,
                             float softmax_scale, void *stream);
 
+/*
+ * gqa_attn_prefill_chunk -- causal attention of a chunk of a sequence against
+ * its KV cache: the T_q query rows are the tokens q_start .. q_start + T_q - 1,
+ * and query row i sees keys j <= q_start + i (ADR-0060, section 0.5.2: the
+ * launch carries the query block's q_start and T_q; section 5.4: each KV tile is
+ * wholly past, wholly future or partial for the query block; V07, section 12:
+ * causal mask and block classification).  With the chunk at the end of the
+ * cache (q_start = S_kv - T_q) this is the bottom-right aligned causal mask of
+ * chunked prefill; q_start = 0, T_q = S_kv is gqa_attn_prefill_causal.  Same
+ * kernel, tiling and outputs as gqa_attn_prefill_causal.
+ *
+ *   q        [B, T_q, H_q, d]   bf16, device, read-only
+ *   k_cache  [B, S_kv, H_kv, d] bf16, device, read-only (batch stride S_kv*H_kv*d);
+ *            rows at or past q_start + T_q are never read and may hold anything
+ *   v_cache  [B, S_kv, H_kv, d] bf16, device, read-only (same)
+ *   o        [B, T_q, H_q, d]   bf16, device, written (RNE from fp32)
+ *   lse      [B, H_q, T_q]      fp32, device, written (natural log)
+ *
+ * Requires T_q >= 1 and 0 <= q_start <= S_kv - T_q.  Supported: d = 128.
+ */
+int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, void *o,
+                           float *lse, int B, int T_q, int q_start, int S_kv, int H_q, int H_kv,
+                           int d, float softmax_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     declared = g.header_functions()
     assert {"gqa_attn_decode", "gqa_attn_decode_paged", "gqa_attn_prefill_causal",
+            "gqa_attn_prefill_chunk",
             "gqa_lse_merge", "gqa_decode_plan",
             "gqa_decode_partials", "gqa_decode_combine", "gqa_status_string",
             "gqa_last_error", "gqa_version"} <= set(declared)
@@ -162,6 +163,22 @@ def test_prefill_rejects_before_launch(lib, kw, code):
     a.update(kw)
     assert lib.gqa_attn_prefill_causal(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["S"],
                                        a["H_q"], a["H_kv"], a["d"], a["scale"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(o=MIS), ALIGN), (dict(T=0), SHAPE), (dict(S=0), SHAPE),
+    (dict(q_start=-1), SHAPE), (dict(q_start=200), SHAPE),     # q_start + T_q > S_kv
+    (dict(T=300, q_start=0), SHAPE), (dict(H_kv=3), SHAPE), (dict(d=64), UNSUP),
+    (dict(scale=float("inf")), SCALE),
+])
+def test_prefill_chunk_rejects_before_launch(lib, kw, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, B=1, T=100, q_start=150, S=256, H_q=8, H_kv=2, d=128,
+             scale=0.088)
+    a.update(kw)
+    assert lib.gqa_attn_prefill_chunk(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"],
+                                      a["q_start"], a["S"], a["H_q"], a["H_kv"], a["d"],
+                                      a["scale"], None) == code
+    assert lib.gqa_last_error().decode() != ""
 
 
 def test_binding_raises_with_detail():
