@@ -26,6 +26,14 @@ Reported (one JSON line):
   roofline_prefill  prefill_causal, MFMA-bound: 4*S^2*d*H_q/2 FLOP / its mean
                duration vs the 2.5 PFLOP/s bf16 dense peak;
   cpu_baseline the fp64 CPU oracle on the same decode workload (rank 0 only).
+
+Measured after the timed region, each in its own graph loop (not part of a step):
+  decode_paged      the same decode with the cache in 16-token pages of a pool,
+                    read through a block table (gqa_attn_decode_paged);
+  decode_ragged_b8  batched long-context decode, B=8 with lengths uniform on
+                    [4096, 131072], contiguous cache and paged (16-token pages);
+  prefill_chunk     the last 2048 tokens of the 8192-token prompt as one chunk
+                    against the whole cache (gqa_attn_prefill_chunk).
 """
 import argparse
 import json
@@ -41,9 +49,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import gqa_attention_amd as g  # noqa: E402
-from gqa_workloads import LLAMA_DECODE, LLAMA_PREFILL  # noqa: E402
+from gqa_workloads import LLAMA_DECODE, LLAMA_PREFILL, LLAMA_RAGGED_DECODE  # noqa: E402
 from gqa_workloads import accounting as acc  # noqa: E402
-from gqa_workloads.generate import for_config  # noqa: E402
+from gqa_workloads.generate import for_config, paged_decode_inputs  # noqa: E402
 
 METRIC = "decode KV GB/s (% HBM peak) at Llama3-70B GQA; causal prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
@@ -100,6 +108,125 @@ def cpu_baseline(seconds):
             "cpu": platform.processor() or platform.machine()}
 
 
+def graph_ms(fn, n):
+    """Mean time per call of n back-to-back calls fn(0..n-1), captured in a HIP graph,
+    replayed once untimed and once between two events on the launch stream."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def upload_paged(p):
+    return (upload(p["q"]), upload(p["k_pool"]), upload(p["v_pool"]),
+            torch.from_numpy(p["block_table"]).cuda(), torch.from_numpy(p["seqlens"]).cuda())
+
+
+def extra_measurements(K, q_p, k_p, v_p, decode_ms):
+    """Paged decode, batched ragged decode and chunked prefill, outside the timed step."""
+    res = {}
+    page = 16
+
+    # paged decode at the Llama workload (4 copies of the pools, like the unpaged cache)
+    dc = LLAMA_DECODE
+    p = paged_decode_inputs(dc.B, dc.H_q, dc.H_kv, dc.d, page, S_max=dc.S_kv, seed=dc.seed)
+    q, kp, vp, tbl, sl = upload_paged(p)
+    del p
+    pools = [(kp, vp)] + [(kp.clone(), vp.clone()) for _ in range(3)]
+    ws = g.decode_workspace(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
+    o = torch.empty((dc.B, dc.H_q, dc.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((dc.B, dc.H_q), dtype=torch.float32, device="cuda")
+
+    def paged_call(i):
+        k, v = pools[i % len(pools)]
+        g.decode_paged(q, k, v, tbl, sl, num_splits=dc.num_splits, out=o, lse=lse, workspace=ws)
+
+    paged_call(0)
+    ms = graph_ms(paged_call, K)
+    kv = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
+    gbs = kv / (ms * 1e-3) / 1e9
+    res["decode_paged"] = {
+        "workload": f"Llama3-70B decode B=1 S_kv={dc.S_kv}, {page}-token pages in permuted "
+                    f"pool order, {dc.num_splits} splits",
+        "page_size": page, "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "vs_contiguous": round(decode_ms / ms, 4)}
+    del pools, q, kp, vp, tbl, sl
+
+    # batched ragged decode, paged and contiguous (the contiguous cache is gathered from
+    # the pools on the GPU, so both read the same tokens)
+    rc = LLAMA_RAGGED_DECODE
+    p = paged_decode_inputs(rc.B, rc.H_q, rc.H_kv, rc.d, page, seed=rc.seed, ragged=rc.ragged)
+    seqlens = p["seqlens"].tolist()
+    S_max = int(max(seqlens))
+    q, kp, vp, tbl, sl = upload_paged(p)
+    del p
+    kc = torch.zeros((rc.B, S_max, rc.H_kv, rc.d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for b, n in enumerate(seqlens):
+        t = torch.arange(n, device="cuda")
+        rows = tbl[b, t // page].long() * page + t % page
+        kc[b, :n] = kp.view(-1, rc.H_kv, rc.d)[rows]
+        vc[b, :n] = vp.view(-1, rc.H_kv, rc.d)[rows]
+    o = torch.empty((rc.B, rc.H_q, rc.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rc.B, rc.H_q), dtype=torch.float32, device="cuda")
+    ws_c = g.decode_workspace(rc.B, rc.H_q, rc.H_kv, rc.d, S_max, rc.num_splits)
+    ws_p = g.decode_workspace(rc.B, rc.H_q, rc.H_kv, rc.d, tbl.shape[1] * page, rc.num_splits)
+
+    def contig_call(i):
+        g.decode(q, kc, vc, sl, num_splits=rc.num_splits, out=o, lse=lse, workspace=ws_c)
+
+    def paged_b_call(i):
+        g.decode_paged(q, kp, vp, tbl, sl, num_splits=rc.num_splits, out=o, lse=lse,
+                       workspace=ws_p)
+
+    contig_call(0)
+    paged_b_call(0)
+    ms_c = graph_ms(contig_call, K)
+    ms_p = graph_ms(paged_b_call, K)
+    kv = acc.decode_kv_bytes(seqlens, rc.H_kv, rc.d)
+    res["decode_ragged_b8"] = {
+        "workload": f"Llama3-70B batched decode B={rc.B}, lengths uniform on "
+                    f"[{rc.ragged[0]}, {rc.ragged[1]}], {rc.num_splits} splits",
+        "seqlens": seqlens, "kv_bytes": kv,
+        "contiguous": {"us": round(ms_c * 1e3, 2), "gbs": round(kv / ms_c / 1e6, 1),
+                       "frac_hbm_peak": round(kv / ms_c / 1e6 / HBM_PEAK_GBS, 4),
+                       "tokens_per_s": round(rc.B / (ms_c * 1e-3), 1)},
+        "paged": {"page_size": page, "us": round(ms_p * 1e3, 2),
+                  "gbs": round(kv / ms_p / 1e6, 1),
+                  "frac_hbm_peak": round(kv / ms_p / 1e6 / HBM_PEAK_GBS, 4)}}
+    del q, kp, vp, tbl, sl, kc, vc, ws_c, ws_p
+
+    # chunked prefill: the prompt's last 2048 tokens against its whole 8192-token cache
+    pc = LLAMA_PREFILL
+    T, q_start = 2048, pc.S - 2048
+    qc = q_p[:, q_start:].contiguous()
+    oc = torch.empty_like(qc)
+    lc = torch.empty((pc.B, pc.H_q, T), dtype=torch.float32, device="cuda")
+
+    def chunk_call(i):
+        g.prefill_chunk(qc, k_p, v_p, q_start=q_start, out=oc, lse=lc)
+
+    chunk_call(0)
+    ms = graph_ms(chunk_call, K)
+    flop = acc.prefill_chunk_flop(pc.B, T, q_start, pc.H_q, pc.d)
+    tf = flop / (ms * 1e-3) / 1e12
+    res["prefill_chunk"] = {
+        "workload": f"Llama3-70B chunked prefill: T_q={T} rows at q_start={q_start}, "
+                    f"S_kv={pc.S}", "flop": flop, "ms": round(ms, 4), "tflops": round(tf, 1),
+        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +235,8 @@ def main():
     ap.add_argument("--kv-copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the paged, batched and chunked measurements after the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 512 MiB device copy (torch copy_), whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the kernels' HBM traffic")
@@ -257,6 +386,8 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
+    if not args.no_extra:
+        out.update(extra_measurements(K, q_p, k_p, v_p, decode_ms))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -33,6 +33,13 @@ def prefill_causal_flop(B: int, S: int, H_q: int, d: int) -> float:
     return B * 4.0 * S * S * d * H_q / 2.0
 
 
+def prefill_chunk_flop(B: int, T: int, q_start: int, H_q: int, d: int) -> float:
+    """Chunked causal prefill FLOP on the same convention: the chunk's rows see the
+    q_start keys before it in full and its own T x T block as a half square,
+    4*d*H_q*(T*q_start + T^2/2) per sequence (q_start = 0 gives the whole-prompt figure)."""
+    return B * 4.0 * d * H_q * (T * q_start + T * T / 2.0)
+
+
 def prefill_causal_flop_exact(B: int, S: int, H_q: int, d: int) -> int:
     """FLOP over the kept (i, j <= i) pairs only: 4*d per pair, S(S+1)/2 pairs per head."""
     return B * H_q * 4 * d * (S * (S + 1) // 2)
