@@ -270,7 +270,7 @@ def main():
     def decode_call(i):
         k, v = kv_copies[i % len(kv_copies)]
         g.decode_partials(q_d, k, v, None, ws, num_splits=dc.num_splits)
-        g.decode_combine(None, ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
+        g.decode_combine(ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
                          num_splits=dc.num_splits)
 
     def split_call(i):
@@ -278,7 +278,7 @@ def main():
         g.decode_partials(q_d, k, v, None, ws, num_splits=dc.num_splits)
 
     def merge_call(i):
-        g.decode_combine(None, ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
+        g.decode_combine(ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
                          num_splits=dc.num_splits)
 
     def prefill_call(i):

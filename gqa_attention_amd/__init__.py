@@ -53,13 +53,13 @@ def load_library(path=LIBRARY):
     L.gqa_version.argtypes = []
     L.gqa_version.restype = ctypes.c_char_p
     L.gqa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
-                                  ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(cs)]
+                                  ctypes.POINTER(cs)]
     L.gqa_decode_plan.restype = ci
     L.gqa_attn_decode.argtypes = [vp, vp, vp, i32p, vp, f32p, ci, ci, ci, ci, ci, cf, ci, vp, cs, vp]
     L.gqa_attn_decode.restype = ci
     L.gqa_decode_partials.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci, ci, cf, ci, vp, cs, vp]
     L.gqa_decode_partials.restype = ci
-    L.gqa_decode_combine.argtypes = [i32p, vp, f32p, ci, ci, ci, ci, ci, ci, vp, cs, vp]
+    L.gqa_decode_combine.argtypes = [vp, f32p, ci, ci, ci, ci, ci, ci, vp, cs, vp]
     L.gqa_decode_combine.restype = ci
     L.gqa_attn_decode_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci, ci,
                                         ci, cf, ci, vp, cs, vp]
@@ -113,17 +113,15 @@ def _scale(d, softmax_scale):
 
 
 def decode_plan(B, H_q, H_kv, d, S_max, num_splits=0):
-    """Split plan of a decode launch as a dict: chunks, chunk_keys, slabs (per chunk),
-    slab_keys, states (partial states per row = chunks * slabs) and workspace_bytes."""
+    """Split plan of a decode launch as a dict: partitions (of the batch's 16-key tiles,
+    one workgroup each per head-group row), states (partial-state slots per query head)
+    and workspace_bytes."""
     L = load_library()
-    P, chunk, slabs, slab = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    P, N = ctypes.c_int(), ctypes.c_int()
     ws = ctypes.c_size_t()
     _check(L.gqa_decode_plan(B, H_q, H_kv, d, S_max, num_splits, ctypes.byref(P),
-                             ctypes.byref(chunk), ctypes.byref(slabs), ctypes.byref(slab),
-                             ctypes.byref(ws)))
-    return {"chunks": P.value, "chunk_keys": chunk.value, "slabs": slabs.value,
-            "slab_keys": slab.value, "states": P.value * slabs.value,
-            "workspace_bytes": ws.value}
+                             ctypes.byref(N), ctypes.byref(ws)))
+    return {"partitions": P.value, "states": N.value, "workspace_bytes": ws.value}
 
 
 def decode_workspace(B, H_q, H_kv, d, S_max, num_splits=0, device="cuda"):
@@ -201,30 +199,30 @@ def decode_partials(q, k_cache, v_cache, seqlens, workspace, softmax_scale=None,
         _stream(q.device)))
 
 
-def decode_combine(seqlens, workspace, out, lse, H_kv, S_max, num_splits=0):
+def decode_combine(workspace, out, lse, H_kv, S_max, num_splits=0):
     """Stage 2 of decode: merge the workspace's partials into ``out`` and ``lse``."""
     _need(out, "out", torch.bfloat16, 3)
     _need(lse, "lse", torch.float32, 2)
     B, H_q, d = out.shape
     _check(load_library().gqa_decode_combine(
-        _ptr(seqlens), _ptr(out), _ptr(lse), B, H_q, H_kv, d, S_max, num_splits, _ptr(workspace),
+        _ptr(out), _ptr(lse), B, H_q, H_kv, d, S_max, num_splits, _ptr(workspace),
         workspace.numel(), _stream(out.device)))
 
 
 def workspace_views(workspace, B, H_q, H_kv, d, S_max, num_splits=0):
-    """(m2 [B,H_q,N], l [B,H_q,N], o [B,H_q,N,d]) float32 views of a decode workspace,
-    N = chunks * slabs, state index chunk * slabs + slab.  The workspace stores the states
-    state-major ([B][N][H_q], O [B][N][H_q][d]); the views are permuted to head-major."""
+    """Views of a decode workspace: (seg [B, 2] int32 -- first state slot and slot count of
+    each sequence --, m2 [N, H_q], l [N, H_q], o [N, H_q, d] float32), N state slots."""
     N = decode_plan(B, H_q, H_kv, d, S_max, num_splits)["states"]
-    rows = B * H_q * N
     a256 = lambda n: (n + 255) // 256 * 256
-    off_l = a256(rows * 4)
-    off_o = off_l + a256(rows * 4)
+    off_m2 = a256(B * 2 * 4)
+    off_l = off_m2 + a256(N * H_q * 4)
+    off_o = off_l + a256(N * H_q * 4)
     f = workspace.view(torch.uint8)
-    m2 = f[:rows * 4].view(torch.float32).view(B, N, H_q).permute(0, 2, 1)
-    l = f[off_l:off_l + rows * 4].view(torch.float32).view(B, N, H_q).permute(0, 2, 1)
-    o = f[off_o:off_o + rows * d * 4].view(torch.float32).view(B, N, H_q, d).permute(0, 2, 1, 3)
-    return m2, l, o
+    seg = f[:B * 2 * 4].view(torch.int32).view(B, 2)
+    m2 = f[off_m2:off_m2 + N * H_q * 4].view(torch.float32).view(N, H_q)
+    l = f[off_l:off_l + N * H_q * 4].view(torch.float32).view(N, H_q)
+    o = f[off_o:off_o + N * H_q * d * 4].view(torch.float32).view(N, H_q, d)
+    return seg, m2, l, o
 
 
 def lse_merge(part_m2, part_l, part_o, split_counts=None, out=None, lse=None):

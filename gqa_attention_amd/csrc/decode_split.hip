@@ -1,11 +1,18 @@
 // decode_split.hip -- stage 1 of split-KV decode on gfx950.
 //
-// The keys of a sequence are cut into chunks and every chunk into slabs.  One
-// workgroup per (slab, group of up to 8 KV heads, sequence b) sweeps the slab's
-// keys with an online softmax and writes the slab's partial state (m2, l, O) for
-// every query head of those KV heads ("Attention Kernel lineage" (V07), section 17: split-K
-// partial kernel; section 2: running (m, l, O) update; ADR-0060 "AHBM GQA Fused
-// Attention", section 3: per-tile op sequence of the decode sweep).
+// Every sequence's keys are cut into 16-key tiles, and the tiles of all the
+// sequences of the batch, taken in order, into W equal contiguous partitions,
+// one per workgroup (W is about one per compute unit).  A workgroup sweeps its
+// partition with an online softmax for a group of up to 8 KV heads and, each
+// time its partition leaves a sequence, writes that sequence's partial state
+// (m2, l, O) for every query head of those KV heads ("Attention Kernel lineage"
+// (V07), section 17: split-K partial kernel, partitions of the key axis;
+// section 2: running (m, l, O) update; ADR-0060 "AHBM GQA Fused Attention",
+// section 3: per-tile op sequence of the decode sweep).  So the work is split
+// evenly however ragged the lengths are, a workgroup streams without a break
+// from its first tile to its last (the next tile's loads are issued before a
+// finished state is stored), and a sequence gets one state per workgroup that
+// touches it -- about W + B states per query head for the whole batch.
 //
 // GQA M-fold (ADR-0060 TL;DR and section 5.2; V07 section 14): the G query heads
 // of a KV head share every K/V tile, so each K/V byte is read from HBM once.
@@ -23,11 +30,11 @@
 // The 8 waves of a workgroup are spread over its KV heads, so at any moment the
 // workgroup streams whole [kv head][d] runs of consecutive cache rows (a probe on
 // MI355X read this pattern at ~6 TB/s against ~4.9 TB/s when each workgroup
-// owned one head's 256-byte slices of a longer key range).  The waves of one head
-// take interleaved 32-key tiles (the K-split of V07 section 7/8) with the next
-// tile's loads in flight while the current one is computed (ADR-0060 TL;DR,
-// software pipelining); with one wave per head the state is written straight
-// from registers, otherwise the waves merge through LDS (V07 section 8).
+// owned one head's 256-byte slices of a longer key range).  With fewer KV heads
+// than waves, the waves of one head take interleaved tiles (the K-split of V07
+// sections 7-8) and merge their states through LDS before a state is written.
+// Each wave keeps the next tile's loads in flight while it computes the current
+// one (ADR-0060 TL;DR, software pipelining).
 //
 // Scores are kept in log2 units: s2 = (q.k) * tau * log2(e), folded into one
 // fp32 multiplier applied to the fp32 accumulator (V07 section 2, exp2 trick).
@@ -37,9 +44,9 @@
 namespace gqa {
 namespace {
 
-constexpr int kTile = 16;   // keys per tile: one 16-row matrix-core tile
-constexpr int kDepth = 2;   // tiles in flight per wave
+constexpr int kTile = 16;      // keys per tile: one 16-row matrix-core tile
 constexpr int kWaves = 8;
+constexpr int kWindow = 64;    // paged: table lookups fetched at once, one per lane
 
 template <int D>
 struct DecodeTraits {
@@ -182,198 +189,295 @@ __device__ __forceinline__ void finish_state(WaveState<D> &st) {
     for (int dt = 0; dt < DecodeTraits<D>::NDT; ++dt) st.o[dt] *= f;
 }
 
+// Length of sequence b as the kernel uses it: seqlens[b] clamped to [0, S_max].
+__device__ __forceinline__ int seq_len(const DecodeSplitArgs &a, int b) {
+    return a.seqlens ? min(max(a.seqlens[b], 0), a.S_max) : a.S_max;
+}
+
+// Q^T fragments (B operand) of sequence b: column = query head h0 + row16, k-slots = d.
+// Columns past the group's last head repeat that head; their results are never stored.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[DecodeTraits<D>::KS], const DecodeSplitArgs &a,
+                                       int b, int h0, int nh, int row16, int grp) {
+    const uint16_t *qrow = a.q + ((size_t)b * a.H_q + h0 + min(row16, nh - 1)) * D + grp * (D / 4);
+#pragma unroll
+    for (int ks = 0; ks < DecodeTraits<D>::KS; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 8));
+}
+
 // Paged: the cache is a pool of pages of a.page consecutive key rows ([page][row][H_kv][d]),
 // and key t of sequence b is row t % page of page block_table[b][t / page] (V07 section
 // 16, logical token to page map; section 17, the decode kernel reads through the table).
-// Chunks and slabs start at multiples of 32 keys and a page holds a multiple of 16, so a
-// 16-key tile never crosses a page: each tile is one table lookup plus the contiguous
-// read of the unpaged cache.  The lookups of a wave's tiles (at most 8 of them) are
-// loaded once, one per lane, before the sweep (the table is read when the workgroup
-// starts, as V07 section 17 describes), and each tile takes its entry with a lane read.
+// Tiles start at multiples of 16 keys and a page holds a multiple of 16, so a tile never
+// crosses a page: each tile is one table lookup plus the contiguous read of the unpaged
+// cache.  A wave fetches the lookups of its next 64 tiles at once, one per lane (the table
+// is read ahead of the sweep, as V07 section 17 describes), and each tile takes its entry
+// with a lane read.
 template <int D, bool Paged>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitArgs a, int n_hg) {
     using T = DecodeTraits<D>;
-    // V staging during the sweep, then (several waves per head) the cross-wave merge
+    // V staging during the sweep; at a state boundary (several waves per head) the
+    // cross-wave merge
     constexpr int kStageBytes = kWaves * kTile * T::VPITCH * 2;
     constexpr int kMergeBytes = kWaves * 16 * (D + 2) * 4;
     __shared__ __attribute__((aligned(16)))
     uint16_t smem[(kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes) / 2];
-
-    const int p = blockIdx.x / a.slabs, sl = blockIdx.x % a.slabs;
-    const int hgrp = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
-    const int b = blockIdx.z;
-    const int G = a.H_q / a.H_kv;
-    const int Sb = a.seqlens ? min(max(a.seqlens[b], 0), a.S_max) : a.S_max;
-    const int c0 = p * a.chunk;
-    if (c0 >= Sb) return;  // the whole chunk is past the sequence end: its states are never read
-    const int c1 = min(c0 + a.chunk, Sb);
-    const int s0 = c0 + sl * a.slab;
-    const int s1 = min(s0 + a.slab, c1);
+    __shared__ int32_t pre[kMaxDecodeBatch + 1];   // pre[b]: tiles of sequences 0 .. b-1
+    __shared__ uint8_t last[kMaxDecodeBatch];      // keys in sequence b's last tile (1..16)
 
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row16 = lane & 15, grp = lane >> 4;
+    const int G = a.H_q / a.H_kv;
+    const int hgrp = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
     // wave w sweeps KV head hw of this workgroup's group; the wph waves of one head take
-    // interleaved 16-key tiles of the slab (phase = first tile)
+    // interleaved tiles of the partition (phase = first tile)
     const int wph = kWaves / a.hpw;
     const int hw = w % a.hpw, phase = w / a.hpw;
     const int hk = hgrp * a.hpw + hw;
     const int h0 = hk * G + hg * 16;
     const int nh = min(16, G - hg * 16);
-    // this slab's states: [b][state][H_q], state = p * slabs + sl
-    const size_t n_states = (size_t)a.P * a.slabs;
-    const size_t srow = ((size_t)b * n_states + (size_t)p * a.slabs + sl) * a.H_q;
 
-    if (s0 >= s1) {  // a slab past the end of a live chunk: mark its states empty
-        if (phase == 0 && lane < nh) {
-            a.part_m2[srow + h0 + lane] = neg_inf();
-            a.part_l[srow + h0 + lane] = 0.f;
+    // ---- running tile counts of the sequences ----
+    // Up to 64 sequences: every wave scans them in its own registers (lane b holds
+    // pre[b + 1] and last[b]), with no LDS and no barrier; more: wave 0 scans them into LDS.
+    const bool small = a.B <= 64;
+    int incl = 0, lastv = 0;
+    if (small) {
+        const int len = lane < a.B ? seq_len(a, lane) : 0;
+        incl = (len + kTile - 1) / kTile;
+        lastv = len - (incl - 1) * kTile;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int x = __shfl_up(incl, off);
+            if (lane >= off) incl += x;
         }
-        return;
+    } else {
+        if (w == 0) {
+            int carry = 0;
+            if (lane == 0) pre[0] = 0;
+            for (int base = 0; base < a.B; base += 64) {
+                const int b = base + lane;
+                const int len = b < a.B ? seq_len(a, b) : 0;
+                int n = (len + kTile - 1) / kTile;
+                if (b < a.B) last[b] = (uint8_t)(len - (n - 1) * kTile);
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int x = __shfl_up(n, off);
+                    if (lane >= off) n += x;
+                }
+                if (b < a.B) pre[b + 1] = carry + n;
+                carry += __shfl(n, 63);
+            }
+        }
+        __syncthreads();
     }
 
-    // Q^T fragments (B operand): column = query head h0 + row16, k-slots = d.  Columns past
-    // the group's last head repeat that head; their results are never stored.
-    bf16x8 qf[T::KS];
+    // pre[i] for a uniform i (scalar register), and for a per-lane i
+    auto P = [&](int i) {
+        return small ? (i == 0 ? 0 : __builtin_amdgcn_readlane(incl, i - 1))
+                     : __builtin_amdgcn_readfirstlane(pre[i]);
+    };
+    auto P_lane = [&](int i) {
+        const int v = small ? __shfl(incl, max(i - 1, 0)) : pre[i];
+        return i == 0 ? 0 : v;
+    };
+    // length of sequence b (which has tiles [lo, hi), hi > lo)
+    auto L = [&](int b, int lo, int hi) {
+        const int lt = small ? __builtin_amdgcn_readlane(lastv, b)
+                             : __builtin_amdgcn_readfirstlane((int)last[b]);
+        return (hi - lo - 1) * kTile + lt;
+    };
+
+    // ---- this workgroup's partition [t0, t1) of the batch's tiles ----
+    // W partitions, no more than there are tiles, so that none is empty: then the
+    // partitions that touch a sequence are consecutive and each holds a state of it
+    const int tot = P(a.B);
+    const int W = min((int)gridDim.x, tot), x = blockIdx.x;
+    // workgroup (0, 0) records where each sequence's states are for the merge: partition
+    // x holds its state of sequence b in slot x + b (unique: partitions advance with b)
+    if (blockIdx.x == 0 && blockIdx.y == 0 && (!small || w == 0)) {
+        for (int b = small ? lane : threadIdx.x; b < (small ? 64 : a.B); b += kWaves * 64) {
+            const int lo = P_lane(b), hi = P_lane(b + 1);
+            int first = 0, n = 0;
+            if (hi > lo) {
+                const int x0 = (int)((long)lo * W / tot), x1 = (int)((long)(hi - 1) * W / tot);
+                first = x0 + b;
+                n = x1 - x0 + 1;
+            }
+            if (b < a.B) {
+                a.seg[2 * b] = first;
+                a.seg[2 * b + 1] = n;
+            }
+        }
+    }
+    if (x >= W) return;     // no tiles left for this workgroup
+    const int t0 = (int)(((long)x * tot + W - 1) / W);
+    const int t1 = (int)(((long)(x + 1) * tot + W - 1) / W);
+
+    // the sequence holding tile t0: the last b with pre[b] <= t0 (it has tiles)
+    int cb = 0;
     {
-        const uint16_t *qrow =
-            a.q + ((size_t)b * a.H_q + h0 + min(row16, nh - 1)) * D + grp * (D / 4);
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 8));
+        int hi = a.B - 1;
+        while (cb < hi) {
+            const int mid = (cb + hi + 1) >> 1;
+            if (P(mid) <= t0) cb = mid;
+            else hi = mid - 1;
+        }
     }
 
     const size_t kv_row = (size_t)a.H_kv * D;
-    // unpaged: this sequence's cache, head hk; paged: the pool, head hk
-    const size_t head_off = Paged ? (size_t)hk * D : ((size_t)b * a.S_max * a.H_kv + hk) * D;
-    const uint16_t *kbase = a.k + head_off;
-    const uint16_t *vbase = a.v + head_off;
+    // unpaged: sequence 0's cache, head hk (plus b * S_max rows per sequence); paged: the
+    // pool, head hk
+    const uint16_t *kbase = a.k + (size_t)hk * D;
+    const uint16_t *vbase = a.v + (size_t)hk * D;
     uint16_t *vs = smem + w * kTile * T::VPITCH;
 
-    WaveState<D> st;
-    st.m = neg_inf();
-    st.l = 0.f;
-    st.lw = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // This wave's tiles are phase, phase + wph, ...; tile t starts at key0(t).  kDepth tiles
-    // are in flight in a ring of register sets: as soon as tile t's scores are formed and
-    // its V is staged, tile t + kDepth is loaded into the freed set, before the softmax and
-    // P.V of tile t.  Tiles past the end read zeros without touching memory, so every
-    // iteration issues the same loads and the load counter only drains the oldest tile.
-    const int ntiles = (s1 - s0 + kTile - 1) / kTile;
-    const int n_w = phase < ntiles ? (ntiles - 1 - phase) / wph + 1 : 0;
     TileOffsets<D> toff;
     toff.k = (uint32_t)((row16 * kv_row + grp * (D / 4)) * 2);
 #pragma unroll
     for (int i = 0; i < T::NVI; ++i)
         toff.v[i] = (uint32_t)(((i * T::RPI + lane / T::LPR) * kv_row + (lane % T::LPR) * 8) * 2);
-    auto key0 = [&](int t) { return s0 + (phase + t * wph) * kTile; };
-    // Paged: lane t holds the pool row of this wave's tile t (-1: no tile, or a table
-    // entry outside the pool, which then reads as zeros instead of faulting).
-    int prow = -1;
-    if constexpr (Paged) {
-        if (lane < n_w) {
-            const int key = key0(lane);
-            const int pg = a.block_table[(size_t)b * a.max_blocks + key / a.page];
-            if ((unsigned)pg < (unsigned)a.num_pages) prow = pg * a.page + key % a.page;
-        }
-    }
-    // Tile t of this wave: the address of its first row (in kt, vt) and the bytes that
-    // hold live keys (rows at or past the slab end read as zeros).
-    // (All of it is uniform; readfirstlane keeps the buffer resources in scalar registers.)
-    auto issue = [&](TileRegs<D> &r, int t) {
-        const int k0 = key0(t);
-        if constexpr (Paged) {
-            const int pr = __builtin_amdgcn_readlane(prow, t & 63);
-            const uint32_t live = (uint32_t)min(max(s1 - k0, 0), kTile);
-            const size_t row = (size_t)max(pr, 0) * kv_row;
-            const uint32_t bytes = __builtin_amdgcn_readfirstlane(
-                pr >= 0 ? live * (uint32_t)kv_row * 2u : 0u);
-            load_tile<D>(r, kbase + row, vbase + row, bytes, toff);
-        } else {
-            const size_t row = (size_t)k0 * kv_row;
-            load_tile<D>(r, kbase + row, vbase + row,
-                         (uint32_t)max(s1 - k0, 0) * (uint32_t)kv_row * 2u, toff);
-        }
-    };
-    TileRegs<D> ring[kDepth];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-        issue(ring[j], j);
-        __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: oldest tile first
-    }
-    // whole rounds of kDepth tiles (no exit inside a round, so every pass through the loop
-    // has the same loads outstanding), then the last n_w % kDepth tiles with no new loads
-    const int n_full = n_w - n_w % kDepth;
-    int t = 0;
-    for (; t < n_full; t += kDepth) {
-#pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-            const f32x4 sc = score_tile<D>(ring[j], qf, vs, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(ring[j], t + j + kDepth);
-            softmax_pv<D>(st, sc, vs, key0(t + j), s1, a.scale_log2, lane);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kDepth - 1; ++j) {
-        if (t + j >= n_w) break;
-        const f32x4 sc = score_tile<D>(ring[j], qf, vs, lane);
-        softmax_pv<D>(st, sc, vs, key0(t + j), s1, a.scale_log2, lane);
-    }
 
-    finish_state<D>(st);
-
-    if (wph == 1) {
-        // one wave per head: its registers hold the slab's whole state
-        if (row16 < nh) {
-            const size_t row = srow + h0 + row16;
-            float *orow = a.part_o + row * D + grp * 4;
-#pragma unroll
-            for (int dt = 0; dt < T::NDT; ++dt) *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[dt];
-            if (grp == 0) {
-                a.part_m2[row] = st.m;
-                a.part_l[row] = st.l;
+    // ---- issue side: the next tile this wave loads, and its sequence ----
+    int it = t0 + phase;                       // flattened tile index
+    int ib = cb, ilo = P(cb), ihi = P(cb + 1), ilen = L(cb, ilo, ihi);
+    int issued = 0;                            // tiles issued by this wave (paged windows)
+    int pw = -1;                               // paged: pool row of window tile `lane`
+    // Load tile `it` into r (past the partition end: zero bytes, no memory traffic).  All of
+    // it is uniform; readfirstlane keeps the buffer resources in scalar registers.
+    auto issue = [&](TileRegs<D> &r) {
+        uint32_t bytes = 0;
+        size_t row = 0;
+        if (it < t1) {
+            while (it >= ihi) {                // next sequence with tiles
+                ++ib;
+                ilo = ihi;
+                ihi = P(ib + 1);
+                if (ihi > ilo) ilen = L(ib, ilo, ihi);
             }
+            const int k0 = (it - ilo) * kTile;
+            bytes = (uint32_t)min(ilen - k0, kTile) * (uint32_t)kv_row * 2u;
+            if constexpr (!Paged) row = ((size_t)ib * a.S_max + k0) * kv_row;
         }
-        return;
-    }
+        if constexpr (Paged) {
+            if ((issued & (kWindow - 1)) == 0) {
+                // lane l: the wave's tile issued + l, i.e. flattened tile it + l * wph
+                pw = -1;
+                const int tl = it + lane * wph;
+                // its sequence: the last b with pre[b] <= tl, by a search whose every step
+                // all lanes take (the small-batch table is read across lanes)
+                const int tc = min(tl, t1 - 1);
+                int bl = 0;
+                for (int step = small ? 32 : kMaxDecodeBatch / 2; step > 0; step >>= 1) {
+                    const int mid = bl + step;
+                    const int pm = P_lane(min(mid, a.B));
+                    if (mid < a.B && pm <= tc) bl = mid;
+                }
+                const int pb = P_lane(bl);
+                if (tl < t1) {
+                    const int key = (tl - pb) * kTile;
+                    const int pg = a.block_table[(size_t)bl * a.max_blocks + key / a.page];
+                    if ((unsigned)pg < (unsigned)a.num_pages) pw = pg * a.page + key % a.page;
+                }
+            }
+            const int pr = __builtin_amdgcn_readlane(pw, issued & (kWindow - 1));
+            row = (size_t)max(pr, 0) * kv_row;
+            if (pr < 0) bytes = 0;             // an entry outside the pool reads as zeros
+        }
+        bytes = __builtin_amdgcn_readfirstlane(bytes);
+        load_tile<D>(r, kbase + row, vbase + row, bytes, toff);
+        it += wph;
+        ++issued;
+    };
 
-    // several waves per head: merge their states through LDS (reusing the V staging area):
-    // red[w][head][0..D) = O^T column, [D] = m, [D+1] = l
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(smem);
-    constexpr int RS = D + 2;
-    float *mine = red + (w * 16 + row16) * RS;
-#pragma unroll
-    for (int dt = 0; dt < T::NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mine[dt * 16 + grp * 4 + i] = st.o[dt][i];
-    if (grp == 0) {
-        mine[D] = st.m;
-        mine[D + 1] = st.l;
-    }
-    __syncthreads();
+    bf16x8 qf[T::KS];
+    load_q<D>(qf, a, cb, h0, nh, row16, grp);
+    TileRegs<D> ring;
+    __builtin_amdgcn_sched_barrier(0);
+    issue(ring);
 
-    for (int idx = threadIdx.x; idx < a.hpw * nh * D; idx += kWaves * 64) {
-        const int hw2 = idx / (nh * D), h = (idx / D) % nh, d = idx % D;
-        float M = neg_inf();
-        for (int ph = 0; ph < wph; ++ph) M = fmaxf(M, red[((hw2 + a.hpw * ph) * 16 + h) * RS + D]);
-        float L = 0.f, O = 0.f;
-        for (int ph = 0; ph < wph; ++ph) {
-            const float *rw = red + ((hw2 + a.hpw * ph) * 16 + h) * RS;
-            const float al = exp2_fast(rw[D] - M);  // a wave without tiles: 2^-inf = 0
-            L += al * rw[D + 1];
-            O += al * rw[d];
+    // ---- sweep: one state per sequence the partition touches ----
+    int tw = t0 + phase;                       // next tile this wave computes
+    while (true) {
+        const int slo = P(cb), shend = P(cb + 1);
+        const int shi = min(shend, t1);
+        const int len = L(cb, slo, shend);
+        WaveState<D> st;
+        st.m = neg_inf();
+        st.l = 0.f;
+        st.lw = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (; tw < shi; tw += wph) {
+            const f32x4 sc = score_tile<D>(ring, qf, vs, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(ring);                       // the next tile's loads go out first
+            softmax_pv<D>(st, sc, vs, (tw - slo) * kTile, len, a.scale_log2, lane);
         }
-        const int hk2 = hgrp * a.hpw + hw2;
-        const size_t row = srow + hk2 * G + hg * 16 + h;
-        a.part_o[row * D + d] = O;
-        if (d == 0) {
-            a.part_m2[row] = M;
-            a.part_l[row] = L;
+        finish_state<D>(st);
+
+        // the next sequence with tiles; its Q is requested before this state is stored
+        const bool more = shi < t1;
+        int nb = cb;
+        if (more) {
+            ++nb;
+            while (P(nb + 1) == P(nb)) ++nb;
+            load_q<D>(qf, a, nb, h0, nh, row16, grp);
         }
+        const size_t srow = (size_t)(x + cb) * a.H_q;   // states: [slot][H_q]
+
+        if (wph == 1) {
+            // one wave per head: its registers hold the whole state
+            if (row16 < nh) {
+                const size_t row = srow + h0 + row16;
+                float *orow = a.part_o + row * D + grp * 4;
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; ++dt)
+                    *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[dt];
+                if (grp == 0) {
+                    a.part_m2[row] = st.m;
+                    a.part_l[row] = st.l;
+                }
+            }
+        } else {
+            // several waves per head: merge their states through LDS (in the V staging
+            // area, which every wave has finished reading):
+            // red[w][head][0..D) = O^T column, [D] = m, [D+1] = l
+            __syncthreads();
+            float *red = reinterpret_cast<float *>(smem);
+            constexpr int RS = D + 2;
+            float *mine = red + (w * 16 + row16) * RS;
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mine[dt * 16 + grp * 4 + i] = st.o[dt][i];
+            if (grp == 0) {
+                mine[D] = st.m;
+                mine[D + 1] = st.l;
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < a.hpw * nh * D; idx += kWaves * 64) {
+                const int hw2 = idx / (nh * D), h = (idx / D) % nh, d = idx % D;
+                float M = neg_inf();
+                for (int ph = 0; ph < wph; ++ph)
+                    M = fmaxf(M, red[((hw2 + a.hpw * ph) * 16 + h) * RS + D]);
+                float L = 0.f, O = 0.f;
+                for (int ph = 0; ph < wph; ++ph) {
+                    const float *rw = red + ((hw2 + a.hpw * ph) * 16 + h) * RS;
+                    const float al = exp2_fast(rw[D] - M);   // a wave without tiles: 0
+                    L += al * rw[D + 1];
+                    O += al * rw[d];
+                }
+                const size_t row = srow + (hgrp * a.hpw + hw2) * G + hg * 16 + h;
+                a.part_o[row * D + d] = O;
+                if (d == 0) {
+                    a.part_m2[row] = M;
+                    a.part_l[row] = L;
+                }
+            }
+            __syncthreads();   // the staging area is reused by the next sequence
+        }
+        if (!more) break;
+        cb = nb;
     }
 }
 
@@ -381,7 +485,7 @@ template <int D>
 hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
     const int G = a.H_q / a.H_kv;
     const int n_hg = (G + 15) / 16;
-    dim3 grid(a.P * a.slabs, (a.H_kv / a.hpw) * n_hg, a.B);
+    dim3 grid(a.units, (a.H_kv / a.hpw) * n_hg);
     if (a.block_table)
         hipLaunchKernelGGL((decode_split_kernel<D, true>), grid, dim3(kWaves * 64), 0, stream, a,
                            n_hg);

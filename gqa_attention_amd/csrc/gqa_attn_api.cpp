@@ -36,8 +36,6 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 constexpr int kMaxSplits = 65535;
 constexpr int kGridYZ = 65535;
-constexpr int kSplitAlign = 32;       // chunk lengths are multiples of the kernel's key tile
-constexpr int kAutoChunk = 1024;       // num_splits = 0: chunks of 1024 keys
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kPagedTile = 16;         // a page holds whole 16-key tiles of the decode sweep
 constexpr int kMaxPage = 1 << 16;
@@ -45,14 +43,15 @@ constexpr int kMaxPage = 1 << 16;
 bool decode_head_size_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
 struct Plan {
-    int P, chunk;       // chunks of the longest sequence, keys per chunk
-    int slab, slabs;    // keys per slab, slabs per chunk
+    int units;          // partitions of the batch's tiles (workgroups per head-group row)
     int hpw;            // KV heads swept together by one workgroup
-    size_t off_l, off_o, bytes;
+    int slots;          // partial-state slots per query head: units + B - 1
+    size_t off_m2, off_l, off_o, bytes;
 };
 
 constexpr int kDecodeWaves = 8;        // waves per decode workgroup
-constexpr int kSlabTilesPerWave = 4;   // 32-key tiles per wave in a full slab
+constexpr int kDecodeTile = 16;        // keys per tile of the decode sweep
+constexpr int kTargetWorkgroups = 256; // auto partition count: one workgroup per MI355X CU
 
 int check_heads(int B, int H_q, int H_kv) {
     if (B <= 0 || H_q <= 0 || H_kv <= 0)
@@ -68,39 +67,33 @@ int make_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *
     if (!decode_head_size_ok(d))
         return fail(GQA_ERR_UNSUPPORTED, "decode head size d=%d (supported: 32, 64, 128)", d);
     if (S_max <= 0) return fail(GQA_ERR_BAD_SHAPE, "S_max=%d must be positive", S_max);
+    if (B > gqa::kMaxDecodeBatch)
+        return fail(GQA_ERR_BAD_SHAPE, "decode batch B=%d exceeds %d", B, gqa::kMaxDecodeBatch);
+    const long tiles = (long)B * ((S_max + kDecodeTile - 1) / kDecodeTile);
+    if (tiles > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B * ceil(S_max/16) = %ld exceeds 2^31 - 1", tiles);
     if (num_splits < 0 || num_splits > kMaxSplits)
         return fail(GQA_ERR_SPLITS, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
     const int G = H_q / H_kv;
     const long n_hg = (G + 15) / 16;
-    if ((long)H_kv * n_hg > kGridYZ || B > kGridYZ)
-        return fail(GQA_ERR_BAD_SHAPE, "B=%d or H_kv*ceil(G/16)=%ld exceeds %d", B,
-                    (long)H_kv * n_hg, kGridYZ);
-    long chunk;
-    if (num_splits > 0)
-        chunk = ((long)S_max + num_splits - 1) / num_splits;
-    else
-        chunk = S_max < kAutoChunk ? S_max : kAutoChunk;
-    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-    long P = ((long)S_max + chunk - 1) / chunk;
     // KV heads per workgroup: the largest power of two <= 8 that divides H_kv; the
     // workgroup's 8 waves are spread evenly over them
-    int hpw = 8;
+    int hpw = kDecodeWaves;
     while (H_kv % hpw) hpw /= 2;
-    const long wph = kDecodeWaves / hpw;
-    long slab = 32L * kSlabTilesPerWave * wph;
-    if (slab > chunk) slab = chunk;
-    const long slabs = (chunk + slab - 1) / slab;
-    if (P * slabs > 0x7FFFFFFFL)
-        return fail(GQA_ERR_SPLITS, "too many chunk slabs (%ld)", P * slabs);
-    pl->P = (int)P;
-    pl->chunk = (int)chunk;
-    pl->slab = (int)slab;
-    pl->slabs = (int)slabs;
+    const long rows = (long)(H_kv / hpw) * n_hg;
+    if (rows > kGridYZ)
+        return fail(GQA_ERR_BAD_SHAPE, "H_kv/%d * ceil(G/16) = %ld exceeds %d", hpw, rows, kGridYZ);
+    // at least num_splits partitions, and at least enough workgroups to fill the device
+    const long fill = (kTargetWorkgroups + rows - 1) / rows;
+    const long units = num_splits > fill ? num_splits : fill;
+    pl->units = (int)units;
     pl->hpw = hpw;
-    const size_t rows = (size_t)B * H_q * (size_t)P * (size_t)slabs;
-    pl->off_l = align256(rows * sizeof(float));
-    pl->off_o = pl->off_l + align256(rows * sizeof(float));
-    pl->bytes = pl->off_o + align256(rows * (size_t)d * sizeof(float));
+    pl->slots = (int)(units + B - 1);
+    const size_t states = (size_t)pl->slots * H_q;
+    pl->off_m2 = align256((size_t)B * 2 * sizeof(int32_t));
+    pl->off_l = pl->off_m2 + align256(states * sizeof(float));
+    pl->off_o = pl->off_l + align256(states * sizeof(float));
+    pl->bytes = pl->off_o + align256(states * (size_t)d * sizeof(float));
     return GQA_OK;
 }
 
@@ -155,7 +148,8 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
     a.seqlens = seqlens;
-    a.part_m2 = reinterpret_cast<float *>(base);
+    a.seg = reinterpret_cast<int32_t *>(base);
+    a.part_m2 = reinterpret_cast<float *>(base + pl.off_m2);
     a.part_l = reinterpret_cast<float *>(base + pl.off_l);
     a.part_o = reinterpret_cast<float *>(base + pl.off_o);
     a.B = B;
@@ -163,10 +157,7 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.H_kv = H_kv;
     a.d = d;
     a.S_max = S_max;
-    a.chunk = pl.chunk;
-    a.P = pl.P;
-    a.slab = pl.slab;
-    a.slabs = pl.slabs;
+    a.units = pl.units;
     a.hpw = pl.hpw;
     a.scale_log2 = scale * kLog2e;
     a.block_table = nullptr;
@@ -176,21 +167,18 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     return a;
 }
 
-gqa::MergeArgs combine_args(const int32_t *seqlens, void *o, float *lse, int B, int H_q, int d,
-                            int S_max, const Plan &pl, const void *ws) {
+gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Plan &pl,
+                            const void *ws) {
     const char *base = static_cast<const char *>(ws);
     gqa::MergeArgs m;
-    m.part_m2 = reinterpret_cast<const float *>(base);
+    m.part_m2 = reinterpret_cast<const float *>(base + pl.off_m2);
     m.part_l = reinterpret_cast<const float *>(base + pl.off_l);
     m.part_o = reinterpret_cast<const float *>(base + pl.off_o);
-    m.counts = seqlens;
-    m.counts_are_lengths = 1;
-    m.chunk = pl.chunk;
-    m.slabs = pl.slabs;
-    m.S_max = S_max;
-    m.P = pl.P * pl.slabs;
-    m.batch_stride = (long)m.P * H_q;   // workspace: [B][state][H_q]
-    m.head_stride = 1;
+    m.seg = reinterpret_cast<const int32_t *>(base);
+    m.counts = nullptr;
+    m.P = pl.slots;
+    m.batch_stride = 0;
+    m.head_stride = 1;                  // workspace: [slot][H_q]
     m.state_stride = H_q;
     m.o = static_cast<uint16_t *>(o);
     m.lse = lse;
@@ -257,16 +245,13 @@ const char *gqa_last_error(void) { return g_err; }
 
 const char *gqa_version(void) { return "gqa_attn 0.1.0 (gfx950)"; }
 
-int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, int *chunks_out,
-                    int *chunk_keys_out, int *slabs_out, int *slab_keys_out,
-                    size_t *workspace_bytes_out) {
+int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
+                    int *partitions_out, int *states_out, size_t *workspace_bytes_out) {
     Plan pl;
     int rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl);
     if (rc) return rc;
-    if (chunks_out) *chunks_out = pl.P;
-    if (chunk_keys_out) *chunk_keys_out = pl.chunk;
-    if (slabs_out) *slabs_out = pl.slabs;
-    if (slab_keys_out) *slab_keys_out = pl.slab;
+    if (partitions_out) *partitions_out = pl.units;
+    if (states_out) *states_out = pl.slots;
     if (workspace_bytes_out) *workspace_bytes_out = pl.bytes;
     return ok();
 }
@@ -288,16 +273,15 @@ int gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
     return ok();
 }
 
-int gqa_decode_combine(const int32_t *seqlens, void *o, float *lse, int B, int H_q, int H_kv,
-                       int d, int S_max, int num_splits, const void *workspace,
-                       size_t workspace_bytes, void *stream) {
+int gqa_decode_combine(void *o, float *lse, int B, int H_q, int H_kv, int d, int S_max,
+                       int num_splits, const void *workspace, size_t workspace_bytes,
+                       void *stream) {
     Plan pl;
     int rc;
     if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
     if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
-    if (seqlens && !aligned(seqlens, 4)) return fail(GQA_ERR_ALIGNMENT, "seqlens misaligned");
     if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
-    auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
     if ((rc = hip_status(gqa::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "lse_merge")))
         return rc;
     return ok();
@@ -317,7 +301,7 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
     auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
                         workspace);
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split"))) return rc;
-    auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -353,7 +337,7 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.num_pages = num_pages;
     a.max_blocks = max_blocks;
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
-    auto m = combine_args(seqlens, o, lse, B, H_q, d, S_max, pl, workspace);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -380,10 +364,7 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
     m.part_l = part_l;
     m.part_o = part_o;
     m.counts = split_counts;
-    m.counts_are_lengths = 0;
-    m.chunk = 1;
-    m.slabs = 1;
-    m.S_max = 0;
+    m.seg = nullptr;
     m.P = max_splits;
     m.batch_stride = (long)H_q * max_splits;   // caller's partials: [B][H_q][P]
     m.head_stride = max_splits;

@@ -10,19 +10,22 @@
 
 namespace gqa {
 
-// Split-KV plan: the keys of a sequence are cut into chunks of `chunk` keys (P chunks for
-// the longest sequence) and every chunk into `slabs` slabs of `slab` keys (the last ragged).
-// One workgroup sweeps one slab for `hpw` KV heads at once, so it reads whole runs of the
-// cache's [token][kv head][d] rows; each (query head, chunk, slab) gets one partial state,
-// stored state-major: [B][chunk * slabs + slab][H_q] (O: [..][d]), so the states a
-// workgroup writes are contiguous.
+// Largest batch of one decode launch: every workgroup keeps the running tile counts of the
+// batch's sequences in LDS.
+constexpr int kMaxDecodeBatch = 8192;
+
+// Split-KV plan: the 16-key tiles of all sequences of the batch, in order, are cut into
+// `units` equal contiguous partitions, one workgroup each (per group of `hpw` KV heads and
+// 16-head slice of a group, blockIdx.y).  Partition x writes its partial state of sequence b
+// (m2, l, O for every query head of its KV heads) in state slot x + b; states are stored
+// slot-major, [slot][H_q] (O: [slot][H_q][d]), and seg[b] = {first slot, count} of b.
 struct DecodeSplitArgs {
     const uint16_t *q, *k, *v;  // bf16 bit patterns
     const int32_t *seqlens;     // [B] or nullptr
     float *part_m2, *part_l, *part_o;
+    int32_t *seg;               // [B][2], written by workgroup (0, 0)
     int B, H_q, H_kv, d, S_max;
-    int chunk, P;               // keys per chunk, chunks of the longest sequence
-    int slab, slabs;            // keys per slab, slabs per chunk
+    int units;                  // partitions (workgroups along x)
     int hpw;                    // KV heads per workgroup (divides H_kv and the wave count)
     float scale_log2;           // softmax_scale * log2(e)
     // Paged cache when block_table is not null: k and v are pools [num_pages][page][H_kv][d]
@@ -32,14 +35,17 @@ struct DecodeSplitArgs {
     int page, num_pages, max_blocks;
 };
 
-// Partial state (b, h, p) sits at index b*batch_stride + h*head_stride + p*state_stride of
-// the m2 and l arrays, and at d times that index in the O array.
+// Partial states to merge for (b, h):
+//   seg != nullptr (decode workspace): states p < seg[2b+1], at index
+//     (seg[2b] + p) * state_stride + h * head_stride;
+//   otherwise (caller's partials): states p < (counts ? clamp(counts[b], 0, P) : P), at index
+//     b * batch_stride + h * head_stride + p * state_stride.
+// The O array holds d values per index.
 struct MergeArgs {
     const float *part_m2, *part_l, *part_o;
+    const int32_t *seg;         // [B][2] or nullptr
     const int32_t *counts;      // [B] or nullptr
-    int counts_are_lengths;     // 1: counts are sequence lengths, states = ceil(len/chunk)*slabs
-    int chunk, slabs, S_max;    // used when counts_are_lengths
-    int P;                      // states per row when counts is nullptr (and the upper bound)
+    int P;
     long batch_stride, head_stride, state_stride;
     uint16_t *o;                // bf16 out [B, H_q, d]
     float *lse;                 // [B, H_q]

@@ -57,18 +57,16 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = 2 * w + (lane >> 5), hl = lane & 31;
 
-    int n = a.P;
-    if (a.counts) {
-        int c = a.counts[b];
-        if (a.counts_are_lengths) {
-            c = min(max(c, 0), a.S_max);
-            n = (c + a.chunk - 1) / a.chunk * a.slabs;
-        } else {
-            n = min(max(c, 0), a.P);
-        }
+    int n;
+    size_t row0;
+    if (a.seg) {
+        n = a.seg[2 * b + 1];
+        row0 = (size_t)a.seg[2 * b] * a.state_stride + (size_t)h * a.head_stride;
+    } else {
+        n = a.counts ? min(max(a.counts[b], 0), a.P) : a.P;
+        row0 = (size_t)b * a.batch_stride + (size_t)h * a.head_stride;
     }
     const size_t row = (size_t)b * a.H_q + h;
-    const size_t row0 = (size_t)b * a.batch_stride + (size_t)h * a.head_stride;
     const size_t ss = a.state_stride;
     const float *m2 = a.part_m2 + row0;
     const float *lp = a.part_l + row0;

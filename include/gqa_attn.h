@@ -67,32 +67,30 @@ const char *gqa_version(void);
 
 /*
  * Split-KV plan of a decode launch (V07, section 17, split-K decode: the key
- * axis of every sequence is cut into partitions whose partial states a second
- * stage merges; ADR-0060, section 4: the partial states are combined in two
- * levels).
+ * axis is cut into partitions whose partial states a second stage merges;
+ * ADR-0060, section 4: the partial states are combined in two levels).
  *
- * The keys of each sequence are cut into contiguous chunks of `chunk_keys`
- * keys, and every chunk into `slabs` contiguous slabs of `slab_keys` keys (the
- * last chunk and the last slab of a chunk may be ragged).  chunk_keys is
- * ceil(S_max / num_splits) rounded up to a multiple of 32, so a sequence of the
- * longest length S_max gets `chunks` = ceil(S_max / chunk_keys) <= num_splits
- * chunks and a sequence of length S_b gets ceil(S_b / chunk_keys).
- * num_splits = 0 lets the library choose (chunks of 1024 keys).  One workgroup
- * sweeps one slab for up to 8 KV heads at once (slab_keys is 128 keys per wave
- * of each head, at most a chunk), so it streams whole runs of consecutive cache
- * rows; every (query head, chunk, slab) gets one partial state, and the merge
- * combines all of a row's states (the merge is associative: V07, section 3).
+ * Each sequence's keys [0, seqlen) are cut into 16-key tiles; the tiles of all
+ * sequences of the batch, in order (sequence 0's first), are cut into
+ * `partitions` equal contiguous ranges, and one workgroup sweeps each range for
+ * a group of up to 8 KV heads.  Every time a range leaves a sequence it yields
+ * that sequence's partial state, so a sequence gets one state per range that
+ * touches it, however ragged the lengths; the merge combines them (the merge is
+ * associative: V07, section 3).  partitions = max(num_splits, the number that
+ * fills the device: 256 workgroups in total); num_splits = 0 lets the library
+ * choose.  A launch whose batch has fewer tiles than that uses one partition
+ * per tile.  Partition x and sequence b share state slot x + b, so there are
+ * `states` = partitions + B - 1 slots per query head.
  *
- * Outputs (any may be NULL): *chunks_out, *chunk_keys_out, *slabs_out (slabs
- * per chunk), *slab_keys_out, *workspace_bytes_out (decode workspace the
- * launch needs).
+ * Outputs (any may be NULL): *partitions_out, *states_out, *workspace_bytes_out
+ * (decode workspace the launch needs).
  *
  * Supported: d in {32, 64, 128}; any G = H_q / H_kv (groups above 16 query
- * heads run as several workgroups per KV head); 0 <= num_splits <= 65535.
+ * heads run as several workgroups per KV head); 1 <= B <= 8192;
+ * B * ceil(S_max / 16) < 2^31; 0 <= num_splits <= 65535.
  */
 int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
-                    int *chunks_out, int *chunk_keys_out, int *slabs_out, int *slab_keys_out,
-                    size_t *workspace_bytes_out);
+                    int *partitions_out, int *states_out, size_t *workspace_bytes_out);
 
 /*
  * gqa_attn_decode -- one query token per sequence against its KV cache.
@@ -100,10 +98,10 @@ int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
  * The G query heads of a KV head are folded into the rows of one matrix
  * product so each K/V tile is read from HBM once for all of them (ADR-0060,
  * TL;DR and section 5.2: M-fold; V07, section 14, GQA kernel layout).  Each
- * slab of the split plan (see gqa_decode_plan) runs an online-softmax sweep
- * (V07, section 2: running (m, l, O) update; section 7: deferred division),
- * then a separate merge kernel combines the partial states of all slabs of all
- * chunks (V07, section 3 merge formula; section 17, second stage of split-K
+ * partition of the split plan (see gqa_decode_plan) runs an online-softmax
+ * sweep (V07, section 2: running (m, l, O) update; section 7: deferred
+ * division), then a separate merge kernel combines each sequence's partial
+ * states (V07, section 3 merge formula; section 17, second stage of split-K
  * decode).
  * There is no causal mask: the query sees every cached key [0, seqlen)
  * (ADR-0060, section 5.2).
@@ -119,13 +117,13 @@ int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
  *   lse      [B, H_q]           fp32, device, written (natural log)
  *   workspace / workspace_bytes: device scratch of at least the size
  *            gqa_decode_plan reports for the same arguments (256-byte aligned).
- *            Layout, with N = chunks * slabs partial states per row, state index
- *            n = chunk * slabs + slab, stored state-major so that the states one
- *            workgroup writes are contiguous: m2 [B][N][H_q] fp32 (running max, log2
- *            units), then l [B][N][H_q] fp32, then O [B][N][H_q][d] fp32
- *            (unnormalised), each region starting at a 256-byte boundary.  States of
- *            chunks past a sequence's end are not written; a slab past the end inside
- *            a live chunk gets m2 = -inf (its O is not written).
+ *            Layout, with N = `states` slots per query head, each region starting
+ *            at a 256-byte boundary: seg [B][2] int32 (first slot and number of
+ *            slots of each sequence's states), then m2 [N][H_q] fp32 (running max,
+ *            log2 units), l [N][H_q] fp32, O [N][H_q][d] fp32 (unnormalised).
+ *            Sequence b's states are slots seg[b][0] .. seg[b][0] + seg[b][1] - 1;
+ *            other slots are not written.  A state is defined up to a common
+ *            shift of its (m2, l, O).
  *
  * Calls that share a workspace on overlapping streams race.
  */
@@ -140,7 +138,8 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
  * arguments and workspace layout (V07, section 17: stage 1 writes the partial
  * (m, l, O) of every partition, stage 2 merges them).  gqa_decode_partials
  * runs the split-KV sweep and fills the workspace; gqa_decode_combine runs the
- * merge kernel on it.  Calling them in this order on one stream is exactly
+ * merge kernel on it (the workspace carries each sequence's slot range, so the
+ * merge needs no lengths).  Calling them in this order on one stream is exactly
  * gqa_attn_decode.
  */
 int gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
@@ -149,7 +148,7 @@ int gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                         float softmax_scale, int num_splits,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-int gqa_decode_combine(const int32_t *seqlens, void *o, float *lse,
+int gqa_decode_combine(void *o, float *lse,
                        int B, int H_q, int H_kv, int d, int S_max, int num_splits,
                        const void *workspace, size_t workspace_bytes, void *stream);
 

@@ -47,38 +47,29 @@ def test_status_strings(lib):
 
 
 @pytest.mark.parametrize("args,expect", [
-    # (B, H_q, H_kv, d, S_max, num_splits) -> (chunks, chunk_keys, slabs, slab_keys)
-    ((1, 64, 8, 128, 32768, 32), (32, 1024, 8, 128)),   # Llama decode: 32 chunks of 1024 keys
-    ((1, 8, 2, 32, 512, 4), (4, 128, 1, 128)),          # tiny decode: 4 chunks of 128 keys
-    ((8, 64, 8, 128, 131072, 64), (64, 2048, 16, 128)),  # ragged decode bound: 2048-key chunks
-    ((8, 64, 8, 128, 131000, 64), (64, 2048, 16, 128)),  # chunk rounded up to a multiple of 32
-    ((1, 64, 8, 128, 100, 32), (4, 32, 1, 32)),          # chunk rounded up to the 32-key tile
-    ((1, 8, 1, 128, 5000, 2), (2, 2528, 3, 1024)),       # one KV head: 8 waves, 1024-key slabs
-    ((1, 24, 6, 64, 1000, 1), (1, 1024, 2, 512)),        # 6 KV heads: 2 per workgroup
+    # (B, H_q, H_kv, d, S_max, num_splits) -> partitions (workgroups per head-group row)
+    ((1, 64, 8, 128, 32768, 32), 256),     # Llama decode: 8 heads per workgroup, 256 partitions
+    ((1, 64, 8, 128, 32768, 0), 256),      # auto: one workgroup per CU
+    ((8, 64, 8, 128, 131072, 64), 256),    # ragged decode: the same 256, whatever the lengths
+    ((1, 64, 8, 128, 32768, 1000), 1000),  # num_splits above the fill count is kept
+    ((1, 8, 2, 32, 512, 4), 256),          # tiny decode: most partitions empty
+    ((1, 32, 1, 32, 257, 2), 128),         # G = 32: two head-group rows share the 256
+    ((1, 24, 6, 64, 1000, 1), 86),         # 6 KV heads: 2 per workgroup, 3 rows
 ])
 def test_decode_plan(args, expect):
     plan = g.decode_plan(*args)
-    assert (plan["chunks"], plan["chunk_keys"], plan["slabs"], plan["slab_keys"]) == expect
-    B, H_q, _, d, S_max, _ = args
-    rows = B * H_q * plan["states"]
+    assert plan["partitions"] == expect
+    B, H_q, _, d, _, _ = args
+    assert plan["states"] == expect + B - 1
     a256 = lambda n: (n + 255) // 256 * 256
-    assert plan["workspace_bytes"] == 2 * a256(rows * 4) + a256(rows * d * 4)
-    P, chunk = plan["chunks"], plan["chunk_keys"]
-    assert (P - 1) * chunk < S_max <= P * chunk
-    assert (plan["slabs"] - 1) * plan["slab_keys"] < chunk <= plan["slabs"] * plan["slab_keys"]
-
-
-def test_decode_plan_auto_uses_1024_key_chunks():
-    plan = g.decode_plan(1, 64, 8, 128, 32768, 0)
-    assert plan["chunk_keys"] == 1024 and plan["chunks"] == 32
-    plan = g.decode_plan(1, 8, 2, 32, 100, 0)
-    assert plan["chunk_keys"] == 128 and plan["chunks"] == 1     # short sequence: one chunk
+    n = plan["states"] * H_q
+    assert plan["workspace_bytes"] == a256(B * 8) + 2 * a256(n * 4) + a256(n * d * 4)
 
 
 def test_decode_plan_workspace_size_at_llama_shape():
-    # 32 chunks x 8 slabs x 64 heads x (m, l, 128-wide O) fp32 partial states
+    # 256 partitions x 64 heads x (m, l, 128-wide O) fp32 partial states, plus the slot table
     plan = g.decode_plan(1, 64, 8, 128, 32768, 32)
-    assert plan["workspace_bytes"] == 32 * 8 * 64 * (128 + 2) * 4
+    assert plan["workspace_bytes"] == 256 + 256 * 64 * (128 + 2) * 4
 
 
 @pytest.mark.parametrize("args,code", [
@@ -88,9 +79,11 @@ def test_decode_plan_workspace_size_at_llama_shape():
     ((1, 64, 8, 96, 1024, 0), UNSUP),        # head size without a kernel
     ((1, 64, 8, 128, 1024, -1), SPLITS),
     ((1, 64, 8, 128, 1024, 70000), SPLITS),
+    ((8193, 8, 2, 32, 16, 0), SHAPE),        # batch above the LDS sequence table
+    ((4096, 8, 2, 32, 1 << 30, 0), SHAPE),   # B * ceil(S_max / 16) >= 2^31
 ])
 def test_decode_plan_rejects(lib, args, code):
-    rc = lib.gqa_decode_plan(*args, None, None, None, None, None)
+    rc = lib.gqa_decode_plan(*args, None, None, None)
     assert rc == code
     assert lib.gqa_last_error().decode() != ""
 
@@ -117,8 +110,8 @@ def test_decode_rejects_before_launch(lib, kw, code):
 def test_stage_calls_reject_before_launch(lib):
     assert lib.gqa_decode_partials(None, A, A, None, 1, 8, 2, 32, 512, 0.1, 4, A, 1 << 30,
                                    None) == NULLP
-    assert lib.gqa_decode_combine(None, A, A, 1, 8, 2, 32, 512, 4, A, 10, None) == WS
-    assert lib.gqa_decode_combine(None, MIS, A, 1, 8, 2, 32, 512, 4, A, 1 << 30, None) == ALIGN
+    assert lib.gqa_decode_combine(A, A, 1, 8, 2, 32, 512, 4, A, 10, None) == WS
+    assert lib.gqa_decode_combine(MIS, A, 1, 8, 2, 32, 512, 4, A, 1 << 30, None) == ALIGN
 
 
 def _paged(lib, q=A, kp=A, vp=A, tbl=A, seqlens=None, o=A, lse=A, B=1, H_q=8, H_kv=2, d=32,

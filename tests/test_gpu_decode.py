@@ -15,10 +15,20 @@ from parity import check, to_f64
 pytestmark = pytest.mark.gpu
 
 
+def poisoned_workspace(B, H_q, H_kv, d, S_max, num_splits):
+    """A decode workspace filled with 0xFF bytes (NaN floats): a state slot the kernel
+    did not write but the merge read would turn the output into NaN."""
+    ws = g.decode_workspace(B, H_q, H_kv, d, S_max, num_splits)
+    ws.fill_(0xFF)
+    return ws
+
+
 def run_decode(inp, num_splits, use_seqlens=True, scale=None):
     q, k, v = (to_gpu_bf16(inp[x]) for x in ("q", "k", "v"))
     sl = to_gpu_i32(inp["seqlens"]) if use_seqlens else None
-    o, lse = g.decode(q, k, v, sl, softmax_scale=scale, num_splits=num_splits)
+    B, S_max, H_kv, d = inp["k"].shape
+    ws = poisoned_workspace(B, inp["q"].shape[1], H_kv, d, S_max, num_splits)
+    o, lse = g.decode(q, k, v, sl, softmax_scale=scale, num_splits=num_splits, workspace=ws)
     torch.cuda.synchronize()
     return o, lse
 
@@ -59,7 +69,12 @@ CASES = [
     (1, 8, 2, 128, 1, 1),               # a single cached key
     (1, 8, 2, 32, 33, 1),               # one ragged tile past a full one
     (3, 8, 2, 128, (1, 5000), 16),      # ragged lengths, tiny to long
-    (2, 64, 8, 128, 2048, 64),          # 32-key chunks: one tile per workgroup
+    (2, 64, 8, 128, 2048, 64),          # more partitions than the fill count
+    (64, 8, 2, 64, (0, 300), 0),        # many short sequences, some empty: partitions
+                                        # cross several sequence boundaries
+    (300, 8, 1, 128, (1, 50), 0),       # MQA (8 waves per head) at ~2 tiles per partition
+    (5, 16, 2, 128, (1000, 3000), 0),   # 4 waves per head, boundaries inside partitions
+    (2, 8, 2, 32, (1, 20), 0),          # fewer tiles than partitions: most are empty
 ]
 
 
@@ -114,36 +129,64 @@ def test_decode_zero_scale_and_custom_scale(gpu_available):
             assert np.max(np.abs(to_f64(lse) - math.log(500))) < 1e-5
 
 
+def slot_key_ranges(seqlens, S_max, partitions):
+    """Host restatement of the split plan: {(b, slot): (j0, j1)} -- the keys of sequence b
+    whose partial state partition x = slot - b holds (16-key tiles of all sequences in
+    order, cut into `partitions` equal contiguous ranges)."""
+    tiles = [-(-min(max(int(n), 0), S_max) // 16) for n in seqlens]
+    pre = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int64)
+    tot = int(pre[-1])
+    W = min(partitions, tot)        # no partition is left without tiles
+    beg = [(x * tot + W - 1) // W for x in range(W + 1)]
+    out = {}
+    for b, n in enumerate(seqlens):
+        n = min(max(int(n), 0), S_max)
+        for x in range(W):
+            lo, hi = max(beg[x], pre[b]), min(beg[x + 1], pre[b + 1])
+            if lo < hi:
+                out[(b, x + b)] = (int(lo - pre[b]) * 16, min(int(hi - pre[b]) * 16, n))
+    return out
+
+
 def test_decode_stages_equal_one_call_and_are_deterministic(gpu_available):
-    inp = decode_inputs(1, 64, 8, 128, S_max=8192, seed=10)
+    inp = decode_inputs(3, 64, 8, 128, ragged=(100, 6000), seed=10)
     q, k, v = (to_gpu_bf16(inp[x]) for x in ("q", "k", "v"))
-    say("decode determinism and stage split")
-    o1, l1 = g.decode(q, k, v, None, num_splits=8)
-    o2, l2 = g.decode(q, k, v, None, num_splits=8)
-    ws = g.decode_workspace(1, 64, 8, 128, 8192, 8)
-    g.decode_partials(q, k, v, None, ws, num_splits=8)
+    sl = to_gpu_i32(inp["seqlens"])
+    S = inp["S_max"]
+    say(f"decode determinism and stage split, seqlens={inp['seqlens'].tolist()}")
+    o1, l1 = g.decode(q, k, v, sl, num_splits=8)
+    o2, l2 = g.decode(q, k, v, sl, num_splits=8)
+    ws = g.decode_workspace(3, 64, 8, 128, S, 8)
+    g.decode_partials(q, k, v, sl, ws, num_splits=8)
     o3 = torch.empty_like(o1)
     l3 = torch.empty_like(l1)
-    g.decode_combine(None, ws, o3, l3, H_kv=8, S_max=8192, num_splits=8)
+    g.decode_combine(ws, o3, l3, H_kv=8, S_max=S, num_splits=8)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
-    # the workspace holds one partial state per (chunk, slab): they match the oracle's
-    plan = g.decode_plan(1, 64, 8, 128, 8192, 8)
-    m2, lp, op = g.workspace_views(ws, 1, 64, 8, 128, 8192, 8)
-    chunk, slabs, slab = plan["chunk_keys"], plan["slabs"], plan["slab_keys"]
-    for p, sl in ((0, 0), (3, slabs - 1), (7, 2)):
-        j0 = p * chunk + sl * slab
-        j1 = min(j0 + slab, (p + 1) * chunk)
-        m_ref, l_ref, o_ref = oracle.decode_partial(inp["q"], inp["k"], inp["v"], j0, j1)
-        n = p * slabs + sl
+    # the workspace holds one partial state per (partition, sequence) pair: the slot table
+    # and a sample of the states match the plan restated on the host and the oracle
+    plan = g.decode_plan(3, 64, 8, 128, S, 8)
+    seg, m2, lp, op = g.workspace_views(ws, 3, 64, 8, 128, S, 8)
+    ranges = slot_key_ranges(inp["seqlens"], S, plan["partitions"])
+    seg = seg.cpu().numpy()
+    for b in range(3):
+        slots = sorted(sl_ for (bb, sl_) in ranges if bb == b)
+        assert seg[b, 0] == slots[0] and seg[b, 1] == len(slots)
+        assert slots == list(range(slots[0], slots[0] + len(slots)))
+    picks = sorted(ranges)[::max(1, len(ranges) // 6)]
+    for b, slot in picks:
+        j0, j1 = ranges[(b, slot)]
+        m_ref, l_ref, o_ref = oracle.decode_partial(inp["q"][b:b + 1], inp["k"][b:b + 1],
+                                                    inp["v"][b:b + 1], j0, j1)
         # a state is defined up to a common shift: the kernel's stored max may trail the
-        # slab's true max by up to 2^8 in log2 units; l and O are relative to it
-        m_gpu = to_f64(m2[..., n]) * math.log(2.0)
+        # range's true max by up to 2^8 in log2 units; l and O are relative to it
+        m_gpu = to_f64(m2[slot]) * math.log(2.0)
+        m_ref, l_ref, o_ref = m_ref[0], l_ref[0], o_ref[0]
         assert np.all(m_gpu <= m_ref + 1e-4) and np.all(m_gpu >= m_ref - 8 * math.log(2.0) - 1e-4)
         shift = np.exp(m_gpu - m_ref)
-        np.testing.assert_allclose(to_f64(lp[..., n]), l_ref / shift, rtol=5e-3)
-        got = to_f64(op[..., n, :])
+        np.testing.assert_allclose(to_f64(lp[slot]), l_ref / shift, rtol=5e-3)
+        got = to_f64(op[slot])
         want = o_ref / shift[..., None]
         assert np.linalg.norm(got - want) / np.linalg.norm(want) < 5e-3
 

@@ -28,7 +28,11 @@ def upload(p):
 
 def run_paged(p, num_splits=0, use_seqlens=True):
     q, kp, vp, tbl, sl = upload(p)
-    o, lse = g.decode_paged(q, kp, vp, tbl, sl if use_seqlens else None, num_splits=num_splits)
+    B, H_q, d = p["q"].shape
+    ws = g.decode_workspace(B, H_q, p["k_pool"].shape[2], d, p["S_max"], num_splits)
+    ws.fill_(0xFF)        # NaN in every slot: one read without being written shows
+    o, lse = g.decode_paged(q, kp, vp, tbl, sl if use_seqlens else None, num_splits=num_splits,
+                            workspace=ws)
     torch.cuda.synchronize()
     return o, lse
 
