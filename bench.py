@@ -3,8 +3,9 @@
 
 One step is one pass over both entry points of the library on synthetic bf16
 N(0,1) inputs at Llama3-70B head shapes (H_q=64, H_kv=8, G=8, d=128):
-  1. split-KV decode of one token against a 32768-token cache in 32 chunks
-     (decode_split kernel, then the lse_merge kernel), and
+  1. split-KV decode of one token against a 32768-token cache, split into at
+     least 32 partitions (the library raises it to one workgroup per CU: 256
+     partitions of 128 keys; decode_split kernel, then the lse_merge kernel), and
   2. causal prefill of an 8192-token prompt (prefill_causal kernel).
 Inputs are resident in HBM before the timed region.  The decode reads one of
 ``--kv-copies`` distinct copies of the cache per step (4 x 128 MiB by default),
@@ -63,9 +64,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("243b6eb04cc08272", 143_295_866),
-    "lse_merge": ("b9c1048188cb8ec4", 9_540_201),
-    "prefill_causal": ("9817723fdbd09895", 421_950_158),
+    "decode_split": ("82cf24dad0dfc092", 143_033_444),
+    "lse_merge": ("6e1b89a44c4920f5", 9_541_007),
+    "prefill_causal": ("820f829619befa29", 421_864_135),
 }
 
 
@@ -258,6 +259,7 @@ def main():
     kv_copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.kv_copies - 1)]
     del dinp
     ws = g.decode_workspace(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
+    plan = g.decode_plan(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
     o_d = torch.empty((dc.B, dc.H_q, dc.d), dtype=torch.bfloat16, device="cuda")
     lse_d = torch.empty((dc.B, dc.H_q), dtype=torch.float32, device="cuda")
 
@@ -353,10 +355,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "Llama3-70B GQA attention: decode B=1 S_kv=32768 (32 splits) + "
-                        "causal prefill B=1 S=8192",
+            "workload": "Llama3-70B GQA attention: decode B=1 S_kv=32768 (num_splits 32, "
+                        f"{plan['partitions']} partitions) + causal prefill B=1 S=8192",
             "H_q": 64, "H_kv": 8, "d": 128,
             "decode": {"B": dc.B, "S_kv": dc.S_kv, "num_splits": dc.num_splits,
+                       "partitions": plan["partitions"],
                        "kv_copies": len(kv_copies)},
             "prefill": {"B": pc.B, "S": pc.S},
         },
