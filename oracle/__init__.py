@@ -165,6 +165,34 @@ def prefill_chunk(q, k, v, q_start=None, tau=None, nthreads=0, lib=None):
     return o, lse.reshape(B, H_q, T)
 
 
+def decode_tokens(q, k, v, seqlens=None, tau=None, nthreads=0, lib=None):
+    """Decode of T query tokens per sequence, the last T of its cached keys: token i of
+    sequence b sits at position L_b - T + i (L_b = seqlens[b], keys [0, L_b) cached) and
+    sees keys j <= L_b - T + i -- the G query heads' T tokens are the G*T rows that the
+    M-fold stacks (ADR-0060 sections 0.5.2 and 5.2).  Per sequence this is the causal
+    chunk of ``prefill_chunk`` with q_start = L_b - T; a token whose position is negative
+    (L_b < T) sees no key and gets O = 0, LSE = -inf.
+
+    q [B, T, H_q, d]; k, v [B, S_max, H_kv, d]; seqlens int32 [B] or None (= S_max).
+    Returns (o [B, T, H_q, d], lse [B, H_q, T]) in float64.
+    """
+    B, T, H_q, d = q.shape
+    S_max = k.shape[1]
+    lens = np.full(B, S_max) if seqlens is None else np.asarray(seqlens)
+    o = np.zeros((B, T, H_q, d), dtype=np.float64)
+    lse = np.full((B, H_q, T), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(min(max(int(lens[b]), 0), S_max))
+        first = max(T - L, 0)              # tokens before it have negative positions
+        if first >= T:
+            continue
+        ob, lb = prefill_chunk(q[b:b + 1, first:], k[b:b + 1, :L], v[b:b + 1, :L],
+                               q_start=L - T + first, tau=tau, nthreads=nthreads, lib=lib)
+        o[b, first:] = ob[0]
+        lse[b, :, first:] = lb[0]
+    return o, lse
+
+
 def gather_pages(pool, block_table, seqlens, page_size):
     """The cache of every sequence in logical token order, read out of a paged pool.
 

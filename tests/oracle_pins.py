@@ -448,4 +448,33 @@ def pin_paged_worked_example(lib):
         assert np.array_equal(oc[0], o[r]) and np.array_equal(lc[0], lse[r])
 
 
+# ---------------------------------------------------------------------------
+# Decode of T tokens per sequence (the M-fold of G*T rows, ADR-0060 section 5.2).
+
+def pin_decode_tokens_reduces_to_decode_and_chunks(lib):
+    """T = 1 is the one-token decode; for T > 1 each sequence's tokens are the rows of its
+    whole-prompt causal prefill at the last T positions; a token with a negative position
+    (length below T) sees nothing."""
+    inp = decode_inputs(3, 8, 2, 16, ragged=(5, 40), seed=34)
+    q1 = inp["q"][:, None].copy()
+    o, lse = oracle.decode_tokens(q1, inp["k"], inp["v"], inp["seqlens"], lib=lib)
+    od, ld = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seqlens"], lib=lib)
+    assert np.array_equal(o[:, 0], od) and np.array_equal(lse[..., 0], ld)
+    T = 4
+    pin = prefill_inputs(3, 40, 8, 2, 16, seed=35)
+    lens = np.array([40, 17, 4], dtype=np.int32)
+    qs = np.stack([pin["q"][b, lens[b] - T:lens[b]] for b in range(3)])
+    o, lse = oracle.decode_tokens(qs, pin["k"], pin["v"], lens, lib=lib)
+    for b in range(3):
+        n = int(lens[b])
+        of, lf = oracle.prefill_causal(pin["q"][b:b + 1, :n].copy(), pin["k"][b:b + 1, :n].copy(),
+                                       pin["v"][b:b + 1, :n].copy(), lib=lib)
+        assert np.array_equal(o[b], of[0, n - T:]) and np.array_equal(lse[b], lf[0, :, n - T:])
+    short = np.array([40, 2, 0], dtype=np.int32)
+    o, lse = oracle.decode_tokens(qs, pin["k"], pin["v"], short, lib=lib)
+    assert np.all(o[1, :2] == 0) and np.all(lse[1, :, :2] == -np.inf)
+    assert np.all(np.isfinite(lse[1, :, 2:]))
+    assert np.all(o[2] == 0) and np.all(lse[2] == -np.inf)
+
+
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
