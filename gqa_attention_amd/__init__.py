@@ -64,6 +64,12 @@ def load_library(path=LIBRARY):
     L.gqa_attn_decode_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci, ci,
                                         ci, cf, ci, vp, cs, vp]
     L.gqa_attn_decode_paged.restype = ci
+    L.gqa_decode_tokens_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci),
+                                         ctypes.POINTER(ci), ctypes.POINTER(cs)]
+    L.gqa_decode_tokens_plan.restype = ci
+    L.gqa_attn_decode_tokens.argtypes = [vp, vp, vp, i32p, vp, f32p, ci, ci, ci, ci, ci, ci, cf,
+                                         ci, vp, cs, vp]
+    L.gqa_attn_decode_tokens.restype = ci
     L.gqa_lse_merge.argtypes = [f32p, f32p, f32p, i32p, ci, vp, f32p, ci, ci, ci, vp]
     L.gqa_lse_merge.restype = ci
     L.gqa_attn_prefill_causal.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, cf, vp]
@@ -187,6 +193,44 @@ def decode_paged(q, k_pool, v_pool, block_table, seqlens=None, softmax_scale=Non
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seqlens), _ptr(o), _ptr(l),
         B, H_q, H_kv, d, page, num_pages, max_blocks, _scale(d, softmax_scale), num_splits,
         _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return o, l
+
+
+def decode_tokens_plan(B, T_q, H_q, H_kv, d, S_max, num_splits=0):
+    """Split plan of a multi-token decode (see decode_plan)."""
+    L = load_library()
+    P, N = ctypes.c_int(), ctypes.c_int()
+    ws = ctypes.c_size_t()
+    _check(L.gqa_decode_tokens_plan(B, T_q, H_q, H_kv, d, S_max, num_splits, ctypes.byref(P),
+                                    ctypes.byref(N), ctypes.byref(ws)))
+    return {"partitions": P.value, "states": N.value, "workspace_bytes": ws.value}
+
+
+def decode_tokens(q, k_cache, v_cache, seqlens=None, softmax_scale=None, num_splits=0, out=None,
+                  lse=None, workspace=None):
+    """Decode of T_q tokens per sequence (the last T_q cached positions, causal among them):
+    q [B,T_q,H_q,d], caches [B,S_max,H_kv,d] bf16 -> (o [B,T_q,H_q,d], lse [B,H_q,T_q])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, T, H_q, d = q.shape
+    Bk, S_max, H_kv, dk = k_cache.shape
+    if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, "
+                         f"v {tuple(v_cache.shape)}")
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, 1)
+        if seqlens.shape[0] != B:
+            raise ValueError("seqlens must have B entries")
+    if workspace is None:
+        nbytes = decode_tokens_plan(B, T, H_q, H_kv, d, S_max, num_splits)["workspace_bytes"]
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H_q, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(load_library().gqa_attn_decode_tokens(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(l), B, T, H_q, H_kv,
+        d, S_max, _scale(d, softmax_scale), num_splits, _ptr(workspace), workspace.numel(),
+        _stream(q.device)))
     return o, l
 
 

@@ -92,6 +92,10 @@ __device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kt, co
 // passes it by more than this, so P <= 2^kSlack in between (exact: a common shift
 // cancels in O / l, V07 section 3).
 constexpr float kSlack = 8.f;
+// Running max before a column's first live key: finite, so that 2^(kNoMax - kNoMax) = 1
+// and 2^(-inf - kNoMax) = 0 (no -inf - -inf); a state that never saw a live key is
+// stored with m2 = -inf, the empty state of the merge.
+constexpr float kNoMax = -1e30f;
 
 template <int D>
 struct WaveState {
@@ -120,14 +124,15 @@ __device__ __forceinline__ f32x4 score_tile(const TileRegs<D> &r,
     return s;
 }
 
-// Second half: online softmax of the tile's scores and O^T += V^T . P^T.
+// Second half: online softmax of the tile's scores and O^T += V^T . P^T.  key_end is this
+// lane's column's bound: its query sees keys below it.
 template <int D>
 __device__ __forceinline__ void softmax_pv(WaveState<D> &st, f32x4 s, const uint16_t *vs,
                                            int key0, int key_end, float scale_log2, int lane) {
     using T = DecodeTraits<D>;
     const int row16 = lane & 15, grp = lane >> 4;
 
-    // scale to log2 units; keys past the slab/sequence end are masked
+    // scale to log2 units; keys at or past the column's bound are masked
     float s2[4];
     float mx = neg_inf();
 #pragma unroll
@@ -136,14 +141,16 @@ __device__ __forceinline__ void softmax_pv(WaveState<D> &st, f32x4 s, const uint
         s2[i] = x;
         mx = fmaxf(mx, x);
     }
-    // Each lane holds 4 of a head's 16 scores.  Only when one of them passes the shared
-    // max by the slack (always on the first tile, where m = -inf) do the head's 4 lanes
-    // agree on a new max and rescale; otherwise no cross-lane step is needed.
+    // Each lane holds 4 of a column's 16 scores.  Only when one of them passes the shared
+    // max by the slack (always on the first live key, as m starts at kNoMax) do the
+    // column's 4 lanes agree on a new max and rescale; otherwise no cross-lane step is
+    // needed.  A column with no live key yet keeps m = kNoMax, so its alpha is 1 and its
+    // P is 0 when another column moves the wave into the rescale.
     if (__any(mx > st.m + kSlack)) {
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
         const float m_new = fmaxf(st.m, mx);
-        const float alpha = exp2_fast(st.m - m_new);   // 0 on the first tile
+        const float alpha = exp2_fast(st.m - m_new);   // 0 on a column's first live key
         st.l *= alpha;
         st.lw *= alpha;
 #pragma unroll
@@ -194,12 +201,16 @@ __device__ __forceinline__ int seq_len(const DecodeSplitArgs &a, int b) {
     return a.seqlens ? min(max(a.seqlens[b], 0), a.S_max) : a.S_max;
 }
 
-// Q^T fragments (B operand) of sequence b: column = query head h0 + row16, k-slots = d.
-// Columns past the group's last head repeat that head; their results are never stored.
+// Q^T fragments (B operand) of sequence b: column row16 of this wave's 16-column group is
+// query row (g, i) = (head hk * G + g, token i) of the G * T rows folded for KV head hk
+// (q is [B][T][H_q][d]); k-slots = d.  Columns past the group's last row repeat that row;
+// their results are never stored.
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[DecodeTraits<D>::KS], const DecodeSplitArgs &a,
-                                       int b, int h0, int nh, int row16, int grp) {
-    const uint16_t *qrow = a.q + ((size_t)b * a.H_q + h0 + min(row16, nh - 1)) * D + grp * (D / 4);
+                                       int b, int hk, int G, int col, int grp) {
+    const int g = col / a.T, i = col % a.T;
+    const uint16_t *qrow =
+        a.q + (((size_t)b * a.T + i) * a.H_q + hk * G + g) * D + grp * (D / 4);
 #pragma unroll
     for (int ks = 0; ks < DecodeTraits<D>::KS; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 8));
 }
@@ -227,14 +238,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row16 = lane & 15, grp = lane >> 4;
     const int G = a.H_q / a.H_kv;
+    const int GT = G * a.T;                 // rows folded per KV head: G heads x T tokens
     const int hgrp = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
     // wave w sweeps KV head hw of this workgroup's group; the wph waves of one head take
     // interleaved tiles of the partition (phase = first tile)
     const int wph = kWaves / a.hpw;
     const int hw = w % a.hpw, phase = w / a.hpw;
     const int hk = hgrp * a.hpw + hw;
-    const int h0 = hk * G + hg * 16;
-    const int nh = min(16, G - hg * 16);
+    const int h0 = hk * GT + hg * 16;      // first state row of this wave's columns
+    const int nh = min(16, GT - hg * 16);
+    const int col = hg * 16 + min(row16, nh - 1);   // this lane's column (g, token)
+    const int tok_gap = a.T - 1 - col % a.T;         // tokens after this column's token
 
     // ---- running tile counts of the sequences ----
     // Up to 64 sequences: every wave scans them in its own registers (lane b holds
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     };
 
     bf16x8 qf[T::KS];
-    load_q<D>(qf, a, cb, h0, nh, row16, grp);
+    load_q<D>(qf, a, cb, hk, G, col, grp);
     TileRegs<D> ring;
     __builtin_amdgcn_sched_barrier(0);
     issue(ring);
@@ -402,18 +416,21 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         const int shi = min(shend, t1);
         const int len = L(cb, slo, shend);
         WaveState<D> st;
-        st.m = neg_inf();
+        st.m = kNoMax;
         st.l = 0.f;
         st.lw = 0.f;
 #pragma unroll
         for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the column's token sits at position len - 1 - tok_gap and sees keys up to it
+        const int key_end = len - tok_gap;
         for (; tw < shi; tw += wph) {
             const f32x4 sc = score_tile<D>(ring, qf, vs, lane);
             __builtin_amdgcn_sched_barrier(0);
             issue(ring);                       // the next tile's loads go out first
-            softmax_pv<D>(st, sc, vs, (tw - slo) * kTile, len, a.scale_log2, lane);
+            softmax_pv<D>(st, sc, vs, (tw - slo) * kTile, key_end, a.scale_log2, lane);
         }
         finish_state<D>(st);
+        if (!(st.l > 0.f)) st.m = neg_inf();   // no live key: the empty state
 
         // the next sequence with tiles; its Q is requested before this state is stored
         const bool more = shi < t1;
@@ -421,9 +438,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         if (more) {
             ++nb;
             while (P(nb + 1) == P(nb)) ++nb;
-            load_q<D>(qf, a, nb, h0, nh, row16, grp);
+            load_q<D>(qf, a, nb, hk, G, col, grp);
         }
-        const size_t srow = (size_t)(x + cb) * a.H_q;   // states: [slot][H_q]
+        const size_t srow = (size_t)(x + cb) * a.H_q * a.T;   // states: [slot][H_q * T]
 
         if (wph == 1) {
             // one wave per head: its registers hold the whole state
@@ -463,14 +480,15 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
                 float L = 0.f, O = 0.f;
                 for (int ph = 0; ph < wph; ++ph) {
                     const float *rw = red + ((hw2 + a.hpw * ph) * 16 + h) * RS;
-                    const float al = exp2_fast(rw[D] - M);   // a wave without tiles: 0
+                    // a wave with no live key for this column adds nothing
+                    const float al = rw[D] == neg_inf() ? 0.f : exp2_fast(rw[D] - M);
                     L += al * rw[D + 1];
                     O += al * rw[d];
                 }
-                const size_t row = srow + (hgrp * a.hpw + hw2) * G + hg * 16 + h;
+                const size_t row = srow + (hgrp * a.hpw + hw2) * GT + hg * 16 + h;
                 a.part_o[row * D + d] = O;
                 if (d == 0) {
-                    a.part_m2[row] = M;
+                    a.part_m2[row] = L > 0.f ? M : neg_inf();
                     a.part_l[row] = L;
                 }
             }
@@ -483,8 +501,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
 
 template <int D>
 hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
-    const int G = a.H_q / a.H_kv;
-    const int n_hg = (G + 15) / 16;
+    const int GT = a.H_q / a.H_kv * a.T;
+    const int n_hg = (GT + 15) / 16;
     dim3 grid(a.units, (a.H_kv / a.hpw) * n_hg);
     if (a.block_table)
         hipLaunchKernelGGL((decode_split_kernel<D, true>), grid, dim3(kWaves * 64), 0, stream, a,

@@ -52,6 +52,7 @@ struct Plan {
 constexpr int kDecodeWaves = 8;        // waves per decode workgroup
 constexpr int kDecodeTile = 16;        // keys per tile of the decode sweep
 constexpr int kTargetWorkgroups = 256; // auto partition count: one workgroup per MI355X CU
+constexpr int kMaxDecodeTokens = 16;   // query tokens per sequence of a multi-token decode
 
 int check_heads(int B, int H_q, int H_kv) {
     if (B <= 0 || H_q <= 0 || H_kv <= 0)
@@ -61,9 +62,11 @@ int check_heads(int B, int H_q, int H_kv) {
     return GQA_OK;
 }
 
-int make_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *pl) {
+int make_plan(int B, int T, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *pl) {
     int rc = check_heads(B, H_q, H_kv);
     if (rc) return rc;
+    if (T < 1 || T > kMaxDecodeTokens)
+        return fail(GQA_ERR_BAD_SHAPE, "T_q=%d outside [1, %d]", T, kMaxDecodeTokens);
     if (!decode_head_size_ok(d))
         return fail(GQA_ERR_UNSUPPORTED, "decode head size d=%d (supported: 32, 64, 128)", d);
     if (S_max <= 0) return fail(GQA_ERR_BAD_SHAPE, "S_max=%d must be positive", S_max);
@@ -75,7 +78,7 @@ int make_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *
     if (num_splits < 0 || num_splits > kMaxSplits)
         return fail(GQA_ERR_SPLITS, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
     const int G = H_q / H_kv;
-    const long n_hg = (G + 15) / 16;
+    const long n_hg = ((long)G * T + 15) / 16;   // 16-row groups of a KV head's G * T rows
     // KV heads per workgroup: the largest power of two <= 8 that divides H_kv; the
     // workgroup's 8 waves are spread evenly over them
     int hpw = kDecodeWaves;
@@ -89,7 +92,7 @@ int make_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits, Plan *
     pl->units = (int)units;
     pl->hpw = hpw;
     pl->slots = (int)(units + B - 1);
-    const size_t states = (size_t)pl->slots * H_q;
+    const size_t states = (size_t)pl->slots * H_q * T;
     pl->off_m2 = align256((size_t)B * 2 * sizeof(int32_t));
     pl->off_l = pl->off_m2 + align256(states * sizeof(float));
     pl->off_o = pl->off_l + align256(states * sizeof(float));
@@ -141,7 +144,7 @@ int decode_common_checks(const void *q, const void *k, const void *v, const int3
 
 gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
                                 const int32_t *seqlens, int B, int H_q, int H_kv, int d, int S_max,
-                                float scale, const Plan &pl, void *ws) {
+                                float scale, const Plan &pl, void *ws, int T = 1) {
     char *base = static_cast<char *>(ws);
     gqa::DecodeSplitArgs a;
     a.q = static_cast<const uint16_t *>(q);
@@ -157,6 +160,7 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.H_kv = H_kv;
     a.d = d;
     a.S_max = S_max;
+    a.T = T;
     a.units = pl.units;
     a.hpw = pl.hpw;
     a.scale_log2 = scale * kLog2e;
@@ -168,7 +172,7 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
 }
 
 gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Plan &pl,
-                            const void *ws) {
+                            const void *ws, int T = 1) {
     const char *base = static_cast<const char *>(ws);
     gqa::MergeArgs m;
     m.part_m2 = reinterpret_cast<const float *>(base + pl.off_m2);
@@ -178,13 +182,14 @@ gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Pl
     m.counts = nullptr;
     m.P = pl.slots;
     m.batch_stride = 0;
-    m.head_stride = 1;                  // workspace: [slot][H_q]
-    m.state_stride = H_q;
+    m.head_stride = 1;                  // workspace: [slot][H_q * T]
+    m.state_stride = (long)H_q * T;
     m.o = static_cast<uint16_t *>(o);
     m.lse = lse;
     m.B = B;
     m.H_q = H_q;
     m.d = d;
+    m.T = T;
     return m;
 }
 
@@ -248,7 +253,7 @@ const char *gqa_version(void) { return "gqa_attn 0.1.0 (gfx950)"; }
 int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
                     int *partitions_out, int *states_out, size_t *workspace_bytes_out) {
     Plan pl;
-    int rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl);
+    int rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl);
     if (rc) return rc;
     if (partitions_out) *partitions_out = pl.units;
     if (states_out) *states_out = pl.slots;
@@ -262,7 +267,7 @@ int gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                         size_t workspace_bytes, void *stream) {
     Plan pl;
     int rc;
-    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
     if ((rc = decode_common_checks(q, k_cache, v_cache, seqlens, softmax_scale))) return rc;
     if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
     auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
@@ -278,7 +283,7 @@ int gqa_decode_combine(void *o, float *lse, int B, int H_q, int H_kv, int d, int
                        void *stream) {
     Plan pl;
     int rc;
-    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
     if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
     if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
     auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
@@ -293,7 +298,7 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                     size_t workspace_bytes, void *stream) {
     Plan pl;
     int rc;
-    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
     if ((rc = decode_common_checks(q, k_cache, v_cache, seqlens, softmax_scale))) return rc;
     if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
     if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
@@ -323,7 +328,7 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
     const int S_max = max_blocks * page_size;
     Plan pl;
     int rc;
-    if ((rc = make_plan(B, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
     if ((rc = decode_common_checks(q, k_pool, v_pool, seqlens, softmax_scale))) return rc;
     if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
     if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
@@ -338,6 +343,36 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.max_blocks = max_blocks;
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
     auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
+    if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
+    return ok();
+}
+
+int gqa_decode_tokens_plan(int B, int T_q, int H_q, int H_kv, int d, int S_max, int num_splits,
+                           int *partitions_out, int *states_out, size_t *workspace_bytes_out) {
+    Plan pl;
+    int rc = make_plan(B, T_q, H_q, H_kv, d, S_max, num_splits, &pl);
+    if (rc) return rc;
+    if (partitions_out) *partitions_out = pl.units;
+    if (states_out) *states_out = pl.slots;
+    if (workspace_bytes_out) *workspace_bytes_out = pl.bytes;
+    return ok();
+}
+
+int gqa_attn_decode_tokens(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *seqlens, void *o, float *lse, int B, int T_q, int H_q,
+                           int H_kv, int d, int S_max, float softmax_scale, int num_splits,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, T_q, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = decode_common_checks(q, k_cache, v_cache, seqlens, softmax_scale))) return rc;
+    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
+                        workspace, T_q);
+    if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (tokens)"))) return rc;
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q);
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -365,6 +400,7 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
     m.part_o = part_o;
     m.counts = split_counts;
     m.seg = nullptr;
+    m.T = 1;
     m.P = max_splits;
     m.batch_stride = (long)H_q * max_splits;   // caller's partials: [B][H_q][P]
     m.head_stride = max_splits;

@@ -16,15 +16,19 @@ constexpr int kMaxDecodeBatch = 8192;
 
 // Split-KV plan: the 16-key tiles of all sequences of the batch, in order, are cut into
 // `units` equal contiguous partitions, one workgroup each (per group of `hpw` KV heads and
-// 16-head slice of a group, blockIdx.y).  Partition x writes its partial state of sequence b
-// (m2, l, O for every query head of its KV heads) in state slot x + b; states are stored
-// slot-major, [slot][H_q] (O: [slot][H_q][d]), and seg[b] = {first slot, count} of b.
+// 16-row slice of a group's rows, blockIdx.y).  A KV head's rows are its G query heads times
+// the T query tokens of a sequence (T = 1: one-token decode), row (h, i) = h * T + i; token
+// i is the sequence's position len - T + i and sees keys up to it.  Partition x writes its
+// partial state of sequence b (m2, l, O of every row of its KV heads) in state slot x + b;
+// states are stored slot-major, [slot][H_q * T] (O: [..][d]), and seg[b] = {first slot,
+// count} of b.
 struct DecodeSplitArgs {
-    const uint16_t *q, *k, *v;  // bf16 bit patterns
+    const uint16_t *q, *k, *v;  // bf16 bit patterns; q [B][T][H_q][d]
     const int32_t *seqlens;     // [B] or nullptr
     float *part_m2, *part_l, *part_o;
     int32_t *seg;               // [B][2], written by workgroup (0, 0)
     int B, H_q, H_kv, d, S_max;
+    int T;                      // query tokens per sequence
     int units;                  // partitions (workgroups along x)
     int hpw;                    // KV heads per workgroup (divides H_kv and the wave count)
     float scale_log2;           // softmax_scale * log2(e)
@@ -35,21 +39,21 @@ struct DecodeSplitArgs {
     int page, num_pages, max_blocks;
 };
 
-// Partial states to merge for (b, h):
+// Partial states to merge for (b, r), r = h * T + i the row of query head h, token i:
 //   seg != nullptr (decode workspace): states p < seg[2b+1], at index
-//     (seg[2b] + p) * state_stride + h * head_stride;
-//   otherwise (caller's partials): states p < (counts ? clamp(counts[b], 0, P) : P), at index
-//     b * batch_stride + h * head_stride + p * state_stride.
-// The O array holds d values per index.
+//     (seg[2b] + p) * state_stride + r * head_stride;
+//   otherwise (caller's partials, T = 1): states p < (counts ? clamp(counts[b], 0, P) : P),
+//     at index b * batch_stride + r * head_stride + p * state_stride.
+// The O array holds d values per index.  Outputs: o [B][T][H_q][d], lse [B][H_q][T].
 struct MergeArgs {
     const float *part_m2, *part_l, *part_o;
     const int32_t *seg;         // [B][2] or nullptr
     const int32_t *counts;      // [B] or nullptr
     int P;
     long batch_stride, head_stride, state_stride;
-    uint16_t *o;                // bf16 out [B, H_q, d]
-    float *lse;                 // [B, H_q]
-    int B, H_q, d;
+    uint16_t *o;                // bf16 out
+    float *lse;
+    int B, H_q, d, T;
 };
 
 // Causal prefill of T query rows per sequence, row i being token q_start + i (sees keys

@@ -1,6 +1,7 @@
 // lse_merge.hip -- stage 2 of split-KV decode on gfx950: merge partial states.
 //
-// For each (sequence b, query head h), over its partials p < n_b
+// For each (sequence b, query row: head h and, for a multi-token decode, token i),
+// over its partials p < n_b
 // ("Attention Kernel lineage" (V07), section 3 merge formula and section 17,
 // second stage of split-K decode; ADR-0060 "AHBM GQA Fused Attention",
 // section 4, merge of (m, l, O) triplets):
@@ -53,7 +54,8 @@ template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
     constexpr int DPL = D / 32;           // columns per lane of a half-wave
     __shared__ float red[kHalves][D + 2];
-    const int h = blockIdx.x, b = blockIdx.y;
+    const int r = blockIdx.x, b = blockIdx.y;     // row r = h * T + i
+    const int h = r / a.T, i = r % a.T;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = 2 * w + (lane >> 5), hl = lane & 31;
 
@@ -61,12 +63,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
     size_t row0;
     if (a.seg) {
         n = a.seg[2 * b + 1];
-        row0 = (size_t)a.seg[2 * b] * a.state_stride + (size_t)h * a.head_stride;
+        row0 = (size_t)a.seg[2 * b] * a.state_stride + (size_t)r * a.head_stride;
     } else {
         n = a.counts ? min(max(a.counts[b], 0), a.P) : a.P;
-        row0 = (size_t)b * a.batch_stride + (size_t)h * a.head_stride;
+        row0 = (size_t)b * a.batch_stride + (size_t)r * a.head_stride;
     }
-    const size_t row = (size_t)b * a.H_q + h;
     const size_t ss = a.state_stride;
     const float *m2 = a.part_m2 + row0;
     const float *lp = a.part_l + row0;
@@ -123,13 +124,16 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
         o += al * red[i][d];
     }
     const float inv = empty ? 0.f : 1.f / Lt;
-    a.o[row * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
-    if (d == 0) a.lse[row] = empty ? neg_inf() : kLn2 * (Mt + __builtin_log2f(Lt));
+    a.o[(((size_t)b * a.T + i) * a.H_q + h) * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
+    if (d == 0)
+        a.lse[((size_t)b * a.H_q + h) * a.T + i] =
+            empty ? neg_inf() : kLn2 * (Mt + __builtin_log2f(Lt));
 }
 
 template <int D>
 hipError_t launch(const MergeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q, a.B), dim3(kMergeWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q * a.T, a.B), dim3(kMergeWaves * 64), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

@@ -193,6 +193,40 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gqa_attn_decode_tokens -- decode of T_q query tokens per sequence (a short
+ * chunk: speculative decoding, small chunked prefill) against its KV cache.
+ *
+ * The T_q tokens of sequence b are the last T_q of its seqlens[b] cached keys:
+ * token i sits at position seqlens[b] - T_q + i and sees keys j <= that
+ * position (causal among the new tokens).  The G query heads' T_q tokens are
+ * folded into the rows of one matrix product, G * T_q rows per KV head, so each
+ * K/V tile is read once for all of them (ADR-0060, section 5.2: Q [G, T_q, d]
+ * reshaped to [G * T_q, d] with the KV tile shared by every row; section 0.5.2:
+ * T_q is the width of the launch's query block).  Groups of more than 16 rows
+ * run as several workgroups per KV head.  Otherwise as gqa_attn_decode, which
+ * is the T_q = 1 case.
+ *
+ *   q        [B, T_q, H_q, d]    bf16, device, read-only
+ *   k_cache, v_cache, seqlens: as gqa_attn_decode; a token whose position is
+ *            negative (seqlens[b] < T_q) sees no key: O = 0, LSE = -inf.
+ *   o        [B, T_q, H_q, d]    bf16, device, written
+ *   lse      [B, H_q, T_q]       fp32, device, written (natural log)
+ *   workspace: at least the size gqa_decode_tokens_plan reports for the same
+ *            arguments; layout as gqa_attn_decode with H_q * T_q rows per slot
+ *            (row h * T_q + i).
+ *
+ * Supported: 1 <= T_q <= 16 (longer chunks: gqa_attn_prefill_chunk); the rest
+ * as gqa_attn_decode.
+ */
+int gqa_decode_tokens_plan(int B, int T_q, int H_q, int H_kv, int d, int S_max, int num_splits,
+                           int *partitions_out, int *states_out, size_t *workspace_bytes_out);
+
+int gqa_attn_decode_tokens(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *seqlens, void *o, float *lse, int B, int T_q, int H_q,
+                           int H_kv, int d, int S_max, float softmax_scale, int num_splits,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gqa_lse_merge -- merge caller-provided partial states (V07, section 3:
  * M = max m_p, a_p = 2^(m_p - M), L = sum a_p l_p, O = sum a_p O_p / L;
  * section 17, second stage).  Partial maxima are in log2 units of the scaled

@@ -24,7 +24,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     declared = g.header_functions()
     assert {"gqa_attn_decode", "gqa_attn_decode_paged", "gqa_attn_prefill_causal",
-            "gqa_attn_prefill_chunk",
+            "gqa_attn_prefill_chunk", "gqa_attn_decode_tokens", "gqa_decode_tokens_plan",
             "gqa_lse_merge", "gqa_decode_plan",
             "gqa_decode_partials", "gqa_decode_combine", "gqa_status_string",
             "gqa_last_error", "gqa_version"} <= set(declared)
@@ -133,6 +133,23 @@ def _paged(lib, q=A, kp=A, vp=A, tbl=A, seqlens=None, o=A, lse=A, B=1, H_q=8, H_
 def test_paged_decode_rejects_before_launch(lib, kw, code):
     assert _paged(lib, **kw) == code
     assert lib.gqa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("T,code", [(0, SHAPE), (17, SHAPE), (-1, SHAPE)])
+def test_decode_tokens_rejects_token_count(lib, T, code):
+    assert lib.gqa_decode_tokens_plan(1, T, 8, 2, 32, 512, 0, None, None, None) == code
+    assert lib.gqa_attn_decode_tokens(A, A, A, None, A, A, 1, T, 8, 2, 32, 512, 0.1, 0, A,
+                                      1 << 30, None) == code
+
+
+def test_decode_tokens_plan_folds_rows():
+    # 8 heads x 4 tokens = 32 rows per KV head: two 16-row groups, so 128 partitions per row
+    p4 = g.decode_tokens_plan(1, 4, 64, 8, 128, 32768, 0)
+    assert p4["partitions"] == 128 and p4["states"] == 128
+    a256 = lambda n: (n + 255) // 256 * 256
+    n = 128 * 64 * 4
+    assert p4["workspace_bytes"] == 256 + 2 * a256(n * 4) + a256(n * 128 * 4)
+    assert g.decode_tokens_plan(2, 1, 64, 8, 128, 1000, 0) == g.decode_plan(2, 64, 8, 128, 1000, 0)
 
 
 @pytest.mark.parametrize("kw,code", [
