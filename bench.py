@@ -33,6 +33,9 @@ Measured after the timed region, each in its own graph loop (not part of a step)
                     read through a block table (gqa_attn_decode_paged);
   decode_ragged_b8  batched long-context decode, B=8 with lengths uniform on
                     [4096, 131072], contiguous cache and paged (16-token pages);
+  decode_tokens     4 query tokens per sequence against the 32768-token cache
+                    (gqa_attn_decode_tokens), beside the same call through the
+                    chunked-prefill kernel;
   prefill_chunk     the last 2048 tokens of the 8192-token prompt as one chunk
                     against the whole cache (gqa_attn_prefill_chunk).
 """
@@ -131,7 +134,7 @@ def upload_paged(p):
             torch.from_numpy(p["block_table"]).cuda(), torch.from_numpy(p["seqlens"]).cuda())
 
 
-def extra_measurements(K, q_p, k_p, v_p, decode_ms):
+def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
     """Paged decode, batched ragged decode and chunked prefill, outside the timed step."""
     res = {}
     page = 16
@@ -205,6 +208,37 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms):
                   "gbs": round(kv / ms_p / 1e6, 1),
                   "frac_hbm_peak": round(kv / ms_p / 1e6 / HBM_PEAK_GBS, 4)}}
     del q, kp, vp, tbl, sl, kc, vc, ws_c, ws_p
+
+    # a few query tokens per sequence (speculative decoding): the M-fold decode against the
+    # same tokens through the chunked-prefill kernel
+    T = 4
+    qt = torch.randn((dc.B, T, dc.H_q, dc.d), device="cuda").to(torch.bfloat16)
+    ws_t = torch.empty(g.decode_tokens_plan(dc.B, T, dc.H_q, dc.H_kv, dc.d, dc.S_kv,
+                                            dc.num_splits)["workspace_bytes"],
+                       dtype=torch.uint8, device="cuda")
+    ot = torch.empty_like(qt)
+    lt = torch.empty((dc.B, dc.H_q, T), dtype=torch.float32, device="cuda")
+
+    def tokens_call(i):       # cycling over the cache copies, like the one-token decode
+        k, v = kv_copies[i % len(kv_copies)]
+        g.decode_tokens(qt, k, v, None, num_splits=dc.num_splits, out=ot, lse=lt, workspace=ws_t)
+
+    def tokens_chunk_call(i):
+        k, v = kv_copies[i % len(kv_copies)]
+        g.prefill_chunk(qt, k, v, out=ot, lse=lt)
+
+    tokens_call(0)
+    tokens_chunk_call(0)
+    ms_t = graph_ms(tokens_call, K)
+    ms_tc = graph_ms(tokens_chunk_call, K)
+    kv = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
+    res["decode_tokens"] = {
+        "workload": f"Llama3-70B decode of T_q={T} tokens, B=1, S_kv={dc.S_kv} "
+                    f"(G*T_q = {dc.H_q // dc.H_kv * T} rows per KV head)",
+        "us": round(ms_t * 1e3, 2), "gbs": round(kv / (ms_t * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(kv / (ms_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "prefill_chunk_kernel_us": round(ms_tc * 1e3, 2)}
+    del qt, ws_t, ot, lt
 
     # chunked prefill: the prompt's last 2048 tokens against its whole 8192-token cache
     pc = LLAMA_PREFILL
@@ -390,7 +424,7 @@ def main():
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
     if not args.no_extra:
-        out.update(extra_measurements(K, q_p, k_p, v_p, decode_ms))
+        out.update(extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
