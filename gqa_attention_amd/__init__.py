@@ -62,7 +62,7 @@ def load_library(path=LIBRARY):
     L.gqa_decode_combine.argtypes = [vp, f32p, ci, ci, ci, ci, ci, ci, vp, cs, vp]
     L.gqa_decode_combine.restype = ci
     L.gqa_attn_decode_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci, ci,
-                                        ci, cf, ci, vp, cs, vp]
+                                        ci, ci, cf, ci, vp, cs, vp]
     L.gqa_attn_decode_paged.restype = ci
     L.gqa_decode_tokens_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci),
                                          ctypes.POINTER(ci), ctypes.POINTER(cs)]
@@ -169,13 +169,17 @@ def decode(q, k_cache, v_cache, seqlens=None, softmax_scale=None, num_splits=0, 
 
 def decode_paged(q, k_pool, v_pool, block_table, seqlens=None, softmax_scale=None, num_splits=0,
                  out=None, lse=None, workspace=None):
-    """Split-KV GQA decode over a paged cache: q [B,H_q,d]; pools [num_pages,page,H_kv,d] bf16;
-    block_table [B,max_blocks] int32 -> (o [B,H_q,d], lse [B,H_q])."""
-    _need(q, "q", torch.bfloat16, 3)
+    """Split-KV GQA decode over a paged cache: pools [num_pages,page,H_kv,d] bf16;
+    block_table [B,max_blocks] int32.  q [B,H_q,d] (one token per sequence) -> (o [B,H_q,d],
+    lse [B,H_q]), or q [B,T_q,H_q,d] (the last T_q positions) -> (o [B,T_q,H_q,d],
+    lse [B,H_q,T_q])."""
+    one = q.dim() == 3
+    q4 = q.unsqueeze(1) if one else q
+    _need(q4, "q", torch.bfloat16, 4)
     _need(k_pool, "k_pool", torch.bfloat16, 4)
     _need(v_pool, "v_pool", torch.bfloat16, 4)
     _need(block_table, "block_table", torch.int32, 2)
-    B, H_q, d = q.shape
+    B, T, H_q, d = q4.shape
     num_pages, page, H_kv, dk = k_pool.shape
     if dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, pools {tuple(k_pool.shape)} / "
@@ -186,14 +190,18 @@ def decode_paged(q, k_pool, v_pool, block_table, seqlens=None, softmax_scale=Non
         if seqlens.shape[0] != B:
             raise ValueError("seqlens must have B entries")
     if workspace is None:
-        workspace = decode_workspace(B, H_q, H_kv, d, max_blocks * page, num_splits, q.device)
-    o = torch.empty((B, H_q, d), dtype=torch.bfloat16, device=q.device) if out is None else out
-    l = torch.empty((B, H_q), dtype=torch.float32, device=q.device) if lse is None else lse
+        nbytes = decode_tokens_plan(B, T, H_q, H_kv, d, max_blocks * page,
+                                    num_splits)["workspace_bytes"]
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H_q) if one else (B, H_q, T), dtype=torch.float32, device=q.device)
     _check(load_library().gqa_attn_decode_paged(
-        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seqlens), _ptr(o), _ptr(l),
-        B, H_q, H_kv, d, page, num_pages, max_blocks, _scale(d, softmax_scale), num_splits,
-        _ptr(workspace), workspace.numel(), _stream(q.device)))
-    return o, l
+        _ptr(q4), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seqlens), _ptr(out),
+        _ptr(lse), B, T, H_q, H_kv, d, page, num_pages, max_blocks, _scale(d, softmax_scale),
+        num_splits, _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out, lse
 
 
 def decode_tokens_plan(B, T_q, H_q, H_kv, d, S_max, num_splits=0):

@@ -313,7 +313,7 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
 
 int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           const int32_t *block_table, const int32_t *seqlens, void *o, float *lse,
-                          int B, int H_q, int H_kv, int d, int page_size, int num_pages,
+                          int B, int T_q, int H_q, int H_kv, int d, int page_size, int num_pages,
                           int max_blocks, float softmax_scale, int num_splits, void *workspace,
                           size_t workspace_bytes, void *stream) {
     if (page_size < kPagedTile || page_size % kPagedTile != 0 || page_size > kMaxPage)
@@ -328,7 +328,7 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
     const int S_max = max_blocks * page_size;
     Plan pl;
     int rc;
-    if ((rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = make_plan(B, T_q, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
     if ((rc = decode_common_checks(q, k_pool, v_pool, seqlens, softmax_scale))) return rc;
     if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
     if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
@@ -336,13 +336,13 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
     if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     auto a = split_args(q, k_pool, v_pool, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
-                        workspace);
+                        workspace, T_q);
     a.block_table = block_table;
     a.page = page_size;
     a.num_pages = num_pages;
     a.max_blocks = max_blocks;
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
-    auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q);
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }

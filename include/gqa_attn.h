@@ -160,11 +160,13 @@ int gqa_decode_combine(void *o, float *lse,
  * row t % page_size of page block_table[b][t / page_size] ("Attention Kernel
  * lineage" (V07), section 16: block pool, block table and the logical-token-to-
  * page map; section 17: paged decode, split-K over the key axis with a second
- * merge stage).  Everything else -- the M-fold of the G query heads, the split
- * plan, the merge, the outputs -- is that of gqa_attn_decode, with
- * S_max = max_blocks * page_size.
+ * merge stage).  Everything else -- the M-fold of the query rows, the split
+ * plan, the merge, the outputs -- is that of gqa_attn_decode_tokens (T_q query
+ * tokens per sequence, the last T_q positions; T_q = 1 is gqa_attn_decode), with
+ * S_max = max_blocks * page_size; its workspace is sized by
+ * gqa_decode_tokens_plan (T_q = 1: gqa_decode_plan).
  *
- *   q           [B, H_q, d]                        bf16, device, read-only
+ *   q           [B, T_q, H_q, d]                   bf16, device, read-only
  *   k_pool      [num_pages, page_size, H_kv, d]    bf16, device, read-only
  *   v_pool      [num_pages, page_size, H_kv, d]    bf16, device, read-only
  *               (K and V are two pools with one page numbering; a page's K rows
@@ -177,18 +179,18 @@ int gqa_decode_combine(void *o, float *lse,
  *               Pages may be shared between sequences.
  *   seqlens     [B] int32, device, or NULL (= max_blocks * page_size tokens each),
  *               clamped to [0, max_blocks * page_size] on the device.
- *   o, lse      as gqa_attn_decode.
+ *   o, lse      [B, T_q, H_q, d] bf16 and [B, H_q, T_q] fp32, as
+ *               gqa_attn_decode_tokens (for T_q = 1 the layouts of gqa_attn_decode).
  *   page_size   tokens per page: a multiple of 16 in [16, 65536].
  *   num_pages, max_blocks: pool size and table width; num_pages * page_size and
  *               max_blocks * page_size must be below 2^31.
- *   workspace   as gqa_attn_decode, sized by gqa_decode_plan with
- *               S_max = max_blocks * page_size.
+ *   workspace   sized by gqa_decode_tokens_plan with S_max = max_blocks * page_size.
  *
  * Calls that share a workspace on overlapping streams race.
  */
 int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           const int32_t *block_table, const int32_t *seqlens, void *o, float *lse,
-                          int B, int H_q, int H_kv, int d, int page_size, int num_pages,
+                          int B, int T_q, int H_q, int H_kv, int d, int page_size, int num_pages,
                           int max_blocks, float softmax_scale, int num_splits,
                           void *workspace, size_t workspace_bytes, void *stream);
 

@@ -114,9 +114,10 @@ def test_stage_calls_reject_before_launch(lib):
     assert lib.gqa_decode_combine(MIS, A, 1, 8, 2, 32, 512, 4, A, 1 << 30, None) == ALIGN
 
 
-def _paged(lib, q=A, kp=A, vp=A, tbl=A, seqlens=None, o=A, lse=A, B=1, H_q=8, H_kv=2, d=32,
-           page=16, num_pages=64, max_blocks=32, scale=0.17, splits=4, ws=A, ws_bytes=1 << 30):
-    return lib.gqa_attn_decode_paged(q, kp, vp, tbl, seqlens, o, lse, B, H_q, H_kv, d, page,
+def _paged(lib, q=A, kp=A, vp=A, tbl=A, seqlens=None, o=A, lse=A, B=1, T=1, H_q=8, H_kv=2,
+           d=32, page=16, num_pages=64, max_blocks=32, scale=0.17, splits=4, ws=A,
+           ws_bytes=1 << 30):
+    return lib.gqa_attn_decode_paged(q, kp, vp, tbl, seqlens, o, lse, B, T, H_q, H_kv, d, page,
                                      num_pages, max_blocks, scale, splits, ws, ws_bytes, None)
 
 
@@ -128,7 +129,7 @@ def _paged(lib, q=A, kp=A, vp=A, tbl=A, seqlens=None, o=A, lse=A, B=1, H_q=8, H_
     (dict(num_pages=0), SHAPE), (dict(max_blocks=0), SHAPE),
     (dict(num_pages=1 << 27, page=32), SHAPE),     # num_pages * page_size overflows 31 bits
     (dict(ws_bytes=100), WS), (dict(d=96), UNSUP), (dict(H_kv=3), SHAPE),
-    (dict(scale=float("nan")), SCALE),
+    (dict(scale=float("nan")), SCALE), (dict(T=0), SHAPE), (dict(T=17), SHAPE),
 ])
 def test_paged_decode_rejects_before_launch(lib, kw, code):
     assert _paged(lib, **kw) == code

@@ -151,3 +151,25 @@ def test_paged_entry_outside_pool_reads_zeros(gpu_available):
     zp["block_table"] = zt
     o_ref, lse_ref = oracle_paged(zp)
     check(to_f64(o), to_f64(lse), o_ref, lse_ref, "entries outside the pool")
+
+
+def test_paged_multi_token_decode(gpu_available):
+    """T_q = 4 query tokens per sequence over a paged cache: against the oracle (the
+    multi-token decode of the gathered caches) and bitwise against the unpaged kernel."""
+    p = paged_decode_inputs(3, 16, 2, 128, 16, ragged=(2, 3000), seed=44)
+    rng = np.random.default_rng(45)
+    from gqa_workloads.generate import bf16_bits_from_f32
+    q4 = bf16_bits_from_f32(rng.standard_normal((3, 4, 16, 128), dtype=np.float32))
+    p["seqlens"][0] = 2                          # two tokens at negative positions
+    q, kp, vp, tbl, sl = upload(p)
+    qg = to_gpu_bf16(q4)
+    say(f"paged multi-token decode seqlens={p['seqlens'].tolist()}")
+    o, lse = g.decode_paged(qg, kp, vp, tbl, sl)
+    k = oracle.gather_pages(p["k_pool"], p["block_table"], p["seqlens"], 16)
+    v = oracle.gather_pages(p["v_pool"], p["block_table"], p["seqlens"], 16)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_tokens(q4, k, v, p["seqlens"])
+    check(to_f64(o), to_f64(lse), o_ref, lse_ref, "paged T=4")
+    ou, lu = g.decode_tokens(qg, to_gpu_bf16(k), to_gpu_bf16(v), sl)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ou) and torch.equal(lse, lu)
