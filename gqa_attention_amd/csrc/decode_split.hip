@@ -97,103 +97,119 @@ constexpr float kSlack = 8.f;
 // stored with m2 = -inf, the empty state of the merge.
 constexpr float kNoMax = -1e30f;
 
-template <int D>
+// A wave's running state for its CB blocks of 16 columns.
+template <int D, int CB>
 struct WaveState {
-    float m;                          // running max shared by the 4 lanes of a head (log2 units)
-    float l;                          // this lane's share of the denominator (fp32 P)
-    float lw;                         // the same from the bf16-rounded P that enters P.V
-    f32x4 o[DecodeTraits<D>::NDT];    // O^T tiles: d = 16*dt + 4*grp + r, head = lane%16
+    float m[CB];                         // running max shared by a column's 4 lanes (log2 units)
+    float l[CB];                         // this lane's share of the denominator (fp32 P)
+    float lw[CB];                        // the same from the bf16-rounded P that enters P.V
+    f32x4 o[CB][DecodeTraits<D>::NDT];   // O^T tiles: d = 16*dt + 4*grp + r, column lane%16
 };
 
-// First half of a tile: S^T = K . Q^T (rows: keys key0 + 4*(lane/16) + r, column: head
-// lane%16) and the V tile staged row-major in the wave's LDS area.  After it the tile's
-// registers are free for the next prefetch.
-template <int D>
-__device__ __forceinline__ f32x4 score_tile(const TileRegs<D> &r,
-                                            const bf16x8 (&qf)[DecodeTraits<D>::KS],
-                                            uint16_t *vs, int lane) {
+// First half of a tile: S^T = K . Q^T for each block of 16 columns (rows: keys key0 +
+// 4*(lane/16) + r, column lane%16 of the block), sharing each K fragment, and the V tile
+// staged row-major in the wave's LDS area.  After it the tile's registers are free for the
+// next prefetch.
+template <int D, int CB>
+__device__ __forceinline__ void score_tile(const TileRegs<D> &r,
+                                           const bf16x8 (&qf)[CB][DecodeTraits<D>::KS],
+                                           uint16_t *vs, int lane, f32x4 (&s)[CB]) {
     using T = DecodeTraits<D>;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) s = mfma16(as_bf16x8(r.k[ks]), qf[ks], s);
+    for (int bk = 0; bk < CB; ++bk) s[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+        for (int bk = 0; bk < CB; ++bk) s[bk] = mfma16(as_bf16x8(r.k[ks]), qf[bk][ks], s[bk]);
 #pragma unroll
     for (int i = 0; i < T::NVI; ++i) {
         uint16_t *dst = vs + (i * T::RPI + lane / T::LPR) * T::VPITCH + (lane % T::LPR) * 8;
         *reinterpret_cast<u32x4 *>(dst) = r.v[i];
     }
-    return s;
 }
 
-// Second half: online softmax of the tile's scores and O^T += V^T . P^T.  key_end is this
-// lane's column's bound: its query sees keys below it.
-template <int D>
-__device__ __forceinline__ void softmax_pv(WaveState<D> &st, f32x4 s, const uint16_t *vs,
-                                           int key0, int key_end, float scale_log2, int lane) {
+// Second half: online softmax of the tile's scores and O^T += V^T . P^T, for each block
+// of columns.  key_end[bk] is this lane's column's bound: its query sees keys below it.
+template <int D, int CB>
+__device__ __forceinline__ void softmax_pv(WaveState<D, CB> &st, const f32x4 (&s)[CB],
+                                           const uint16_t *vs, int key0, const int (&key_end)[CB],
+                                           float scale_log2, int lane) {
     using T = DecodeTraits<D>;
     const int row16 = lane & 15, grp = lane >> 4;
+    s16x4 pf[CB];
+#pragma unroll
+    for (int bk = 0; bk < CB; ++bk) {
+        // scale to log2 units; keys at or past the column's bound are masked
+        float s2[4];
+        float mx = neg_inf();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = key0 + grp * 4 + i < key_end[bk] ? s[bk][i] * scale_log2 : neg_inf();
+            s2[i] = x;
+            mx = fmaxf(mx, x);
+        }
+        // Each lane holds 4 of a column's 16 scores.  Only when one of them passes the
+        // shared max by the slack (always on the first live key, as m starts at kNoMax) do
+        // the column's 4 lanes agree on a new max and rescale; otherwise no cross-lane step
+        // is needed.  A column with no live key yet keeps m = kNoMax, so its alpha is 1 and
+        // its P is 0 when another column moves the wave into the rescale.
+        if (__any(mx > st.m[bk] + kSlack)) {
+            mx = wave_max_xor(mx, 16);
+            mx = wave_max_xor(mx, 32);
+            const float m_new = fmaxf(st.m[bk], mx);
+            const float alpha = exp2_fast(st.m[bk] - m_new);   // 0 on a column's first live key
+            st.l[bk] *= alpha;
+            st.lw[bk] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt) st.o[bk][dt] *= alpha;
+            st.m[bk] = m_new;
+        }
 
-    // scale to log2 units; keys at or past the column's bound are masked
-    float s2[4];
-    float mx = neg_inf();
+        float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x = key0 + grp * 4 + i < key_end ? s[i] * scale_log2 : neg_inf();
-        s2[i] = x;
-        mx = fmaxf(mx, x);
+        for (int j = 0; j < 4; ++j) {
+            p[j] = exp2_fast(s2[j] - st.m[bk]);
+            st.l[bk] += p[j];
+        }
+        // P^T as the B operand of the 16x16x16 product: keys 4*grp + j, column lane%16
+        const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        pf[bk] = __builtin_bit_cast(s16x4, pw);
+        st.lw[bk] = add_bf16_pair(pw[0], st.lw[bk]);
+        st.lw[bk] = add_bf16_pair(pw[1], st.lw[bk]);
     }
-    // Each lane holds 4 of a column's 16 scores.  Only when one of them passes the shared
-    // max by the slack (always on the first live key, as m starts at kNoMax) do the
-    // column's 4 lanes agree on a new max and rescale; otherwise no cross-lane step is
-    // needed.  A column with no live key yet keeps m = kNoMax, so its alpha is 1 and its
-    // P is 0 when another column moves the wave into the rescale.
-    if (__any(mx > st.m + kSlack)) {
-        mx = wave_max_xor(mx, 16);
-        mx = wave_max_xor(mx, 32);
-        const float m_new = fmaxf(st.m, mx);
-        const float alpha = exp2_fast(st.m - m_new);   // 0 on a column's first live key
-        st.l *= alpha;
-        st.lw *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] *= alpha;
-        st.m = m_new;
-    }
-
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        p[j] = exp2_fast(s2[j] - st.m);
-        st.l += p[j];
-    }
-    // P^T as the B operand of the 16x16x16 product: keys 4*grp + j, head lane%16
-    const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    const s16x4 pf = __builtin_bit_cast(s16x4, pw);
-    st.lw = add_bf16_pair(pw[0], st.lw);
-    st.lw = add_bf16_pair(pw[1], st.lw);
 
     __builtin_amdgcn_wave_barrier();
     // O^T += V^T . P^T.  V^T fragment of lane (row16, grp): column d = 16*dt + row16,
     // keys 4*grp + 0..3, via one LDS transpose read whose lanes point at row
-    // 4*grp + row16/4, columns 16*dt + 4*(row16%4).
+    // 4*grp + row16/4, columns 16*dt + 4*(row16%4); one read serves every block.
     const uint16_t *vrow = vs + (4 * grp + (row16 >> 2)) * T::VPITCH + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < T::NDT; ++dt) {
         const s16x4 vf = __builtin_bit_cast(s16x4, lds_read_tr16(vrow + dt * 16));
-        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, st.o[dt], 0, 0, 0);
+#pragma unroll
+        for (int bk = 0; bk < CB; ++bk)
+            st.o[bk][dt] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[bk], st.o[bk][dt], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 }
 
-// End of a wave's sweep: add up the head's four lane shares of l and lw, and scale O^T
-// by l / lw so that O / l is the convex combination of V with the rounded weights.
-template <int D>
-__device__ __forceinline__ void finish_state(WaveState<D> &st) {
-    st.l += __shfl_xor(st.l, 16);
-    st.l += __shfl_xor(st.l, 32);
-    st.lw += __shfl_xor(st.lw, 16);
-    st.lw += __shfl_xor(st.lw, 32);
-    const float f = st.lw > 0.f ? st.l / st.lw : 0.f;
+// End of a state: add up each column's four lane shares of l and lw, and scale O^T by
+// l / lw so that O / l is the convex combination of V with the rounded weights; a column
+// that saw no live key gets the empty state (m2 = -inf).
+template <int D, int CB>
+__device__ __forceinline__ void finish_state(WaveState<D, CB> &st) {
 #pragma unroll
-    for (int dt = 0; dt < DecodeTraits<D>::NDT; ++dt) st.o[dt] *= f;
+    for (int bk = 0; bk < CB; ++bk) {
+        st.l[bk] += __shfl_xor(st.l[bk], 16);
+        st.l[bk] += __shfl_xor(st.l[bk], 32);
+        st.lw[bk] += __shfl_xor(st.lw[bk], 16);
+        st.lw[bk] += __shfl_xor(st.lw[bk], 32);
+        const float f = st.lw[bk] > 0.f ? st.l[bk] / st.lw[bk] : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DecodeTraits<D>::NDT; ++dt) st.o[bk][dt] *= f;
+        if (!(st.l[bk] > 0.f)) st.m[bk] = neg_inf();
+    }
 }
 
 // Length of sequence b as the kernel uses it: seqlens[b] clamped to [0, S_max].
@@ -223,7 +239,10 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[DecodeTraits<D>::KS], const 
 // cache.  A wave fetches the lookups of its next 64 tiles at once, one per lane (the table
 // is read ahead of the sweep, as V07 section 17 describes), and each tile takes its entry
 // with a lane read.
-template <int D, bool Paged>
+//
+// A wave folds CB blocks of 16 columns (CB = 2 when a KV head has more than 16 rows, G * T
+// > 16), so up to 32 rows share each K fragment, V^T fragment and tile load.
+template <int D, bool Paged, int CB>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitArgs a, int n_hg) {
     using T = DecodeTraits<D>;
     // V staging during the sweep; at a state boundary (several waves per head) the
@@ -245,10 +264,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     const int wph = kWaves / a.hpw;
     const int hw = w % a.hpw, phase = w / a.hpw;
     const int hk = hgrp * a.hpw + hw;
-    const int h0 = hk * GT + hg * 16;      // first state row of this wave's columns
-    const int nh = min(16, GT - hg * 16);
-    const int col = hg * 16 + min(row16, nh - 1);   // this lane's column (g, token)
-    const int tok_gap = a.T - 1 - col % a.T;         // tokens after this column's token
+    constexpr int CW = 16 * CB;             // columns (rows of the KV head) per wave
+    const int h0 = hk * GT + hg * CW;      // first state row of this wave's columns
+    // block bk: nhb[bk] live columns (<= 0: none; its lanes repeat the last row and are
+    // never stored); this lane's column (g, token) and the tokens after its token
+    int nhb[CB], colb[CB], gapb[CB];
+#pragma unroll
+    for (int bk = 0; bk < CB; ++bk) {
+        nhb[bk] = min(16, GT - hg * CW - bk * 16);
+        colb[bk] = min(hg * CW + bk * 16 + row16, GT - 1);
+        gapb[bk] = a.T - 1 - colb[bk] % a.T;
+    }
 
     // ---- running tile counts of the sequences ----
     // Up to 64 sequences: every wave scans them in its own registers (lane b holds
@@ -403,8 +429,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         ++issued;
     };
 
-    bf16x8 qf[T::KS];
-    load_q<D>(qf, a, cb, hk, G, col, grp);
+    bf16x8 qf[CB][T::KS];
+#pragma unroll
+    for (int bk = 0; bk < CB; ++bk) load_q<D>(qf[bk], a, cb, hk, G, colb[bk], grp);
     TileRegs<D> ring;
     __builtin_amdgcn_sched_barrier(0);
     issue(ring);
@@ -415,22 +442,26 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         const int slo = P(cb), shend = P(cb + 1);
         const int shi = min(shend, t1);
         const int len = L(cb, slo, shend);
-        WaveState<D> st;
-        st.m = kNoMax;
-        st.l = 0.f;
-        st.lw = 0.f;
+        WaveState<D, CB> st;
+        // a column's token sits at position len - 1 - gap and sees keys up to it
+        int key_end[CB];
 #pragma unroll
-        for (int dt = 0; dt < T::NDT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // the column's token sits at position len - 1 - tok_gap and sees keys up to it
-        const int key_end = len - tok_gap;
+        for (int bk = 0; bk < CB; ++bk) {
+            st.m[bk] = kNoMax;
+            st.l[bk] = 0.f;
+            st.lw[bk] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt) st.o[bk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            key_end[bk] = len - gapb[bk];
+        }
         for (; tw < shi; tw += wph) {
-            const f32x4 sc = score_tile<D>(ring, qf, vs, lane);
+            f32x4 sc[CB];
+            score_tile<D, CB>(ring, qf, vs, lane, sc);
             __builtin_amdgcn_sched_barrier(0);
             issue(ring);                       // the next tile's loads go out first
-            softmax_pv<D>(st, sc, vs, (tw - slo) * kTile, key_end, a.scale_log2, lane);
+            softmax_pv<D, CB>(st, sc, vs, (tw - slo) * kTile, key_end, a.scale_log2, lane);
         }
-        finish_state<D>(st);
-        if (!(st.l > 0.f)) st.m = neg_inf();   // no live key: the empty state
+        finish_state<D, CB>(st);
 
         // the next sequence with tiles; its Q is requested before this state is stored
         const bool more = shi < t1;
@@ -438,27 +469,34 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         if (more) {
             ++nb;
             while (P(nb + 1) == P(nb)) ++nb;
-            load_q<D>(qf, a, nb, hk, G, col, grp);
+#pragma unroll
+            for (int bk = 0; bk < CB; ++bk) load_q<D>(qf[bk], a, nb, hk, G, colb[bk], grp);
         }
         const size_t srow = (size_t)(x + cb) * a.H_q * a.T;   // states: [slot][H_q * T]
 
         if (wph == 1) {
             // one wave per head: its registers hold the whole state
-            if (row16 < nh) {
-                const size_t row = srow + h0 + row16;
-                float *orow = a.part_o + row * D + grp * 4;
 #pragma unroll
-                for (int dt = 0; dt < T::NDT; ++dt)
-                    *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[dt];
-                if (grp == 0) {
-                    a.part_m2[row] = st.m;
-                    a.part_l[row] = st.l;
+            for (int bk = 0; bk < CB; ++bk) {
+                if (row16 < nhb[bk]) {
+                    const size_t row = srow + h0 + bk * 16 + row16;
+                    float *orow = a.part_o + row * D + grp * 4;
+#pragma unroll
+                    for (int dt = 0; dt < T::NDT; ++dt)
+                        *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[bk][dt];
+                    if (grp == 0) {
+                        a.part_m2[row] = st.m[bk];
+                        a.part_l[row] = st.l[bk];
+                    }
                 }
             }
         } else {
             // several waves per head: merge their states through LDS (in the V staging
-            // area, which every wave has finished reading):
-            // red[w][head][0..D) = O^T column, [D] = m, [D+1] = l
+            // area, which every wave has finished reading), one block of columns at a time:
+            // red[w][column][0..D) = O^T column, [D] = m, [D+1] = l
+#pragma unroll
+            for (int bk = 0; bk < CB; ++bk) {
+            const int nh = nhb[bk];
             __syncthreads();
             float *red = reinterpret_cast<float *>(smem);
             constexpr int RS = D + 2;
@@ -466,10 +504,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mine[dt * 16 + grp * 4 + i] = st.o[dt][i];
+                for (int i = 0; i < 4; ++i) mine[dt * 16 + grp * 4 + i] = st.o[bk][dt][i];
             if (grp == 0) {
-                mine[D] = st.m;
-                mine[D + 1] = st.l;
+                mine[D] = st.m[bk];
+                mine[D + 1] = st.l[bk];
             }
             __syncthreads();
             for (int idx = threadIdx.x; idx < a.hpw * nh * D; idx += kWaves * 64) {
@@ -485,12 +523,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
                     L += al * rw[D + 1];
                     O += al * rw[d];
                 }
-                const size_t row = srow + (hgrp * a.hpw + hw2) * GT + hg * 16 + h;
+                const size_t row = srow + (hgrp * a.hpw + hw2) * GT + hg * CW + bk * 16 + h;
                 a.part_o[row * D + d] = O;
                 if (d == 0) {
                     a.part_m2[row] = L > 0.f ? M : neg_inf();
                     a.part_l[row] = L;
                 }
+            }
             }
             __syncthreads();   // the staging area is reused by the next sequence
         }
@@ -499,18 +538,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     }
 }
 
-template <int D>
-hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
+template <int D, int CB>
+hipError_t launch_cb(const DecodeSplitArgs &a, hipStream_t stream) {
     const int GT = a.H_q / a.H_kv * a.T;
-    const int n_hg = (GT + 15) / 16;
+    const int n_hg = (GT + 16 * CB - 1) / (16 * CB);
     dim3 grid(a.units, (a.H_kv / a.hpw) * n_hg);
     if (a.block_table)
-        hipLaunchKernelGGL((decode_split_kernel<D, true>), grid, dim3(kWaves * 64), 0, stream, a,
-                           n_hg);
+        hipLaunchKernelGGL((decode_split_kernel<D, true, CB>), grid, dim3(kWaves * 64), 0, stream,
+                           a, n_hg);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, false>), grid, dim3(kWaves * 64), 0, stream, a,
-                           n_hg);
+        hipLaunchKernelGGL((decode_split_kernel<D, false, CB>), grid, dim3(kWaves * 64), 0, stream,
+                           a, n_hg);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch(const DecodeSplitArgs &a, hipStream_t stream) {
+    return a.cb == 2 ? launch_cb<D, 2>(a, stream) : launch_cb<D, 1>(a, stream);
 }
 
 }  // namespace

@@ -45,6 +45,7 @@ bool decode_head_size_ok(int d) { return d == 32 || d == 64 || d == 128; }
 struct Plan {
     int units;          // partitions of the batch's tiles (workgroups per head-group row)
     int hpw;            // KV heads swept together by one workgroup
+    int cb;             // 16-column blocks per wave (2 when a KV head has > 16 rows)
     int slots;          // partial-state slots per query head: units + B - 1
     size_t off_m2, off_l, off_o, bytes;
 };
@@ -78,7 +79,10 @@ int make_plan(int B, int T, int H_q, int H_kv, int d, int S_max, int num_splits,
     if (num_splits < 0 || num_splits > kMaxSplits)
         return fail(GQA_ERR_SPLITS, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
     const int G = H_q / H_kv;
-    const long n_hg = ((long)G * T + 15) / 16;   // 16-row groups of a KV head's G * T rows
+    // a wave folds up to 2 blocks of 16 of a KV head's G * T rows; more run as further
+    // workgroup rows
+    const int cb = (long)G * T > 16 ? 2 : 1;
+    const long n_hg = ((long)G * T + 16 * cb - 1) / (16 * cb);
     // KV heads per workgroup: the largest power of two <= 8 that divides H_kv; the
     // workgroup's 8 waves are spread evenly over them
     int hpw = kDecodeWaves;
@@ -91,6 +95,7 @@ int make_plan(int B, int T, int H_q, int H_kv, int d, int S_max, int num_splits,
     const long units = num_splits > fill ? num_splits : fill;
     pl->units = (int)units;
     pl->hpw = hpw;
+    pl->cb = cb;
     pl->slots = (int)(units + B - 1);
     const size_t states = (size_t)pl->slots * H_q * T;
     pl->off_m2 = align256((size_t)B * 2 * sizeof(int32_t));
@@ -163,6 +168,7 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.T = T;
     a.units = pl.units;
     a.hpw = pl.hpw;
+    a.cb = pl.cb;
     a.scale_log2 = scale * kLog2e;
     a.block_table = nullptr;
     a.page = 0;

@@ -31,6 +31,7 @@ struct DecodeSplitArgs {
     int T;                      // query tokens per sequence
     int units;                  // partitions (workgroups along x)
     int hpw;                    // KV heads per workgroup (divides H_kv and the wave count)
+    int cb;                     // 16-column blocks per wave: 2 when G * T > 16, else 1
     float scale_log2;           // softmax_scale * log2(e)
     // Paged cache when block_table is not null: k and v are pools [num_pages][page][H_kv][d]
     // and key t of sequence b is row t % page of page block_table[b * max_blocks + t / page]

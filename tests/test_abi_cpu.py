@@ -53,7 +53,8 @@ def test_status_strings(lib):
     ((8, 64, 8, 128, 131072, 64), 256),    # ragged decode: the same 256, whatever the lengths
     ((1, 64, 8, 128, 32768, 1000), 1000),  # num_splits above the fill count is kept
     ((1, 8, 2, 32, 512, 4), 256),          # tiny decode: most partitions empty
-    ((1, 32, 1, 32, 257, 2), 128),         # G = 32: two head-group rows share the 256
+    ((1, 32, 1, 32, 257, 2), 256),         # G = 32: one wave folds both 16-column blocks
+    ((1, 48, 1, 32, 257, 2), 128),         # G = 48: two workgroup rows of 32 columns
     ((1, 24, 6, 64, 1000, 1), 86),         # 6 KV heads: 2 per workgroup, 3 rows
 ])
 def test_decode_plan(args, expect):
@@ -144,11 +145,14 @@ def test_decode_tokens_rejects_token_count(lib, T, code):
 
 
 def test_decode_tokens_plan_folds_rows():
-    # 8 heads x 4 tokens = 32 rows per KV head: two 16-row groups, so 128 partitions per row
+    # 8 heads x 4 tokens = 32 rows per KV head: one wave folds both 16-column blocks
     p4 = g.decode_tokens_plan(1, 4, 64, 8, 128, 32768, 0)
-    assert p4["partitions"] == 128 and p4["states"] == 128
+    assert p4["partitions"] == 256 and p4["states"] == 256
+    # 8 heads x 8 tokens = 64 rows: two workgroup rows of 32, so 128 partitions per row
+    p8 = g.decode_tokens_plan(1, 8, 64, 8, 128, 32768, 0)
+    assert p8["partitions"] == 128
     a256 = lambda n: (n + 255) // 256 * 256
-    n = 128 * 64 * 4
+    n = 256 * 64 * 4
     assert p4["workspace_bytes"] == 256 + 2 * a256(n * 4) + a256(n * 128 * 4)
     assert g.decode_tokens_plan(2, 1, 64, 8, 128, 1000, 0) == g.decode_plan(2, 64, 8, 128, 1000, 0)
 
