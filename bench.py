@@ -33,6 +33,7 @@ Measured after the timed region, each in its own graph loop (not part of a step)
                     read through a block table (gqa_attn_decode_paged);
   decode_ragged_b8  batched long-context decode, B=8 with lengths uniform on
                     [4096, 131072], contiguous cache and paged (16-token pages);
+  prefill_long      causal prefill at S=65536 (1% of key rows scaled by 8), 3 calls;
   decode_tokens     4 query tokens per sequence against the 32768-token cache
                     (gqa_attn_decode_tokens), beside the same call through the
                     chunked-prefill kernel;
@@ -53,7 +54,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import gqa_attention_amd as g  # noqa: E402
-from gqa_workloads import LLAMA_DECODE, LLAMA_PREFILL, LLAMA_RAGGED_DECODE  # noqa: E402
+from gqa_workloads import LLAMA_DECODE, LLAMA_LONG_PREFILL, LLAMA_PREFILL, \
+    LLAMA_RAGGED_DECODE  # noqa: E402
 from gqa_workloads import accounting as acc  # noqa: E402
 from gqa_workloads.generate import for_config, paged_decode_inputs  # noqa: E402
 
@@ -239,6 +241,33 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
         "frac_hbm_peak": round(kv / (ms_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "prefill_chunk_kernel_us": round(ms_tc * 1e3, 2)}
     del qt, ws_t, ot, lt
+
+    # long-context causal prefill: S = 65536, K rows with 1% of them scaled by 8 (drawn on the
+    # GPU here: the figure is a timing; parity at this size is in the tests)
+    lc = LLAMA_LONG_PREFILL
+    gen = torch.Generator(device="cuda").manual_seed(lc.seed)
+    ql = torch.randn((lc.B, lc.S, lc.H_q, lc.d), device="cuda", generator=gen).to(torch.bfloat16)
+    kl = torch.randn((lc.B, lc.S, lc.H_kv, lc.d), device="cuda", generator=gen)
+    out_rows = torch.rand((lc.B, lc.S, lc.H_kv, 1), device="cuda", generator=gen) < lc.outlier_frac
+    kl = (kl.to(torch.bfloat16).float() * torch.where(out_rows, lc.outlier_scale, 1.0)).to(
+        torch.bfloat16)
+    vl = torch.randn((lc.B, lc.S, lc.H_kv, lc.d), device="cuda", generator=gen).to(torch.bfloat16)
+    ol = torch.empty_like(ql)
+    ll = torch.empty((lc.B, lc.H_q, lc.S), dtype=torch.float32, device="cuda")
+
+    def long_call(i):
+        g.prefill_causal(ql, kl, vl, out=ol, lse=ll)
+
+    long_call(0)
+    n_long = 3
+    ms = graph_ms(long_call, n_long)
+    flop = acc.prefill_causal_flop(lc.B, lc.S, lc.H_q, lc.d)
+    tf = flop / (ms * 1e-3) / 1e12
+    res["prefill_long"] = {
+        "workload": f"Llama3-70B causal prefill B={lc.B} S={lc.S}, 1% of key rows x8",
+        "calls": n_long, "flop": flop, "ms": round(ms, 3), "tflops": round(tf, 1),
+        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del ql, kl, vl, ol, ll, out_rows
 
     # chunked prefill: the prompt's last 2048 tokens against its whole 8192-token cache
     pc = LLAMA_PREFILL

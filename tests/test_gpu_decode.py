@@ -219,3 +219,21 @@ def test_lse_merge_fuzz_against_oracle_merge(gpu_available):
                                                  o_in.reshape(-1, P, d))
             check(to_f64(og).reshape(-1, d), to_f64(lg).reshape(-1), o_ref, lse_ref,
                   f"merge {trial} counts={use_counts}")
+
+
+def test_decode_kv_reads_independent_of_group_size(gpu_available):
+    """The same 32768-token cache (8 KV heads) read by 64 query heads (G = 8) and by 8
+    (G = 1): both match the oracle, and under a FETCH_SIZE counter pass both launches read
+    the cache's bytes once -- the M-fold reuses each K/V tile for all G heads of its group
+    (ADR-0060 section 11 item 2)."""
+    inp = decode_inputs(1, 64, 8, 128, S_max=32768, seed=12)
+    q64 = inp["q"]
+    rng = np.random.default_rng(13)
+    q8 = bf16_bits_from_f32(rng.standard_normal((1, 8, 128), dtype=np.float32))
+    k, v = to_gpu_bf16(inp["k"]), to_gpu_bf16(inp["v"])
+    for q in (q64, q8):
+        say(f"decode S=32768 H_q={q.shape[1]} H_kv=8")
+        o, lse = g.decode(to_gpu_bf16(q), k, v, None)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.decode(q, inp["k"], inp["v"])
+        check(to_f64(o), to_f64(lse), o_ref, lse_ref, f"H_q={q.shape[1]}")
