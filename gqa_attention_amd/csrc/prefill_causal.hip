@@ -249,20 +249,6 @@ __device__ __forceinline__ void half_step(const WaveCtx &x, int u, const f32x16 
     // (masking the scores of step n_sub, which no step uses, is harmless)
     if (u + 1 >= x.mask_from) mask_half(sn, (u + 1) * kHalf, x.row, x.hf);
     st.mx = half_max(sn);
-    // issue order: each score product with one K fragment read and a share of the
-    // softmax, then each P.V product with its two V reads and a share of the rest
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix core
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // vector ALU
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
 }
 
 // One LDS tile kb (KI = kb % 4 names its K buffer; V buffers rotate mod 3 at run time).
