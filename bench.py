@@ -69,9 +69,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("82cf24dad0dfc092", 143_033_444),
-    "lse_merge": ("6e1b89a44c4920f5", 9_541_007),
-    "prefill_causal": ("820f829619befa29", 421_864_135),
+    "decode_split": ("bf3b59e0667514e5", 143_032_902),
+    "lse_merge": ("ceae8259a6b21c5b", 9_550_287),
+    "prefill_causal": ("e415cbf712475006", 421_813_828),
 }
 
 
