@@ -6,7 +6,7 @@ float32 and rounded to bfloat16 with round-to-nearest-even done on the bit
 pattern here, so the result does not depend on any library's conversion.
 
 Each tensor draws from its own PCG64 stream spawned from the workload seed
-(Q, K, V, lengths, outlier mask), so changing one shape does not shift another
+(Q, K, V, lengths, outlier mask, pages, output gradient), so changing one shape does not shift another
 tensor's values.
 
 Layouts (row-major, innermost last):
@@ -15,12 +15,14 @@ Layouts (row-major, innermost last):
           block_table int32 [B, max_blocks];  seqlens int32 [B]
   prefill q [B, S, H_q, d];   k, v [B, S, H_kv, d]
   chunk   q [B, T, H_q, d];   k, v [B, S_kv, H_kv, d]
+  bwd     prefill inputs and dO [B, S, H_q, d] (the gradient of the output)
 """
 import numpy as np
 
 BF16_QUIET_NAN = np.uint16(0x7FC0)
 
-_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_LEN, _STREAM_OUTLIER, _STREAM_PAGES = range(6)
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_LEN, _STREAM_OUTLIER, _STREAM_PAGES, _STREAM_DOUT = \
+    range(7)
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
@@ -42,7 +44,7 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
 def _streams(seed: int):
     # child i of the seed sequence depends only on i, so adding streams shifts none
     return [np.random.Generator(np.random.PCG64(s))
-            for s in np.random.SeedSequence(seed).spawn(6)]
+            for s in np.random.SeedSequence(seed).spawn(7)]
 
 
 def _normal_bf16(rng, shape, chunk_rows: int = 1 << 22) -> np.ndarray:
@@ -166,6 +168,16 @@ def prefill_inputs(B, S, H_q, H_kv, d, seed=0, outlier_frac=0.0, outlier_scale=1
         rows = k[mask]
         k[mask] = bf16_bits_from_f32(f32_from_bf16_bits(rows) * scale)
     return {"q": q, "k": k, "v": v, "outlier_mask": mask}
+
+
+def prefill_bwd_inputs(B, S, H_q, H_kv, d, seed=0, outlier_frac=0.0, outlier_scale=1.0):
+    """Inputs of one backward launch of causal prefill: the forward's q, k, v (the same
+    bytes as ``prefill_inputs`` with the same arguments) and the output gradient
+    dO [B, S, H_q, d], N(0, 1) in bf16 from a stream of its own."""
+    p = prefill_inputs(B, S, H_q, H_kv, d, seed=seed, outlier_frac=outlier_frac,
+                       outlier_scale=outlier_scale)
+    p["do"] = _normal_bf16(_streams(seed)[_STREAM_DOUT], (B, S, H_q, d))
+    return p
 
 
 def for_config(cfg, nan_fill=True):

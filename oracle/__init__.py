@@ -9,6 +9,11 @@ Every function takes bf16 inputs as numpy uint16 bit patterns (the layouts of
 in ``oracle.c``; the header of that file states the definitions and cites the
 passages they follow.
 
+Functions: decode, paged decode, multi-token decode, whole-prompt and chunked causal
+prefill (all rows or selected rows), the partial state and merge of split-KV decode,
+and the backward of whole-prompt causal prefill (dQ per query row, dK and dV per key row
+of a KV head, or all of them).
+
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, invariants, special cases and a brute-force check built on
 library routines) and by the planted-mistake checks in
@@ -55,6 +60,12 @@ def _bind(lib):
     lib.oracle_decode_partial.restype = ci
     lib.oracle_merge_states.argtypes = [f64p, f64p, f64p, cl, ci, ci, f64p, f64p]
     lib.oracle_merge_states.restype = ci
+    lib.oracle_prefill_causal_bwd_rows.argtypes = [u16p, u16p, u16p, u16p, f64p, f64p, f64p,
+                                                   ci, ci, ci, ci, ci, cd, i32p, cl, ci]
+    lib.oracle_prefill_causal_bwd_rows.restype = ci
+    lib.oracle_prefill_causal_bwd_keys.argtypes = [u16p, u16p, u16p, u16p, f64p, f64p, f64p, f64p,
+                                                   ci, ci, ci, ci, ci, cd, i32p, cl, ci]
+    lib.oracle_prefill_causal_bwd_keys.restype = ci
     return lib
 
 
@@ -250,3 +261,78 @@ def merge_states(m, l, o, lib=None):
     lse = np.zeros(R, dtype=np.float64)
     lib.oracle_merge_states(m, l, o, R, P, d, o_out, lse)
     return o_out, lse
+
+
+def prefill_causal_bwd_rows(q, k, v, do, rows, tau=None, nthreads=0, lib=None):
+    """Backward of causal prefill, query side, on selected rows (b, h, i): the gradient
+    dQ_i = tau sum_j P_ij (dP_ij - D_i) k_j with dP_ij = dO_i . v_j and D_i = sum_j P_ij dP_ij
+    ("Attention Kernel lineage" (V07), section 6.1).
+
+    q, do [B, S, H_q, d]; k, v [B, S, H_kv, d] (uint16 bf16 bits); rows int [n, 3].
+    Returns (dq [n, d], lse [n], D [n]) in float64.
+    """
+    lib = lib or load()
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    tau = 1.0 / np.sqrt(d) if tau is None else float(tau)
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 3)
+    n = rows.shape[0]
+    dq = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    D = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_prefill_causal_bwd_rows(_u16(q), _u16(k), _u16(v), _u16(do), dq, lse, D,
+                                            B, S, H_q, H_kv, d, tau, rows, n,
+                                            nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_causal_bwd_rows rejected its arguments (code {rc})")
+    return dq, lse, D
+
+
+def prefill_causal_bwd_keys(q, k, v, do, lse, D, keys, tau=None, nthreads=0, lib=None):
+    """Backward of causal prefill, key side, on selected key rows (b, g, j) of the KV heads:
+    dK_j = tau sum_h sum_{i >= j} dS_ij q_i and dV_j = sum_h sum_{i >= j} P_ij dO_i over the
+    G query heads h of KV head g, with P_ij = exp(s_ij - LSE_i) re-formed from each row's
+    LSE (V07 section 6.4) and dS_ij = P_ij (dP_ij - D_i).
+
+    lse, D [B, H_q, S] float64 for every row (``prefill_causal_bwd_rows``); keys int [n, 3].
+    Returns (dk [n, d], dv [n, d]) in float64.
+    """
+    lib = lib or load()
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    tau = 1.0 / np.sqrt(d) if tau is None else float(tau)
+    keys = np.ascontiguousarray(keys, dtype=np.int32).reshape(-1, 3)
+    n = keys.shape[0]
+    dk = np.zeros((n, d), dtype=np.float64)
+    dv = np.zeros((n, d), dtype=np.float64)
+    rc = lib.oracle_prefill_causal_bwd_keys(_u16(q), _u16(k), _u16(v), _u16(do),
+                                            np.ascontiguousarray(lse, dtype=np.float64),
+                                            np.ascontiguousarray(D, dtype=np.float64), dk, dv,
+                                            B, S, H_q, H_kv, d, tau, keys, n,
+                                            nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_causal_bwd_keys rejected its arguments (code {rc})")
+    return dk, dv
+
+
+def prefill_causal_bwd(q, k, v, do, tau=None, nthreads=0, lib=None):
+    """Backward of causal prefill on every row and key.
+
+    Returns (dq [B, S, H_q, d], dk [B, S, H_kv, d], dv [B, S, H_kv, d], lse [B, H_q, S],
+    D [B, H_q, S]) in float64.
+    """
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H_q), np.arange(S), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
+    dq, lse, D = prefill_causal_bwd_rows(q, k, v, do, rows, tau=tau, nthreads=nthreads, lib=lib)
+    lse = lse.reshape(B, H_q, S)
+    D = D.reshape(B, H_q, S)
+    b, g, j = np.meshgrid(np.arange(B), np.arange(H_kv), np.arange(S), indexing="ij")
+    keys = np.stack([b.ravel(), g.ravel(), j.ravel()], axis=1)
+    dk, dv = prefill_causal_bwd_keys(q, k, v, do, lse, D, keys, tau=tau, nthreads=nthreads,
+                                     lib=lib)
+    dq = dq.reshape(B, H_q, S, d).transpose(0, 2, 1, 3).copy()
+    dk = dk.reshape(B, H_kv, S, d).transpose(0, 2, 1, 3).copy()
+    dv = dv.reshape(B, H_kv, S, d).transpose(0, 2, 1, 3).copy()
+    return dq, dk, dv, lse, D

@@ -326,3 +326,155 @@ int oracle_merge_states(const double *m, const double *l, const double *o, long 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Backward of whole-prompt causal prefill.
+ *
+ * Forward (the definition above): s_ij = tau q_i.k_j for j <= i, P_ij = exp(s_ij - LSE_i),
+ * O_i = sum_j P_ij v_j.  Given the output gradient dO, the input gradients are
+ * ("Attention Kernel lineage" (V07), section 6.1, gradient formulas):
+ *   dP_ij = dO_i . v_j           D_i   = sum_j P_ij dP_ij   (the row-wise dot)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = tau sum_j dS_ij k_j  dK_j  = tau sum_i dS_ij q_i  dV_j = sum_i P_ij dO_i
+ * with i, j over the causal pairs j <= i.  With grouped heads, K and V of head g are used
+ * by the G query heads h with floor(h / G) = g (V07 section 14), so dK and dV of head g
+ * add up the contributions of those G heads.
+ *
+ * Phase 1 (one query row i of head h): the score row, the three-pass softmax, dP_i, D_i
+ * and dS_i, then dQ_i; LSE_i and D_i are kept for phase 2.
+ * Phase 2 (one key row j of KV head g): for every query row i >= j of the G heads it forms
+ * P_ij = exp(s_ij - LSE_i) again and dS_ij from dP_ij and D_i (section 6.4: the backward
+ * recomputes P from the row's LSE), and sums dK_j and dV_j.
+ * Layouts: q, dO [B, S, H_q, d]; k, v [B, S, H_kv, d] (bf16 bits); dq [B, S, H_q, d],
+ * dk, dv [B, S, H_kv, d], lse and D [B, H_q, S] (double). */
+
+struct bwd_rows_ctx {
+    const uint16_t *q, *k, *v, *dout;
+    const int32_t *rows;
+    double *dq, *lse, *D;
+    int B, S, H_q, H_kv, d;
+    double tau;
+};
+
+static void bwd_row(void *p, long r, double *s, double *qd)
+{
+    struct bwd_rows_ctx *c = (struct bwd_rows_ctx *)p;
+    int b = c->rows[3 * r], h = c->rows[3 * r + 1], i = c->rows[3 * r + 2];
+    int G = c->H_q / c->H_kv;
+    int g = h / G;
+    int d = c->d;
+    size_t kv_stride = (size_t)c->H_kv * d;
+    size_t qoff = (((size_t)b * c->S + i) * c->H_q + h) * d;
+    const uint16_t *k0 = c->k + ((size_t)b * c->S * c->H_kv + g) * d;
+    const uint16_t *v0 = c->v + ((size_t)b * c->S * c->H_kv + g) * d;
+    double *dp = s + c->S;          /* scratch: s[0..S), dp[0..S), dod[0..d) */
+    double *dod = s + 2 * (size_t)c->S;
+    int n = i + 1;                  /* keys 0 .. i */
+    for (int x = 0; x < d; ++x) {
+        qd[x] = bf16_to_double(c->q[qoff + x]);
+        dod[x] = bf16_to_double(c->dout[qoff + x]);
+    }
+    for (int j = 0; j < n; ++j) {
+        const uint16_t *kj = k0 + (size_t)j * kv_stride;
+        const uint16_t *vj = v0 + (size_t)j * kv_stride;
+        double dot = 0.0, dpj = 0.0;
+        for (int x = 0; x < d; ++x) {
+            dot += qd[x] * bf16_to_double(kj[x]);
+            dpj += dod[x] * bf16_to_double(vj[x]);
+        }
+        s[j] = c->tau * dot;
+        dp[j] = dpj;
+    }
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) l += exp(s[j] - m);
+    for (int j = 0; j < n; ++j) s[j] = exp(s[j] - m) / l;   /* s now holds P_i */
+    double D = 0.0;
+    for (int j = 0; j < n; ++j) D += s[j] * dp[j];
+    double *dq = c->dq + (size_t)r * d;
+    for (int x = 0; x < d; ++x) dq[x] = 0.0;
+    for (int j = 0; j < n; ++j) {
+        double ds = s[j] * (dp[j] - D);
+        const uint16_t *kj = k0 + (size_t)j * kv_stride;
+        for (int x = 0; x < d; ++x) dq[x] += ds * bf16_to_double(kj[x]);
+    }
+    for (int x = 0; x < d; ++x) dq[x] *= c->tau;
+    c->lse[r] = m + log(l);
+    c->D[r] = D;
+}
+
+/* Phase 1 on selected rows (b, h, i): dq [nrows, d], lse [nrows], D [nrows]. */
+int oracle_prefill_causal_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   const uint16_t *dout, double *dq, double *lse, double *D,
+                                   int B, int S, int H_q, int H_kv, int d, double tau,
+                                   const int32_t *rows, long nrows, int nthreads)
+{
+    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
+    for (long r = 0; r < nrows; ++r) {
+        int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H_q || i < 0 || i >= S) return -2;
+    }
+    struct bwd_rows_ctx c = {q, k, v, dout, rows, dq, lse, D, B, S, H_q, H_kv, d, tau};
+    return run_rows(bwd_row, &c, nrows, nthreads, 2 * S + d, d);
+}
+
+struct bwd_keys_ctx {
+    const uint16_t *q, *k, *v, *dout;
+    const double *lse, *D;
+    const int32_t *keys;
+    double *dk, *dv;
+    int B, S, H_q, H_kv, d;
+    double tau;
+};
+
+static void bwd_key(void *p, long r, double *s, double *kd)
+{
+    struct bwd_keys_ctx *c = (struct bwd_keys_ctx *)p;
+    int b = c->keys[3 * r], g = c->keys[3 * r + 1], j = c->keys[3 * r + 2];
+    int G = c->H_q / c->H_kv;
+    int d = c->d;
+    double *vd = s;                 /* scratch: vd[0..d) */
+    size_t koff = (((size_t)b * c->S + j) * c->H_kv + g) * d;
+    for (int x = 0; x < d; ++x) {
+        kd[x] = bf16_to_double(c->k[koff + x]);
+        vd[x] = bf16_to_double(c->v[koff + x]);
+    }
+    double *dk = c->dk + (size_t)r * d, *dv = c->dv + (size_t)r * d;
+    for (int x = 0; x < d; ++x) dk[x] = dv[x] = 0.0;
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+        const double *lse = c->lse + ((size_t)b * c->H_q + h) * c->S;
+        const double *D = c->D + ((size_t)b * c->H_q + h) * c->S;
+        for (int i = j; i < c->S; ++i) {   /* query rows that see key j */
+            size_t qoff = (((size_t)b * c->S + i) * c->H_q + h) * d;
+            double dot = 0.0, dpij = 0.0;
+            for (int x = 0; x < d; ++x) {
+                dot += bf16_to_double(c->q[qoff + x]) * kd[x];
+                dpij += bf16_to_double(c->dout[qoff + x]) * vd[x];
+            }
+            double pij = exp(c->tau * dot - lse[i]);
+            double ds = pij * (dpij - D[i]);
+            for (int x = 0; x < d; ++x) {
+                dv[x] += pij * bf16_to_double(c->dout[qoff + x]);
+                dk[x] += c->tau * ds * bf16_to_double(c->q[qoff + x]);
+            }
+        }
+    }
+}
+
+/* Phase 2 on selected key rows (b, g, j), given LSE and D of every row [B, H_q, S] (from
+ * phase 1): dk, dv [nkeys, d]. */
+int oracle_prefill_causal_bwd_keys(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   const uint16_t *dout, const double *lse, const double *D,
+                                   double *dk, double *dv, int B, int S, int H_q, int H_kv, int d,
+                                   double tau, const int32_t *keys, long nkeys, int nthreads)
+{
+    if (H_kv <= 0 || H_q % H_kv != 0) return -1;
+    for (long r = 0; r < nkeys; ++r) {
+        int b = keys[3 * r], g = keys[3 * r + 1], j = keys[3 * r + 2];
+        if (b < 0 || b >= B || g < 0 || g >= H_kv || j < 0 || j >= S) return -2;
+    }
+    struct bwd_keys_ctx c = {q, k, v, dout, lse, D, keys, dk, dv, B, S, H_q, H_kv, d, tau};
+    return run_rows(bwd_key, &c, nkeys, nthreads, d, d);
+}

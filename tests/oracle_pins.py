@@ -16,7 +16,7 @@ from scipy.special import logsumexp, softmax
 
 import oracle
 from gqa_workloads.generate import bf16_bits_from_f32, chunk_inputs, decode_inputs, \
-    f32_from_bf16_bits, paged_decode_inputs, prefill_inputs
+    f32_from_bf16_bits, paged_decode_inputs, prefill_bwd_inputs, prefill_inputs
 
 BF16_ONE = 0x3F80
 
@@ -475,6 +475,124 @@ def pin_decode_tokens_reduces_to_decode_and_chunks(lib):
     assert np.all(o[1, :2] == 0) and np.all(lse[1, :, :2] == -np.inf)
     assert np.all(np.isfinite(lse[1, :, 2:]))
     assert np.all(o[2] == 0) and np.all(lse[2] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# Backward of causal prefill (V07 section 6.1, gradient formulas; section 6.4, recompute of
+# P from the row's LSE).  The gradient of the scalar L = sum(O * dO) with respect to q, k
+# and v is exactly what the backward returns for output gradient dO, so central
+# differences of a library-routine forward pin every formula, index and scale in it.
+
+def _np_causal_forward(q, k, v, tau):
+    """Causal GQA attention on float64 arrays with scipy's softmax (head h reads KV head
+    floor(h / G)): q [B, S, H_q, d]; k, v [B, S, H_kv, d] -> o [B, S, H_q, d]."""
+    B, S, H_q, _ = q.shape
+    G = H_q // k.shape[2]
+    above = np.triu(np.ones((S, S), dtype=bool), 1)
+    o = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H_q):
+            s = tau * (q[b, :, h] @ k[b, :, h // G].T)
+            s[above] = -np.inf
+            o[b, :, h] = softmax(s, axis=1) @ v[b, :, h // G]
+    return o
+
+
+def pin_bwd_finite_differences(lib):
+    """Every coordinate of dq, dk, dv of a tiny case (two query heads per KV head, a scale
+    that is not 1/sqrt(d)) against central differences of sum(O * dO)."""
+    p = prefill_bwd_inputs(1, 5, 4, 2, 6, seed=71)
+    q, k, v, do = (_f64(p[x]) for x in ("q", "k", "v", "do"))
+    tau = 0.37
+    dq, dk, dv, _, _ = oracle.prefill_causal_bwd(p["q"], p["k"], p["v"], p["do"], tau=tau,
+                                                 nthreads=2, lib=lib)
+    h = 1e-6
+    for arr, grad, name in ((q, dq, "dq"), (k, dk, "dk"), (v, dv, "dv")):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            x0 = arr[idx]
+            arr[idx] = x0 + h
+            lp = float(np.sum(_np_causal_forward(q, k, v, tau) * do))
+            arr[idx] = x0 - h
+            lm = float(np.sum(_np_causal_forward(q, k, v, tau) * do))
+            arr[idx] = x0
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(grad - fd).max()
+        assert err <= 1e-7 + 1e-6 * np.abs(fd).max(), (name, err)
+
+
+def pin_bwd_torch_autograd(lib):
+    """A larger case (B = 2, ragged-looking S = 23, three query heads per KV head) against
+    torch's fp64 autograd of the plain definition on the CPU."""
+    import torch
+    p = prefill_bwd_inputs(2, 23, 6, 2, 16, seed=72)
+    tau = 0.21
+    q, k, v = (torch.from_numpy(_f64(p[x])).requires_grad_(True) for x in ("q", "k", "v"))
+    do = torch.from_numpy(_f64(p["do"]))
+    G = 3
+    kr = k.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)      # [B, H_q, S, d]
+    vr = v.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    s = tau * torch.matmul(q.permute(0, 2, 1, 3), kr.transpose(-1, -2).contiguous())
+    s = s.masked_fill(torch.triu(torch.ones(23, 23, dtype=torch.bool), 1), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vr).permute(0, 2, 1, 3)
+    (o * do).sum().backward()
+    dq, dk, dv, _, _ = oracle.prefill_causal_bwd(p["q"], p["k"], p["v"], p["do"], tau=tau,
+                                                 nthreads=4, lib=lib)
+    for mine, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        ref = ref.numpy()
+        assert np.abs(mine - ref).max() <= 1e-10 * (1 + np.abs(ref).max())
+
+
+def pin_bwd_invariants(lib):
+    """Rows of P sum to one, so the dV rows of a KV head add up to the dO rows of its query
+    heads; rows of dS sum to zero (sum_j P_ij (dP_ij - D_i) = D_i - D_i), so the dK rows of
+    a KV head add up to zero."""
+    p = prefill_bwd_inputs(2, 40, 8, 2, 16, seed=73)
+    dq, dk, dv, _, _ = oracle.prefill_causal_bwd(p["q"], p["k"], p["v"], p["do"], nthreads=4,
+                                                 lib=lib)
+    do = _f64(p["do"])
+    for b in range(2):
+        for g in range(2):
+            want = do[b][:, 4 * g:4 * g + 4].sum(axis=(0, 1))
+            _rel_close(dv[b, :, g].sum(axis=0), want, rtol=1e-12, atol=1e-12)
+            assert np.abs(dk[b, :, g].sum(axis=0)).max() <= 1e-12 * np.abs(dk[b, :, g]).sum()
+
+
+def pin_bwd_single_token_and_gqa(lib):
+    """S = 1: P = [1] and dS = 0, so dq = dk = 0 and dv sums the group's dO.  Grouped heads
+    equal MHA on K/V repeated per query head, with dk, dv summed over each group."""
+    p = prefill_bwd_inputs(1, 1, 4, 2, 8, seed=74)
+    dq, dk, dv, lse, D = oracle.prefill_causal_bwd(p["q"], p["k"], p["v"], p["do"], lib=lib)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    do = _f64(p["do"])
+    _rel_close(dv[0, 0], do[0, 0].reshape(2, 2, 8).sum(axis=1), rtol=1e-15, atol=0)
+    p = prefill_bwd_inputs(1, 19, 6, 2, 8, seed=75)
+    kr, vr = (np.repeat(p[x], 3, axis=2) for x in ("k", "v"))
+    g = oracle.prefill_causal_bwd(p["q"], p["k"], p["v"], p["do"], nthreads=4, lib=lib)
+    m = oracle.prefill_causal_bwd(p["q"], kr, vr, p["do"], nthreads=4, lib=lib)
+    _rel_close(g[0], m[0], rtol=1e-13, atol=1e-15)
+    for t in (1, 2):
+        _rel_close(g[t], m[t].reshape(1, 19, 2, 3, 8).sum(axis=3), rtol=1e-12, atol=1e-14)
+
+
+def pin_bwd_row_and_key_subsets(lib):
+    """The row and key functions on a subset give the rows of the whole backward, and the
+    LSE the backward keeps is the forward's."""
+    p = prefill_bwd_inputs(2, 21, 4, 1, 8, seed=76)
+    dq, dk, dv, lse, D = oracle.prefill_causal_bwd(p["q"], p["k"], p["v"], p["do"], nthreads=3,
+                                                   lib=lib)
+    rows = np.array([[1, 3, 20], [0, 0, 0], [1, 2, 7]], dtype=np.int32)
+    dqr, lser, Dr = oracle.prefill_causal_bwd_rows(p["q"], p["k"], p["v"], p["do"], rows,
+                                                   lib=lib)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.array_equal(dqr[n], dq[b, i, h]) and lser[n] == lse[b, h, i] and Dr[n] == D[b, h, i]
+    keys = np.array([[0, 0, 20], [1, 0, 0], [1, 0, 9]], dtype=np.int32)
+    dkr, dvr = oracle.prefill_causal_bwd_keys(p["q"], p["k"], p["v"], p["do"], lse, D, keys,
+                                              lib=lib)
+    for n, (b, g, j) in enumerate(keys):
+        assert np.array_equal(dkr[n], dk[b, j, g]) and np.array_equal(dvr[n], dv[b, j, g])
+    _, lse_f = oracle.prefill_causal(p["q"], p["k"], p["v"], lib=lib)
+    _rel_close(lse, lse_f, rtol=1e-14, atol=1e-14)
 
 
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -42,6 +42,22 @@ MUTANTS = {
                               "double e = exp(s[j] - m);\n        l += exp(s[j]);"),
     "partial_wrong_start": ("(((size_t)b * c->S_max + c->j0) * c->H_kv + g) * c->d;\n    const uint16_t *v0",
                             "(((size_t)b * c->S_max) * c->H_kv + g) * c->d;\n    const uint16_t *v0"),
+    "bwd_D_dropped": ("double ds = s[j] * (dp[j] - D);", "double ds = s[j] * dp[j];"),
+    "bwd_dq_without_scale": ("for (int x = 0; x < d; ++x) dq[x] *= c->tau;", ""),
+    "bwd_dp_from_k": ("dpj += dod[x] * bf16_to_double(vj[x]);",
+                      "dpj += dod[x] * bf16_to_double(kj[x]);"),
+    "bwd_rows_exclude_diagonal": ("int n = i + 1;                  /* keys 0 .. i */",
+                                  "int n = i;"),
+    "bwd_dk_from_k": ("dk[x] += c->tau * ds * bf16_to_double(c->q[qoff + x]);",
+                      "dk[x] += c->tau * ds * kd[x];"),
+    "bwd_dv_weighted_by_ds": ("dv[x] += pij * bf16_to_double(c->dout[qoff + x]);",
+                              "dv[x] += ds * bf16_to_double(c->dout[qoff + x]);"),
+    "bwd_keys_head_map_modulo": ("for (int h = g * G; h < (g + 1) * G; ++h) {",
+                                 "for (int h = g; h < c->H_q; h += c->H_kv) {"),
+    "bwd_keys_skip_diagonal_row": ("for (int i = j; i < c->S; ++i) {", "for (int i = j + 1; i < c->S; ++i) {"),
+    "bwd_keys_lse_of_key_row": ("double pij = exp(c->tau * dot - lse[i]);",
+                                "double pij = exp(c->tau * dot - lse[j]);"),
+    "bwd_keys_D_of_key_row": ("double ds = pij * (dpij - D[i]);", "double ds = pij * (dpij - D[j]);"),
     "q_widening_offset": ("for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[c]);",
                           "for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[(c + 1) % d]);"),
 }
