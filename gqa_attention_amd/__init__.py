@@ -76,6 +76,11 @@ def load_library(path=LIBRARY):
     L.gqa_attn_prefill_causal.restype = ci
     L.gqa_attn_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, ci, ci, cf, vp]
     L.gqa_attn_prefill_chunk.restype = ci
+    L.gqa_prefill_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    L.gqa_prefill_bwd_workspace_bytes.restype = cs
+    L.gqa_attn_prefill_causal_bwd.argtypes = [vp, vp, vp, vp, f32p, vp, vp, vp, vp, ci, ci, ci, ci,
+                                              ci, cf, vp, cs, vp]
+    L.gqa_attn_prefill_causal_bwd.restype = ci
     if path == LIBRARY:
         _lib = L
     return L
@@ -333,3 +338,43 @@ def prefill_chunk(q, k_cache, v_cache, q_start=None, softmax_scale=None, out=Non
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l), B, T, qs, S_kv, H_q, H_kv, d,
         _scale(d, softmax_scale), _stream(q.device)))
     return o, l
+
+
+def prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d):
+    """Workspace bytes of ``prefill_causal_bwd`` (per-row statistics and the fp32 shares
+    of dK, dV of every query head)."""
+    n = load_library().gqa_prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d)
+    if n == 0:
+        raise ValueError(f"invalid backward sizes B={B} S={S} H_q={H_q} H_kv={H_kv} d={d}")
+    return n
+
+
+def prefill_bwd_workspace(B, S, H_q, H_kv, d, device="cuda"):
+    return torch.empty(prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d), dtype=torch.uint8,
+                       device=device)
+
+
+def prefill_causal_bwd(q, k, v, o, lse, d_o, softmax_scale=None, workspace=None, out=None):
+    """Backward of causal GQA prefill: from the forward's q, k, v, its o and lse and the
+    output gradient d_o, returns (dq [B,S,H_q,d], dk [B,S,H_kv,d], dv [B,S,H_kv,d]) bf16.
+    ``out`` may give the three output tensors."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _need(t, name, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    if (tuple(k.shape) != (B, S, H_kv, d) or tuple(v.shape) != tuple(k.shape) or
+            tuple(o.shape) != tuple(q.shape) or tuple(d_o.shape) != tuple(q.shape) or
+            tuple(lse.shape) != (B, H_q, S)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}, o {tuple(o.shape)}, d_o {tuple(d_o.shape)}, "
+                         f"lse {tuple(lse.shape)}")
+    ws = prefill_bwd_workspace(B, S, H_q, H_kv, d, q.device) if workspace is None else workspace
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    _check(load_library().gqa_attn_prefill_causal_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, S, H_q, H_kv, d, _scale(d, softmax_scale), _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq, dk, dv

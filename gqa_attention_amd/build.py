@@ -16,7 +16,8 @@ LIBRARY = os.path.join(HERE, "libgqa_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gqa_attn_api.cpp", "decode_split.hip", "lse_merge.hip", "prefill_causal.hip"]
+SOURCES = ["gqa_attn_api.cpp", "decode_split.hip", "lse_merge.hip", "prefill_causal.hip",
+           "prefill_bwd.hip"]
 
 # Packed fp32 VALU instructions are switched off for every kernel; the host pass
 # prints a harmless "not a recognized feature" warning for it.

@@ -440,4 +440,58 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
                    softmax_scale, stream);
 }
 
+size_t gqa_prefill_bwd_workspace_bytes(int B, int S, int H_q, int H_kv, int d) {
+    if (B <= 0 || S <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0 || d != 128) return 0;
+    return gqa::prefill_bwd_workspace_bytes(B, S, H_q);
+}
+
+int gqa_attn_prefill_causal_bwd(const void *q, const void *k, const void *v, const void *o,
+                                const float *lse, const void *d_o, void *dq, void *dk, void *dv,
+                                int B, int S, int H_q, int H_kv, int d, float softmax_scale,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    int rc;
+    if ((rc = check_heads(B, H_q, H_kv))) return rc;
+    if (S <= 0) return fail(GQA_ERR_BAD_SHAPE, "S=%d must be positive", S);
+    if (d != 128)
+        return fail(GQA_ERR_UNSUPPORTED, "prefill backward head size d=%d (supported: 128)", d);
+    const long n_kb = (S + 255) / 256;
+    if (n_kb * (long)B * H_q > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*H_q*ceil(S/256) exceeds the grid limit");
+    if ((long)B * S * H_kv * (d / 4) / 256 > 0x7FFFFFFFL ||
+        (long)B * H_q * ((S + 63) / 64) * 4 > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*S*H exceeds the grid limit");
+    if ((rc = check_bf16(q, "q")) || (rc = check_bf16(k, "k")) || (rc = check_bf16(v, "v")) ||
+        (rc = check_bf16(o, "o")) || (rc = check_bf16(d_o, "d_o")) || (rc = check_f32(lse, "lse")) ||
+        (rc = check_bf16(dq, "dq")) || (rc = check_bf16(dk, "dk")) || (rc = check_bf16(dv, "dv")))
+        return rc;
+    if ((rc = check_scale(softmax_scale))) return rc;
+    const size_t need = gqa::prefill_bwd_workspace_bytes(B, S, H_q);
+    if (!workspace) return fail(GQA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(workspace, 256)) return fail(GQA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    gqa::BwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<const uint16_t *>(o);
+    a.dout = static_cast<const uint16_t *>(d_o);
+    a.lse = lse;
+    a.dq = static_cast<uint16_t *>(dq);
+    a.dk = static_cast<uint16_t *>(dk);
+    a.dv = static_cast<uint16_t *>(dv);
+    a.stats = a.part_dk = a.part_dv = nullptr;
+    a.B = B;
+    a.S = S;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.d = d;
+    a.scale = softmax_scale;
+    a.scale_log2 = softmax_scale * kLog2e;
+    if ((rc = hip_status(gqa::launch_prefill_bwd(a, workspace, static_cast<hipStream_t>(stream)),
+                         "prefill_causal_bwd")))
+        return rc;
+    return ok();
+}
+
 }  // extern "C"

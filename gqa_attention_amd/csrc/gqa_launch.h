@@ -69,6 +69,23 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+// Backward of whole-prompt causal prefill: q, o, dout, dq [B][S][H_q][d]; k, v, dk, dv
+// [B][S][H_kv][d] (bf16); lse [B][H_q][S] (natural log, the forward's).  The launcher lays
+// its workspace out as per-row statistics (lse in log2 units and D = dO . O per 64-row
+// block) and the fp32 per-query-head shares of dK and dV.
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    float *stats, *part_dk, *part_dv;   // set by the launcher inside the workspace
+    int B, S, H_q, H_kv, d;
+    float scale;                        // softmax_scale (tau)
+    float scale_log2;                   // tau * log2(e)
+};
+
+size_t prefill_bwd_workspace_bytes(int B, int S, int H_q);
+hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream);
+
 hipError_t launch_decode_split(const DecodeSplitArgs &a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream);

@@ -1,0 +1,522 @@
+// prefill_bwd.hip -- backward of whole-prompt causal GQA prefill on gfx950.
+//
+// Given the forward's O and LSE and the output gradient dO, the input gradients are
+// ("Attention Kernel lineage" (V07), section 6.1):
+//   P_ij = exp(s_ij - LSE_i)    dP_ij = dO_i . v_j    D_i = sum_j P_ij dP_ij = dO_i . O_i
+//   dS_ij = P_ij (dP_ij - D_i)  dQ_i = tau sum_j dS_ij k_j
+//   dK_j = tau sum_i dS_ij q_i  dV_j = sum_i P_ij dO_i      (causal pairs j <= i)
+// and a KV head's dK and dV add up the contributions of its G query heads (section 14).
+// P is never stored: each kernel forms it again from the row's LSE (section 6.3, recompute).
+//
+// Four launches:
+//   bwd_prep   D_i as the row-wise dot of O and dO (section 6.2) and LSE in log2 units, kept
+//              per 64-row block as [lse2 x 64 | D x 64] so one DMA fetches a block's pair;
+//   bwd_dq     query-block outer, key tiles inner, dQ accumulated in registers: no atomics
+//              (section 8: Q outer removes the dQ atomics of the section 6.4 loop);
+//   bwd_dkdv   key-block outer, query tiles inner (the loop of section 6.4 without its dQ
+//              update), one workgroup per (key block, query head): each query head's share
+//              of dK and dV goes to an fp32 workspace slot of its own;
+//   bwd_reduce adds the G slots of each KV head in a fixed order (the split then two-stage
+//              reduce of section 6.5), so results are deterministic.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 32 keys x 32 query rows per wave step):
+//   dq kernel   S^T = K.Q^T and dP^T = V.dO^T (K, V rows from LDS; Q, dO fragments in
+//               registers); a lane owns one query row, so LSE and D are per-lane scalars;
+//               dQ^T += K^T.dS^T takes dS^T straight from the score registers (B operand)
+//               and K^T through the LDS transpose read.
+//   dkdv kernel S = Q.K^T and dP = dO.V^T (Q, dO rows from LDS; K fragments in registers,
+//               V rows from the workgroup's V block in LDS); a lane owns one key;
+//               dV^T += dO^T.P and dK^T += Q^T.dS take P and dS straight from the score
+//               registers and dO^T, Q^T through the LDS transpose read.
+// Tiles that are read both by rows and transposed store 16-byte chunk c of row r at chunk
+// position c ^ (4 (r % 4) + (r / 4) % 4): sixteen consecutive rows then fall on sixteen
+// distinct positions (row reads), and so do four consecutive rows of one 64-byte column
+// group (transpose reads).
+#include "gqa_device.h"
+#include "gqa_launch.h"
+
+namespace gqa {
+namespace {
+
+constexpr int D = 128;
+constexpr int kRowBytes = D * 2;               // one row of one head: 256 bytes
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStatRows = 64;                  // rows per statistics block
+constexpr int kStatFloats = 2 * kStatRows;     // lse2 then D
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// Buffer-resource word 3 of the gfx9 family (32-bit data format, no swizzle).
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+// DMA of 32 consecutive rows (each 256 bytes, row_bytes apart, the first at gbase) into LDS
+// at lds + dst in the swizzled layout.  Wave w copies rows 4w .. 4w+3: lane l lands at row
+// 4w + l/16, chunk position l%16, and fetches the logical chunk stored there (voff is that
+// chunk's byte offset from the group's first row).  Only the first `rows` rows are read;
+// the others arrive as zeros and cost no memory traffic.
+__device__ __forceinline__ void dma_rows32(uint8_t *lds, int dst, const uint16_t *gbase,
+                                           uint32_t row_bytes, int rows, uint32_t voff, int w) {
+    uint32_t bytes = rows <= 0 ? 0u : rows >= 32 ? 32u * row_bytes : (uint32_t)rows * row_bytes;
+    bytes = __builtin_amdgcn_readfirstlane(bytes);
+    const uint64_t base = (uint64_t)gbase;
+    const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, kRsrcWord3};
+    const uint32_t lds_dst = (uint32_t)(uintptr_t)(lds + dst + 4 * w * kRowBytes);
+    // (assembly, so that the compiler adds no wait for the DMA before later LDS reads: the
+    // loops' own waits and barriers order the buffers)
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_dst))
+                 : "memory");
+}
+
+// DMA of up to 1 KiB of contiguous bytes (the first `bytes` of them real, the rest zeros)
+// into lds + dst: lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void dma_bytes1k(uint8_t *lds, int dst, const void *gbase,
+                                            uint32_t bytes, uint32_t voff) {
+    bytes = __builtin_amdgcn_readfirstlane(bytes);
+    const uint64_t base = (uint64_t)gbase;
+    const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, kRsrcWord3};
+    const uint32_t lds_dst = (uint32_t)(uintptr_t)(lds + dst);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_dst))
+                 : "memory");
+}
+
+// Per-lane LDS byte offsets, fixed for a kernel's life.
+//   row[ks]: the 16 bytes of row lane%32 (relative to a 32-row group) that hold reduction
+//            slots d = 16 ks + 8 (lane/32) .. +7 (an A or B operand read along d);
+//   tr[dt][m&1]: the transpose-read start for column group dt (d = 32 dt ..) at row
+//            offset 8m of a 32-row group; rows 16 kk further add 16 kk rows.
+struct Addr {
+    uint32_t row[8];
+    uint32_t tr[4][2];
+};
+
+__device__ __forceinline__ Addr make_addr(int lane) {
+    Addr a;
+    const int r32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+        a.row[ks] = (uint32_t)(r32 * kRowBytes + 16 * ((2 * ks + hf) ^ swz(r32)));
+    // transpose read: lane j of each 16-lane group points at row 4hf + (j%16)/4, 8 bytes
+    // at column 4 (j%4) of its 16-column half of the 64-byte group (see lds_read_tr16)
+    const int vr = 4 * hf + ((lane & 15) >> 2);
+    const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        a.tr[dt][0] = (uint32_t)(vr * kRowBytes + 16 * ((4 * dt + cc) ^ swz(vr)) + 8 * (lane & 1));
+        // row vr + 8: swz(vr + 8) = swz(vr) ^ 2, i.e. the chunk index with bit 1 flipped
+        a.tr[dt][1] = (uint32_t)((vr + 8) * kRowBytes +
+                                 16 * ((4 * dt + cc) ^ swz(vr + 8)) + 8 * (lane & 1));
+    }
+    return a;
+}
+
+// The 8-slot operand of reduction rows 16 kk + {8 (j/4) + 4 hf + j%4} of column lane%32
+// of column group dt, from a swizzled 32-row group at lds + base: two transpose reads
+// (rows 4hf.. and 8 + 4hf..).  Rows 16 further have the same swizzle (swz(r + 16) = swz(r)).
+__device__ __forceinline__ bf16x8 read_tr(const uint8_t *lds, uint32_t base, const Addr &a,
+                                          int dt, int kk) {
+    const uint8_t *p0 = lds + base + a.tr[dt][0] + kk * 16 * kRowBytes;
+    const uint8_t *p1 = lds + base + a.tr[dt][1] + kk * 16 * kRowBytes;
+    const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(p0));
+    const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(p1));
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+__device__ __forceinline__ bf16x8 read_row(const uint8_t *lds, uint32_t base, const Addr &a,
+                                           int ks) {
+    return as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + base + a.row[ks]));
+}
+
+// Elements 8 kk .. 8 kk + 7 of a lane's 16 scores as a bf16 B operand (reduction slot j <->
+// element 8 kk + j, the order the transpose reads deliver the other operand in).
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[16], int kk) {
+    const u32x4 w = {pack_bf16x2(x[8 * kk + 0], x[8 * kk + 1]), pack_bf16x2(x[8 * kk + 2], x[8 * kk + 3]),
+                     pack_bf16x2(x[8 * kk + 4], x[8 * kk + 5]), pack_bf16x2(x[8 * kk + 6], x[8 * kk + 7])};
+    return as_bf16x8(w);
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_prep: one row (b, h, i) per 16 lanes, i over the padded length n_t * 64.
+
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int n_t) {
+    const int sub = threadIdx.x & 15;
+    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const long n_pad = (long)n_t * kStatRows;
+    const long total = (long)a.B * a.H_q * n_pad;
+    if (row >= total) return;   // (whole 16-lane groups leave together)
+    const int i = (int)(row % n_pad);
+    const long bh = row / n_pad;
+    const int h = (int)(bh % a.H_q), b = (int)(bh / a.H_q);
+    float dot = 0.f;
+    if (i < a.S) {
+        const size_t off = (((size_t)b * a.S + i) * a.H_q + h) * D + sub * 8;
+        const bf16x8 o = as_bf16x8(load16(a.o + off));
+        const bf16x8 g = as_bf16x8(load16(a.dout + off));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf((float)o[e], (float)g[e], dot);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 16);
+    if (sub == 0) {
+        float *blk = a.stats + (bh * n_t + i / kStatRows) * kStatFloats;
+        // rows past the end: lse2 = +inf makes every P of the row 0, D = 0
+        blk[i % kStatRows] =
+            i < a.S ? a.lse[bh * a.S + i] * kLog2e : __builtin_inff();
+        blk[kStatRows + i % kStatRows] = i < a.S ? dot : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_dq: workgroup = 256 query rows of one query head (8 waves x 32 rows), key tiles of 64
+// through a ring of two LDS slots (K 16 KiB, V 16 KiB each).
+
+constexpr int kQBr = 256;
+constexpr int kKT = 64;
+constexpr int kTile = kKT * kRowBytes;               // 16 KiB
+constexpr int kDqSlot = 2 * kTile;                   // K then V
+constexpr int kDqLds = 2 * kDqSlot;                  // 64 KiB
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb, int n_t) {
+    __shared__ __attribute__((aligned(256))) uint8_t smem[kDqLds];
+    const int G = a.H_q / a.H_kv;
+    int u = blockIdx.x;
+    const int h = u % a.H_q;
+    u /= a.H_q;
+    const int b = u % a.B;
+    const int qb = n_qb - 1 - u / a.B;     // long-prefix blocks first
+    const int g = h / G;
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31, hf = lane >> 5;
+    const int i0 = qb * kQBr;
+    const int r0 = i0 + 32 * w;            // the wave's first row
+    const int row = r0 + r32;              // the lane's row
+    const int last_row = min(i0 + kQBr, a.S) - 1;
+    const int n_kt = last_row / kKT + 1;   // key tiles of the workgroup
+    // 32-key steps of the wave (up to its last real row's diagonal); the step holding row
+    // r0's diagonal and the ones after it are masked
+    const int n_sub = r0 < a.S ? min(r0 + 31, a.S - 1) / 32 + 1 : 0;
+    const int mask_from = r0 / 32;
+    const Addr ad = make_addr(lane);
+
+    const uint32_t kv_row_bytes = (uint32_t)a.H_kv * kRowBytes;
+    const uint16_t *kbase = a.k + ((size_t)b * a.S * a.H_kv + g) * D;
+    const uint16_t *vbase = a.v + ((size_t)b * a.S * a.H_kv + g) * D;
+    const int lr = 4 * w + lane / 16;
+    const uint32_t voff = (uint32_t)lr * kv_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
+
+    // Q and dO fragments (B operands): column = the lane's row, slots d = 16 ks + 8 hf ..
+    bf16x8 qf[8], gf[8];
+    {
+        const int rr = min(row, a.S - 1);
+        const size_t off = (((size_t)b * a.S + rr) * a.H_q + h) * D + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            qf[ks] = as_bf16x8(load16(a.q + off + 16 * ks));
+            gf[ks] = as_bf16x8(load16(a.dout + off + 16 * ks));
+        }
+    }
+    const float *st = a.stats + (((size_t)b * a.H_q + h) * n_t + min(row, a.S - 1) / kStatRows) *
+                                    kStatFloats;
+    const float lse2 = st[min(row, a.S - 1) % kStatRows];
+    const float Drow = st[kStatRows + min(row, a.S - 1) % kStatRows];
+    const float c = a.scale_log2;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+    auto issue = [&](int t, int slot) {
+        const int k0 = t * kKT;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = k0 + 32 * i;
+            dma_rows32(smem, slot * kDqSlot + 32 * i * kRowBytes, kbase + (size_t)r * a.H_kv * D,
+                       kv_row_bytes, a.S - r, voff, w);
+            dma_rows32(smem, slot * kDqSlot + kTile + 32 * i * kRowBytes,
+                       vbase + (size_t)r * a.H_kv * D, kv_row_bytes, a.S - r, voff, w);
+        }
+    };
+
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < n_kt; ++t) {
+        const int slot = t & 1;
+        issue(t + 1, slot ^ 1);   // (past the last tile it only zero-fills the free slot)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int us = 2 * t + hh;
+            if (us >= n_sub) continue;
+            const uint32_t kh = slot * kDqSlot + hh * 32 * kRowBytes;
+            const uint32_t vh = kh + kTile;
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                s = mfma32(read_row(smem, kh, ad, ks), qf[ks], s);
+                dp = mfma32(read_row(smem, vh, ad, ks), gf[ks], dp);
+            }
+            float ds[16];
+            const bool diag = us >= mask_from;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * us + 8 * (r >> 2) + 4 * hf + (r & 3);
+                float p = exp2_fast(fmaf(s[r], c, -lse2));
+                if (diag && key > row) p = 0.f;
+                ds[r] = p * (dp[r] - Drow);
+            }
+            const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                acc[dt] = mfma32(read_tr(smem, kh, ad, dt, 0), d0, acc[dt]);
+                acc[dt] = mfma32(read_tr(smem, kh, ad, dt, 1), d1, acc[dt]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the next tile's DMA
+        __syncthreads();
+    }
+
+    if (row >= a.S) return;
+    const float tau = a.scale;
+    uint16_t *out = a.dq + (((size_t)b * a.S + row) * a.H_q + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int dd = dt * 32 + rq * 8 + hf * 4;
+            const int r = rq * 4;
+            *reinterpret_cast<u32x2 *>(out + dd) =
+                u32x2{pack_bf16x2(acc[dt][r] * tau, acc[dt][r + 1] * tau),
+                      pack_bf16x2(acc[dt][r + 2] * tau, acc[dt][r + 3] * tau)};
+        }
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_dkdv: workgroup = 256 keys of one KV head against the rows of one query head (8 waves
+// x 32 keys).  LDS: the V block (64 KiB), then a ring of two slots of a 64-row query tile
+// (Q 16 KiB, dO 16 KiB, statistics 1 KiB), then 1 KiB that the other waves' statistics DMA
+// fills with zeros (every wave issues the same DMA count per tile).
+
+constexpr int kKBlk = 256;
+constexpr int kVBlock = kKBlk * kRowBytes;           // 64 KiB
+constexpr int kQTile = kStatRows * kRowBytes;        // 16 KiB
+constexpr int kSlot = 2 * kQTile + 1024;
+constexpr int kRing = kVBlock;
+constexpr int kSink = kRing + 2 * kSlot;
+constexpr int kKvLds = kSink + 1024;                 // 131 KiB: one workgroup per CU
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kb, int n_t,
+                                                               int S_pad) {
+    __shared__ __attribute__((aligned(256))) uint8_t smem[kKvLds];
+    const int G = a.H_q / a.H_kv;
+    int u = blockIdx.x;
+    const int h = u % a.H_q;
+    u /= a.H_q;
+    const int b = u % a.B;
+    const int kb = u / a.B;                // block 0 (every row sees it) first
+    const int g = h / G;
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31, hf = lane >> 5;
+    const int k0 = kb * kKBlk;
+    const int key = k0 + 32 * w + r32;     // the lane's key
+    const int t0 = k0 / kStatRows;         // first query tile (rows k0 ..)
+    const Addr ad = make_addr(lane);
+    const int lr = 4 * w + lane / 16;
+
+    const uint32_t q_row_bytes = (uint32_t)a.H_q * kRowBytes;
+    const uint32_t kv_row_bytes = (uint32_t)a.H_kv * kRowBytes;
+    const uint32_t qvoff = (uint32_t)lr * q_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
+    const uint32_t kvvoff = (uint32_t)lr * kv_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
+    const uint16_t *qbase = a.q + ((size_t)b * a.S * a.H_q + h) * D;
+    const uint16_t *gbase = a.dout + ((size_t)b * a.S * a.H_q + h) * D;
+    const float *stbase = a.stats + ((size_t)b * a.H_q + h) * n_t * kStatFloats;
+
+    // K fragments (B operand of S = Q.K^T): column = the lane's key, slots d = 16 ks + 8 hf ..
+    bf16x8 kf[8];
+    {
+        const size_t off = (((size_t)b * a.S + min(key, a.S - 1)) * a.H_kv + g) * D + hf * 8;
+        const bool live = key < a.S;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const u32x4 x = load16(a.k + off + 16 * ks);
+            kf[ks] = as_bf16x8(live ? x : u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    // the V block: rows k0 .. k0 + 255 of KV head g
+    {
+        const uint16_t *vb = a.v + (((size_t)b * a.S + k0) * a.H_kv + g) * D;
+#pragma unroll
+        for (int i = 0; i < kKBlk / 32; ++i)
+            dma_rows32(smem, 32 * i * kRowBytes, vb + (size_t)32 * i * a.H_kv * D, kv_row_bytes,
+                       a.S - k0 - 32 * i, kvvoff, w);
+    }
+    auto issue = [&](int t, int slot) {
+        const int base = kRing + slot * kSlot;
+        const int r = t * kStatRows;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            dma_rows32(smem, base + 32 * i * kRowBytes, qbase + (size_t)(r + 32 * i) * a.H_q * D,
+                       q_row_bytes, a.S - r - 32 * i, qvoff, w);
+            dma_rows32(smem, base + kQTile + 32 * i * kRowBytes,
+                       gbase + (size_t)(r + 32 * i) * a.H_q * D, q_row_bytes, a.S - r - 32 * i,
+                       qvoff, w);
+        }
+        // statistics block t (512 bytes) by wave 0; the other waves zero-fill the sink
+        const bool mine = w == 0 && t < n_t;
+        dma_bytes1k(smem, mine ? base + 2 * kQTile : kSink,
+                    stbase + (size_t)min(t, n_t - 1) * kStatFloats, mine ? 512u : 0u,
+                    16u * (uint32_t)lane);
+    };
+
+    f32x16 dv[4], dk[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dv[dt][r] = dk[dt][r] = 0.f;
+    const float c = a.scale_log2;
+
+    issue(t0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = t0; t < n_t; ++t) {
+        const int slot = (t - t0) & 1;
+        issue(t + 1, slot ^ 1);
+        const uint32_t base = kRing + slot * kSlot;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int us = 2 * (t - t0) + hh;   // 32-row step relative to the key block
+            if (us < w) continue;               // rows all before the wave's keys
+            const uint32_t qh = base + hh * 32 * kRowBytes;
+            const uint32_t gh = qh + kQTile;
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                s = mfma32(read_row(smem, qh, ad, ks), kf[ks], s);
+                dp = mfma32(read_row(smem, gh, ad, ks),
+                            read_row(smem, 32 * w * kRowBytes, ad, ks), dp);
+            }
+            // lse2 and D of the lane's 16 rows 32 hh + 8 q + 4 hf + (0..3)
+            const uint8_t *stp = smem + base + 2 * kQTile;
+            float p[16], ds[16];
+            const bool diag = us == w;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int rr = 32 * hh + 8 * q4 + 4 * hf;
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(stp + 4 * rr);
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(stp + 4 * (kStatRows + rr));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * q4 + j;
+                    float pv = exp2_fast(fmaf(s[r], c, -l4[j]));
+                    // diagonal step: rows k0 + 32 w + (8 q4 + 4 hf + j), keys k0 + 32 w + r32
+                    if (diag && r32 > 8 * q4 + 4 * hf + j) pv = 0.f;
+                    p[r] = pv;
+                    ds[r] = pv * (dp[r] - d4[j]);
+                }
+            }
+            const bf16x8 p0 = pack8(p, 0), p1 = pack8(p, 1);
+            const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                dv[dt] = mfma32(read_tr(smem, gh, ad, dt, 0), p0, dv[dt]);
+                dv[dt] = mfma32(read_tr(smem, gh, ad, dt, 1), p1, dv[dt]);
+                dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 0), d0, dk[dt]);
+                dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 1), d1, dk[dt]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the next tile's DMA
+        __syncthreads();
+    }
+
+    // this query head's share: rows of the fp32 slot [b][h][key][d] (keys past S are padding)
+    const float tau = a.scale;
+    const size_t off = (((size_t)b * a.H_q + h) * S_pad + key) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int dd = dt * 32 + rq * 8 + hf * 4;
+            const int r = rq * 4;
+            *reinterpret_cast<f32x4 *>(a.part_dk + off + dd) =
+                f32x4{dk[dt][r] * tau, dk[dt][r + 1] * tau, dk[dt][r + 2] * tau, dk[dt][r + 3] * tau};
+            *reinterpret_cast<f32x4 *>(a.part_dv + off + dd) =
+                f32x4{dv[dt][r], dv[dt][r + 1], dv[dt][r + 2], dv[dt][r + 3]};
+        }
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_reduce: dK, dV of (b, j, g) = the sum of the G query heads' slots, in head order.
+
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int S_pad) {
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    const long total = (long)a.B * a.S * a.H_kv * (D / 4);
+    if (t >= total) return;
+    const int c4 = (int)(t % (D / 4));
+    long x = t / (D / 4);
+    const int g = (int)(x % a.H_kv);
+    x /= a.H_kv;
+    const int j = (int)(x % a.S);
+    const int b = (int)(x / a.S);
+    const int G = a.H_q / a.H_kv;
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < G; ++e) {
+        const size_t off = (((size_t)b * a.H_q + g * G + e) * S_pad + j) * D + 4 * c4;
+        sk += *reinterpret_cast<const f32x4 *>(a.part_dk + off);
+        sv += *reinterpret_cast<const f32x4 *>(a.part_dv + off);
+    }
+    const size_t o = (((size_t)b * a.S + j) * a.H_kv + g) * D + 4 * c4;
+    *reinterpret_cast<u32x2 *>(a.dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+    *reinterpret_cast<u32x2 *>(a.dv + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+}
+
+}  // namespace
+
+size_t prefill_bwd_workspace_bytes(int B, int S, int H_q) {
+    const size_t n_t = (size_t)(S + kStatRows - 1) / kStatRows;
+    const size_t S_pad = (size_t)(S + kKBlk - 1) / kKBlk * kKBlk;
+    const size_t stats = (size_t)B * H_q * n_t * kStatFloats * sizeof(float);
+    const size_t part = (size_t)B * H_q * S_pad * D * sizeof(float);
+    return ((stats + 255) & ~size_t(255)) + 2 * part;
+}
+
+hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream) {
+    if (a.d != D) return hipErrorInvalidValue;
+    const int n_t = (a.S + kStatRows - 1) / kStatRows;
+    const int n_qb = (a.S + kQBr - 1) / kQBr;
+    const int n_kb = (a.S + kKBlk - 1) / kKBlk;
+    const int S_pad = n_kb * kKBlk;
+    char *base = static_cast<char *>(ws);
+    const size_t stats = (size_t)a.B * a.H_q * n_t * kStatFloats * sizeof(float);
+    a.stats = reinterpret_cast<float *>(base);
+    a.part_dk = reinterpret_cast<float *>(base + ((stats + 255) & ~size_t(255)));
+    a.part_dv = a.part_dk + (size_t)a.B * a.H_q * S_pad * D;
+
+    const long prep_rows = (long)a.B * a.H_q * n_t * kStatRows;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((prep_rows + 15) / 16)), dim3(256), 0,
+                       stream, a, n_t);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((long)n_qb * a.B * a.H_q)), dim3(kThreads),
+                       0, stream, a, n_qb, n_t);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((long)n_kb * a.B * a.H_q)),
+                       dim3(kThreads), 0, stream, a, n_kb, n_t, S_pad);
+    const long red = (long)a.B * a.S * a.H_kv * (D / 4);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((red + 255) / 256)), dim3(256), 0,
+                       stream, a, S_pad);
+    return hipGetLastError();
+}
+
+}  // namespace gqa

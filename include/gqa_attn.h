@@ -297,6 +297,42 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
                            float *lse, int B, int T_q, int q_start, int S_kv, int H_q, int H_kv,
                            int d, float softmax_scale, void *stream);
 
+/*
+ * gqa_prefill_bwd_workspace_bytes -- device workspace (bytes, 256-byte aligned
+ * start required) of gqa_attn_prefill_causal_bwd for these sizes, or 0 if the
+ * sizes are invalid.  It holds each row's statistics and the fp32 shares of dK
+ * and dV of every query head: about 2 * B * H_q * S * d * 4 bytes.
+ */
+size_t gqa_prefill_bwd_workspace_bytes(int B, int S, int H_q, int H_kv, int d);
+
+/*
+ * gqa_attn_prefill_causal_bwd -- backward of gqa_attn_prefill_causal: given the
+ * forward's inputs, its output O and LSE, and the gradient dO of the output,
+ * writes the gradients of q, k and v (V07, section 6.1):
+ *   P_ij = exp(tau q_i.k_j - LSE_i) (j <= i),  dP_ij = dO_i . v_j,
+ *   D_i = dO_i . O_i (section 6.2),  dS_ij = P_ij (dP_ij - D_i),
+ *   dQ_i = tau sum_j dS_ij k_j,  dK_j = tau sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i,
+ * with dK and dV of a KV head summed over its G query heads (section 14).  P is
+ * formed again from LSE, never stored (section 6.3).  dQ is accumulated with the
+ * query block outer and dK, dV with the key block outer, so no atomics are used
+ * (section 8; section 6.5); dK and dV add the query heads' fp32 shares in a fixed
+ * order, so results are bitwise reproducible.
+ *
+ *   q, o, d_o  [B, S, H_q, d]  bf16, device, read-only (o: the forward's output)
+ *   k, v       [B, S, H_kv, d] bf16, device, read-only
+ *   lse        [B, H_q, S]     fp32, device, read-only (the forward's LSE)
+ *   dq         [B, S, H_q, d]  bf16, device, written (RNE from fp32)
+ *   dk, dv     [B, S, H_kv, d] bf16, device, written (RNE from fp32)
+ *   workspace  gqa_prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d) bytes, device,
+ *              256-byte aligned; scratch, contents on entry ignored
+ *
+ * Supported: d = 128.
+ */
+int gqa_attn_prefill_causal_bwd(const void *q, const void *k, const void *v, const void *o,
+                                const float *lse, const void *d_o, void *dq, void *dk, void *dv,
+                                int B, int S, int H_q, int H_kv, int d, float softmax_scale,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,8 +60,9 @@ def _bind(lib):
     lib.oracle_decode_partial.restype = ci
     lib.oracle_merge_states.argtypes = [f64p, f64p, f64p, cl, ci, ci, f64p, f64p]
     lib.oracle_merge_states.restype = ci
-    lib.oracle_prefill_causal_bwd_rows.argtypes = [u16p, u16p, u16p, u16p, f64p, f64p, f64p,
-                                                   ci, ci, ci, ci, ci, cd, i32p, cl, ci]
+    lib.oracle_prefill_causal_bwd_rows.argtypes = [u16p, u16p, u16p, u16p, ctypes.c_void_p, f64p,
+                                                   f64p, f64p, ci, ci, ci, ci, ci, cd, i32p, cl,
+                                                   ci]
     lib.oracle_prefill_causal_bwd_rows.restype = ci
     lib.oracle_prefill_causal_bwd_keys.argtypes = [u16p, u16p, u16p, u16p, f64p, f64p, f64p, f64p,
                                                    ci, ci, ci, ci, ci, cd, i32p, cl, ci]
@@ -263,10 +264,12 @@ def merge_states(m, l, o, lib=None):
     return o_out, lse
 
 
-def prefill_causal_bwd_rows(q, k, v, do, rows, tau=None, nthreads=0, lib=None):
+def prefill_causal_bwd_rows(q, k, v, do, rows, D=None, tau=None, nthreads=0, lib=None):
     """Backward of causal prefill, query side, on selected rows (b, h, i): the gradient
     dQ_i = tau sum_j P_ij (dP_ij - D_i) k_j with dP_ij = dO_i . v_j and D_i = sum_j P_ij dP_ij
-    ("Attention Kernel lineage" (V07), section 6.1).
+    ("Attention Kernel lineage" (V07), section 6.1).  ``D`` [n] (optional) replaces the
+    exact D_i: the method forms D_i = dO_i . O_i from the stored forward output (section
+    6.2), so with a rounded O it differs slightly from the exact value.
 
     q, do [B, S, H_q, d]; k, v [B, S, H_kv, d] (uint16 bf16 bits); rows int [n, 3].
     Returns (dq [n, d], lse [n], D [n]) in float64.
@@ -279,8 +282,11 @@ def prefill_causal_bwd_rows(q, k, v, do, rows, tau=None, nthreads=0, lib=None):
     n = rows.shape[0]
     dq = np.zeros((n, d), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
+    D_in = None if D is None else np.ascontiguousarray(D, dtype=np.float64).reshape(n)
     D = np.zeros(n, dtype=np.float64)
-    rc = lib.oracle_prefill_causal_bwd_rows(_u16(q), _u16(k), _u16(v), _u16(do), dq, lse, D,
+    rc = lib.oracle_prefill_causal_bwd_rows(_u16(q), _u16(k), _u16(v), _u16(do),
+                                            None if D_in is None else
+                                            D_in.ctypes.data_as(ctypes.c_void_p), dq, lse, D,
                                             B, S, H_q, H_kv, d, tau, rows, n,
                                             nthreads or default_threads())
     if rc != 0:
@@ -315,17 +321,21 @@ def prefill_causal_bwd_keys(q, k, v, do, lse, D, keys, tau=None, nthreads=0, lib
     return dk, dv
 
 
-def prefill_causal_bwd(q, k, v, do, tau=None, nthreads=0, lib=None):
+def prefill_causal_bwd(q, k, v, do, o=None, tau=None, nthreads=0, lib=None):
     """Backward of causal prefill on every row and key.
 
-    Returns (dq [B, S, H_q, d], dk [B, S, H_kv, d], dv [B, S, H_kv, d], lse [B, H_q, S],
-    D [B, H_q, S]) in float64.
+    ``o`` [B, S, H_q, d] (optional, uint16 bf16 bits): a stored forward output; D_i is then
+    dO_i . O_i from it (V07 section 6.2, as the method forms D) instead of the exact row-wise
+    dot of P and dP.  Returns (dq [B, S, H_q, d], dk [B, S, H_kv, d], dv [B, S, H_kv, d],
+    lse [B, H_q, S], D [B, H_q, S]) in float64.
     """
     B, S, H_q, d = q.shape
     H_kv = k.shape[2]
     b, h, i = np.meshgrid(np.arange(B), np.arange(H_q), np.arange(S), indexing="ij")
     rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
-    dq, lse, D = prefill_causal_bwd_rows(q, k, v, do, rows, tau=tau, nthreads=nthreads, lib=lib)
+    D_in = None if o is None else stored_output_D(o, do).reshape(-1)   # rows in (b, h, i) order
+    dq, lse, D = prefill_causal_bwd_rows(q, k, v, do, rows, D=D_in, tau=tau, nthreads=nthreads,
+                                         lib=lib)
     lse = lse.reshape(B, H_q, S)
     D = D.reshape(B, H_q, S)
     b, g, j = np.meshgrid(np.arange(B), np.arange(H_kv), np.arange(S), indexing="ij")
@@ -336,3 +346,16 @@ def prefill_causal_bwd(q, k, v, do, tau=None, nthreads=0, lib=None):
     dk = dk.reshape(B, H_kv, S, d).transpose(0, 2, 1, 3).copy()
     dv = dv.reshape(B, H_kv, S, d).transpose(0, 2, 1, 3).copy()
     return dq, dk, dv, lse, D
+
+
+def stored_output_D(o, do):
+    """D [B, H_q, S] = dO_i . O_i of a stored bf16 output (V07 section 6.2), in float64
+    (products of bf16 values are exact in float64)."""
+    o64 = _f32_of_bits(o).astype(np.float64)
+    do64 = _f32_of_bits(do).astype(np.float64)
+    return np.einsum("bshd,bshd->bhs", o64, do64)
+
+
+def _f32_of_bits(bits):
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32)

@@ -351,6 +351,7 @@ int oracle_merge_states(const double *m, const double *l, const double *o, long 
 struct bwd_rows_ctx {
     const uint16_t *q, *k, *v, *dout;
     const int32_t *rows;
+    const double *D_in;
     double *dq, *lse, *D;
     int B, S, H_q, H_kv, d;
     double tau;
@@ -393,6 +394,7 @@ static void bwd_row(void *p, long r, double *s, double *qd)
     for (int j = 0; j < n; ++j) s[j] = exp(s[j] - m) / l;   /* s now holds P_i */
     double D = 0.0;
     for (int j = 0; j < n; ++j) D += s[j] * dp[j];
+    if (c->D_in) D = c->D_in[r];   /* D_i = dO_i . O_i of a stored output (section 6.2) */
     double *dq = c->dq + (size_t)r * d;
     for (int x = 0; x < d; ++x) dq[x] = 0.0;
     for (int j = 0; j < n; ++j) {
@@ -405,18 +407,22 @@ static void bwd_row(void *p, long r, double *s, double *qd)
     c->D[r] = D;
 }
 
-/* Phase 1 on selected rows (b, h, i): dq [nrows, d], lse [nrows], D [nrows]. */
+/* Phase 1 on selected rows (b, h, i): dq [nrows, d], lse [nrows], D [nrows].
+ * D_in [nrows] or NULL: when given, dS uses D_in[r] in place of the exact row-wise dot --
+ * the D_i = dO_i . O_i of section 6.2 taken from a stored (rounded) forward output O,
+ * as the method computes it -- and D[r] returns D_in[r]. */
 int oracle_prefill_causal_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                   const uint16_t *dout, double *dq, double *lse, double *D,
-                                   int B, int S, int H_q, int H_kv, int d, double tau,
-                                   const int32_t *rows, long nrows, int nthreads)
+                                   const uint16_t *dout, const double *D_in, double *dq,
+                                   double *lse, double *D, int B, int S, int H_q, int H_kv,
+                                   int d, double tau, const int32_t *rows, long nrows,
+                                   int nthreads)
 {
     if (H_kv <= 0 || H_q % H_kv != 0) return -1;
     for (long r = 0; r < nrows; ++r) {
         int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
         if (b < 0 || b >= B || h < 0 || h >= H_q || i < 0 || i >= S) return -2;
     }
-    struct bwd_rows_ctx c = {q, k, v, dout, rows, dq, lse, D, B, S, H_q, H_kv, d, tau};
+    struct bwd_rows_ctx c = {q, k, v, dout, rows, D_in, dq, lse, D, B, S, H_q, H_kv, d, tau};
     return run_rows(bwd_row, &c, nrows, nthreads, 2 * S + d, d);
 }
 

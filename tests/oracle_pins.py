@@ -595,4 +595,28 @@ def pin_bwd_row_and_key_subsets(lib):
     _rel_close(lse, lse_f, rtol=1e-14, atol=1e-14)
 
 
+def pin_bwd_stored_output_D(lib):
+    """D taken from the caller: the exact D reproduces the exact gradient, and D shifted by
+    delta_i moves dQ_i by -tau delta_i sum_j P_ij k_j -- attention with K as the values --
+    while dK and dV follow the same formula (dV does not depend on D)."""
+    p = prefill_bwd_inputs(1, 30, 4, 2, 16, seed=77)
+    B, S, H_q, d = p["q"].shape
+    tau = 0.3
+    rows = np.stack(np.meshgrid([0], np.arange(H_q), np.arange(S), indexing="ij"),
+                    axis=-1).reshape(-1, 3).astype(np.int32)
+    dq0, lse, D0 = oracle.prefill_causal_bwd_rows(p["q"], p["k"], p["v"], p["do"], rows, tau=tau,
+                                                  nthreads=2, lib=lib)
+    dq1, _, D1 = oracle.prefill_causal_bwd_rows(p["q"], p["k"], p["v"], p["do"], rows, D=D0,
+                                                tau=tau, nthreads=2, lib=lib)
+    assert np.array_equal(D1, D0)
+    _rel_close(dq1, dq0, rtol=1e-14, atol=1e-15)
+    delta = np.linspace(-1.5, 2.0, rows.shape[0])
+    dq2, _, D2 = oracle.prefill_causal_bwd_rows(p["q"], p["k"], p["v"], p["do"], rows,
+                                                D=D0 + delta, tau=tau, nthreads=2, lib=lib)
+    assert np.array_equal(D2, D0 + delta)
+    ok, _ = oracle.prefill_causal(p["q"], p["k"], p["k"], tau=tau, lib=lib)   # sum_j P_ij k_j
+    ok = ok[0].transpose(1, 0, 2).reshape(-1, d)                              # rows (h, i)
+    _rel_close(dq2 - dq0, -tau * delta[:, None] * ok, rtol=1e-9, atol=1e-12)
+
+
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -58,3 +58,50 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     assert rel_l2 <= O_REL_L2, f"{what}: rel-L2 {rel_l2} > {O_REL_L2}; stats {stats}"
     assert lse_err <= LSE_MAX_ABS, f"{what}: LSE error {lse_err} > {LSE_MAX_ABS}; stats {stats}"
     return stats
+
+
+# Gradients of the causal-prefill backward (bf16 outputs).  Each element is a sum of
+# products in which one bf16 operand was rounded on the GPU (P or dS, relative error
+# <= 2^-8 each), D comes from the bf16-rounded forward output, and the result is rounded
+# to bf16 (<= 2^-8 relative).  The products have mixed signs (the rows of dS sum to zero),
+# so an element's error scales with the magnitude of its row's terms, not with the element
+# itself: a query row that sees few keys has large dS terms and a small, cancelled sum.
+# The bar per tensor, with rows the last axis (one query or key vector):
+#   every element |g - g_ref| <= GRAD_REL |g_ref| + GRAD_ROW rms(row of g_ref)
+#                                + GRAD_TENSOR rms(g_ref),
+#   ||g - g_ref||_2 / ||g_ref||_2 <= GRAD_REL_L2 (twice the forward's O bound: two
+#   rounded operands in the chain instead of one).
+# The tensor term and GRAD_ABS cover rows whose exact gradient is zero (dQ of query row 0:
+# its only key gives dS = dP - D = 0, which the GPU forms as the difference of two fp32
+# dot products of d = 128 terms summed in different orders; the residue, about
+# 2^-24 |dO| |v| ~ 1e-6 before the factor tau |k|, stays far below 1e-5).
+GRAD_REL = 2.0 ** -6
+GRAD_ROW = 2.0 ** -4
+GRAD_TENSOR = 2.0 ** -8
+GRAD_ABS = 1e-5
+GRAD_REL_L2 = 1e-2
+
+
+def check_grad(g_gpu, g_ref, what=""):
+    """Assert the gradient bar above; returns error statistics."""
+    g = np.asarray(g_gpu, dtype=np.float64)
+    ref = np.asarray(g_ref, dtype=np.float64)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    rms_row = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+    err = np.abs(g - ref)
+    bound = GRAD_REL * np.abs(ref) + GRAD_ROW * rms_row + GRAD_TENSOR * rms + GRAD_ABS
+    denom = np.linalg.norm(ref)
+    rel_l2 = float(np.linalg.norm(g - ref) / denom) if denom > 0 else 0.0
+    stats = {"max_abs": float(err.max()) if err.size else 0.0, "rms_ref": rms,
+             "max_err_over_bound": float((err / bound).max()) if err.size else 0.0,
+             "rel_l2": rel_l2, "n": int(err.size)}
+    bad = err > bound
+    if np.any(bad):
+        idx = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond the bound; worst at {idx}: "
+                             f"gpu {g[idx]!r} ref {ref[idx]!r} row rms "
+                             f"{float(rms_row[idx[:-1]][0])!r}; stats {stats}")
+    assert rel_l2 <= GRAD_REL_L2, f"{what}: rel-L2 {rel_l2} > {GRAD_REL_L2}; stats {stats}"
+    return stats

@@ -58,6 +58,7 @@ MUTANTS = {
     "bwd_keys_lse_of_key_row": ("double pij = exp(c->tau * dot - lse[i]);",
                                 "double pij = exp(c->tau * dot - lse[j]);"),
     "bwd_keys_D_of_key_row": ("double ds = pij * (dpij - D[i]);", "double ds = pij * (dpij - D[j]);"),
+    "bwd_stored_D_ignored": ("    if (c->D_in) D = c->D_in[r];", ""),
     "q_widening_offset": ("for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[c]);",
                           "for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[(c + 1) % d]);"),
 }
