@@ -137,7 +137,8 @@ def upload_paged(p):
 
 
 def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
-    """Paged decode, batched ragged decode and chunked prefill, outside the timed step."""
+    """Paged, batched ragged and multi-token decode, long and chunked prefill, and the
+    prefill backward, outside the timed step."""
     res = {}
     page = 16
 
@@ -287,6 +288,29 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
         "workload": f"Llama3-70B chunked prefill: T_q={T} rows at q_start={q_start}, "
                     f"S_kv={pc.S}", "flop": flop, "ms": round(ms, 4), "tflops": round(tf, 1),
         "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    # backward of the causal prefill at the Llama workload (S = 8192): the forward's O and
+    # LSE, a random output gradient, the four launches of one backward call per step
+    do_p = torch.randn(q_p.shape, device="cuda", generator=torch.Generator(
+        device="cuda").manual_seed(pc.seed + 1)).to(torch.bfloat16)
+    o_f, lse_f = g.prefill_causal(q_p, k_p, v_p)
+    ws_b = g.prefill_bwd_workspace(pc.B, pc.S, pc.H_q, pc.H_kv, pc.d)
+    grads = (torch.empty_like(q_p), torch.empty_like(k_p), torch.empty_like(v_p))
+
+    def bwd_call(i):
+        g.prefill_causal_bwd(q_p, k_p, v_p, o_f, lse_f, do_p, workspace=ws_b, out=grads)
+
+    bwd_call(0)
+    n_bwd = max(2, K // 4)
+    ms = graph_ms(bwd_call, n_bwd)
+    flop = acc.prefill_causal_bwd_flop(pc.B, pc.S, pc.H_q, pc.d)
+    tf = flop / (ms * 1e-3) / 1e12
+    res["prefill_bwd"] = {
+        "workload": f"Llama3-70B causal prefill backward B={pc.B} S={pc.S} (dQ, dK, dV from O, "
+                    f"LSE and dO; five products counted)",
+        "calls": n_bwd, "flop": flop, "ms": round(ms, 4), "tflops": round(tf, 1),
+        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+        "workspace_mib": round(ws_b.numel() / 2 ** 20, 1)}
+    del do_p, o_f, lse_f, ws_b, grads
     torch.cuda.synchronize()
     return res
 

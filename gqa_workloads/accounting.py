@@ -8,6 +8,9 @@ the method must touch, not what a kernel happens to move.
 * Attention FLOP: 4 * N^2 * d per head (two N x N x d products, 2 FLOP per
   multiply-add) -- same page, section 4 (FlashAttention keeps the FLOP of the
   naive form).  Under a causal mask half of the square is kept: 4*S^2*d*H_q/2.
+* Backward FLOP: the gradient formulas (same page, section 6.1) need four N x N x d
+  products (dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q) and P again, which is
+  formed from Q K^T and the row's LSE (section 6.3): five products, 2.5x the forward.
 * Causal tile keep ratio 1/2 + B_c/(2N) -- same page, section 12.
 * Score-matrix storage N^2 * sizeof(dtype) per head -- same page, section 1.
 """
@@ -31,6 +34,12 @@ def decode_flop(seqlens, H_q: int, d: int) -> int:
 def prefill_causal_flop(B: int, S: int, H_q: int, d: int) -> float:
     """Causal prefill FLOP as the workload metric counts it: 4*S^2*d*H_q/2 per sequence."""
     return B * 4.0 * S * S * d * H_q / 2.0
+
+
+def prefill_causal_bwd_flop(B: int, S: int, H_q: int, d: int) -> float:
+    """Backward of causal prefill: five S x S x d products per head under the causal mask,
+    5*S^2*d*H_q per sequence (2.5x ``prefill_causal_flop``)."""
+    return B * 5.0 * 2.0 * S * S * d * H_q / 2.0
 
 
 def prefill_chunk_flop(B: int, T: int, q_start: int, H_q: int, d: int) -> float:

@@ -62,3 +62,9 @@ def test_causal_tile_count_rectangular():
     # B_r = 128 rows, B_c = 64 keys: q-block r keeps keys up to its last row
     assert acc.causal_tiles_kept(256, 128, 64) == 2 + 4
     assert acc.causal_tiles_kept(200, 128, 64) == 2 + 4   # ragged last block: rows 128..199
+
+
+def test_backward_flop_is_five_products():
+    """Five causal S x S x d products per head: 2.5x the forward (two products)."""
+    assert acc.prefill_causal_bwd_flop(1, 8192, 64, 128) == 2.5 * acc.prefill_causal_flop(1, 8192, 64, 128)
+    assert acc.prefill_causal_bwd_flop(2, 10, 3, 4) == 2 * 5 * 10 * 10 * 4 * 3
