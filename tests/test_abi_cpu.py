@@ -196,6 +196,38 @@ def test_prefill_chunk_rejects_before_launch(lib, kw, code):
     assert lib.gqa_last_error().decode() != ""
 
 
+def test_prefill_bwd_workspace_size(lib):
+    """Statistics [B, H_q, ceil(S/64), 128] fp32 (256-byte aligned), then two fp32 shares
+    [B, H_q, S rounded up to 256, d]; 0 for invalid sizes."""
+    B, S, H_q, H_kv, d = 2, 300, 8, 2, 128
+    stats = B * H_q * 5 * 128 * 4
+    part = B * H_q * 512 * d * 4
+    assert lib.gqa_prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d) == \
+        ((stats + 255) // 256) * 256 + 2 * part
+    for bad in ((0, S, H_q, H_kv, d), (B, 0, H_q, H_kv, d), (B, S, H_q, 3, d), (B, S, H_q, H_kv, 64)):
+        assert lib.gqa_prefill_bwd_workspace_bytes(*bad) == 0
+
+
+BWD_WS = 1 << 30
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(dk=None), NULLP), (dict(lse=None), NULLP), (dict(do=MIS), ALIGN),
+    (dict(lse=ctypes.c_void_p(0x10002)), ALIGN), (dict(dv=MIS), ALIGN), (dict(H_kv=3), SHAPE),
+    (dict(S=0), SHAPE), (dict(B=0), SHAPE), (dict(d=64), UNSUP), (dict(scale=float("nan")), SCALE),
+    (dict(ws=None), WS), (dict(ws=ctypes.c_void_p(0x10010)), WS), (dict(ws_bytes=4096), WS),
+])
+def test_prefill_bwd_rejects_before_launch(lib, kw, code):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, S=256, H_q=8, H_kv=2, d=128,
+             scale=0.088, ws=A, ws_bytes=BWD_WS)
+    a.update(kw)
+    assert lib.gqa_attn_prefill_causal_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"],
+                                           a["dq"], a["dk"], a["dv"], a["B"], a["S"], a["H_q"],
+                                           a["H_kv"], a["d"], a["scale"], a["ws"], a["ws_bytes"],
+                                           None) == code
+    assert lib.gqa_last_error().decode() != ""
+
+
 def test_binding_raises_with_detail():
     with pytest.raises(g.GQAError) as ei:
         g.decode_plan(1, 64, 7, 128, 1024, 0)
