@@ -11,8 +11,9 @@ passages they follow.
 
 Functions: decode, paged decode, multi-token decode, whole-prompt and chunked causal
 prefill (all rows or selected rows), the partial state and merge of split-KV decode,
-and the backward of whole-prompt causal prefill (dQ per query row, dK and dV per key row
-of a KV head, or all of them).
+the backward of whole-prompt causal prefill (dQ per query row, dK and dV per key row of a
+KV head, or all of them), and the FP8 (E4M3) paged KV cache: the format, per-token
+quantisation into pages, and decode over the dequantised pages.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, invariants, special cases and a brute-force check built on
@@ -67,6 +68,16 @@ def _bind(lib):
     lib.oracle_prefill_causal_bwd_keys.argtypes = [u16p, u16p, u16p, u16p, f64p, f64p, f64p, f64p,
                                                    ci, ci, ci, ci, ci, cd, i32p, cl, ci]
     lib.oracle_prefill_causal_bwd_keys.restype = ci
+    lib.oracle_e4m3_value.argtypes = [ci]
+    lib.oracle_e4m3_value.restype = cd
+    lib.oracle_e4m3_encode.argtypes = [cd]
+    lib.oracle_e4m3_encode.restype = ci
+    lib.oracle_e4m3_scale_exponent.argtypes = [cd]
+    lib.oracle_e4m3_scale_exponent.restype = ci
+    lib.oracle_quantize_fp8_rows.argtypes = [u16p, cl, ci,
+                                             np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS"),
+                                             np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")]
+    lib.oracle_quantize_fp8_rows.restype = None
     return lib
 
 
@@ -359,3 +370,90 @@ def stored_output_D(o, do):
 def _f32_of_bits(bits):
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
         np.float32)
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 KV cache ("Attention Kernel lineage" (V07), section 17.7): each page of a pool holds
+# its page_size token rows of E4M3 codes ([page_size][H_kv][d] bytes) followed by the
+# page_size per-token fp32 scales.  The arithmetic (E4M3 values, encoding, the scale of a
+# row) is in oracle.c; the functions below only lay rows out in pages.
+
+def e4m3_table(lib=None):
+    """The value of every E4M3 code (float64 [256]; NaN for 0x7F and 0xFF)."""
+    lib = lib or load()
+    return np.array([lib.oracle_e4m3_value(c) for c in range(256)])
+
+
+def quantize_fp8_rows(x, lib=None):
+    """Quantise rows of bf16 values (uint16 bits, last axis = one row): returns (codes
+    uint8, same shape; scales float32, one per row), each row with one power-of-two scale."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    width = x.shape[-1]
+    rows = x.reshape(-1, width)
+    codes = np.zeros(rows.shape, dtype=np.uint8)
+    scales = np.zeros(rows.shape[0], dtype=np.float32)
+    lib.oracle_quantize_fp8_rows(rows, rows.shape[0], width, codes, scales)
+    return codes.reshape(x.shape), scales.reshape(x.shape[:-1])
+
+
+def fp8_page_bytes(page_size, H_kv, d):
+    """Bytes of one FP8 page: the codes of its rows, then one fp32 scale per row."""
+    return page_size * H_kv * d + 4 * page_size
+
+
+def quantize_to_pages(x, seqlens, block_table, page_size, num_pages, fill=0, lib=None):
+    """The FP8 pool of a cache x [B, S_max, H_kv, d] (bf16 bits): token t < seqlens[b] of
+    sequence b is quantised as one row (its H_kv * d values) into row t % page_size of page
+    block_table[b, t // page_size] (V07 section 16, logical token to page).  Bytes of
+    slots no live token maps to keep ``fill``.  Returns uint8 [num_pages, page bytes]."""
+    B, S_max, H_kv, d = x.shape
+    pb = fp8_page_bytes(page_size, H_kv, d)
+    pool = np.full((num_pages, pb), fill, dtype=np.uint8)
+    codes, scales = quantize_fp8_rows(x.reshape(B, S_max, H_kv * d), lib=lib)
+    data = page_size * H_kv * d
+    for b in range(B):
+        for t in range(int(seqlens[b])):
+            pg, r = int(block_table[b, t // page_size]), t % page_size
+            pool[pg, r * H_kv * d:(r + 1) * H_kv * d] = codes[b, t]
+            pool[pg, data + 4 * r:data + 4 * r + 4] = np.frombuffer(scales[b, t].tobytes(), np.uint8)
+    return pool
+
+
+def dequantize_pages(pool, page_size, H_kv, d, lib=None):
+    """Every slot of an FP8 pool as bf16 bits [num_pages, page_size, H_kv, d]: code value
+    times its row's scale.  With power-of-two scales the product is exactly a bfloat16;
+    anything else raises."""
+    table = e4m3_table(lib)
+    n = pool.shape[0]
+    data = page_size * H_kv * d
+    codes = pool[:, :data].reshape(n, page_size, H_kv, d)
+    scales = pool[:, data:data + 4 * page_size].copy().view(np.float32).reshape(n, page_size)
+    vals = table[codes] * scales.astype(np.float64)[:, :, None, None]
+    if np.isnan(vals).any():
+        raise ValueError("NaN code in the pool")
+    with np.errstate(over="ignore"):      # (an overflow fails the exactness check below)
+        f32 = vals.astype(np.float32)
+    bits = (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    back = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if not np.array_equal(back, vals):
+        raise ValueError("a dequantised value is not exactly a bfloat16")
+    return bits
+
+
+def decode_paged_fp8(q, k_pool, v_pool, block_table, seqlens, page_size, tau=None, nthreads=0,
+                     lib=None):
+    """Decode (one or T_q tokens per sequence) over FP8 pools: the pools dequantised
+    (exactly, as bf16) and then the paged decode definition."""
+    H_kv = None
+    d = q.shape[-1]
+    data_plus = k_pool.shape[1]
+    H_kv = (data_plus - 4 * page_size) // (page_size * d)
+    kb = dequantize_pages(k_pool, page_size, H_kv, d, lib=lib)
+    vb = dequantize_pages(v_pool, page_size, H_kv, d, lib=lib)
+    if q.ndim == 4:
+        k = gather_pages(kb, block_table, seqlens, page_size)
+        v = gather_pages(vb, block_table, seqlens, page_size)
+        return decode_tokens(q, k, v, seqlens, tau=tau, nthreads=nthreads, lib=lib)
+    return decode_paged(q, kb, vb, block_table, seqlens, page_size, tau=tau, nthreads=nthreads,
+                        lib=lib)

@@ -484,3 +484,76 @@ int oracle_prefill_causal_bwd_keys(const uint16_t *q, const uint16_t *k, const u
     struct bwd_keys_ctx c = {q, k, v, dout, lse, D, keys, dk, dv, B, S, H_q, H_kv, d, tau};
     return run_rows(bwd_key, &c, nkeys, nthreads, d, d);
 }
+
+/* ------------------------------------------------------------------------- */
+/* FP8 KV cache ("Attention Kernel lineage" (V07), section 17.7: a per-token scale kept
+ * with each page, the page's B_p scalars appended after its rows, and dequantisation
+ * fused into the load; section 9.5: E4M3 values with fp32 accumulation).
+ *
+ * E4M3 as the OCP 8-bit floating-point specification defines it (its "E4M3" encoding,
+ * without infinities): bit 7 is the sign, bits 6..3 a biased exponent (bias 7), bits
+ * 2..0 the mantissa.  Exponent field 0 holds zero and the subnormals m * 2^-9; field e > 0
+ * holds (1 + m/8) * 2^(e - 7); 0x7F and 0xFF are NaN, so the largest finite value is
+ * 0x7E = 1.75 * 2^8 = 448.
+ *
+ * A token's row (its H_kv * d values of one pool) is quantised with one scale 2^e, e the
+ * smallest integer with max |x| <= 448 * 2^e (clamped to [-126, 127]; an all-zero row
+ * takes -126), and codes the E4M3 values nearest to x * 2^-e, ties to the even code.
+ * The scale is a power of two so that x * 2^-e is exact and code * 2^e is exactly a
+ * bfloat16 (4 significant bits), which the tests use. */
+
+double oracle_e4m3_value(int code)
+{
+    code &= 0xFF;
+    int sign = code >> 7, ex = (code >> 3) & 15, man = code & 7;
+    if (ex == 15 && man == 7) return NAN;
+    double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);
+    return sign ? -mag : mag;
+}
+
+/* The code of the finite E4M3 value nearest to y (ties: the code with an even mantissa);
+ * |y| beyond 448 gives +-448, NaN gives 0x7F.  The non-negative finite codes 0x00..0x7E
+ * have ascending values, so the two neighbours of |y| are found by bisection. */
+int oracle_e4m3_encode(double y)
+{
+    if (y != y) return 0x7F;
+    int sign = signbit(y) ? 0x80 : 0;
+    double a = fabs(y);
+    if (a >= 448.0) return sign | 0x7E;
+    int lo = 0, hi = 0x7E;                  /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (oracle_e4m3_value(mid) <= a) lo = mid;
+        else hi = mid;
+    }
+    double dlo = a - oracle_e4m3_value(lo), dhi = oracle_e4m3_value(hi) - a;
+    int c = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1) == 0 ? lo : hi);
+    return sign | c;
+}
+
+/* The scale exponent of a row whose largest magnitude is amax (see above). */
+int oracle_e4m3_scale_exponent(double amax)
+{
+    if (!(amax > 0.0)) return -126;
+    int e = -126;
+    while (e < 127 && amax > ldexp(448.0, e)) ++e;
+    return e;
+}
+
+/* Quantise nrows rows of `width` bf16 values: codes [nrows][width], scales [nrows]. */
+void oracle_quantize_fp8_rows(const uint16_t *x, long nrows, int width, uint8_t *codes,
+                              float *scales)
+{
+    for (long r = 0; r < nrows; ++r) {
+        const uint16_t *row = x + (size_t)r * width;
+        double amax = 0.0;
+        for (int i = 0; i < width; ++i) {
+            double a = fabs(bf16_to_double(row[i]));
+            if (a > amax) amax = a;
+        }
+        int e = oracle_e4m3_scale_exponent(amax);
+        for (int i = 0; i < width; ++i)
+            codes[(size_t)r * width + i] = (uint8_t)oracle_e4m3_encode(ldexp(bf16_to_double(row[i]), -e));
+        scales[r] = (float)ldexp(1.0, e);
+    }
+}

@@ -619,4 +619,123 @@ def pin_bwd_stored_output_D(lib):
     _rel_close(dq2 - dq0, -tau * delta[:, None] * ok, rtol=1e-9, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# FP8 KV cache (V07 section 17.7; E4M3 as the OCP 8-bit floating-point specification
+# defines it).
+
+def pin_fp8_e4m3_values(lib):
+    """Values the E4M3 definition fixes: zero, the subnormals m * 2^-9, the smallest normal
+    2^-6, one, the largest finite 448, NaN at 0x7F and 0xFF; ascending codes give ascending
+    values (no gap, no repeat), the sign bit mirrors them, and within a binade consecutive
+    values are 2^(e-3) apart."""
+    t = oracle.e4m3_table(lib)
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5,
+            0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x40: 2.0, 0x7D: 416.0, 0x7E: 448.0,
+            0x81: -(2.0 ** -9), 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in want.items():
+        assert t[c] == v, (hex(c), t[c], v)
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isfinite(t[:0x7F]).all()
+    assert np.all(np.diff(t[:0x7F]) > 0)
+    assert np.array_equal(t[0x80:0xFF], -t[:0x7F]) and np.signbit(t[0x80])
+    for ex in range(1, 16):
+        vals = t[8 * ex:min(8 * ex + 8, 0x7F)]
+        assert np.allclose(np.diff(vals), 2.0 ** (ex - 7 - 3))
+
+
+def pin_fp8_encode_nearest_even(lib):
+    """Every finite value encodes to its own code; the midpoint of two neighbours goes to
+    the one with the even mantissa, and a value one step off the midpoint to the nearer;
+    beyond 448 saturates; NaN gives 0x7F."""
+    t = oracle.e4m3_table(lib)[:0x7F]
+    enc = lib.oracle_e4m3_encode
+    for c in range(0x7F):
+        assert enc(float(t[c])) == c and enc(float(-t[c])) == (0x80 | c), hex(c)
+    for c in range(0x7E):
+        mid = (t[c] + t[c + 1]) / 2
+        assert enc(float(mid)) == (c if c % 2 == 0 else c + 1), hex(c)
+        assert enc(float(np.nextafter(mid, 0.0))) == c and enc(float(np.nextafter(mid, 1e9))) == c + 1
+    assert enc(1e6) == 0x7E and enc(-1e6) == 0xFE and enc(float("nan")) == 0x7F
+    assert enc(2.0 ** -11) == 0 and enc(-(2.0 ** -11)) == 0x80
+
+
+def pin_fp8_quantize_rows(lib):
+    """Per-token quantisation: the scale is the smallest power of two 2^e with
+    max|x| <= 448 * 2^e; every value dequantises to within half an E4M3 step of x (relative
+    2^-4 in the normal range, 2^-10 * 2^e below it), exactly as a bfloat16; an all-zero
+    row takes 2^-126 and zero codes."""
+    rng = np.random.default_rng(81)
+    rows = rng.standard_normal((40, 96)).astype(np.float32)
+    rows *= np.exp2(rng.integers(-30, 30, size=(40, 1))).astype(np.float32)
+    rows[3] = 0.0
+    rows[4] = 0.0
+    rows[4, 17] = 3.0e5
+    x = bf16_bits_from_f32(rows)
+    codes, scales = oracle.quantize_fp8_rows(x, lib)
+    xv = _f64(x)
+    t = oracle.e4m3_table(lib)
+    for r in range(40):
+        e = np.log2(float(scales[r]))
+        assert e == int(e)
+        amax = np.abs(xv[r]).max()
+        if amax == 0:
+            assert e == -126 and np.all(codes[r] == 0)
+            continue
+        assert amax <= 448 * 2.0 ** e and amax > 448 * 2.0 ** (e - 1)
+        deq = t[codes[r]] * 2.0 ** e
+        y = np.abs(xv[r]) * 2.0 ** -e
+        half_step = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 4),
+                             2.0 ** -10) * 2.0 ** e
+        assert np.all(np.abs(deq - xv[r]) <= half_step * (1 + 1e-12))
+        assert np.array_equal(_f64(bf16_bits_from_f32(deq.astype(np.float32))), deq)
+
+
+def pin_fp8_page_layout(lib):
+    """V07 section 17.7's page: B_p token rows of codes, then the B_p per-token scales
+    appended.  A worked example, byte by byte: two sequences of 20 and 5 tokens, pages of
+    16 rows of one KV head of d = 8, tables [[2, 0], [1, -1]]; and the dequantised pool,
+    gathered in token order, equals the dequantised rows."""
+    rng = np.random.default_rng(82)
+    x = bf16_bits_from_f32(rng.standard_normal((2, 20, 1, 8)).astype(np.float32))
+    table = np.array([[2, 0], [1, -1]], dtype=np.int32)
+    lens = np.array([20, 5], dtype=np.int32)
+    pool = oracle.quantize_to_pages(x, lens, table, 16, 3, fill=0xAB, lib=lib)
+    assert pool.shape == (3, 16 * 8 + 64)
+    codes, scales = oracle.quantize_fp8_rows(x.reshape(2, 20, 8), lib)
+    for b, n in ((0, 20), (1, 5)):
+        for tok in range(n):
+            pg, r = table[b, tok // 16], tok % 16
+            assert np.array_equal(pool[pg, 8 * r:8 * r + 8], codes[b, tok])
+            assert pool[pg, 128 + 4 * r:132 + 4 * r].view(np.float32)[0] == scales[b, tok]
+    assert np.all(pool[0, 8 * 4:128] == 0xAB) and np.all(pool[1, 8 * 5:128] == 0xAB)
+    deq = oracle.dequantize_pages(np.where(pool == 0xAB, 0, pool).astype(np.uint8), 16, 1, 8, lib)
+    got = oracle.gather_pages(deq, table, lens, 16)
+    want = oracle.e4m3_table(lib)[codes] * scales[..., None].astype(np.float64)
+    assert np.array_equal(_f64(got[0, :20]).reshape(20, 8), want[0])
+    assert np.array_equal(_f64(got[1, :5]).reshape(5, 8), want[1, :5])
+
+
+def pin_fp8_decode_lossless_cache(lib):
+    """A cache whose rows are already E4M3 values times a power of two (with 448 * 2^e in
+    each row, so the quantiser picks that exponent) quantises losslessly: the decode over its
+    FP8 pages equals the decode over the bf16 cache, bit for bit."""
+    rng = np.random.default_rng(83)
+    B, S, H_kv, d, page = 2, 48, 2, 16, 16
+    t = oracle.e4m3_table(lib)
+    def cache():
+        c = rng.integers(0, 0x7F, size=(B, S, H_kv * d))
+        c |= rng.integers(0, 2, size=c.shape) << 7
+        c[:, :, 5] = 0x7E
+        e = rng.integers(-12, 4, size=(B, S, 1))
+        return bf16_bits_from_f32((t[c] * 2.0 ** e).astype(np.float32)).reshape(B, S, H_kv, d)
+    k, v = cache(), cache()
+    q = bf16_bits_from_f32(rng.standard_normal((B, 8, d)).astype(np.float32))
+    lens = np.array([48, 21], dtype=np.int32)
+    table = np.array([[4, 1, 0], [2, 3, -1]], dtype=np.int32)
+    kp = oracle.quantize_to_pages(k, lens, table, page, 5, lib=lib)
+    vp = oracle.quantize_to_pages(v, lens, table, page, 5, lib=lib)
+    o8, l8 = oracle.decode_paged_fp8(q, kp, vp, table, lens, page, nthreads=2, lib=lib)
+    o, l = oracle.decode(q, k, v, lens, nthreads=2, lib=lib)
+    assert np.array_equal(o8, o) and np.array_equal(l8, l)
+
+
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -59,6 +59,16 @@ MUTANTS = {
                                 "double pij = exp(c->tau * dot - lse[j]);"),
     "bwd_keys_D_of_key_row": ("double ds = pij * (dpij - D[i]);", "double ds = pij * (dpij - D[j]);"),
     "bwd_stored_D_ignored": ("    if (c->D_in) D = c->D_in[r];", ""),
+    "fp8_ties_to_odd": ("((lo & 1) == 0 ? lo : hi)", "((lo & 1) == 1 ? lo : hi)"),
+    "fp8_subnormal_step": ("ldexp((double)man, -9)", "ldexp((double)man, -10)"),
+    "fp8_exponent_bias_8": ("ldexp(1.0 + man / 8.0, ex - 7)", "ldexp(1.0 + man / 8.0, ex - 8)"),
+    "fp8_encode_drops_sign": ("    return sign | c;\n}", "    return c;\n}"),
+    "fp8_scale_not_minimal": ("while (e < 127 && amax > ldexp(448.0, e)) ++e;",
+                              "while (e < 127 && amax >= ldexp(448.0, e)) ++e;"),
+    "fp8_scale_one_binade_low": ("while (e < 127 && amax > ldexp(448.0, e)) ++e;",
+                                 "while (e < 127 && amax > ldexp(896.0, e)) ++e;"),
+    "fp8_quantise_without_scale": ("oracle_e4m3_encode(ldexp(bf16_to_double(row[i]), -e))",
+                                   "oracle_e4m3_encode(bf16_to_double(row[i]))"),
     "q_widening_offset": ("for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[c]);",
                           "for (int c = 0; c < d; ++c) qd[c] = bf16_to_double(q[(c + 1) % d]);"),
 }
@@ -112,3 +122,33 @@ def test_planted_gather_mistake_is_caught(kind, monkeypatch, oracle_lib):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin detects the gather mistake {kind}"
+
+
+# Planted mistakes in the FP8 page layout (Python): V07 section 17.7 appends a page's
+# per-token scales after its rows; scales written first, or rows at the wrong stride, must
+# fail a pin.
+def _pages_variant(kind):
+    real = oracle.quantize_to_pages
+
+    def quantize_to_pages(x, seqlens, block_table, page_size, num_pages, fill=0, lib=None):
+        pool = real(x, seqlens, block_table, page_size, num_pages, fill=fill, lib=lib)
+        B, S_max, H_kv, d = x.shape
+        data = page_size * H_kv * d
+        if kind == "scales_first":
+            return np.concatenate([pool[:, data:], pool[:, :data]], axis=1)
+        rows = pool[:, :data].reshape(num_pages, page_size, H_kv * d)
+        return np.concatenate([np.roll(rows, 1, axis=1).reshape(num_pages, data), pool[:, data:]],
+                              axis=1)
+    return quantize_to_pages
+
+
+@pytest.mark.parametrize("kind", ["scales_first", "row_stride"])
+def test_planted_fp8_page_mistake_is_caught(kind, monkeypatch, oracle_lib):
+    monkeypatch.setattr(oracle, "quantize_to_pages", _pages_variant(kind))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(oracle_lib)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects the FP8 page mistake {kind}"
