@@ -76,6 +76,13 @@ def load_library(path=LIBRARY):
     L.gqa_attn_prefill_causal.restype = ci
     L.gqa_attn_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, ci, ci, cf, vp]
     L.gqa_attn_prefill_chunk.restype = ci
+    L.gqa_fp8_page_bytes.argtypes = [ci, ci, ci]
+    L.gqa_fp8_page_bytes.restype = cs
+    L.gqa_kv_quantize_fp8.argtypes = [vp, i32p, i32p, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    L.gqa_kv_quantize_fp8.restype = ci
+    L.gqa_attn_decode_paged_fp8.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci,
+                                            ci, ci, ci, cf, ci, vp, cs, vp]
+    L.gqa_attn_decode_paged_fp8.restype = ci
     L.gqa_prefill_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.gqa_prefill_bwd_workspace_bytes.restype = cs
     L.gqa_attn_prefill_causal_bwd.argtypes = [vp, vp, vp, vp, f32p, vp, vp, vp, vp, ci, ci, ci, ci,
@@ -378,3 +385,61 @@ def prefill_causal_bwd(q, k, v, o, lse, d_o, softmax_scale=None, workspace=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
         B, S, H_q, H_kv, d, _scale(d, softmax_scale), _ptr(ws), ws.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+def fp8_page_bytes(page_size, H_kv, d):
+    """Bytes of one FP8 page: page_size rows of H_kv*d E4M3 codes, then page_size fp32 scales."""
+    return load_library().gqa_fp8_page_bytes(page_size, H_kv, d)
+
+
+def kv_quantize_fp8(x, block_table, seqlens=None, pool=None, num_pages=None, page_size=16):
+    """Quantise a bf16 cache x [B, S_max, H_kv, d] into the pages of an FP8 pool (uint8
+    [num_pages, page bytes]) through block_table [B, max_blocks]; returns the pool."""
+    _need(x, "x", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    B, S_max, H_kv, d = x.shape
+    pb = fp8_page_bytes(page_size, H_kv, d)
+    if pool is None:
+        if num_pages is None:
+            raise ValueError("give pool or num_pages")
+        pool = torch.zeros((num_pages, pb), dtype=torch.uint8, device=x.device)
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or pool.shape[1] != pb or not pool.is_contiguous():
+        raise ValueError(f"pool must be contiguous uint8 [num_pages, {pb}]")
+    _check(load_library().gqa_kv_quantize_fp8(
+        _ptr(x), _ptr(seqlens), _ptr(block_table), _ptr(pool), B, S_max, H_kv, d, page_size,
+        pool.shape[0], block_table.shape[1], _stream(x.device)))
+    return pool
+
+
+def decode_paged_fp8(q, k_pool, v_pool, block_table, seqlens=None, page_size=16, H_kv=None,
+                     softmax_scale=None, num_splits=0, out=None, lse=None, workspace=None):
+    """Decode over FP8 pools (uint8 [num_pages, page bytes]); q [B, H_q, d] or
+    [B, T_q, H_q, d] bf16.  H_kv is needed to read the page layout (default: H_q's KV heads
+    from the page size).  Returns (o, lse) as ``decode_paged``."""
+    _need(q, "q", torch.bfloat16, q.dim())
+    _need(block_table, "block_table", torch.int32, 2)
+    if q.dim() == 3:
+        B, H_q, d = q.shape
+        T = 1
+    else:
+        B, T, H_q, d = q.shape
+    num_pages, pb = k_pool.shape
+    if H_kv is None:
+        H_kv = (pb - 4 * page_size) // (page_size * d)
+    if fp8_page_bytes(page_size, H_kv, d) != pb or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError(f"pool shape {tuple(k_pool.shape)} is not pages of {page_size} rows "
+                         f"of {H_kv}x{d}")
+    max_blocks = block_table.shape[1]
+    S_max = max_blocks * page_size
+    if workspace is None:
+        nbytes = (decode_plan(B, H_q, H_kv, d, S_max, num_splits) if T == 1 else
+                  decode_tokens_plan(B, T, H_q, H_kv, d, S_max, num_splits))["workspace_bytes"]
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = (torch.empty((B, H_q) if T == 1 else (B, H_q, T), dtype=torch.float32, device=q.device)
+         if lse is None else lse)
+    _check(load_library().gqa_attn_decode_paged_fp8(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seqlens), _ptr(o), _ptr(l),
+        B, T, H_q, H_kv, d, page_size, num_pages, max_blocks, _scale(d, softmax_scale),
+        num_splits, _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return o, l

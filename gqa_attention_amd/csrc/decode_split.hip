@@ -57,12 +57,26 @@ struct DecodeTraits {
     static constexpr int NDT = D / 16;          // 16-wide d tiles of O^T
     static constexpr int VPITCH = D + 16;       // staged V row pitch (bf16): 16-B aligned,
                                                 // 4 consecutive rows on disjoint banks
+    // FP8 pages: rows of D one-byte codes
+    static constexpr int LPR8 = D / 16;         // lanes per V row (16 codes each)
+    static constexpr int RPI8 = 64 / LPR8;      // V rows per wave load
+    static constexpr int NVI8 = kTile / RPI8;   // V loads per lane per tile
 };
 
-template <int D>
+template <int D, bool Fp8>
 struct TileRegs {
     u32x4 k[DecodeTraits<D>::KS];
     u32x4 v[DecodeTraits<D>::NVI];
+};
+
+// FP8 pages: the lane's 8 * KS K codes (the same key row and d-slots as the bf16 tile, in
+// half the bytes), its share of the V tile's codes, and the fp32 per-token scales of the
+// lane's four keys 4*(lane/16) .. +3 for K (its scores) and for V (its P values).
+template <int D>
+struct TileRegs<D, true> {
+    u32x4 k[DecodeTraits<D>::KS / 2];
+    u32x4 v[DecodeTraits<D>::NVI8];
+    u32x4 ksc, vsc;
 };
 
 // Per-lane byte offsets of a tile's loads from the tile's first key row (loop invariant).
@@ -72,12 +86,46 @@ struct TileOffsets {
     uint32_t v[DecodeTraits<D>::NVI];         // V: row i*RPI + lane/LPR, 16 B at lane%LPR
 };
 
+template <int D>
+struct TileOffsets8 {
+    uint32_t k;                               // K codes: row lane%16, byte (lane/16) * D/4
+    uint32_t v[DecodeTraits<D>::NVI8];        // V codes: row i*RPI8 + lane/LPR8, 16 B at lane%LPR8
+};
+
+// Eight E4M3 codes (two dwords, lowest byte first) as eight bf16 values: exact, since every
+// E4M3 value is a bfloat16.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// FP8 tile: codes of 16 key rows from kt / vt (rows row_bytes apart; `bytes` of them real)
+// and the per-token scales from kst / vst (`sbytes` real); the rest reads as zeros.
+template <int D>
+__device__ __forceinline__ void load_tile8(TileRegs<D, true> &r, const uint8_t *kt,
+                                           const uint8_t *vt, const uint8_t *kst, const uint8_t *vst,
+                                           uint32_t bytes, uint32_t sbytes,
+                                           const TileOffsets8<D> &off, int grp) {
+    using T = DecodeTraits<D>;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kt, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt, bytes);
+#pragma unroll
+    for (int j = 0; j < T::KS / 2; ++j) r.k[j] = buffer_load16(rk, off.k, j * 16);
+#pragma unroll
+    for (int i = 0; i < T::NVI8; ++i) r.v[i] = buffer_load16(rv, off.v[i], 0);
+    r.ksc = buffer_load16(make_rsrc(kst, sbytes), 16u * (uint32_t)grp, 0);
+    r.vsc = buffer_load16(make_rsrc(vst, sbytes), 16u * (uint32_t)grp, 0);
+}
+
 // Load a 16-key tile of one KV head whose first key row (that head's slice of it) sits at
 // kt / vt, with the following rows kv_row elements apart.  Only the first `bytes` bytes
 // from kt / vt are read; the rest of the tile reads as zeros and costs no memory traffic,
 // so a tile that lies wholly past the end (bytes = 0) may be "loaded" unconditionally.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *kt, const uint16_t *vt,
+__device__ __forceinline__ void load_tile(TileRegs<D, false> &r, const uint16_t *kt, const uint16_t *vt,
                                           uint32_t bytes, const TileOffsets<D> &off) {
     using T = DecodeTraits<D>;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kt, bytes);
@@ -111,7 +159,7 @@ struct WaveState {
 // staged row-major in the wave's LDS area.  After it the tile's registers are free for the
 // next prefetch.
 template <int D, int CB>
-__device__ __forceinline__ void score_tile(const TileRegs<D> &r,
+__device__ __forceinline__ void score_tile(const TileRegs<D, false> &r,
                                            const bf16x8 (&qf)[CB][DecodeTraits<D>::KS],
                                            uint16_t *vs, int lane, f32x4 (&s)[CB]) {
     using T = DecodeTraits<D>;
@@ -128,12 +176,43 @@ __device__ __forceinline__ void score_tile(const TileRegs<D> &r,
     }
 }
 
+// The same from FP8 codes: K and V converted to bf16 in registers (exactly) in the order of
+// the bf16 path, V staged as bf16 rows; the scores still lack the per-token K scale.
+template <int D, int CB>
+__device__ __forceinline__ void score_tile8(const TileRegs<D, true> &r,
+                                            const bf16x8 (&qf)[CB][DecodeTraits<D>::KS],
+                                            uint16_t *vs, int lane, f32x4 (&s)[CB]) {
+    using T = DecodeTraits<D>;
+#pragma unroll
+    for (int bk = 0; bk < CB; ++bk) s[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < T::KS / 2; ++j) {
+        const bf16x8 k0 = e4m3x8_to_bf16(r.k[j][0], r.k[j][1]);
+        const bf16x8 k1 = e4m3x8_to_bf16(r.k[j][2], r.k[j][3]);
+#pragma unroll
+        for (int bk = 0; bk < CB; ++bk) s[bk] = mfma16(k0, qf[bk][2 * j], s[bk]);
+#pragma unroll
+        for (int bk = 0; bk < CB; ++bk) s[bk] = mfma16(k1, qf[bk][2 * j + 1], s[bk]);
+    }
+#pragma unroll
+    for (int i = 0; i < T::NVI8; ++i) {
+        uint16_t *dst = vs + (i * T::RPI8 + lane / T::LPR8) * T::VPITCH + (lane % T::LPR8) * 16;
+        *reinterpret_cast<bf16x8 *>(dst) = e4m3x8_to_bf16(r.v[i][0], r.v[i][1]);
+        *reinterpret_cast<bf16x8 *>(dst + 8) = e4m3x8_to_bf16(r.v[i][2], r.v[i][3]);
+    }
+}
+
 // Second half: online softmax of the tile's scores and O^T += V^T . P^T, for each block
 // of columns.  key_end[bk] is this lane's column's bound: its query sees keys below it.
-template <int D, int CB>
+// FP8 pages: ksc / vsc are the per-token scales of the lane's four keys; a score is scaled
+// by its key's K scale, and P by its key's V scale on its way into the P.V product (the row
+// sums keep the unscaled P).  With power-of-two scales both are exact, so the result equals
+// that of bf16 pages holding the dequantised values.
+template <int D, int CB, bool Fp8>
 __device__ __forceinline__ void softmax_pv(WaveState<D, CB> &st, const f32x4 (&s)[CB],
                                            const uint16_t *vs, int key0, const int (&key_end)[CB],
-                                           float scale_log2, int lane) {
+                                           float scale_log2, int lane, const float (&ksc)[4],
+                                           const float (&vsc)[4]) {
     using T = DecodeTraits<D>;
     const int row16 = lane & 15, grp = lane >> 4;
     s16x4 pf[CB];
@@ -144,7 +223,8 @@ __device__ __forceinline__ void softmax_pv(WaveState<D, CB> &st, const f32x4 (&s
         float mx = neg_inf();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float x = key0 + grp * 4 + i < key_end[bk] ? s[bk][i] * scale_log2 : neg_inf();
+            const float c = Fp8 ? scale_log2 * ksc[i] : scale_log2;
+            const float x = key0 + grp * 4 + i < key_end[bk] ? s[bk][i] * c : neg_inf();
             s2[i] = x;
             mx = fmaxf(mx, x);
         }
@@ -173,7 +253,13 @@ __device__ __forceinline__ void softmax_pv(WaveState<D, CB> &st, const f32x4 (&s
         }
         // P^T as the B operand of the 16x16x16 product: keys 4*grp + j, column lane%16
         const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-        pf[bk] = __builtin_bit_cast(s16x4, pw);
+        if constexpr (Fp8) {
+            const u32x2 pv = {pack_bf16x2(p[0] * vsc[0], p[1] * vsc[1]),
+                              pack_bf16x2(p[2] * vsc[2], p[3] * vsc[3])};
+            pf[bk] = __builtin_bit_cast(s16x4, pv);
+        } else {
+            pf[bk] = __builtin_bit_cast(s16x4, pw);
+        }
         st.lw[bk] = add_bf16_pair(pw[0], st.lw[bk]);
         st.lw[bk] = add_bf16_pair(pw[1], st.lw[bk]);
     }
@@ -242,7 +328,11 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[DecodeTraits<D>::KS], const 
 //
 // A wave folds CB blocks of 16 columns (CB = 2 when a KV head has more than 16 rows, G * T
 // > 16), so up to 32 rows share each K fragment, V^T fragment and tile load.
-template <int D, bool Paged, int CB>
+//
+// FP8 pages (Fp8, paged only): the pools are byte pools of pages of a.page_bytes bytes --
+// a.page rows of [H_kv][D] E4M3 codes, then the page's a.page fp32 per-token scales
+// (V07 section 17.7) -- read in half the bytes and dequantised in registers.
+template <int D, bool Paged, int CB, bool Fp8>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitArgs a, int n_hg) {
     using T = DecodeTraits<D>;
     // V staging during the sweep; at a state boundary (several waves per head) the
@@ -376,16 +466,22 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
 #pragma unroll
     for (int i = 0; i < T::NVI; ++i)
         toff.v[i] = (uint32_t)(((i * T::RPI + lane / T::LPR) * kv_row + (lane % T::LPR) * 8) * 2);
+    TileOffsets8<D> toff8;                     // FP8: byte offsets, rows kv_row bytes apart
+    toff8.k = (uint32_t)(row16 * kv_row + grp * (D / 4));
+#pragma unroll
+    for (int i = 0; i < T::NVI8; ++i)
+        toff8.v[i] = (uint32_t)((i * T::RPI8 + lane / T::LPR8) * kv_row + (lane % T::LPR8) * 16);
 
     // ---- issue side: the next tile this wave loads, and its sequence ----
     int it = t0 + phase;                       // flattened tile index
     int ib = cb, ilo = P(cb), ihi = P(cb + 1), ilen = L(cb, ilo, ihi);
     int issued = 0;                            // tiles issued by this wave (paged windows)
     int pw = -1;                               // paged: pool row of window tile `lane`
+    int ppg = -1, prw = 0;                     // FP8: its page and row within the page
     // Load tile `it` into r (past the partition end: zero bytes, no memory traffic).  All of
     // it is uniform; readfirstlane keeps the buffer resources in scalar registers.
-    auto issue = [&](TileRegs<D> &r) {
-        uint32_t bytes = 0;
+    auto issue = [&](TileRegs<D, Fp8> &r) {
+        uint32_t bytes = 0, nkeys = 0;
         size_t row = 0;
         if (it < t1) {
             while (it >= ihi) {                // next sequence with tiles
@@ -395,7 +491,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
                 if (ihi > ilo) ilen = L(ib, ilo, ihi);
             }
             const int k0 = (it - ilo) * kTile;
-            bytes = (uint32_t)min(ilen - k0, kTile) * (uint32_t)kv_row * 2u;
+            nkeys = (uint32_t)min(ilen - k0, kTile);
+            bytes = nkeys * (uint32_t)kv_row * 2u;
             if constexpr (!Paged) row = ((size_t)ib * a.S_max + k0) * kv_row;
         }
         if constexpr (Paged) {
@@ -416,15 +513,30 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
                 if (tl < t1) {
                     const int key = (tl - pb) * kTile;
                     const int pg = a.block_table[(size_t)bl * a.max_blocks + key / a.page];
-                    if ((unsigned)pg < (unsigned)a.num_pages) pw = pg * a.page + key % a.page;
+                    if ((unsigned)pg < (unsigned)a.num_pages) {
+                        pw = pg * a.page + key % a.page;
+                        ppg = pg;
+                        prw = key % a.page;
+                    }
                 }
             }
             const int pr = __builtin_amdgcn_readlane(pw, issued & (kWindow - 1));
             row = (size_t)max(pr, 0) * kv_row;
-            if (pr < 0) bytes = 0;             // an entry outside the pool reads as zeros
+            if (pr < 0) nkeys = bytes = 0;     // an entry outside the pool reads as zeros
+            if constexpr (Fp8) {
+                const int pgi = max(__builtin_amdgcn_readlane(ppg, issued & (kWindow - 1)), 0);
+                const int rr = __builtin_amdgcn_readlane(prw, issued & (kWindow - 1));
+                nkeys = __builtin_amdgcn_readfirstlane(nkeys);
+                const uint8_t *pk = reinterpret_cast<const uint8_t *>(a.k) + (size_t)pgi * a.page_bytes;
+                const uint8_t *pv = reinterpret_cast<const uint8_t *>(a.v) + (size_t)pgi * a.page_bytes;
+                const size_t rowb = (size_t)rr * kv_row + (size_t)hk * D;
+                const size_t sc = (size_t)a.page * kv_row + 4u * (size_t)rr;
+                load_tile8<D>(r, pk + rowb, pv + rowb, pk + sc, pv + sc, nkeys * (uint32_t)kv_row,
+                              nkeys * 4u, toff8, grp);
+            }
         }
         bytes = __builtin_amdgcn_readfirstlane(bytes);
-        load_tile<D>(r, kbase + row, vbase + row, bytes, toff);
+        if constexpr (!Fp8) load_tile<D>(r, kbase + row, vbase + row, bytes, toff);
         it += wph;
         ++issued;
     };
@@ -432,7 +544,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
     bf16x8 qf[CB][T::KS];
 #pragma unroll
     for (int bk = 0; bk < CB; ++bk) load_q<D>(qf[bk], a, cb, hk, G, colb[bk], grp);
-    TileRegs<D> ring;
+    TileRegs<D, Fp8> ring;
     __builtin_amdgcn_sched_barrier(0);
     issue(ring);
 
@@ -456,10 +568,24 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         }
         for (; tw < shi; tw += wph) {
             f32x4 sc[CB];
-            score_tile<D, CB>(ring, qf, vs, lane, sc);
+            float ksc[4] = {1.f, 1.f, 1.f, 1.f}, vsc[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (Fp8) {
+                score_tile8<D, CB>(ring, qf, vs, lane, sc);
+                // (whole-vector casts: a bit cast of one vector element reads element 0)
+                const f32x4 kf4 = __builtin_bit_cast(f32x4, ring.ksc);
+                const f32x4 vf4 = __builtin_bit_cast(f32x4, ring.vsc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ksc[i] = kf4[i];
+                    vsc[i] = vf4[i];
+                }
+            } else {
+                score_tile<D, CB>(ring, qf, vs, lane, sc);
+            }
             __builtin_amdgcn_sched_barrier(0);
             issue(ring);                       // the next tile's loads go out first
-            softmax_pv<D, CB>(st, sc, vs, (tw - slo) * kTile, key_end, a.scale_log2, lane);
+            softmax_pv<D, CB, Fp8>(st, sc, vs, (tw - slo) * kTile, key_end, a.scale_log2, lane,
+                                   ksc, vsc);
         }
         finish_state<D, CB>(st);
 
@@ -543,12 +669,19 @@ hipError_t launch_cb(const DecodeSplitArgs &a, hipStream_t stream) {
     const int GT = a.H_q / a.H_kv * a.T;
     const int n_hg = (GT + 16 * CB - 1) / (16 * CB);
     dim3 grid(a.units, (a.H_kv / a.hpw) * n_hg);
-    if (a.block_table)
-        hipLaunchKernelGGL((decode_split_kernel<D, true, CB>), grid, dim3(kWaves * 64), 0, stream,
-                           a, n_hg);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<D, false, CB>), grid, dim3(kWaves * 64), 0, stream,
-                           a, n_hg);
+    if (a.fp8) {
+        if constexpr (D == 128)
+            hipLaunchKernelGGL((decode_split_kernel<D, true, CB, true>), grid, dim3(kWaves * 64), 0,
+                               stream, a, n_hg);
+        else
+            return hipErrorInvalidValue;
+    } else if (a.block_table) {
+        hipLaunchKernelGGL((decode_split_kernel<D, true, CB, false>), grid, dim3(kWaves * 64), 0,
+                           stream, a, n_hg);
+    } else {
+        hipLaunchKernelGGL((decode_split_kernel<D, false, CB, false>), grid, dim3(kWaves * 64), 0,
+                           stream, a, n_hg);
+    }
     return hipGetLastError();
 }
 

@@ -174,6 +174,8 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.page = 0;
     a.num_pages = 0;
     a.max_blocks = 0;
+    a.fp8 = 0;
+    a.page_bytes = 0;
     return a;
 }
 
@@ -230,6 +232,46 @@ int prefill(const void *q, const void *k, const void *v, void *o, float *lse, in
     if ((rc = hip_status(gqa::launch_prefill_causal(a, static_cast<hipStream_t>(stream)),
                          "prefill_causal")))
         return rc;
+    return ok();
+}
+
+// Paged decode over bf16 pools (fp8 = 0) or FP8 pages (fp8 = 1).
+int decode_paged(const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                 const int32_t *seqlens, void *o, float *lse, int B, int T_q, int H_q, int H_kv,
+                 int d, int page_size, int num_pages, int max_blocks, float softmax_scale,
+                 int num_splits, void *workspace, size_t workspace_bytes, void *stream, int fp8) {
+    if (page_size < kPagedTile || page_size % kPagedTile != 0 || page_size > kMaxPage)
+        return fail(GQA_ERR_BAD_SHAPE, "page_size=%d must be a multiple of %d in [%d, %d]",
+                    page_size, kPagedTile, kPagedTile, kMaxPage);
+    if (num_pages <= 0 || max_blocks <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "num_pages=%d and max_blocks=%d must be positive",
+                    num_pages, max_blocks);
+    if ((long)num_pages * page_size > 0x7FFFFFFFL || (long)max_blocks * page_size > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE,
+                    "num_pages*page_size and max_blocks*page_size must fit in 31 bits");
+    if (fp8 && d != 128)
+        return fail(GQA_ERR_UNSUPPORTED, "FP8 decode head size d=%d (supported: 128)", d);
+    const int S_max = max_blocks * page_size;
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, T_q, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = decode_common_checks(q, k_pool, v_pool, seqlens, softmax_scale))) return rc;
+    if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
+    if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
+    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto a = split_args(q, k_pool, v_pool, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
+                        workspace, T_q);
+    a.block_table = block_table;
+    a.page = page_size;
+    a.num_pages = num_pages;
+    a.max_blocks = max_blocks;
+    a.fp8 = fp8;
+    a.page_bytes = fp8 ? (size_t)page_size * H_kv * d + 4u * (size_t)page_size : 0;
+    if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q);
+    if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
 
@@ -322,34 +364,64 @@ int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           int B, int T_q, int H_q, int H_kv, int d, int page_size, int num_pages,
                           int max_blocks, float softmax_scale, int num_splits, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    if (page_size < kPagedTile || page_size % kPagedTile != 0 || page_size > kMaxPage)
-        return fail(GQA_ERR_BAD_SHAPE, "page_size=%d must be a multiple of %d in [%d, %d]",
-                    page_size, kPagedTile, kPagedTile, kMaxPage);
-    if (num_pages <= 0 || max_blocks <= 0)
-        return fail(GQA_ERR_BAD_SHAPE, "num_pages=%d and max_blocks=%d must be positive",
-                    num_pages, max_blocks);
-    if ((long)num_pages * page_size > 0x7FFFFFFFL || (long)max_blocks * page_size > 0x7FFFFFFFL)
-        return fail(GQA_ERR_BAD_SHAPE,
-                    "num_pages*page_size and max_blocks*page_size must fit in 31 bits");
-    const int S_max = max_blocks * page_size;
-    Plan pl;
+    return decode_paged(q, k_pool, v_pool, block_table, seqlens, o, lse, B, T_q, H_q, H_kv, d,
+                        page_size, num_pages, max_blocks, softmax_scale, num_splits, workspace,
+                        workspace_bytes, stream, 0);
+}
+
+size_t gqa_fp8_page_bytes(int page_size, int H_kv, int d) {
+    if (page_size <= 0 || H_kv <= 0 || d <= 0) return 0;
+    return (size_t)page_size * H_kv * d + 4u * (size_t)page_size;
+}
+
+int gqa_attn_decode_paged_fp8(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *block_table, const int32_t *seqlens, void *o,
+                              float *lse, int B, int T_q, int H_q, int H_kv, int d, int page_size,
+                              int num_pages, int max_blocks, float softmax_scale, int num_splits,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_paged(q, k_pool, v_pool, block_table, seqlens, o, lse, B, T_q, H_q, H_kv, d,
+                        page_size, num_pages, max_blocks, softmax_scale, num_splits, workspace,
+                        workspace_bytes, stream, 1);
+}
+
+int gqa_kv_quantize_fp8(const void *x, const int32_t *seqlens, const int32_t *block_table,
+                        void *pool, int B, int S_max, int H_kv, int d, int page_size,
+                        int num_pages, int max_blocks, void *stream) {
+    if (B <= 0 || S_max <= 0 || H_kv <= 0 || d <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "B=%d, S_max=%d, H_kv=%d, d=%d must be positive", B, S_max,
+                    H_kv, d);
+    if (d % 8 != 0) return fail(GQA_ERR_UNSUPPORTED, "FP8 quantisation needs d %% 8 == 0 (d=%d)", d);
+    if (page_size <= 0 || num_pages <= 0 || max_blocks <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "page_size=%d, num_pages=%d, max_blocks=%d must be positive",
+                    page_size, num_pages, max_blocks);
+    if ((long)max_blocks * page_size < S_max)
+        return fail(GQA_ERR_BAD_SHAPE, "max_blocks*page_size=%ld is below S_max=%d",
+                    (long)max_blocks * page_size, S_max);
+    if ((long)B * S_max > 0x7FFFFFFFL || (long)H_kv * d > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*S_max and H_kv*d must fit in 31 bits");
     int rc;
-    if ((rc = make_plan(B, T_q, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
-    if ((rc = decode_common_checks(q, k_pool, v_pool, seqlens, softmax_scale))) return rc;
+    if ((rc = check_bf16(x, "x"))) return rc;
+    if (!pool) return fail(GQA_ERR_NULL_POINTER, "pool is NULL");
+    if (!aligned(pool, 16)) return fail(GQA_ERR_ALIGNMENT, "pool is not 16-byte aligned");
     if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
     if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
-    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
-    if ((rc = check_workspace(workspace, workspace_bytes, pl))) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    auto a = split_args(q, k_pool, v_pool, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
-                        workspace, T_q);
+    if (seqlens && !aligned(seqlens, 4)) return fail(GQA_ERR_ALIGNMENT, "seqlens misaligned");
+    gqa::KvQuantArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.seqlens = seqlens;
     a.block_table = block_table;
+    a.pool = static_cast<uint8_t *>(pool);
+    a.B = B;
+    a.S_max = S_max;
+    a.H_kv = H_kv;
+    a.d = d;
     a.page = page_size;
     a.num_pages = num_pages;
     a.max_blocks = max_blocks;
-    if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
-    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q);
-    if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
+    a.page_bytes = gqa_fp8_page_bytes(page_size, H_kv, d);
+    if ((rc = hip_status(gqa::launch_kv_quantize_fp8(a, static_cast<hipStream_t>(stream)),
+                         "kv_quantize_fp8")))
+        return rc;
     return ok();
 }
 

@@ -38,7 +38,25 @@ struct DecodeSplitArgs {
     // (page a multiple of 16; S_max = max_blocks * page).
     const int32_t *block_table;
     int page, num_pages, max_blocks;
+    // FP8 pages (paged only, d = 128): k and v are byte pools of pages of page_bytes bytes,
+    // [page][H_kv][d] E4M3 codes followed by `page` fp32 per-token scales.
+    int fp8;
+    size_t page_bytes;
 };
+
+// Per-token E4M3 quantisation of a cache x [B][S_max][H_kv][d] (bf16) into the pages of an
+// FP8 pool: token t < len(b) of sequence b goes to row t % page of page
+// block_table[b][t / page] (an entry outside [0, num_pages) is skipped).
+struct KvQuantArgs {
+    const uint16_t *x;
+    const int32_t *seqlens;     // [B] or nullptr (= S_max)
+    const int32_t *block_table; // [B][max_blocks]
+    uint8_t *pool;
+    int B, S_max, H_kv, d, page, num_pages, max_blocks;
+    size_t page_bytes;          // page * H_kv * d + 4 * page
+};
+
+hipError_t launch_kv_quantize_fp8(const KvQuantArgs &a, hipStream_t stream);
 
 // Partial states to merge for (b, r), r = h * T + i the row of query head h, token i:
 //   seg != nullptr (decode workspace): states p < seg[2b+1], at index

@@ -298,6 +298,63 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
                            int d, float softmax_scale, void *stream);
 
 /*
+ * FP8 (E4M3) paged KV cache (V07, section 17.7: a per-token scale kept with each
+ * page, its page_size scalars appended after the page's rows, dequantisation fused
+ * into the load; section 9.5: E4M3 values, fp32 accumulation).  A pool is an array
+ * of num_pages pages of gqa_fp8_page_bytes(page_size, H_kv, d) bytes each:
+ *
+ *   bytes [0, page_size*H_kv*d)           E4M3 codes, [page_size][H_kv][d]
+ *   bytes [page_size*H_kv*d, +4*page_size) fp32 scales, one per page row (token)
+ *
+ * (K and V are two such pools with one page numbering.)  A token's row holds
+ * code(x) with x = value(code) * scale.  E4M3 is the OCP 8-bit floating-point
+ * format: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 holds the
+ * subnormals m * 2^-9; 0x7F and 0xFF are NaN; the largest finite value is 448.
+ */
+
+/* Bytes of one FP8 page (0 for non-positive sizes). */
+size_t gqa_fp8_page_bytes(int page_size, int H_kv, int d);
+
+/*
+ * gqa_kv_quantize_fp8 -- write a bf16 cache into the pages of an FP8 pool (the
+ * cache-writing step upstream of attention): token t < seqlens[b] of sequence b
+ * (NULL seqlens: every t < S_max) is stored in row t % page_size of page
+ * block_table[b][t / page_size] as E4M3 codes of its H_kv * d values with one
+ * scale 2^e, e the smallest integer with max |x| <= 448 * 2^e (clamped to
+ * [-126, 127]; an all-zero row takes -126); each code is the E4M3 value nearest
+ * to x * 2^-e, ties to even.  A power-of-two scale makes every dequantised value
+ * exactly a bfloat16.  Slots no live token maps to, and tokens whose table entry
+ * is outside [0, num_pages), are not written.
+ *
+ *   x            [B, S_max, H_kv, d] bf16, device, read-only
+ *   seqlens      [B] int32, device, or NULL
+ *   block_table  [B, max_blocks] int32, device, read-only (max_blocks*page_size >= S_max)
+ *   pool         num_pages * gqa_fp8_page_bytes(...) bytes, device, 16-byte aligned, written
+ *
+ * Supported: d a multiple of 8.
+ */
+int gqa_kv_quantize_fp8(const void *x, const int32_t *seqlens, const int32_t *block_table,
+                        void *pool, int B, int S_max, int H_kv, int d, int page_size,
+                        int num_pages, int max_blocks, void *stream);
+
+/*
+ * gqa_attn_decode_paged_fp8 -- gqa_attn_decode_paged over FP8 pools: the same
+ * arguments, plan, workspace and outputs, with k_pool and v_pool FP8 pools as
+ * above.  Codes are converted to bf16 in registers (exactly), each score is
+ * scaled by its key's K scale and each weight by its key's V scale as the tiles
+ * are consumed, so the cache is read in about half the bytes of bf16 pages.  With
+ * the power-of-two scales of gqa_kv_quantize_fp8 the results are those of
+ * gqa_attn_decode_paged over bf16 pages holding the dequantised values, bit for bit.
+ *
+ * Supported: d = 128; page_size a multiple of 16.
+ */
+int gqa_attn_decode_paged_fp8(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *block_table, const int32_t *seqlens, void *o,
+                              float *lse, int B, int T_q, int H_q, int H_kv, int d, int page_size,
+                              int num_pages, int max_blocks, float softmax_scale, int num_splits,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gqa_prefill_bwd_workspace_bytes -- device workspace (bytes, 256-byte aligned
  * start required) of gqa_attn_prefill_causal_bwd for these sizes, or 0 if the
  * sizes are invalid.  It holds each row's statistics and the fp32 shares of dK

@@ -1,0 +1,162 @@
+"""FP8 (E4M3) paged KV cache on the GPU ("Attention Kernel lineage" (V07), section 17.7).
+
+* The quantiser (``gqa_kv_quantize_fp8``) against the oracle's per-token quantisation into
+  pages: identical bytes, codes and scales, with the slots no token maps to untouched.
+* The FP8 decode (``gqa_attn_decode_paged_fp8``) over the oracle's pools: against the
+  oracle's decode over the dequantised pages, and -- since every dequantised value is a
+  bfloat16 -- bit for bit against the bf16 paged decode over those dequantised pages.  The
+  FP8 pools carry NaN codes (0x7F) in every slot no token maps to, so a read of one shows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_amd as g
+import oracle
+from gpu_util import say, to_gpu_bf16, to_gpu_i32
+from gqa_workloads import LLAMA_DECODE
+from gqa_workloads.generate import bf16_bits_from_f32, paged_decode_inputs
+from parity import check, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def logical_caches(p):
+    """The contiguous caches [B, max_blocks * page, H_kv, d] that a paged input holds."""
+    return tuple(oracle.gather_pages(p[x], p["block_table"], p["seqlens"], p["page_size"])
+                 for x in ("k_pool", "v_pool"))
+
+
+def oracle_pools(p, xk, xv, fill):
+    n = p["k_pool"].shape[0]
+    return tuple(oracle.quantize_to_pages(x, p["seqlens"], p["block_table"], p["page_size"], n,
+                                          fill=fill) for x in (xk, xv))
+
+
+def nan_poisoned(pool, p, H_kv, d):
+    """A copy of an FP8 pool with NaN codes (0x7F) in every code slot no token maps to."""
+    page = p["page_size"]
+    out = pool.copy()
+    live = np.zeros((pool.shape[0], page), dtype=bool)
+    for b, n in enumerate(p["seqlens"]):
+        for t in range(int(n)):
+            live[p["block_table"][b, t // page], t % page] = True
+    codes = out[:, :page * H_kv * d].reshape(pool.shape[0], page, H_kv * d)
+    codes[~live] = 0x7F
+    return out
+
+
+QUANT_CASES = [
+    # (B, H_kv, d, page, lengths)
+    (3, 8, 128, 16, (1, 700)),     # Llama KV heads, ragged, pages of 16
+    (2, 2, 64, 32, (30, 300)),     # d = 64, pages of 32
+    (2, 1, 8, 48, (1, 100)),       # a row of 8 values (most lanes idle), pages of 48
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[str(c) for c in QUANT_CASES])
+def test_quantize_matches_oracle(case, gpu_available):
+    B, H_kv, d, page, ragged = case
+    p = paged_decode_inputs(B, 8, H_kv, d, page, ragged=ragged, seed=700 + d + page,
+                            nan_fill=False)
+    xk, xv = logical_caches(p)
+    # special rows: all zero, large (scale above one), tiny (scale near the bottom)
+    rng = np.random.default_rng(701)
+    xk[0, 0] = 0
+    if p["seqlens"][0] > 2:
+        xk[0, 1] = bf16_bits_from_f32(rng.standard_normal((H_kv, d)).astype(np.float32) * 3e4)
+        xk[0, 2] = bf16_bits_from_f32(rng.standard_normal((H_kv, d)).astype(np.float32) * 1e-30)
+    n = p["k_pool"].shape[0]
+    pb = g.fp8_page_bytes(page, H_kv, d)
+    assert pb == oracle.fp8_page_bytes(page, H_kv, d)
+    tbl, sl = to_gpu_i32(p["block_table"]), to_gpu_i32(p["seqlens"])
+    for name, x in (("k", xk), ("v", xv)):
+        say(f"fp8 quantise {case} {name}")
+        pool = torch.full((n, pb), 0xAB, dtype=torch.uint8, device="cuda")
+        g.kv_quantize_fp8(to_gpu_bf16(x), tbl, sl, pool=pool, page_size=page)
+        torch.cuda.synchronize()
+        ref = oracle.quantize_to_pages(x, p["seqlens"], p["block_table"], page, n, fill=0xAB)
+        got = pool.cpu().numpy()
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{name}: {len(bad)} bytes differ, first at {bad[:4].tolist()}"
+
+
+def fp8_decode_case(p, H_kv, d, num_splits, q=None):
+    """FP8 decode over the oracle's pools against the oracle, and bitwise against the bf16
+    paged decode over the dequantised pages."""
+    xk, xv = logical_caches(p)
+    kq, vq = oracle_pools(p, xk, xv, fill=0)
+    kb = oracle.dequantize_pages(kq, p["page_size"], H_kv, d)
+    vb = oracle.dequantize_pages(vq, p["page_size"], H_kv, d)
+    q = p["q"] if q is None else q
+    qg = to_gpu_bf16(q)
+    tbl, sl = to_gpu_i32(p["block_table"]), to_gpu_i32(p["seqlens"])
+    k8 = torch.from_numpy(nan_poisoned(kq, p, H_kv, d)).cuda()
+    v8 = torch.from_numpy(nan_poisoned(vq, p, H_kv, d)).cuda()
+    o8, l8 = g.decode_paged_fp8(qg, k8, v8, tbl, sl, page_size=p["page_size"], H_kv=H_kv,
+                                num_splits=num_splits)
+    ob, lb = g.decode_paged(qg, to_gpu_bf16(kb), to_gpu_bf16(vb), tbl, sl, num_splits=num_splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, ob) and torch.equal(l8, lb), "FP8 decode differs from bf16 on dequantised pages"
+    o_ref, l_ref = oracle.decode_paged_fp8(q, kq, vq, p["block_table"], p["seqlens"],
+                                           p["page_size"])
+    return check(to_f64(o8), to_f64(l8), o_ref, l_ref, "fp8 decode")
+
+
+DECODE_CASES = [
+    # (B, H_q, H_kv, page, lengths, num_splits)
+    (3, 16, 2, 16, (1, 900), 4),
+    (2, 8, 1, 32, (200, 2000), 0),     # MQA
+    (4, 64, 8, 16, (1, 40), 1),        # lengths below one tile, one chunk
+    (2, 24, 6, 64, (3000, 5000), 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
+def test_fp8_decode_shapes(case, gpu_available):
+    B, H_q, H_kv, page, ragged, splits = case
+    p = paged_decode_inputs(B, H_q, H_kv, 128, page, ragged=ragged, seed=710 + H_q + page,
+                            nan_fill=False)
+    say(f"fp8 decode {case} seqlens={p['seqlens'].tolist()}")
+    say(f"  {fp8_decode_case(p, H_kv, 128, splits)}")
+
+
+def test_fp8_decode_llama_s32768(gpu_available):
+    """The Llama3-70B decode (S_kv = 32768, 64 query heads, 8 KV heads, 32 splits) over
+    FP8 pages of 16 tokens in permuted pool order."""
+    cfg = LLAMA_DECODE
+    p = paged_decode_inputs(1, cfg.H_q, cfg.H_kv, cfg.d, 16, S_max=cfg.S_kv, seed=cfg.seed,
+                            nan_fill=False)
+    say(f"fp8 decode {cfg.name}")
+    say(f"  {fp8_decode_case(p, cfg.H_kv, cfg.d, cfg.num_splits)}")
+
+
+def test_fp8_multi_token_decode(gpu_available):
+    """T_q = 4 query tokens per sequence over FP8 pages (32 rows per KV head)."""
+    p = paged_decode_inputs(3, 16, 2, 128, 16, ragged=(2, 3000), seed=720, nan_fill=False)
+    p["seqlens"][0] = 2                           # two tokens at negative positions
+    rng = np.random.default_rng(721)
+    q4 = bf16_bits_from_f32(rng.standard_normal((3, 4, 16, 128)).astype(np.float32))
+    say(f"fp8 multi-token decode seqlens={p['seqlens'].tolist()}")
+    say(f"  {fp8_decode_case(p, 2, 128, 0, q=q4)}")
+
+
+def test_fp8_gpu_quantised_pool_decodes(gpu_available):
+    """The whole FP8 path on the GPU -- quantise, then decode -- equals the decode over the
+    oracle's pools (the quantiser's bytes are the oracle's)."""
+    p = paged_decode_inputs(2, 16, 2, 128, 16, ragged=(500, 1500), seed=730, nan_fill=False)
+    xk, xv = logical_caches(p)
+    n = p["k_pool"].shape[0]
+    pb = g.fp8_page_bytes(16, 2, 128)
+    tbl, sl = to_gpu_i32(p["block_table"]), to_gpu_i32(p["seqlens"])
+    say("fp8 quantise then decode on the GPU")
+    kg = g.kv_quantize_fp8(to_gpu_bf16(xk), tbl, sl, num_pages=n, page_size=16)
+    vg = g.kv_quantize_fp8(to_gpu_bf16(xv), tbl, sl, num_pages=n, page_size=16)
+    qg = to_gpu_bf16(p["q"])
+    o1, l1 = g.decode_paged_fp8(qg, kg, vg, tbl, sl, page_size=16, H_kv=2)
+    kq, vq = oracle_pools(p, xk, xv, fill=0)
+    o2, l2 = g.decode_paged_fp8(qg, torch.from_numpy(kq).cuda(), torch.from_numpy(vq).cuda(), tbl,
+                                sl, page_size=16, H_kv=2)
+    torch.cuda.synchronize()
+    assert kg.shape == (n, pb)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
