@@ -210,7 +210,69 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
         "paged": {"page_size": page, "us": round(ms_p * 1e3, 2),
                   "gbs": round(kv / ms_p / 1e6, 1),
                   "frac_hbm_peak": round(kv / ms_p / 1e6 / HBM_PEAK_GBS, 4)}}
-    del q, kp, vp, tbl, sl, kc, vc, ws_c, ws_p
+    # the same batch over FP8 pages (V07 section 17.7): the caches quantised on the GPU into
+    # pools with the same page numbering
+    k8 = g.kv_quantize_fp8(kc, tbl, sl, num_pages=kp.shape[0], page_size=page)
+    v8 = g.kv_quantize_fp8(vc, tbl, sl, num_pages=kp.shape[0], page_size=page)
+
+    def paged8_b_call(i):
+        g.decode_paged_fp8(q, k8, v8, tbl, sl, page_size=page, H_kv=rc.H_kv,
+                           num_splits=rc.num_splits, out=o, lse=lse, workspace=ws_p)
+
+    paged8_b_call(0)
+    ms_8 = graph_ms(paged8_b_call, K)
+    kv8 = acc.decode_kv_bytes_fp8(seqlens, rc.H_kv, rc.d)
+    res["decode_ragged_b8"]["paged_fp8"] = {
+        "page_size": page, "us": round(ms_8 * 1e3, 2), "bytes": kv8,
+        "gbs": round(kv8 / ms_8 / 1e6, 1), "frac_hbm_peak": round(kv8 / ms_8 / 1e6 / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(rc.B / (ms_8 * 1e-3), 1), "vs_bf16_paged": round(ms_p / ms_8, 3)}
+    del q, kp, vp, tbl, sl, kc, vc, ws_c, ws_p, k8, v8
+
+    # Llama decode (S = 32768) over FP8 pages of 16 tokens in permuted pool order: four
+    # quantised copies of the cache (from the bench's four bf16 copies), and the quantiser's
+    # own time on one copy
+    dc = LLAMA_DECODE
+    n_pages = dc.S_kv // page
+    gen = torch.Generator(device="cuda").manual_seed(dc.seed)
+    tbl8 = torch.randperm(n_pages + 3, generator=gen, device="cuda")[:n_pages].to(
+        torch.int32).view(1, n_pages)
+    sl8 = torch.full((1,), dc.S_kv, dtype=torch.int32, device="cuda")
+    pools8 = [(g.kv_quantize_fp8(k, tbl8, sl8, num_pages=n_pages + 3, page_size=page),
+               g.kv_quantize_fp8(v, tbl8, sl8, num_pages=n_pages + 3, page_size=page))
+              for k, v in kv_copies]
+    q8 = torch.randn((dc.B, dc.H_q, dc.d), device="cuda", generator=gen).to(torch.bfloat16)
+    o8 = torch.empty((dc.B, dc.H_q, dc.d), dtype=torch.bfloat16, device="cuda")
+    l8 = torch.empty((dc.B, dc.H_q), dtype=torch.float32, device="cuda")
+    ws8 = g.decode_workspace(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
+
+    def fp8_call(i):
+        k, v = pools8[i % len(pools8)]
+        g.decode_paged_fp8(q8, k, v, tbl8, sl8, page_size=page, H_kv=dc.H_kv,
+                           num_splits=dc.num_splits, out=o8, lse=l8, workspace=ws8)
+
+    def quant_call(i):
+        k, v = kv_copies[i % len(kv_copies)]
+        g.kv_quantize_fp8(k, tbl8, sl8, pool=pools8[0][0], page_size=page)
+        g.kv_quantize_fp8(v, tbl8, sl8, pool=pools8[0][1], page_size=page)
+
+    fp8_call(0)
+    ms8 = graph_ms(fp8_call, K)
+    quant_call(0)
+    ms_q = graph_ms(quant_call, K)
+    fp8_call(0)   # (the pools are rewritten with the same values)
+    b8 = acc.decode_kv_bytes_fp8([dc.S_kv], dc.H_kv, dc.d)
+    bf16_bytes = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
+    res["decode_paged_fp8"] = {
+        "workload": f"Llama3-70B decode B=1 S_kv={dc.S_kv} over FP8 (E4M3) pages of {page} tokens "
+                    f"with per-token scales, permuted pool order, {dc.num_splits} splits",
+        "us": round(ms8 * 1e3, 2), "bytes": b8, "gbs": round(b8 / ms8 / 1e6, 1),
+        "frac_hbm_peak": round(b8 / ms8 / 1e6 / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(dc.B / (ms8 * 1e-3), 1),
+        "bf16_equivalent_gbs": round(bf16_bytes / ms8 / 1e6, 1),
+        "vs_bf16_paged": round(res["decode_paged"]["us"] / (ms8 * 1e3), 3),
+        "quantise_us": round(ms_q * 1e3, 2),
+        "quantise_gbs": round((bf16_bytes + b8) / ms_q / 1e6, 1)}
+    del pools8, tbl8, sl8, q8, o8, l8, ws8
 
     # a few query tokens per sequence (speculative decoding): the M-fold decode against the
     # same tokens through the chunked-prefill kernel

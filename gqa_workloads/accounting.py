@@ -26,6 +26,12 @@ def decode_kv_bytes(seqlens, H_kv: int, d: int, elem_bytes: int = 2) -> int:
     return sum(kv_bytes(int(s), H_kv, d, elem_bytes) for s in seqlens)
 
 
+def decode_kv_bytes_fp8(seqlens, H_kv: int, d: int) -> int:
+    """Bytes one decode launch must read from FP8 pages (same page, section 17.7): per token
+    and pool the H_kv * d one-byte E4M3 codes plus its 4-byte scale."""
+    return sum(2 * int(s) * (H_kv * d + 4) for s in seqlens)
+
+
 def decode_flop(seqlens, H_q: int, d: int) -> int:
     """Q.K^T plus P.V multiply-adds of one decode launch, 2 FLOP each."""
     return sum(4 * int(s) * H_q * d for s in seqlens)

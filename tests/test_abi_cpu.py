@@ -228,6 +228,41 @@ def test_prefill_bwd_rejects_before_launch(lib, kw, code):
     assert lib.gqa_last_error().decode() != ""
 
 
+def test_fp8_page_bytes(lib):
+    """Codes of page_size rows of H_kv*d bytes, then page_size fp32 scales."""
+    assert lib.gqa_fp8_page_bytes(16, 8, 128) == 16 * 8 * 128 + 64
+    assert lib.gqa_fp8_page_bytes(0, 8, 128) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULLP), (dict(pool=None), NULLP), (dict(tbl=None), NULLP), (dict(x=MIS), ALIGN),
+    (dict(pool=ctypes.c_void_p(0x10008)), ALIGN), (dict(sl=ctypes.c_void_p(0x10002)), ALIGN),
+    (dict(B=0), SHAPE), (dict(d=12), UNSUP), (dict(page=0), SHAPE), (dict(max_blocks=1), SHAPE),
+])
+def test_kv_quantize_fp8_rejects_before_launch(lib, kw, code):
+    a = dict(x=A, sl=None, tbl=A, pool=A, B=2, S_max=64, H_kv=8, d=128, page=16, num_pages=8,
+             max_blocks=4)
+    a.update(kw)
+    assert lib.gqa_kv_quantize_fp8(a["x"], a["sl"], a["tbl"], a["pool"], a["B"], a["S_max"],
+                                   a["H_kv"], a["d"], a["page"], a["num_pages"],
+                                   a["max_blocks"], None) == code
+    assert lib.gqa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), UNSUP), (dict(page=24), SHAPE), (dict(tbl=None), NULLP), (dict(q=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(H_kv=3), SHAPE),
+])
+def test_decode_paged_fp8_rejects_before_launch(lib, kw, code):
+    a = dict(q=A, k=A, v=A, tbl=A, sl=None, o=A, lse=A, B=1, T=1, H_q=8, H_kv=2, d=128, page=16,
+             num_pages=8, max_blocks=4, scale=0.088, splits=0, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.gqa_attn_decode_paged_fp8(a["q"], a["k"], a["v"], a["tbl"], a["sl"], a["o"],
+                                         a["lse"], a["B"], a["T"], a["H_q"], a["H_kv"], a["d"],
+                                         a["page"], a["num_pages"], a["max_blocks"], a["scale"],
+                                         a["splits"], a["ws"], a["ws_bytes"], None) == code
+
+
 def test_binding_raises_with_detail():
     with pytest.raises(g.GQAError) as ei:
         g.decode_plan(1, 64, 7, 128, 1024, 0)

@@ -68,3 +68,9 @@ def test_backward_flop_is_five_products():
     """Five causal S x S x d products per head: 2.5x the forward (two products)."""
     assert acc.prefill_causal_bwd_flop(1, 8192, 64, 128) == 2.5 * acc.prefill_causal_flop(1, 8192, 64, 128)
     assert acc.prefill_causal_bwd_flop(2, 10, 3, 4) == 2 * 5 * 10 * 10 * 4 * 3
+
+
+def test_fp8_decode_bytes():
+    """FP8 pages: one byte per cached value plus a 4-byte scale per token and pool."""
+    assert acc.decode_kv_bytes_fp8([32768], 8, 128) == 2 * 32768 * (8 * 128 + 4)
+    assert acc.decode_kv_bytes_fp8([32768], 8, 128) * 2 - acc.decode_kv_bytes([32768], 8, 128) == 2 * 2 * 32768 * 4
