@@ -12,52 +12,47 @@
 // m2 = -inf is empty (a_p = 0); a row with no non-empty partial gets O = 0 and
 // LSE = -inf (the identity state of the merge, V07 section 3).
 //
-// Sixteen waves per (b, h), split into 32 half-waves: half-wave i folds the partials
-// p = i, i+32, ... into a running (M, L, O) with the same online update, its 32 lanes
-// each holding D/32 consecutive columns (16-byte loads at d = 128).  A batch's loads are
-// all issued before any is used, so one memory round trip serves 256 partials of a row.
-// The 32 half-wave states are then merged through LDS, one output column per thread.
-// The order is fixed, so results are run-to-run deterministic.
+// A row's columns are cut into 32-wide slices, one workgroup of 4 waves per (row, slice),
+// so a row's partials are read by D/32 compute units at once.  Each workgroup folds every
+// partial's (m2, l) (the few bytes every slice needs) and its slice of O.  Lane l of a wave
+// takes columns 4*(l%8) .. +3 of the slice and the partials p = 64*w + 8*j + l/8 (+ 256 per
+// round), j < 8: eight 16-byte loads a lane, all in flight together, and only for partials
+// that exist.  The lane states are then merged across the 8 lanes of a column group (three
+// cross-lane steps) and across the 4 waves through LDS.  The order is fixed, so results are
+// run-to-run deterministic.
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
 namespace gqa {
 namespace {
 
-constexpr int kMergeWaves = 16;
-constexpr int kHalves = 2 * kMergeWaves;
-constexpr int kBatch = 8;      // partials per half-wave per memory round trip
+constexpr int kMergeWaves = 4;
+constexpr int kSlice = 32;                 // columns per workgroup
+constexpr int kPerRound = kMergeWaves * 64;  // partials per round (8 per lane)
 
-template <int N>
-struct FloatVec {
-    float v[N];
+struct MState {
+    float m, l, o[4];
 };
 
-template <int N>
-__device__ __forceinline__ FloatVec<N> load_floats(const float *p) {
-    FloatVec<N> r;
-    if constexpr (N == 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(p);
+// Merge state y into x (either may be empty: m = -inf).
+__device__ __forceinline__ void merge_into(MState &x, const MState &y) {
+    const float mn = fmaxf(x.m, y.m);
+    const float ax = x.m == neg_inf() ? 0.f : exp2_fast(x.m - mn);
+    const float ay = y.m == neg_inf() ? 0.f : exp2_fast(y.m - mn);
+    x.l = ax * x.l + ay * y.l;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[i] = x[i];
-    } else if constexpr (N == 2) {
-        const f32x2 x = *reinterpret_cast<const f32x2 *>(p);
-        r.v[0] = x[0];
-        r.v[1] = x[1];
-    } else {
-        r.v[0] = *p;
-    }
-    return r;
+    for (int e = 0; e < 4; ++e) x.o[e] = ax * x.o[e] + ay * y.o[e];
+    x.m = mn;
 }
 
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
-    constexpr int DPL = D / 32;           // columns per lane of a half-wave
-    __shared__ float red[kHalves][D + 2];
-    const int r = blockIdx.x, b = blockIdx.y;     // row r = h * T + i
+    constexpr int NS = D / kSlice;
+    __shared__ float red[kMergeWaves][8][6];
+    const int r = blockIdx.x / NS, q = blockIdx.x % NS, b = blockIdx.y;   // row r = h * T + i
     const int h = r / a.T, i = r % a.T;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int half = 2 * w + (lane >> 5), hl = lane & 31;
+    const int c = lane & 7, s8 = lane >> 3;
 
     int n;
     size_t row0;
@@ -71,69 +66,72 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
     const size_t ss = a.state_stride;
     const float *m2 = a.part_m2 + row0;
     const float *lp = a.part_l + row0;
-    const float *op = a.part_o + row0 * D + hl * DPL;
+    const float *op = a.part_o + row0 * D + q * kSlice + 4 * c;
 
-    float M = neg_inf(), L = 0.f;
-    float acc[DPL];
+    MState st{neg_inf(), 0.f, {0.f, 0.f, 0.f, 0.f}};
+    for (int base = 64 * w; base < n; base += kPerRound) {
+        float mv[8], lv[8];
+        f32x4 ov[8];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    for (int base = half; base < n; base += kHalves * kBatch) {
-        float mv[kBatch], lv[kBatch];
-        FloatVec<DPL> ov[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int p = min(base + j * kHalves, n - 1);   // clamped: loads stay in range
-            mv[j] = m2[p * ss];
-            lv[j] = lp[p * ss];
-            ov[j] = load_floats<DPL>(op + (size_t)p * ss * D);
+        for (int j = 0; j < 8; ++j) {
+            const int p = base + 8 * j + s8;
+            if (p < n) {
+                mv[j] = m2[p * ss];
+                lv[j] = lp[p * ss];
+                ov[j] = *reinterpret_cast<const f32x4 *>(op + (size_t)p * ss * D);
+            } else {
+                mv[j] = neg_inf();
+                lv[j] = 0.f;
+                ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const float mp = mv[j];
-            // past the end, or an empty partial: the state is unchanged
-            const bool use = (base + j * kHalves < n) && (mp != neg_inf());
-            const float m_new = fmaxf(M, mp);
-            const float a_old = exp2_fast(M - m_new);  // 2^-inf = 0 while the state is empty
-            const float a_p = exp2_fast(mp - m_new);
-            L = use ? L * a_old + a_p * lv[j] : L;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[e] = use ? acc[e] * a_old + a_p * ov[j].v[e] : acc[e];
-            M = use ? m_new : M;
+        for (int j = 0; j < 8; ++j) {
+            // past the end, or an empty partial: m = -inf adds nothing
+            const MState y{mv[j], lv[j], {ov[j][0], ov[j][1], ov[j][2], ov[j][3]}};
+            merge_into(st, y);
         }
     }
+    // the 8 lanes of a column group (lane bits 3..5)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) red[half][hl * DPL + e] = acc[e];
-    if (hl == 0) {
-        red[half][D] = M;
-        red[half][D + 1] = L;
+    for (int off = 8; off < 64; off <<= 1) {
+        MState y;
+        y.m = __shfl_xor(st.m, off);
+        y.l = __shfl_xor(st.l, off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y.o[e] = __shfl_xor(st.o[e], off);
+        merge_into(st, y);
+    }
+    if (lane < 8) {
+        red[w][c][0] = st.m;
+        red[w][c][1] = st.l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[w][c][2 + e] = st.o[e];
     }
     __syncthreads();
-
-    // combine the 32 half-wave states: one output column per thread
-    if (threadIdx.x >= D) return;
-    const int d = threadIdx.x;
-    float Mt = neg_inf();
+    if (threadIdx.x >= 8) return;
+    MState t{red[0][c][0], red[0][c][1], {red[0][c][2], red[0][c][3], red[0][c][4], red[0][c][5]}};
 #pragma unroll
-    for (int i = 0; i < kHalves; ++i) Mt = fmaxf(Mt, red[i][D]);
-    const bool empty = (Mt == neg_inf());
-    float Lt = 0.f, o = 0.f;
-#pragma unroll
-    for (int i = 0; i < kHalves; ++i) {
-        const float al = empty ? 0.f : exp2_fast(red[i][D] - Mt);
-        Lt += al * red[i][D + 1];
-        o += al * red[i][d];
+    for (int v = 1; v < kMergeWaves; ++v) {
+        const MState y{red[v][c][0], red[v][c][1],
+                       {red[v][c][2], red[v][c][3], red[v][c][4], red[v][c][5]}};
+        merge_into(t, y);
     }
-    const float inv = empty ? 0.f : 1.f / Lt;
-    a.o[(((size_t)b * a.T + i) * a.H_q + h) * D + d] = (uint16_t)(pack_bf16x2(o * inv, 0.f) & 0xFFFFu);
-    if (d == 0)
+    const bool empty = t.m == neg_inf();
+    const float inv = empty ? 0.f : 1.f / t.l;
+    const u32x2 packed = {pack_bf16x2(t.o[0] * inv, t.o[1] * inv),
+                          pack_bf16x2(t.o[2] * inv, t.o[3] * inv)};
+    *reinterpret_cast<u32x2 *>(a.o + (((size_t)b * a.T + i) * a.H_q + h) * D + q * kSlice + 4 * c) =
+        packed;
+    if (q == 0 && c == 0)
         a.lse[((size_t)b * a.H_q + h) * a.T + i] =
-            empty ? neg_inf() : kLn2 * (Mt + __builtin_log2f(Lt));
+            empty ? neg_inf() : kLn2 * (t.m + __builtin_log2f(t.l));
 }
 
 template <int D>
 hipError_t launch(const MergeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q * a.T, a.B), dim3(kMergeWaves * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q * a.T * (D / kSlice), a.B),
+                       dim3(kMergeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
