@@ -69,9 +69,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("bf3b59e0667514e5", 143_032_902),
-    "lse_merge": ("ceae8259a6b21c5b", 9_550_287),
-    "prefill_causal": ("e415cbf712475006", 421_813_828),
+    "decode_split": ("00fd50e5465ce319", 143_033_338),
+    "lse_merge": ("1dc58e43411ea0e2", 9_527_214),
+    "prefill_causal": ("1def1b795a174f6f", 421_924_486),
 }
 
 
