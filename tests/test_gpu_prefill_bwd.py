@@ -18,7 +18,7 @@ import torch
 import gqa_attention_amd as g
 import oracle
 from gpu_util import say, to_gpu_bf16
-from gqa_workloads import LLAMA_PREFILL
+from gqa_workloads import LLAMA_LONG_PREFILL, LLAMA_PREFILL
 from gqa_workloads.generate import bf16_bits_from_f32, prefill_bwd_inputs
 from parity import GRAD_REL_L2, check_grad, to_f64
 
@@ -145,3 +145,53 @@ def test_bwd_llama_s8192_sampled(gpu_available):
     j = torch.from_numpy(keys[:, 2].astype(np.int64)).to(dk.device)
     say(f"  dk {check_grad(to_f64(dk[0, j, 0]), rk, 'llama dk keys')}")
     say(f"  dv {check_grad(to_f64(dv[0, j, 0]), rv, 'llama dv keys')}")
+
+
+def test_bwd_llama_long_s65536_outliers_sampled(gpu_available):
+    """The long-context workload (S = 65536, 1 % of key rows scaled by 8), forward and
+    backward on the GPU.  The oracle's forward gives the stored O of the checked rows of
+    query heads 0..7 (KV head 0), which replaces the GPU's O there, so both sides form
+    those rows' D from the same O.  Checked: dQ on sampled rows across the whole prompt,
+    and dK, dV of KV head 0 on keys of the last 256 positions, which only the last 256
+    rows of each query head see (so the oracle's key side needs LSE and D of those rows
+    only)."""
+    cfg = LLAMA_LONG_PREFILL
+    S, H_q, G, d = cfg.S, cfg.H_q, cfg.H_q // cfg.H_kv, cfg.d
+    p = prefill_bwd_inputs(cfg.B, S, H_q, cfg.H_kv, d, seed=cfg.seed,
+                           outlier_frac=cfg.outlier_frac, outlier_scale=cfg.outlier_scale)
+    q, k, v, do = (to_gpu_bf16(p[x]) for x in ("q", "k", "v", "do"))
+    say(f"prefill forward {cfg.name}")
+    o, lse = g.prefill_causal(q, k, v)
+    torch.cuda.synchronize()
+    tail = 256
+    rng = np.random.default_rng(933)
+    picked = {(h, i) for h in range(G) for i in range(S - tail, S)}
+    picked |= {(h, i) for h in (0, G - 1) for i in (0, 1, 255, 256, 4095, 32767, 32768)}
+    picked |= {(int(rng.integers(0, G)), int(rng.integers(0, S - tail))) for _ in range(96)}
+    rows = np.array([(0, h, i) for h, i in sorted(picked)], dtype=np.int32)
+    say(f"  oracle forward of {len(rows)} rows of query heads 0..7")
+    o_r, _ = oracle.prefill_causal_rows(p["q"], p["k"], p["v"], rows)
+    o_r_bits = bf16_bits_from_f32(o_r.astype(np.float32))                  # [n, d]
+    hsel = torch.from_numpy(rows[:, 1].astype(np.int64)).to(o.device)
+    isel = torch.from_numpy(rows[:, 2].astype(np.int64)).to(o.device)
+    o[0, isel, hsel] = to_gpu_bf16(o_r_bits)
+    say(f"prefill backward {cfg.name}")
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, do)
+    do_r = p["do"][0, rows[:, 2], rows[:, 1]]                              # [n, d]
+    D_r = oracle.stored_output_D(o_r_bits[None, :, None], do_r[None, :, None]).reshape(-1)
+    say("  oracle backward rows")
+    dq_r, lse_r, D_chk = oracle.prefill_causal_bwd_rows(p["q"], p["k"], p["v"], p["do"], rows,
+                                                        D=D_r)
+    say(f"  dq {check_grad(to_f64(dq[0, isel, hsel]), dq_r, 'long dq rows')}")
+    lse_all = np.zeros((1, H_q, S))
+    D_all = np.zeros((1, H_q, S))
+    lse_all[0, rows[:, 1], rows[:, 2]] = lse_r
+    D_all[0, rows[:, 1], rows[:, 2]] = D_chk
+    keys = sorted({S - tail, S - tail + 1, S - 129, S - 128, S - 2, S - 1,
+                   *rng.integers(S - tail, S, size=10).tolist()})
+    keys = np.array([(0, 0, j) for j in keys], dtype=np.int32)
+    rk, rv = oracle.prefill_causal_bwd_keys(p["q"], p["k"], p["v"], p["do"], lse_all, D_all, keys)
+    j = torch.from_numpy(keys[:, 2].astype(np.int64)).to(dk.device)
+    say(f"  dk {check_grad(to_f64(dk[0, j, 0]), rk, 'long dk keys')}")
+    say(f"  dv {check_grad(to_f64(dv[0, j, 0]), rv, 'long dv keys')}")
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all()
