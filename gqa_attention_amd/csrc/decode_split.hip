@@ -670,7 +670,7 @@ hipError_t launch_cb(const DecodeSplitArgs &a, hipStream_t stream) {
     const int n_hg = (GT + 16 * CB - 1) / (16 * CB);
     dim3 grid(a.units, (a.H_kv / a.hpw) * n_hg);
     if (a.fp8) {
-        if constexpr (D == 128)
+        if constexpr (D >= 64)   // (a lane's K codes are at least one 16-byte load)
             hipLaunchKernelGGL((decode_split_kernel<D, true, CB, true>), grid, dim3(kWaves * 64), 0,
                                stream, a, n_hg);
         else

@@ -249,8 +249,8 @@ int decode_paged(const void *q, const void *k_pool, const void *v_pool, const in
     if ((long)num_pages * page_size > 0x7FFFFFFFL || (long)max_blocks * page_size > 0x7FFFFFFFL)
         return fail(GQA_ERR_BAD_SHAPE,
                     "num_pages*page_size and max_blocks*page_size must fit in 31 bits");
-    if (fp8 && d != 128)
-        return fail(GQA_ERR_UNSUPPORTED, "FP8 decode head size d=%d (supported: 128)", d);
+    if (fp8 && d != 64 && d != 128)
+        return fail(GQA_ERR_UNSUPPORTED, "FP8 decode head size d=%d (supported: 64, 128)", d);
     const int S_max = max_blocks * page_size;
     Plan pl;
     int rc;

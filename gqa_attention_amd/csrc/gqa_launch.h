@@ -38,7 +38,7 @@ struct DecodeSplitArgs {
     // (page a multiple of 16; S_max = max_blocks * page).
     const int32_t *block_table;
     int page, num_pages, max_blocks;
-    // FP8 pages (paged only, d = 128): k and v are byte pools of pages of page_bytes bytes,
+    // FP8 pages (paged only, d = 64 or 128): k and v are byte pools of pages of page_bytes bytes,
     // [page][H_kv][d] E4M3 codes followed by `page` fp32 per-token scales.
     int fp8;
     size_t page_bytes;

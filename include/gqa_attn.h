@@ -346,7 +346,7 @@ int gqa_kv_quantize_fp8(const void *x, const int32_t *seqlens, const int32_t *bl
  * the power-of-two scales of gqa_kv_quantize_fp8 the results are those of
  * gqa_attn_decode_paged over bf16 pages holding the dequantised values, bit for bit.
  *
- * Supported: d = 128; page_size a multiple of 16.
+ * Supported: d in {64, 128}; page_size a multiple of 16.
  */
 int gqa_attn_decode_paged_fp8(const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *block_table, const int32_t *seqlens, void *o,

@@ -250,7 +250,7 @@ def test_kv_quantize_fp8_rejects_before_launch(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=64), UNSUP), (dict(page=24), SHAPE), (dict(tbl=None), NULLP), (dict(q=MIS), ALIGN),
+    (dict(d=32), UNSUP), (dict(page=24), SHAPE), (dict(tbl=None), NULLP), (dict(q=MIS), ALIGN),
     (dict(ws=None), WS), (dict(H_kv=3), SHAPE),
 ])
 def test_decode_paged_fp8_rejects_before_launch(lib, kw, code):

@@ -121,6 +121,28 @@ def test_fp8_decode_shapes(case, gpu_available):
     say(f"  {fp8_decode_case(p, H_kv, 128, splits)}")
 
 
+D64_CASES = [
+    # (B, T_q, H_q, H_kv, page, lengths, num_splits), head size 64
+    (3, 1, 16, 2, 16, (1, 1200), 4),
+    (2, 1, 8, 1, 32, (300, 2500), 0),      # MQA
+    (2, 1, 32, 1, 16, (100, 900), 2),      # G = 32: two workgroup rows per KV head
+    (2, 3, 16, 4, 48, (2, 700), 0),        # T_q = 3 (G * T_q = 12 rows), pages of 48
+]
+
+
+@pytest.mark.parametrize("case", D64_CASES, ids=[str(c) for c in D64_CASES])
+def test_fp8_decode_head_size_64(case, gpu_available):
+    B, T, H_q, H_kv, page, ragged, splits = case
+    p = paged_decode_inputs(B, H_q, H_kv, 64, page, ragged=ragged, seed=740 + H_q + page + T,
+                            nan_fill=False)
+    q = None
+    if T > 1:
+        rng = np.random.default_rng(741)
+        q = bf16_bits_from_f32(rng.standard_normal((B, T, H_q, 64)).astype(np.float32))
+    say(f"fp8 decode d=64 {case} seqlens={p['seqlens'].tolist()}")
+    say(f"  {fp8_decode_case(p, H_kv, 64, splits, q=q)}")
+
+
 def test_fp8_decode_llama_s32768(gpu_available):
     """The Llama3-70B decode (S_kv = 32768, 64 query heads, 8 KV heads, 32 splits) over
     FP8 pages of 16 tokens in permuted pool order."""
