@@ -69,9 +69,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("00fd50e5465ce319", 143_033_338),
-    "lse_merge": ("1dc58e43411ea0e2", 9_527_214),
-    "prefill_causal": ("1def1b795a174f6f", 421_924_486),
+    "decode_split": ("908644572f0038c2", 143_011_157),
+    "lse_merge": ("b638e4490886db4b", 9_527_204),
+    "prefill_causal": ("0bf4cd96fc05bdd6", 422_159_846),
 }
 
 
