@@ -237,3 +237,16 @@ def test_decode_kv_reads_independent_of_group_size(gpu_available):
         torch.cuda.synchronize()
         o_ref, lse_ref = oracle.decode(q, inp["k"], inp["v"])
         check(to_f64(o), to_f64(lse), o_ref, lse_ref, f"H_q={q.shape[1]}")
+
+
+def test_decode_one_million_keys(gpu_available):
+    """A single sequence of 2^20 cached keys (MQA: 8 query heads on one KV head, d = 128; the
+    cache is 512 MiB) with the automatic split plan (256 partitions of 4096 keys), and two
+    sequences of 2^20 and 2^20 - 5 keys with 64 requested splits (a ragged tail)."""
+    S = 1 << 20
+    for B, lens, splits in ((1, None, 0), (2, (S - 5, S), 64)):
+        inp = decode_inputs(B, 8, 1, 128, S_max=None if lens else S, seed=130 + B, ragged=lens)
+        say(f"decode B={B} S_max={inp['S_max']} seqlens={inp['seqlens'].tolist()} splits={splits}")
+        o, lse = run_decode(inp, splits)
+        o_ref, lse_ref = oracle_decode(inp)
+        say(f"  {check(to_f64(o), to_f64(lse), o_ref, lse_ref, f'S=2^20 B={B}')}")
