@@ -201,10 +201,18 @@ gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Pl
     return m;
 }
 
+// A paged cache for prefill (block_table null: contiguous).
+struct PagedCache {
+    const int32_t *block_table = nullptr;
+    int page = 0, num_pages = 0, max_blocks = 0;
+};
+
 // Causal prefill of T query rows (tokens q_start .. q_start + T - 1) against a cache of
-// S rows per sequence; the callers have checked T > 0, S > 0 and 0 <= q_start <= S - T.
+// S rows per sequence; the callers have checked T > 0, S > 0 and 0 <= q_start <= S - T
+// (and, for a paged cache, its pool and table).
 int prefill(const void *q, const void *k, const void *v, void *o, float *lse, int B, int T,
-            int q_start, int S, int H_q, int H_kv, int d, float softmax_scale, void *stream) {
+            int q_start, int S, int H_q, int H_kv, int d, float softmax_scale, void *stream,
+            const PagedCache &pc = PagedCache()) {
     int rc;
     if ((rc = check_heads(B, H_q, H_kv))) return rc;
     if (d != 128) return fail(GQA_ERR_UNSUPPORTED, "prefill head size d=%d (supported: 128)", d);
@@ -229,6 +237,10 @@ int prefill(const void *q, const void *k, const void *v, void *o, float *lse, in
     a.T = T;
     a.q_start = q_start;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.block_table = pc.block_table;
+    a.page = pc.page;
+    a.num_pages = pc.num_pages;
+    a.max_blocks = pc.max_blocks;
     if ((rc = hip_status(gqa::launch_prefill_causal(a, static_cast<hipStream_t>(stream)),
                          "prefill_causal")))
         return rc;
@@ -510,6 +522,42 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
                     S_kv - T_q);
     return prefill(q, k_cache, v_cache, o, lse, B, T_q, q_start, S_kv, H_q, H_kv, d,
                    softmax_scale, stream);
+}
+
+int gqa_attn_prefill_chunk_paged(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *block_table, void *o, float *lse, int B, int T_q,
+                                 int q_start, int H_q, int H_kv, int d, int page_size,
+                                 int num_pages, int max_blocks, float softmax_scale,
+                                 void *stream) {
+    if (T_q <= 0 || q_start < 0)
+        return fail(GQA_ERR_BAD_SHAPE, "T_q=%d must be positive and q_start=%d non-negative", T_q,
+                    q_start);
+    if (page_size < kPagedTile || page_size % kPagedTile != 0 || page_size > kMaxPage)
+        return fail(GQA_ERR_BAD_SHAPE, "page_size=%d must be a multiple of %d in [%d, %d]",
+                    page_size, kPagedTile, kPagedTile, kMaxPage);
+    if (num_pages <= 0 || max_blocks <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "num_pages=%d and max_blocks=%d must be positive",
+                    num_pages, max_blocks);
+    if ((long)num_pages * page_size > 0x7FFFFFFFL || (long)max_blocks * page_size > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE,
+                    "num_pages*page_size and max_blocks*page_size must fit in 31 bits");
+    const long keys = (long)q_start + T_q;        // keys the chunk sees: [0, q_start + T_q)
+    const long blocks = (keys + page_size - 1) / page_size;
+    if (blocks > max_blocks)
+        return fail(GQA_ERR_BAD_SHAPE, "q_start+T_q=%ld keys need %ld blocks, the table has %d",
+                    keys, blocks, max_blocks);
+    if (blocks > gqa::kPrefillMaxPages)
+        return fail(GQA_ERR_UNSUPPORTED, "q_start+T_q=%ld keys span %ld blocks (at most %d: use "
+                    "larger pages)", keys, blocks, gqa::kPrefillMaxPages);
+    if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
+    if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
+    PagedCache pc;
+    pc.block_table = block_table;
+    pc.page = page_size;
+    pc.num_pages = num_pages;
+    pc.max_blocks = max_blocks;
+    return prefill(q, k_pool, v_pool, o, lse, B, T_q, q_start, (int)keys, H_q, H_kv, d,
+                   softmax_scale, stream, pc);
 }
 
 size_t gqa_prefill_bwd_workspace_bytes(int B, int S, int H_q, int H_kv, int d) {

@@ -85,7 +85,15 @@ struct PrefillArgs {
     int B, S, H_q, H_kv, d;
     int T, q_start;
     float scale_log2;
+    // Paged cache when block_table is not null: k and v are pools [num_pages][page][H_kv][d]
+    // and key t of sequence b is row t % page of page block_table[b * max_blocks + t / page]
+    // (page a multiple of 16; at most kPrefillMaxPages blocks of a sequence are visible).
+    const int32_t *block_table;
+    int page, num_pages, max_blocks;
 };
+
+// Blocks of one sequence a paged prefill can see (its table row is staged in LDS).
+constexpr int kPrefillMaxPages = 8192;
 
 // Backward of whole-prompt causal prefill: q, o, dout, dq [B][S][H_q][d]; k, v, dk, dv
 // [B][S][H_kv][d] (bf16); lse [B][H_q][S] (natural log, the forward's).  The launcher lays

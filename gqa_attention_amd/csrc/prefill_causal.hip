@@ -37,6 +37,11 @@
 // Scores are kept in log2 units (s2 = acc * tau * log2(e), one fp32 multiply
 // folded into the exponent's FMA; V07 section 2, exp2 trick).
 //
+// Paged cache (the Paged instantiation; V07 sections 16-17, block table and pool): the
+// sequence's block-table row is staged in LDS when the workgroup starts, and each DMA
+// instruction of a tile, which covers four consecutive rows of one page, takes its page from
+// it; the tiles land in LDS exactly as from a contiguous cache, so the arithmetic is the same.
+//
 // Grid: one workgroup per (q-block, sequence, query head), heaviest q-blocks
 // first (V07 section 12, causal-aware scheduling).  Consecutive workgroups are
 // dispatched round-robin over the 8 XCDs; the index is remapped so that the G
@@ -102,6 +107,40 @@ __device__ __forceinline__ void dma_tile(uint8_t *lds, int dst, const uint16_t *
         const uint32_t lds_dst = (uint32_t)(uintptr_t)(lds + dst + (32 * i + 4 * w) * kRowBytes);
         // Issued as assembly so that the compiler does not add a wait for this DMA before
         // every later LDS read: the tile loop's own waits and barriers order the buffers.
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_dst))
+                     : "memory");
+    }
+}
+
+// The same DMA from a paged cache: wave w's four rows r .. r + 3 (r = k0 + 32 i + 4 w, a
+// multiple of 4) lie in one page, since pages hold a multiple of 16 rows, so each DMA
+// instruction reads from one page: row r % page of page tbl[r / page] (the sequence's table
+// row, staged in LDS), its lane l fetching row l / 16 of the four and the chunk the layout
+// puts at position l % 16 (voff).  Rows at or past S, and pages outside the pool, arrive as
+// zeros and are not read.
+__device__ __forceinline__ void dma_tile_paged(uint8_t *lds, int dst, const uint16_t *pool,
+                                               size_t kv_row, int k0, int S, uint32_t voff, int w,
+                                               const int *tbl, int page, int num_pages) {
+    const uint32_t row_bytes = (uint32_t)kv_row * 2u;
+#pragma unroll
+    for (int i = 0; i < kDmaPerTile; ++i) {
+        const int r = k0 + 32 * i + 4 * w;
+        uint32_t bytes = 0;
+        uint64_t base = (uint64_t)pool;
+        if (r < S) {
+            const int pg = __builtin_amdgcn_readfirstlane(tbl[r / page]);
+            if ((unsigned)pg < (unsigned)num_pages) {
+                bytes = (uint32_t)min(4, S - r) * row_bytes;
+                base = (uint64_t)(pool + ((size_t)pg * page + r % page) * kv_row);
+            }
+        }
+        bytes = __builtin_amdgcn_readfirstlane(bytes);
+        const u32x4 rsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) & 0xFFFFu,
+                            bytes, 0x00020000u};
+        const uint32_t lds_dst = (uint32_t)(uintptr_t)(lds + dst + (32 * i + 4 * w) * kRowBytes);
         asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                      :
                      : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_dst))
@@ -215,9 +254,22 @@ struct WaveCtx {
     int mask_from;            // first step holding a key past some row's diagonal
     int w, row, hf;           // row: this lane's query position q_start + i
     float c;
-    uint32_t koff, voff;   // DMA: this lane's byte offset within its 32-row group
+    uint32_t koff, voff;   // DMA: this lane's byte offset within its 32-row group (paged:
+                           // within its wave's four rows)
     FragAddr fa;
+    const int *tbl;        // paged: the sequence's block-table row, in LDS
+    int page, num_pages;
 };
+
+// One K or V tile DMA, from the contiguous cache or through the block table.
+template <bool Paged>
+__device__ __forceinline__ void dma(const WaveCtx &x, int dst, const uint16_t *base, int k0,
+                                    uint32_t off) {
+    if constexpr (Paged)
+        dma_tile_paged(x.lds, dst, base, x.kv_row, k0, x.S, off, x.w, x.tbl, x.page, x.num_pages);
+    else
+        dma_tile(x.lds, dst, base, x.kv_row, k0, x.S, off, x.w);
+}
 
 struct RowState {
     f32x16 o[4];
@@ -261,29 +313,30 @@ __device__ __forceinline__ void half_step(const WaveCtx &x, int u, const f32x16 
 // refilled only after the next barrier.  The DMA is issued on every tile (past the end
 // it only zero-fills a free buffer), so each wave has exactly 2 * kDmaPerTile of them
 // per tile.
-template <int KI>
+template <int KI, bool Paged>
 __device__ __forceinline__ void tile_step(const WaveCtx &x, int kb, f32x16 &sa, f32x16 &sb,
                                           const bf16x8 (&qf)[8], RowState &st) {
     constexpr int kCur = kKBuf + KI * kTileBytes;
     constexpr int kNext = kKBuf + ((KI + 1) % kNK) * kTileBytes;
     constexpr int kFree = kKBuf + ((KI + 3) % kNK) * kTileBytes;
     const int vcur = kVBuf + (kb % kNV) * kTileBytes;
-    dma_tile(x.lds, kFree, x.kbase, x.kv_row, (kb + 3) * kBc, x.S, x.koff, x.w);
+    dma<Paged>(x, kFree, x.kbase, (kb + 3) * kBc, x.koff);
     uint32_t va[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) va[dt] = x.fa.v[dt] + (uint32_t)vcur;
     half_step(x, 2 * kb, sa, sb, x.lds + kCur + kHalf * kRowBytes, x.lds, va, qf, st);
-    dma_tile(x.lds, kVBuf + ((kb + 2) % kNV) * kTileBytes, x.vbase, x.kv_row, (kb + 2) * kBc,
-             x.S, x.voff, x.w);
+    dma<Paged>(x, kVBuf + ((kb + 2) % kNV) * kTileBytes, x.vbase, (kb + 2) * kBc, x.voff);
     half_step(x, 2 * kb + 1, sb, sa, x.lds + kNext, x.lds + kHalf * kRowBytes, va, qf, st);
     // vmcnt(2 * kDmaPerTile): only this tile's DMA may still be in flight
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerTile));
     __syncthreads();
 }
 
+template <bool Paged>
 __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs a, int n_qb,
                                                                      int remap) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    __shared__ int tbl[Paged ? kPrefillMaxPages : 1];   // paged: the sequence's table row
 
     const int G = a.H_q / a.H_kv;
     // ---- workgroup -> (q-block, b, h) ----
@@ -313,8 +366,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     WaveCtx x;
     x.lds = smem;
     x.kv_row = (size_t)a.H_kv * D;
-    x.kbase = a.k + ((size_t)b * a.S * a.H_kv + hk) * D;
-    x.vbase = a.v + ((size_t)b * a.S * a.H_kv + hk) * D;
+    if constexpr (Paged) {
+        x.kbase = a.k + (size_t)hk * D;          // the pools, head hk
+        x.vbase = a.v + (size_t)hk * D;
+    } else {
+        x.kbase = a.k + ((size_t)b * a.S * a.H_kv + hk) * D;
+        x.vbase = a.v + ((size_t)b * a.S * a.H_kv + hk) * D;
+    }
+    x.tbl = tbl;
+    x.page = a.page;
+    x.num_pages = a.num_pages;
     // keys past the chunk's last token are never visible: they are not even read, so a
     // cache row after it may hold anything (a zero row times a zero weight adds nothing)
     x.S = qs + a.T;
@@ -331,7 +392,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     x.c = fmaxf(a.scale_log2, 1e-30f);
     {
         const int lr = 4 * w + lane / 16;   // DMA row within each 32-row group
-        const uint32_t rowb = (uint32_t)(lr * x.kv_row * 2);
+        // (paged: each DMA instruction starts at the wave's own first row)
+        const uint32_t rowb = (uint32_t)((Paged ? lane / 16 : lr) * x.kv_row * 2);
         x.koff = rowb + 16u * (uint32_t)((lane & 15) ^ k_swz(lr));
         x.voff = rowb + 16u * (uint32_t)((lane & 15) ^ v_swz(lr));
 #pragma unroll
@@ -365,11 +427,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     st.mx = neg_inf();
     f32x16 sa, sb;
 
+    if constexpr (Paged) {
+        // the table entries of the blocks holding keys [0, S), before the first DMA
+        const int n = (x.S + a.page - 1) / a.page;
+        const int32_t *row = a.block_table + (size_t)b * a.max_blocks;
+        for (int i = threadIdx.x; i < n; i += kThreads) tbl[i] = row[i];
+        __syncthreads();
+    }
     // prologue: K(0..2) and V(0..1) into LDS, then the scores of the first step
-    for (int t = 0; t < 3; ++t)
-        dma_tile(smem, kKBuf + t * kTileBytes, x.kbase, x.kv_row, t * kBc, x.S, x.koff, w);
-    for (int t = 0; t < 2; ++t)
-        dma_tile(smem, kVBuf + t * kTileBytes, x.vbase, x.kv_row, t * kBc, x.S, x.voff, w);
+    for (int t = 0; t < 3; ++t) dma<Paged>(x, kKBuf + t * kTileBytes, x.kbase, t * kBc, x.koff);
+    for (int t = 0; t < 2; ++t) dma<Paged>(x, kVBuf + t * kTileBytes, x.vbase, t * kBc, x.voff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (x.n_sub > 0) {
@@ -380,14 +447,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
 
     int kb = 0;
     for (; kb + 3 < x.n_kb; kb += 4) {
-        tile_step<0>(x, kb, sa, sb, qf, st);
-        tile_step<1>(x, kb + 1, sa, sb, qf, st);
-        tile_step<2>(x, kb + 2, sa, sb, qf, st);
-        tile_step<3>(x, kb + 3, sa, sb, qf, st);
+        tile_step<0, Paged>(x, kb, sa, sb, qf, st);
+        tile_step<1, Paged>(x, kb + 1, sa, sb, qf, st);
+        tile_step<2, Paged>(x, kb + 2, sa, sb, qf, st);
+        tile_step<3, Paged>(x, kb + 3, sa, sb, qf, st);
     }
-    if (kb < x.n_kb) tile_step<0>(x, kb, sa, sb, qf, st);
-    if (kb + 1 < x.n_kb) tile_step<1>(x, kb + 1, sa, sb, qf, st);
-    if (kb + 2 < x.n_kb) tile_step<2>(x, kb + 2, sa, sb, qf, st);
+    if (kb < x.n_kb) tile_step<0, Paged>(x, kb, sa, sb, qf, st);
+    if (kb + 1 < x.n_kb) tile_step<1, Paged>(x, kb + 1, sa, sb, qf, st);
+    if (kb + 2 < x.n_kb) tile_step<2, Paged>(x, kb + 2, sa, sb, qf, st);
     __builtin_amdgcn_s_waitcnt(0);   // no DMA left in flight at exit
 
     // ---- epilogue: O = O^T / lw -> bf16, LSE = ln2 * (m + log2 l) ----
@@ -417,8 +484,12 @@ hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream) {
     const long units = (long)n_qb * a.B * a.H_kv;
     const int remap = (units % kXcds) == 0;
     const long blocks = units * (a.H_q / a.H_kv);
-    hipLaunchKernelGGL(prefill_causal_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
-                       n_qb, remap);
+    if (a.block_table)
+        hipLaunchKernelGGL(prefill_causal_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a, n_qb, remap);
+    else
+        hipLaunchKernelGGL(prefill_causal_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a, n_qb, remap);
     return hipGetLastError();
 }
 

@@ -298,6 +298,37 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
                            int d, float softmax_scale, void *stream);
 
 /*
+ * gqa_attn_prefill_chunk_paged -- gqa_attn_prefill_chunk over a paged KV cache:
+ * key t of sequence b is row t % page_size of page block_table[b][t / page_size]
+ * of the pools (V07, section 16: block pool, block table, logical-token-to-page
+ * map; section 17: the attention kernel reads the cache through the table).  The
+ * chunk's T_q query rows are the tokens q_start .. q_start + T_q - 1 of every
+ * sequence of the batch and see keys j <= q_start + i, so the keys read are
+ * [0, q_start + T_q) of each sequence.  The sequence's table row is staged on
+ * chip and each K/V tile is fetched page by page; the results equal those of
+ * gqa_attn_prefill_chunk on the gathered cache bit for bit.
+ *
+ *   q           [B, T_q, H_q, d]                   bf16, device, read-only
+ *   k_pool      [num_pages, page_size, H_kv, d]    bf16, device, read-only
+ *   v_pool      [num_pages, page_size, H_kv, d]    bf16, device, read-only (one page
+ *               numbering with k_pool)
+ *   block_table [B, max_blocks] int32, device, read-only; only the entries of blocks
+ *               holding keys [0, q_start + T_q) are read.  An entry outside
+ *               [0, num_pages) is not dereferenced: its keys read as zeros.  Pool
+ *               rows of those blocks at or past q_start + T_q are never read.
+ *   o, lse      [B, T_q, H_q, d] bf16, [B, H_q, T_q] fp32, device, written
+ *
+ * Requires T_q >= 1, q_start >= 0, ceil((q_start + T_q) / page_size) <= max_blocks
+ * and <= 8192 (GQA_ERR_UNSUPPORTED past it: use larger pages); page_size a multiple
+ * of 16 in [16, 65536].  Supported: d = 128.
+ */
+int gqa_attn_prefill_chunk_paged(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *block_table, void *o, float *lse, int B, int T_q,
+                                 int q_start, int H_q, int H_kv, int d, int page_size,
+                                 int num_pages, int max_blocks, float softmax_scale,
+                                 void *stream);
+
+/*
  * FP8 (E4M3) paged KV cache (V07, section 17.7: a per-token scale kept with each
  * page, its page_size scalars appended after the page's rows, dequantisation fused
  * into the load; section 9.5: E4M3 values, fp32 accumulation).  A pool is an array
