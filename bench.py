@@ -38,7 +38,9 @@ Measured after the timed region, each in its own graph loop (not part of a step)
                     (gqa_attn_decode_tokens), beside the same call through the
                     chunked-prefill kernel;
   prefill_chunk     the last 2048 tokens of the 8192-token prompt as one chunk
-                    against the whole cache (gqa_attn_prefill_chunk).
+                    against the whole cache (gqa_attn_prefill_chunk), and the same
+                    over 16-token pages at permuted pool positions
+                    (gqa_attn_prefill_chunk_paged).
 """
 import argparse
 import json
@@ -350,6 +352,27 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
         "workload": f"Llama3-70B chunked prefill: T_q={T} rows at q_start={q_start}, "
                     f"S_kv={pc.S}", "flop": flop, "ms": round(ms, 4), "tflops": round(tf, 1),
         "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    # the same chunk over a paged cache: 16-token pages at permuted pool positions
+    page = 16
+    nb = pc.S // page
+    order = torch.randperm(nb + 3, generator=torch.Generator().manual_seed(pc.seed + 2)).cuda()
+    kpool = torch.zeros((nb + 3, page, pc.H_kv, pc.d), dtype=torch.bfloat16, device="cuda")
+    vpool = torch.zeros_like(kpool)
+    kpool[order[:nb]] = k_p[0].view(nb, page, pc.H_kv, pc.d)
+    vpool[order[:nb]] = v_p[0].view(nb, page, pc.H_kv, pc.d)
+    table = order[:nb].to(torch.int32).view(1, nb).contiguous()
+    op_c, lp_c = torch.empty_like(qc), torch.empty_like(lc)
+
+    def chunk_paged_call(i):
+        g.prefill_chunk_paged(qc, kpool, vpool, table, q_start, out=op_c, lse=lp_c)
+
+    chunk_paged_call(0)
+    ms_pg = graph_ms(chunk_paged_call, K)
+    tf_pg = flop / (ms_pg * 1e-3) / 1e12
+    res["prefill_chunk"]["paged"] = {
+        "page_size": page, "ms": round(ms_pg, 4), "tflops": round(tf_pg, 1),
+        "frac_bf16_peak": round(tf_pg / BF16_PEAK_TFLOPS, 4), "vs_contiguous": round(ms / ms_pg, 3)}
+    del kpool, vpool
     # backward of the causal prefill at the Llama workload (S = 8192): the forward's O and
     # LSE, a random output gradient, the four launches of one backward call per step
     do_p = torch.randn(q_p.shape, device="cuda", generator=torch.Generator(
