@@ -71,9 +71,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("908644572f0038c2", 143_011_157),
-    "lse_merge": ("b638e4490886db4b", 9_527_204),
-    "prefill_causal": ("0bf4cd96fc05bdd6", 422_159_846),
+    "decode_split": ("24089783a493446d", 143_011_277),
+    "lse_merge": ("7bcd1846637d3cfa", 9_527_136),
+    "prefill_causal": ("4f51172ba4721878", 422_017_270),
 }
 
 
