@@ -42,8 +42,9 @@ def test_graph_replays_match_eager(gpu_available):
 
 
 def test_graph_replays_match_eager_widened_paths(gpu_available):
-    """Paged, multi-token and FP8 decode (with the quantiser in the graph) and the prefill
-    backward, captured together: every replay equals the eager calls bit for bit."""
+    """Paged, multi-token and FP8 decode (with the quantiser in the graph), the chunked
+    prefill over pages and the prefill backward, captured together: every replay equals the
+    eager calls bit for bit."""
     B, H_q, H_kv, d, page = 2, 16, 2, 128, 16
     p = paged_decode_inputs(B, H_q, H_kv, d, page, ragged=(40, 700), seed=33)
     q, kp, vp = (to_gpu_bf16(p[x]) for x in ("q", "k_pool", "v_pool"))
@@ -60,6 +61,15 @@ def test_graph_replays_match_eager_widened_paths(gpu_available):
     first_pages = ftbl[:, 0].long()          # every sequence has at least 40 live tokens
     pinp = prefill_bwd_inputs(1, 200, 8, 2, 128, seed=37)
     pq, pk, pv, pdo = (to_gpu_bf16(pinp[x]) for x in ("q", "k", "v", "do"))
+    # the prompt's last 80 tokens as a chunk over 16-token pages (13 pages, permuted)
+    cq = pq[:, 120:].contiguous()
+    pages = torch.randperm(13, generator=torch.Generator().manual_seed(38)).cuda()
+    kpool = torch.zeros((13, page, 2, d), dtype=torch.bfloat16, device="cuda")
+    vpool = torch.zeros_like(kpool)
+    kpool.view(13 * page, 2, d)[:200] = pk[0]
+    vpool.view(13 * page, 2, d)[:200] = pv[0]
+    kpool, vpool = kpool[pages], vpool[pages]            # page i of the prompt -> slot
+    ctbl = torch.argsort(pages).to(torch.int32).view(1, 13).contiguous()
     say("graph capture: paged, multi-token, FP8 decode, quantiser, prefill backward")
 
     def run(bufs):
@@ -70,6 +80,7 @@ def test_graph_replays_match_eager_widened_paths(gpu_available):
         g.kv_quantize_fp8(vc, ftbl, csl, pool=bufs["fv"], page_size=page)
         g.decode_paged_fp8(q, bufs["fk"], bufs["fv"], ftbl, csl, page_size=page, H_kv=H_kv,
                            num_splits=3, out=bufs["fo"], lse=bufs["flse"], workspace=bufs["ws_f"])
+        g.prefill_chunk_paged(cq, kpool, vpool, ctbl, 120, out=bufs["co"], lse=bufs["clse"])
         g.prefill_causal(pq, pk, pv, out=bufs["so"], lse=bufs["slse"])
         g.prefill_causal_bwd(pq, pk, pv, bufs["so"], bufs["slse"], pdo, workspace=bufs["ws_b"],
                              out=(bufs["dq"], bufs["dk"], bufs["dv"]))
@@ -86,6 +97,7 @@ def test_graph_replays_match_eager_widened_paths(gpu_available):
             "fv": torch.empty((B * nb, pb), dtype=torch.uint8, device="cuda"),
             "fo": torch.empty_like(q), "flse": torch.empty((B, H_q), dtype=torch.float32, device="cuda"),
             "ws_f": g.decode_workspace(B, H_q, H_kv, d, nb * page, 3),
+            "co": torch.empty_like(cq), "clse": torch.empty((1, 8, 80), dtype=torch.float32, device="cuda"),
             "so": torch.empty_like(pq), "slse": torch.empty((1, 8, 200), dtype=torch.float32, device="cuda"),
             "ws_b": g.prefill_bwd_workspace(1, 200, 8, 2, 128),
             "dq": torch.empty_like(pq), "dk": torch.empty_like(pk), "dv": torch.empty_like(pv),
@@ -100,7 +112,8 @@ def test_graph_replays_match_eager_widened_paths(gpu_available):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         run(cap)
-    outs = ("po", "plse", "to", "tlse", "fk", "fv", "fo", "flse", "so", "slse", "dq", "dk", "dv")
+    outs = ("po", "plse", "to", "tlse", "fk", "fv", "fo", "flse", "co", "clse", "so", "slse", "dq",
+            "dk", "dv")
     for r in range(3):
         for name in outs:                    # eager work between replays
             t = cap[name]
