@@ -83,6 +83,8 @@ def load_library(path=LIBRARY):
     L.gqa_fp8_page_bytes.restype = cs
     L.gqa_kv_quantize_fp8.argtypes = [vp, i32p, i32p, vp, ci, ci, ci, ci, ci, ci, ci, vp]
     L.gqa_kv_quantize_fp8.restype = ci
+    L.gqa_kv_dequantize_fp8.argtypes = [vp, i32p, i32p, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    L.gqa_kv_dequantize_fp8.restype = ci
     L.gqa_attn_decode_paged_fp8.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci,
                                             ci, ci, ci, cf, ci, vp, cs, vp]
     L.gqa_attn_decode_paged_fp8.restype = ci
@@ -435,6 +437,22 @@ def kv_quantize_fp8(x, block_table, seqlens=None, pool=None, num_pages=None, pag
         _ptr(x), _ptr(seqlens), _ptr(block_table), _ptr(pool), B, S_max, H_kv, d, page_size,
         pool.shape[0], block_table.shape[1], _stream(x.device)))
     return pool
+
+
+def kv_dequantize_fp8(pool, block_table, S_max, H_kv, d, seqlens=None, page_size=16, out=None):
+    """The live tokens of an FP8 pool (uint8 [num_pages, page bytes]) as a bf16 cache
+    [B, S_max, H_kv, d] (``out``, else a new zero-filled tensor); returns it."""
+    _need(block_table, "block_table", torch.int32, 2)
+    B = block_table.shape[0]
+    pb = fp8_page_bytes(page_size, H_kv, d)
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or pool.shape[1] != pb or not pool.is_contiguous():
+        raise ValueError(f"pool must be contiguous uint8 [num_pages, {pb}]")
+    x = torch.zeros((B, S_max, H_kv, d), dtype=torch.bfloat16, device=pool.device) if out is None else out
+    _need(x, "out", torch.bfloat16, 4)
+    _check(load_library().gqa_kv_dequantize_fp8(
+        _ptr(pool), _ptr(seqlens), _ptr(block_table), _ptr(x), B, S_max, H_kv, d, page_size,
+        pool.shape[0], block_table.shape[1], _stream(pool.device)))
+    return x
 
 
 def decode_paged_fp8(q, k_pool, v_pool, block_table, seqlens=None, page_size=16, H_kv=None,

@@ -437,6 +437,47 @@ int gqa_kv_quantize_fp8(const void *x, const int32_t *seqlens, const int32_t *bl
     return ok();
 }
 
+int gqa_kv_dequantize_fp8(const void *pool, const int32_t *seqlens, const int32_t *block_table,
+                          void *x, int B, int S_max, int H_kv, int d, int page_size, int num_pages,
+                          int max_blocks, void *stream) {
+    if (B <= 0 || S_max <= 0 || H_kv <= 0 || d <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "B=%d, S_max=%d, H_kv=%d, d=%d must be positive", B, S_max,
+                    H_kv, d);
+    if (d % 8 != 0) return fail(GQA_ERR_UNSUPPORTED, "FP8 dequantisation needs d %% 8 == 0 (d=%d)", d);
+    if (page_size <= 0 || num_pages <= 0 || max_blocks <= 0)
+        return fail(GQA_ERR_BAD_SHAPE, "page_size=%d, num_pages=%d, max_blocks=%d must be positive",
+                    page_size, num_pages, max_blocks);
+    if ((long)max_blocks * page_size < S_max)
+        return fail(GQA_ERR_BAD_SHAPE, "max_blocks*page_size=%ld is below S_max=%d",
+                    (long)max_blocks * page_size, S_max);
+    if ((long)B * S_max > 0x7FFFFFFFL || (long)H_kv * d > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*S_max and H_kv*d must fit in 31 bits");
+    int rc;
+    if ((rc = check_bf16(x, "x"))) return rc;
+    if (!pool) return fail(GQA_ERR_NULL_POINTER, "pool is NULL");
+    if (!aligned(pool, 16)) return fail(GQA_ERR_ALIGNMENT, "pool is not 16-byte aligned");
+    if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
+    if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
+    if (seqlens && !aligned(seqlens, 4)) return fail(GQA_ERR_ALIGNMENT, "seqlens misaligned");
+    gqa::KvDequantArgs a;
+    a.pool = static_cast<const uint8_t *>(pool);
+    a.seqlens = seqlens;
+    a.block_table = block_table;
+    a.x = static_cast<uint16_t *>(x);
+    a.B = B;
+    a.S_max = S_max;
+    a.H_kv = H_kv;
+    a.d = d;
+    a.page = page_size;
+    a.num_pages = num_pages;
+    a.max_blocks = max_blocks;
+    a.page_bytes = gqa_fp8_page_bytes(page_size, H_kv, d);
+    if ((rc = hip_status(gqa::launch_kv_dequantize_fp8(a, static_cast<hipStream_t>(stream)),
+                         "kv_dequantize_fp8")))
+        return rc;
+    return ok();
+}
+
 int gqa_decode_tokens_plan(int B, int T_q, int H_q, int H_kv, int d, int S_max, int num_splits,
                            int *partitions_out, int *states_out, size_t *workspace_bytes_out) {
     Plan pl;

@@ -58,6 +58,20 @@ struct KvQuantArgs {
 
 hipError_t launch_kv_quantize_fp8(const KvQuantArgs &a, hipStream_t stream);
 
+// The inverse: token t < len(b) of sequence b is read from row t % page of page
+// block_table[b][t / page] of an FP8 pool and written, dequantised, to x [B][S_max][H_kv][d]
+// (a page outside the pool gives a zero row; rows at or past len(b) are not written).
+struct KvDequantArgs {
+    const uint8_t *pool;
+    const int32_t *seqlens;     // [B] or nullptr (= S_max)
+    const int32_t *block_table; // [B][max_blocks]
+    uint16_t *x;
+    int B, S_max, H_kv, d, page, num_pages, max_blocks;
+    size_t page_bytes;
+};
+
+hipError_t launch_kv_dequantize_fp8(const KvDequantArgs &a, hipStream_t stream);
+
 // Partial states to merge for (b, r), r = h * T + i the row of query head h, token i:
 //   seg != nullptr (decode workspace): states p < seg[2b+1], at index
 //     (seg[2b] + p) * state_stride + r * head_stride;

@@ -11,6 +11,8 @@
 //
 // One wave quantises one token row: a pass for max |x|, a wave reduction, then the codes.
 // This writes the cache (the step upstream of attention); the attention kernels only read.
+// The inverse (kv_dequantize_fp8) writes a pool's live tokens back as a bf16 cache, so that
+// kernels reading bf16 -- the chunked prefill -- can run on an FP8 cache.
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -80,7 +82,50 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void kv_quantize_fp8_kernel(Kv
             __builtin_amdgcn_ldexpf(1.f, e);
 }
 
+// The inverse, one wave per token row: eight codes at a time become bf16 (exactly: every
+// E4M3 value is a bfloat16), are multiplied by the row's power-of-two scale in fp32 (exact)
+// and written as bf16 (exact again, so the row is the dequantised cache the decode reads).
+__global__ __launch_bounds__(kWavesPerBlock * 64) void kv_dequantize_fp8_kernel(KvDequantArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long tok = (long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tok >= (long)a.B * a.S_max) return;          // (whole waves)
+    const int b = (int)(tok / a.S_max), t = (int)(tok % a.S_max);
+    const int len = a.seqlens ? min(max(a.seqlens[b], 0), a.S_max) : a.S_max;
+    if (t >= len) return;
+    const int pg = a.block_table[(size_t)b * a.max_blocks + t / a.page];
+    const int W = a.H_kv * a.d;                       // values per token row (a multiple of 8)
+    uint16_t *row = a.x + ((size_t)b * a.S_max + t) * W;
+    if (pg < 0 || pg >= a.num_pages) {                // a page outside the pool reads as zeros
+        for (int c = lane * 8; c < W; c += 512) *reinterpret_cast<u32x4 *>(row + c) = u32x4{0, 0, 0, 0};
+        return;
+    }
+    const uint8_t *page_base = a.pool + (size_t)pg * a.page_bytes;
+    const uint8_t *src = page_base + (size_t)(t % a.page) * W;
+    const float s = *reinterpret_cast<const float *>(page_base + (size_t)a.page * W + 4 * (t % a.page));
+    for (int c = lane * 8; c < W; c += 512) {
+        const u32x2 codes = *reinterpret_cast<const u32x2 *>(src + c);
+        u32x4 out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes[h], 1.f, false);
+            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes[h], 1.f, true);
+            const uint32_t wl = __builtin_bit_cast(uint32_t, lo), wh = __builtin_bit_cast(uint32_t, hi);
+            out[2 * h] = pack_bf16x2(bf16_lo(wl) * s, bf16_hi(wl) * s);
+            out[2 * h + 1] = pack_bf16x2(bf16_lo(wh) * s, bf16_hi(wh) * s);
+        }
+        *reinterpret_cast<u32x4 *>(row + c) = out;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_kv_dequantize_fp8(const KvDequantArgs &a, hipStream_t stream) {
+    const long toks = (long)a.B * a.S_max;
+    hipLaunchKernelGGL(kv_dequantize_fp8_kernel,
+                       dim3((unsigned)((toks + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kWavesPerBlock * 64), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_quantize_fp8(const KvQuantArgs &a, hipStream_t stream) {
     const long toks = (long)a.B * a.S_max;

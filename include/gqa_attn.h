@@ -369,6 +369,27 @@ int gqa_kv_quantize_fp8(const void *x, const int32_t *seqlens, const int32_t *bl
                         int num_pages, int max_blocks, void *stream);
 
 /*
+ * gqa_kv_dequantize_fp8 -- the inverse of gqa_kv_quantize_fp8: token t < seqlens[b]
+ * of sequence b is read from row t % page_size of page block_table[b][t / page_size]
+ * of an FP8 pool and written to x as bf16 (code value times the row's scale; with
+ * the quantiser's power-of-two scales this is exact, the values the FP8 decode
+ * attends over).  It lets kernels that read a bf16 cache -- the chunked prefill --
+ * run on an FP8 cache (V07, section 17.7: FP8 is the cache's storage format).
+ *
+ *   pool         num_pages * gqa_fp8_page_bytes(...) bytes, device, 16-byte aligned
+ *   seqlens      [B] int32, device, or NULL (= S_max), clamped to [0, S_max]
+ *   block_table  [B, max_blocks] int32, device; max_blocks * page_size >= S_max.  A
+ *                live entry outside [0, num_pages) gives a zero row.
+ *   x            [B, S_max, H_kv, d] bf16, device, 16-byte aligned; rows at or past
+ *                seqlens[b] are not written
+ *
+ * Requires d % 8 == 0 and positive sizes.
+ */
+int gqa_kv_dequantize_fp8(const void *pool, const int32_t *seqlens, const int32_t *block_table,
+                          void *x, int B, int S_max, int H_kv, int d, int page_size, int num_pages,
+                          int max_blocks, void *stream);
+
+/*
  * gqa_attn_decode_paged_fp8 -- gqa_attn_decode_paged over FP8 pools: the same
  * arguments, plan, workspace and outputs, with k_pool and v_pool FP8 pools as
  * above.  Codes are converted to bf16 in registers (exactly), each score is

@@ -269,6 +269,21 @@ def test_kv_quantize_fp8_rejects_before_launch(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULLP), (dict(pool=None), NULLP), (dict(tbl=None), NULLP), (dict(x=MIS), ALIGN),
+    (dict(pool=ctypes.c_void_p(0x10008)), ALIGN), (dict(sl=ctypes.c_void_p(0x10002)), ALIGN),
+    (dict(B=0), SHAPE), (dict(d=12), UNSUP), (dict(page=0), SHAPE), (dict(max_blocks=1), SHAPE),
+])
+def test_kv_dequantize_fp8_rejects_before_launch(lib, kw, code):
+    a = dict(x=A, sl=None, tbl=A, pool=A, B=2, S_max=64, H_kv=8, d=128, page=16, num_pages=8,
+             max_blocks=4)
+    a.update(kw)
+    assert lib.gqa_kv_dequantize_fp8(a["pool"], a["sl"], a["tbl"], a["x"], a["B"], a["S_max"],
+                                     a["H_kv"], a["d"], a["page"], a["num_pages"],
+                                     a["max_blocks"], None) == code
+    assert lib.gqa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
     (dict(d=32), UNSUP), (dict(page=24), SHAPE), (dict(tbl=None), NULLP), (dict(q=MIS), ALIGN),
     (dict(ws=None), WS), (dict(H_kv=3), SHAPE),
 ])

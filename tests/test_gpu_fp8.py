@@ -182,3 +182,61 @@ def test_fp8_gpu_quantised_pool_decodes(gpu_available):
     torch.cuda.synchronize()
     assert kg.shape == (n, pb)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[str(c) for c in QUANT_CASES])
+def test_dequantize_matches_oracle(case, gpu_available):
+    """The inverse of the quantiser: the oracle's pools, and the GPU quantiser's, read back as
+    the oracle's dequantised cache, bit for bit, on every live row (dead rows untouched)."""
+    B, H_kv, d, page, ragged = case
+    p = paged_decode_inputs(B, 8, H_kv, d, page, ragged=ragged, seed=750 + d + page,
+                            nan_fill=False)
+    xk, _ = logical_caches(p)
+    # special rows: all zero, large (scale above one), tiny (scale near the bottom)
+    rng = np.random.default_rng(751)
+    xk[0, 0] = 0
+    if p["seqlens"][0] > 2:
+        xk[0, 1] = bf16_bits_from_f32(rng.standard_normal((H_kv, d)).astype(np.float32) * 3e4)
+        xk[0, 2] = bf16_bits_from_f32(rng.standard_normal((H_kv, d)).astype(np.float32) * 1e-30)
+    n = p["k_pool"].shape[0]
+    S_max = p["block_table"].shape[1] * page
+    kq = oracle.quantize_to_pages(xk, p["seqlens"], p["block_table"], page, n, fill=0)
+    ref = oracle.gather_pages(oracle.dequantize_pages(kq, page, H_kv, d), p["block_table"],
+                              p["seqlens"], page)
+    tbl, sl = to_gpu_i32(p["block_table"]), to_gpu_i32(p["seqlens"])
+    say(f"fp8 dequantise {case}")
+    for name, pool in (("oracle pool", torch.from_numpy(kq).cuda()),
+                       ("gpu pool", g.kv_quantize_fp8(to_gpu_bf16(xk), tbl, sl, num_pages=n,
+                                                      page_size=page))):
+        out = torch.full((B, S_max, H_kv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        g.kv_dequantize_fp8(pool, tbl, S_max, H_kv, d, sl, page_size=page, out=out)
+        torch.cuda.synchronize()
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        for b, ln in enumerate(p["seqlens"]):
+            assert np.array_equal(got[b, :ln], ref[b, :ln]), f"{name}, sequence {b}"
+            assert torch.isnan(out[b, ln:].float()).all(), f"{name}: a dead row was written"
+
+
+def test_prefill_chunk_over_dequantised_fp8_cache(gpu_available):
+    """The chunked prefill on an FP8 cache by composition: dequantise the pools, then run the
+    chunk -- equal to the chunk over the oracle's dequantised cache."""
+    B, H_q, H_kv, d, page, T = 2, 16, 2, 128, 16, 96
+    p = paged_decode_inputs(B, H_q, H_kv, d, page, S_max=400, seed=760, nan_fill=False)
+    xk, xv = logical_caches(p)
+    n = p["k_pool"].shape[0]
+    S_max = p["block_table"].shape[1] * page
+    tbl, sl = to_gpu_i32(p["block_table"]), to_gpu_i32(p["seqlens"])
+    kq, vq = oracle_pools(p, xk, xv, fill=0)
+    say("chunked prefill over a dequantised FP8 cache")
+    k = g.kv_dequantize_fp8(torch.from_numpy(kq).cuda(), tbl, S_max, H_kv, d, sl, page_size=page)
+    v = g.kv_dequantize_fp8(torch.from_numpy(vq).cuda(), tbl, S_max, H_kv, d, sl, page_size=page)
+    rng = np.random.default_rng(761)
+    q = to_gpu_bf16(bf16_bits_from_f32(rng.standard_normal((B, T, H_q, d)).astype(np.float32)))
+    o1, l1 = g.prefill_chunk(q, k[:, :400].contiguous(), v[:, :400].contiguous(), q_start=400 - T)
+    kb = oracle.gather_pages(oracle.dequantize_pages(kq, page, H_kv, d), p["block_table"],
+                             p["seqlens"], page)
+    vb = oracle.gather_pages(oracle.dequantize_pages(vq, page, H_kv, d), p["block_table"],
+                             p["seqlens"], page)
+    o2, l2 = g.prefill_chunk(q, to_gpu_bf16(kb[:, :400]), to_gpu_bf16(vb[:, :400]), q_start=400 - T)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
