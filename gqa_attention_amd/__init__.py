@@ -76,8 +76,8 @@ def load_library(path=LIBRARY):
     L.gqa_attn_prefill_causal.restype = ci
     L.gqa_attn_prefill_chunk.argtypes = [vp, vp, vp, vp, f32p, ci, ci, ci, ci, ci, ci, ci, cf, vp]
     L.gqa_attn_prefill_chunk.restype = ci
-    L.gqa_attn_prefill_chunk_paged.argtypes = [vp, vp, vp, i32p, vp, f32p, ci, ci, ci, ci, ci, ci,
-                                               ci, ci, ci, cf, vp]
+    L.gqa_attn_prefill_chunk_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, f32p, ci, ci, ci, ci, ci,
+                                               ci, ci, ci, ci, cf, vp]
     L.gqa_attn_prefill_chunk_paged.restype = ci
     L.gqa_fp8_page_bytes.argtypes = [ci, ci, ci]
     L.gqa_fp8_page_bytes.restype = cs
@@ -355,8 +355,9 @@ def prefill_chunk(q, k_cache, v_cache, q_start=None, softmax_scale=None, out=Non
 def prefill_chunk_paged(q, k_pool, v_pool, block_table, q_start, softmax_scale=None, out=None,
                         lse=None):
     """Causal prefill of a chunk over a paged cache: q [B,T_q,H_q,d] are the tokens
-    q_start.. of each sequence; pools [num_pages,page,H_kv,d] bf16; block_table
-    [B,max_blocks] int32 -> (o [B,T_q,H_q,d], lse [B,H_q,T_q])."""
+    q_start.. of each sequence (q_start an int, or an int32 device tensor [B] of per-sequence
+    starts); pools [num_pages,page,H_kv,d] bf16; block_table [B,max_blocks] int32 ->
+    (o [B,T_q,H_q,d], lse [B,H_q,T_q])."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k_pool, "k_pool", torch.bfloat16, 4)
     _need(v_pool, "v_pool", torch.bfloat16, 4)
@@ -366,11 +367,17 @@ def prefill_chunk_paged(q, k_pool, v_pool, block_table, q_start, softmax_scale=N
     if dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, pools {tuple(k_pool.shape)} / "
                          f"{tuple(v_pool.shape)}, block_table {tuple(block_table.shape)}")
+    starts = None
+    if torch.is_tensor(q_start):
+        _need(q_start, "q_start", torch.int32, 1)
+        if q_start.shape[0] != B:
+            raise ValueError("q_start must have B entries")
+        starts, q_start = q_start, 0
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H_q, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(load_library().gqa_attn_prefill_chunk_paged(
-        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(o), _ptr(l), B, T,
-        int(q_start), H_q, H_kv, d, page, num_pages, block_table.shape[1],
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(starts), _ptr(o), _ptr(l),
+        B, T, int(q_start), H_q, H_kv, d, page, num_pages, block_table.shape[1],
         _scale(d, softmax_scale), _stream(q.device)))
     return o, l
 

@@ -205,6 +205,8 @@ gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Pl
 struct PagedCache {
     const int32_t *block_table = nullptr;
     int page = 0, num_pages = 0, max_blocks = 0;
+    const int32_t *q_starts = nullptr;
+    int q_start_max = 0;
 };
 
 // Causal prefill of T query rows (tokens q_start .. q_start + T - 1) against a cache of
@@ -241,6 +243,8 @@ int prefill(const void *q, const void *k, const void *v, void *o, float *lse, in
     a.page = pc.page;
     a.num_pages = pc.num_pages;
     a.max_blocks = pc.max_blocks;
+    a.q_starts = pc.q_starts;
+    a.q_start_max = pc.q_start_max;
     if ((rc = hip_status(gqa::launch_prefill_causal(a, static_cast<hipStream_t>(stream)),
                          "prefill_causal")))
         return rc;
@@ -566,10 +570,10 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
 }
 
 int gqa_attn_prefill_chunk_paged(const void *q, const void *k_pool, const void *v_pool,
-                                 const int32_t *block_table, void *o, float *lse, int B, int T_q,
-                                 int q_start, int H_q, int H_kv, int d, int page_size,
-                                 int num_pages, int max_blocks, float softmax_scale,
-                                 void *stream) {
+                                 const int32_t *block_table, const int32_t *q_starts, void *o,
+                                 float *lse, int B, int T_q, int q_start, int H_q, int H_kv, int d,
+                                 int page_size, int num_pages, int max_blocks,
+                                 float softmax_scale, void *stream) {
     if (T_q <= 0 || q_start < 0)
         return fail(GQA_ERR_BAD_SHAPE, "T_q=%d must be positive and q_start=%d non-negative", T_q,
                     q_start);
@@ -592,11 +596,17 @@ int gqa_attn_prefill_chunk_paged(const void *q, const void *k_pool, const void *
                     "larger pages)", keys, blocks, gqa::kPrefillMaxPages);
     if (!block_table) return fail(GQA_ERR_NULL_POINTER, "block_table is NULL");
     if (!aligned(block_table, 4)) return fail(GQA_ERR_ALIGNMENT, "block_table misaligned");
+    if (q_starts && !aligned(q_starts, 4)) return fail(GQA_ERR_ALIGNMENT, "q_starts misaligned");
     PagedCache pc;
     pc.block_table = block_table;
     pc.page = page_size;
     pc.num_pages = num_pages;
     pc.max_blocks = max_blocks;
+    pc.q_starts = q_starts;
+    // the largest start whose keys still fit the table and the staged table row
+    const long cap = (long)(max_blocks < gqa::kPrefillMaxPages ? max_blocks : gqa::kPrefillMaxPages)
+                     * page_size;
+    pc.q_start_max = (int)(cap - T_q);
     return prefill(q, k_pool, v_pool, o, lse, B, T_q, q_start, (int)keys, H_q, H_kv, d,
                    softmax_scale, stream, pc);
 }

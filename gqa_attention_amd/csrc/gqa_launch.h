@@ -104,6 +104,10 @@ struct PrefillArgs {
     // (page a multiple of 16; at most kPrefillMaxPages blocks of a sequence are visible).
     const int32_t *block_table;
     int page, num_pages, max_blocks;
+    // Per-sequence chunk starts (paged, optional): sequence b's rows are the tokens
+    // q_starts[b] .. + T - 1, q_starts[b] clamped to [0, q_start_max].
+    const int32_t *q_starts;
+    int q_start_max;
 };
 
 // Blocks of one sequence a paged prefill can see (its table row is staged in LDS).

@@ -361,7 +361,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     const int r0 = i0 + w * 32;            // this wave's first query row
     const int row = r0 + r32;              // this lane's query row
     const int last_row = min(i0 + kBr, a.T) - 1;
-    const int qs = a.q_start;              // query row i is token qs + i
+    // query row i is token qs + i (per sequence when given, clamped so that every key the
+    // chunk sees lies in the cache)
+    const int qs = a.q_starts ? min(max(a.q_starts[b], 0), a.q_start_max) : a.q_start;
 
     WaveCtx x;
     x.lds = smem;

@@ -316,6 +316,10 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
  *               holding keys [0, q_start + T_q) are read.  An entry outside
  *               [0, num_pages) is not dereferenced: its keys read as zeros.  Pool
  *               rows of those blocks at or past q_start + T_q are never read.
+ *   q_starts    [B] int32, device, or NULL (= q_start for every sequence): sequence b's
+ *               chunk starts at q_starts[b], each sequence at its own position; values
+ *               are clamped on the device to [0, min(max_blocks, 8192) * page_size - T_q]
+ *               (the host checks below then apply to q_start only).
  *   o, lse      [B, T_q, H_q, d] bf16, [B, H_q, T_q] fp32, device, written
  *
  * Requires T_q >= 1, q_start >= 0, ceil((q_start + T_q) / page_size) <= max_blocks
@@ -323,10 +327,10 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
  * of 16 in [16, 65536].  Supported: d = 128.
  */
 int gqa_attn_prefill_chunk_paged(const void *q, const void *k_pool, const void *v_pool,
-                                 const int32_t *block_table, void *o, float *lse, int B, int T_q,
-                                 int q_start, int H_q, int H_kv, int d, int page_size,
-                                 int num_pages, int max_blocks, float softmax_scale,
-                                 void *stream);
+                                 const int32_t *block_table, const int32_t *q_starts, void *o,
+                                 float *lse, int B, int T_q, int q_start, int H_q, int H_kv, int d,
+                                 int page_size, int num_pages, int max_blocks,
+                                 float softmax_scale, void *stream);
 
 /*
  * FP8 (E4M3) paged KV cache (V07, section 17.7: a per-token scale kept with each

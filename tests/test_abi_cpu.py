@@ -200,15 +200,16 @@ def test_prefill_chunk_rejects_before_launch(lib, kw, code):
     (dict(T=0), SHAPE), (dict(q_start=-1), SHAPE), (dict(page=24), SHAPE), (dict(page=0), SHAPE),
     (dict(num_pages=0), SHAPE), (dict(max_blocks=15), SHAPE), (dict(tbl=None), NULLP),
     (dict(tbl=ctypes.c_void_p(0x10002)), ALIGN), (dict(d=64), UNSUP), (dict(H_kv=3), SHAPE),
-    (dict(q=MIS), ALIGN), (dict(scale=-1.0), SCALE),
+    (dict(q=MIS), ALIGN), (dict(scale=-1.0), SCALE), (dict(qs=ctypes.c_void_p(0x10002)), ALIGN),
     # 8193 blocks of 16 keys: past the table row the kernel stages on chip
     (dict(T=1, q_start=8192 * 16, max_blocks=9000), UNSUP),
 ])
 def test_prefill_chunk_paged_rejects_before_launch(lib, kw, code):
-    a = dict(q=A, k=A, v=A, tbl=A, o=A, lse=A, B=1, T=100, q_start=150, H_q=8, H_kv=2, d=128,
-             page=16, num_pages=64, max_blocks=16, scale=0.088)
+    a = dict(q=A, k=A, v=A, tbl=A, qs=None, o=A, lse=A, B=1, T=100, q_start=150, H_q=8, H_kv=2,
+             d=128, page=16, num_pages=64, max_blocks=16, scale=0.088)
     a.update(kw)
-    assert lib.gqa_attn_prefill_chunk_paged(a["q"], a["k"], a["v"], a["tbl"], a["o"], a["lse"],
+    assert lib.gqa_attn_prefill_chunk_paged(a["q"], a["k"], a["v"], a["tbl"], a["qs"], a["o"],
+                                            a["lse"],
                                             a["B"], a["T"], a["q_start"], a["H_q"], a["H_kv"],
                                             a["d"], a["page"], a["num_pages"], a["max_blocks"],
                                             a["scale"], None) == code

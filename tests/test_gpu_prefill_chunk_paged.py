@@ -119,3 +119,26 @@ def test_paged_chunk_llama(gpu_available):
     say(f"paged prefill chunk {cfg.name} T={T} q_start={q_start} pages of 16")
     (oc, lc), (op, lp), _ = run_both(inp, q_start, T, 16, seed=830)
     assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
+def test_paged_chunk_per_sequence_starts(gpu_available):
+    """Each sequence's chunk at its own position (a device array of starts): every sequence
+    of the batched call equals the call for that sequence alone, bit for bit; starts outside
+    [0, table capacity - T_q] are clamped on the device."""
+    B, T, page, keys = 3, 150, 16, 1150
+    inp = chunk_inputs(B, T, keys, 16, 2, 128, seed=840)
+    kp, vp, table = paged_case(inp, keys - T, T, page, seed=841)
+    cap = table.shape[1] * page
+    q = to_gpu_bf16(inp["q"])
+    kpg, vpg, tbl = to_gpu_bf16(kp), to_gpu_bf16(vp), to_gpu_i32(table)
+    for starts in ([0, 333, 1000], [-5, 17, 5000]):
+        say(f"paged prefill chunk, per-sequence starts {starts}")
+        ob, lb = g.prefill_chunk_paged(q, kpg, vpg, tbl, to_gpu_i32(np.array(starts, np.int32)))
+        for b, s in enumerate(starts):
+            s = min(max(s, 0), cap - T)
+            o1, l1 = g.prefill_chunk_paged(q[b:b + 1].contiguous(), kpg, vpg,
+                                           tbl[b:b + 1].contiguous(), s)
+            torch.cuda.synchronize()
+            # bit patterns: a clamped chunk may reach the pool's NaN rows, in both calls alike
+            assert torch.equal(ob[b:b + 1].view(torch.int16), o1.view(torch.int16)), (starts, b)
+            assert torch.equal(lb[b:b + 1].view(torch.int32), l1.view(torch.int32)), (starts, b)
