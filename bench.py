@@ -71,9 +71,9 @@ COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many by
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
 MEASURED_TRAFFIC = {
-    "decode_split": ("50c2266b917ecd49", 143_011_631),
-    "lse_merge": ("df19d77853c9e456", 9_527_218),
-    "prefill_causal": ("e79e3e465c1b4e81", 421_955_494),
+    "decode_split": ("31147fdf07f0e57b", 143_011_422),
+    "lse_merge": ("95db331d632c5be2", 9_527_225),
+    "prefill_causal": ("0acd9c8b9f9c37a4", 422_062_707),
 }
 
 
