@@ -619,6 +619,49 @@ def pin_bwd_stored_output_D(lib):
     _rel_close(dq2 - dq0, -tau * delta[:, None] * ok, rtol=1e-9, atol=1e-12)
 
 
+def pin_bwd_stored_output_D_rows(lib):
+    """D of a stored output (V07 section 6.2: D_i is the row-wise dot of dO_i and O_i),
+    checked element by element against an explicit loop over (b, h, i) with exact sums, in
+    the [B, H_q, S] order the backward's rows use; B = 2 and S != H_q so that a transposed or
+    batch-mixed order cannot pass.  The D that ``prefill_causal_bwd(..., o=...)`` returns is
+    the same array, and its dQ is that of the row-level call fed the loop's D.  With O the
+    forward's own output, D also equals the sum over keys of P_ij dP_ij (the identity that
+    section 6.2 uses to replace that sum), up to the bf16 rounding of the stored O."""
+    B, S, H_q, H_kv, d = 2, 9, 4, 2, 16
+    p = prefill_bwd_inputs(B, S, H_q, H_kv, d, seed=303)
+    q, k, v, do = p["q"], p["k"], p["v"], p["do"]
+    tau = 0.25
+    o64, _ = oracle.prefill_causal(q, k, v, tau=tau, lib=lib)          # [B, S, H_q, d]
+    o = bf16_bits_from_f32(o64.astype(np.float32))
+    D = oracle.stored_output_D(o, do)
+    assert D.shape == (B, H_q, S), D.shape
+    of, dof = _f64(o), _f64(do)
+    ref = np.empty((B, H_q, S))
+    for b in range(B):
+        for h in range(H_q):
+            for i in range(S):
+                ref[b, h, i] = math.fsum(float(of[b, i, h, c]) * float(dof[b, i, h, c])
+                                         for c in range(d))
+    _rel_close(D, ref, rtol=1e-15, atol=1e-300)
+    dq, dk, dv, lse, D_ret = oracle.prefill_causal_bwd(q, k, v, do, o=o, tau=tau, nthreads=2,
+                                                       lib=lib)
+    _rel_close(D_ret, ref, rtol=1e-15, atol=1e-300)
+    rows = np.stack(np.meshgrid(np.arange(B), np.arange(H_q), np.arange(S), indexing="ij"),
+                    axis=-1).reshape(-1, 3).astype(np.int32)
+    dq_r, _, _ = oracle.prefill_causal_bwd_rows(q, k, v, do, rows, D=ref.reshape(-1), tau=tau,
+                                                nthreads=2, lib=lib)
+    _rel_close(dq, dq_r.reshape(B, H_q, S, d).transpose(0, 2, 1, 3), rtol=1e-12, atol=1e-15)
+    # the exact D (sum_j P_ij dP_ij, the oracle's own) against the stored-output D: they
+    # differ only through O's rounding to bf16, at most 2^-8 |O_i| per element (RNE)
+    _, _, D_exact = oracle.prefill_causal_bwd_rows(q, k, v, do, rows, tau=tau, nthreads=2,
+                                                   lib=lib)
+    # (fp64 -> fp32 -> bf16 rounds twice: 2^-24 more at most)
+    bound = (2.0 ** -8 + 2.0 ** -24) * np.einsum("bshc,bshc->bhs", np.abs(o64),
+                                                np.abs(dof)).reshape(-1)
+    err = np.abs(D_exact - ref.reshape(-1))
+    assert np.all(err <= bound + 1e-13), f"max excess {np.max(err - bound)}"
+
+
 # ---------------------------------------------------------------------------
 # FP8 KV cache (V07 section 17.7; E4M3 as the OCP 8-bit floating-point specification
 # defines it).

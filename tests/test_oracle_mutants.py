@@ -152,3 +152,28 @@ def test_planted_fp8_page_mistake_is_caught(kind, monkeypatch, oracle_lib):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin detects the FP8 page mistake {kind}"
+
+
+# Planted mistakes in the stored-output D (Python; V07 section 6.2: D_i = dO_i . O_i): the
+# rows in token-major order instead of (b, h, i), or the output dotted with itself, must fail
+# a pin.
+def _stored_D_variant(kind):
+    def stored_output_D(o, do):
+        o64 = oracle._f32_of_bits(o).astype(np.float64)
+        do64 = oracle._f32_of_bits(do).astype(np.float64)
+        if kind == "token_major_rows":
+            return np.einsum("bshd,bshd->bsh", o64, do64)
+        return np.einsum("bshd,bshd->bhs", o64, o64)
+    return stored_output_D
+
+
+@pytest.mark.parametrize("kind", ["token_major_rows", "o_for_both_factors"])
+def test_planted_stored_D_mistake_is_caught(kind, monkeypatch, oracle_lib):
+    monkeypatch.setattr(oracle, "stored_output_D", _stored_D_variant(kind))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(oracle_lib)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects the stored-D mistake {kind}"
