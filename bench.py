@@ -57,19 +57,23 @@ sys.path.insert(0, ROOT)
 
 import gqa_attention_amd as g  # noqa: E402
 from gqa_workloads import LLAMA_DECODE, LLAMA_LONG_PREFILL, LLAMA_PREFILL, \
-    LLAMA_RAGGED_DECODE  # noqa: E402
+    LLAMA_RAGGED_DECODE, TINY_DECODE  # noqa: E402
 from gqa_workloads import accounting as acc  # noqa: E402
 from gqa_workloads.generate import for_config, paged_decode_inputs  # noqa: E402
 
 METRIC = "decode KV GB/s (% HBM peak) at Llama3-70B GQA; causal prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+BF16_FLOP_PER_CLK_CU = 4096    # CDNA4 dense bf16 matrix-core FLOP per clock per compute unit
 COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many bytes
+REPLAYS = 5                    # timed replays of each graph loop (median and min reported)
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE at this workload
 # (fetch counter x 2.00, write x 1.00, both factors from the plain-copy calibration),
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
 # taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
+TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00 per dispatch at this "
+                  "workload (profiles/hbm_traffic_*.md), valid while the kernel's source "
+                  "digest matches; null otherwise")
 MEASURED_TRAFFIC = {
     "decode_split": ("31147fdf07f0e57b", 143_011_422),
     "lse_merge": ("95db331d632c5be2", 9_527_225),
@@ -97,40 +101,115 @@ def upload(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def cpu_baseline(seconds):
-    """The fp64 oracle on the decode workload, repeated to fill about ``seconds``."""
-    import oracle
-    inp = for_config(LLAMA_DECODE)
-    threads = oracle.default_threads()
-    kv = acc.decode_kv_bytes([LLAMA_DECODE.S_kv], LLAMA_DECODE.H_kv, LLAMA_DECODE.d)
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform's machine name."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _timed(fn, min_seconds=0.0):
+    """(seconds per call, calls): fn repeated until min_seconds have passed (at least once)."""
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.decode(inp["q"], inp["k"], inp["v"], nthreads=threads)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": kv * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"full decode workload (B=1, H_q=64, H_kv=8, d=128, S_kv=32768) "
-                      f"repeated {reps}x in {el:.1f} s, fp64, {threads} threads",
-            "cpu": platform.processor() or platform.machine()}
+        if el >= min_seconds:
+            return el / reps, reps
 
 
-def graph_ms(fn, n):
-    """Mean time per call of n back-to-back calls fn(0..n-1), captured in a HIP graph,
-    replayed once untimed and once between two events on the launch stream."""
+def _prefill_sample_rows(S, H_q, n_i, first_last, seed):
+    """A stratified sample of query rows of a causal prefill, all heads: the first and last
+    `first_last` rows, the rows either side of every 8th 256-row block boundary, and
+    uniform rows, n_i positions in all; rows (b=0, h, i) for every head h."""
+    rng = np.random.default_rng(seed)
+    pos = set(range(first_last)) | set(range(S - first_last, S))
+    for blk in range(256, S, 8 * 256):
+        pos |= {blk - 1, blk}
+    while len(pos) < n_i:
+        pos.add(int(rng.integers(0, S)))
+    pos = np.array(sorted(pos))
+    b, h, i = np.meshgrid([0], np.arange(H_q), pos, indexing="ij")
+    return np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1).astype(np.int32), pos
+
+
+def cpu_baseline(seconds):
+    """The fp64 oracle on the host cores: the decode workload (the reported value, all
+    threads, repeated to fill about ``seconds``), one-thread times of the tiny and the
+    Llama decode, and sampled causal prefills at S = 8192 and S = 65536 with their
+    extrapolation to the whole launch."""
+    import oracle
+    threads = oracle.default_threads()
+    res = {}
+    inp = for_config(LLAMA_DECODE)
+    kv = acc.decode_kv_bytes([LLAMA_DECODE.S_kv], LLAMA_DECODE.H_kv, LLAMA_DECODE.d)
+    sec, reps = _timed(lambda: oracle.decode(inp["q"], inp["k"], inp["v"], nthreads=threads),
+                       seconds)
+    res.update({"value": kv / sec / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"full decode workload (B=1, H_q=64, H_kv=8, d=128, S_kv=32768) "
+                          f"repeated {reps}x in {sec * reps:.1f} s, fp64, {threads} threads",
+                "cpu": cpu_model()})
+    one = {}
+    sec1, _ = _timed(lambda: oracle.decode(inp["q"], inp["k"], inp["v"], nthreads=1))
+    one["llama_decode_s32768"] = {"s": round(sec1, 4), "gbs": round(kv / sec1 / 1e9, 4)}
+    del inp
+    tiny = for_config(TINY_DECODE)
+    kv_t = acc.decode_kv_bytes([TINY_DECODE.S_kv], TINY_DECODE.H_kv, TINY_DECODE.d)
+    sec_t, reps_t = _timed(lambda: oracle.decode(tiny["q"], tiny["k"], tiny["v"], nthreads=1), 0.5)
+    one["tiny_decode_s512"] = {"s": round(sec_t, 7), "gbs": round(kv_t / sec_t / 1e9, 4),
+                               "calls": reps_t}
+    res["one_thread"] = one
+    # causal prefill: a stratified row sample of every head, timed, and its extrapolation to
+    # the whole launch (a row i costs in proportion to its i + 1 keys)
+    for cfg, n_i, tag in ((LLAMA_PREFILL, 512, "prefill_s8192"),
+                          (LLAMA_LONG_PREFILL, 96, "prefill_s65536")):
+        p = for_config(cfg)
+        rows, pos = _prefill_sample_rows(cfg.S, cfg.H_q, n_i, 16, cfg.seed)
+        t0 = time.perf_counter()
+        oracle.prefill_causal_rows(p["q"], p["k"], p["v"], rows, nthreads=threads)
+        el = time.perf_counter() - t0
+        keys_sample = float(np.sum(pos + 1)) * cfg.H_q
+        keys_full = cfg.H_q * cfg.S * (cfg.S + 1) / 2.0
+        flop_sample = 4.0 * cfg.d * keys_sample
+        res[tag] = {"rows": int(rows.shape[0]), "positions": int(pos.size), "heads": cfg.H_q,
+                    "s": round(el, 3), "gflops": round(flop_sample / el / 1e9, 2),
+                    "extrapolated_full_s": round(el * keys_full / keys_sample, 1),
+                    "note": "sampled rows of every head; the full-launch time is an "
+                            "extrapolation by key count, not a measurement"}
+        del p
+    return res
+
+
+def graph_stats(fn, n, replays=REPLAYS):
+    """Time per call of n back-to-back calls fn(0..n-1), captured in a HIP graph, replayed
+    once untimed and `replays` times between two events on the launch stream: returns
+    {mean, median, min} in ms per call over the replays."""
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(n):
             fn(i)
     graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    e1.synchronize()
-    return e0.elapsed_time(e1) / n
+    ts = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / n)
+    return {"mean": float(np.mean(ts)), "median": float(np.median(ts)), "min": float(min(ts))}
+
+
+def graph_ms(fn, n):
+    """Mean time per call (ms) of graph_stats."""
+    return graph_stats(fn, n)["mean"]
 
 
 def upload_paged(p):
@@ -138,7 +217,50 @@ def upload_paged(p):
             torch.from_numpy(p["block_table"]).cuda(), torch.from_numpy(p["seqlens"]).cuda())
 
 
-def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
+def long_prefill_inputs():
+    """q, k, v of the S = 65536 causal prefill with 1% of key rows scaled by 8, drawn on the
+    GPU (timing inputs; parity at this size runs on the generator's bytes in the tests)."""
+    lc = LLAMA_LONG_PREFILL
+    gen = torch.Generator(device="cuda").manual_seed(lc.seed)
+    ql = torch.randn((lc.B, lc.S, lc.H_q, lc.d), device="cuda", generator=gen).to(torch.bfloat16)
+    kl = torch.randn((lc.B, lc.S, lc.H_kv, lc.d), device="cuda", generator=gen)
+    out_rows = torch.rand((lc.B, lc.S, lc.H_kv, 1), device="cuda", generator=gen) < lc.outlier_frac
+    kl = (kl.to(torch.bfloat16).float() * torch.where(out_rows, lc.outlier_scale, 1.0)).to(
+        torch.bfloat16)
+    vl = torch.randn((lc.B, lc.S, lc.H_kv, lc.d), device="cuda", generator=gen).to(torch.bfloat16)
+    return ql, kl, vl
+
+
+def bwd_inputs(q_p, k_p, v_p):
+    """The backward's inputs at the Llama S = 8192 prefill: the forward's O and LSE, a random
+    output gradient, the workspace and the gradient tensors."""
+    pc = LLAMA_PREFILL
+    do_p = torch.randn(q_p.shape, device="cuda", generator=torch.Generator(
+        device="cuda").manual_seed(pc.seed + 1)).to(torch.bfloat16)
+    o_f, lse_f = g.prefill_causal(q_p, k_p, v_p)
+    ws_b = g.prefill_bwd_workspace(pc.B, pc.S, pc.H_q, pc.H_kv, pc.d)
+    grads = (torch.empty_like(q_p), torch.empty_like(k_p), torch.empty_like(v_p))
+    return o_f, lse_f, do_p, ws_b, grads
+
+
+def profile_extra(name, K, q_p, k_p, v_p):
+    """One loop for a counter run: the long prefill, or the prefill backward."""
+    if name == "prefill_long":
+        lc = LLAMA_LONG_PREFILL
+        ql, kl, vl = long_prefill_inputs()
+        ol = torch.empty_like(ql)
+        ll = torch.empty((lc.B, lc.H_q, lc.S), dtype=torch.float32, device="cuda")
+        fn = lambda i: g.prefill_causal(ql, kl, vl, out=ol, lse=ll)   # noqa: E731
+    else:
+        o_f, lse_f, do_p, ws_b, grads = bwd_inputs(q_p, k_p, v_p)
+        fn = lambda i: g.prefill_causal_bwd(q_p, k_p, v_p, o_f, lse_f, do_p,  # noqa: E731
+                                            workspace=ws_b, out=grads)
+    fn(0)
+    torch.cuda.synchronize()
+    return {"ms_per_call": graph_stats(fn, K, replays=2)}
+
+
+def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies, bf16_peak):
     """Paged, batched ragged and multi-token decode, long and chunked prefill, and the
     prefill backward, outside the timed step."""
     res = {}
@@ -310,13 +432,7 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
     # long-context causal prefill: S = 65536, K rows with 1% of them scaled by 8 (drawn on the
     # GPU here: the figure is a timing; parity at this size is in the tests)
     lc = LLAMA_LONG_PREFILL
-    gen = torch.Generator(device="cuda").manual_seed(lc.seed)
-    ql = torch.randn((lc.B, lc.S, lc.H_q, lc.d), device="cuda", generator=gen).to(torch.bfloat16)
-    kl = torch.randn((lc.B, lc.S, lc.H_kv, lc.d), device="cuda", generator=gen)
-    out_rows = torch.rand((lc.B, lc.S, lc.H_kv, 1), device="cuda", generator=gen) < lc.outlier_frac
-    kl = (kl.to(torch.bfloat16).float() * torch.where(out_rows, lc.outlier_scale, 1.0)).to(
-        torch.bfloat16)
-    vl = torch.randn((lc.B, lc.S, lc.H_kv, lc.d), device="cuda", generator=gen).to(torch.bfloat16)
+    ql, kl, vl = long_prefill_inputs()
     ol = torch.empty_like(ql)
     ll = torch.empty((lc.B, lc.H_q, lc.S), dtype=torch.float32, device="cuda")
 
@@ -331,8 +447,8 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
     res["prefill_long"] = {
         "workload": f"Llama3-70B causal prefill B={lc.B} S={lc.S}, 1% of key rows x8",
         "calls": n_long, "flop": flop, "ms": round(ms, 3), "tflops": round(tf, 1),
-        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
-    del ql, kl, vl, ol, ll, out_rows
+        "frac_bf16_peak": round(tf / bf16_peak, 4)}
+    del ql, kl, vl, ol, ll
 
     # chunked prefill: the prompt's last 2048 tokens against its whole 8192-token cache
     pc = LLAMA_PREFILL
@@ -351,7 +467,7 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
     res["prefill_chunk"] = {
         "workload": f"Llama3-70B chunked prefill: T_q={T} rows at q_start={q_start}, "
                     f"S_kv={pc.S}", "flop": flop, "ms": round(ms, 4), "tflops": round(tf, 1),
-        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+        "frac_bf16_peak": round(tf / bf16_peak, 4)}
     # the same chunk over a paged cache: 16-token pages at permuted pool positions
     page = 16
     nb = pc.S // page
@@ -371,15 +487,11 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
     tf_pg = flop / (ms_pg * 1e-3) / 1e12
     res["prefill_chunk"]["paged"] = {
         "page_size": page, "ms": round(ms_pg, 4), "tflops": round(tf_pg, 1),
-        "frac_bf16_peak": round(tf_pg / BF16_PEAK_TFLOPS, 4), "vs_contiguous": round(ms / ms_pg, 3)}
+        "frac_bf16_peak": round(tf_pg / bf16_peak, 4), "vs_contiguous": round(ms / ms_pg, 3)}
     del kpool, vpool
     # backward of the causal prefill at the Llama workload (S = 8192): the forward's O and
     # LSE, a random output gradient, the four launches of one backward call per step
-    do_p = torch.randn(q_p.shape, device="cuda", generator=torch.Generator(
-        device="cuda").manual_seed(pc.seed + 1)).to(torch.bfloat16)
-    o_f, lse_f = g.prefill_causal(q_p, k_p, v_p)
-    ws_b = g.prefill_bwd_workspace(pc.B, pc.S, pc.H_q, pc.H_kv, pc.d)
-    grads = (torch.empty_like(q_p), torch.empty_like(k_p), torch.empty_like(v_p))
+    o_f, lse_f, do_p, ws_b, grads = bwd_inputs(q_p, k_p, v_p)
 
     def bwd_call(i):
         g.prefill_causal_bwd(q_p, k_p, v_p, o_f, lse_f, do_p, workspace=ws_b, out=grads)
@@ -393,11 +505,14 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies):
         "workload": f"Llama3-70B causal prefill backward B={pc.B} S={pc.S} (dQ, dK, dV from O, "
                     f"LSE and dO; five products counted)",
         "calls": n_bwd, "flop": flop, "ms": round(ms, 4), "tflops": round(tf, 1),
-        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+        "frac_bf16_peak": round(tf / bf16_peak, 4),
         "workspace_mib": round(ws_b.numel() / 2 ** 20, 1)}
     del do_p, o_f, lse_f, ws_b, grads
     torch.cuda.synchronize()
     return res
+
+
+PROFILE_LOOPS = ("decode", "split", "merge", "prefill", "prefill_long", "prefill_bwd", "ceiling")
 
 
 def main():
@@ -413,6 +528,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 512 MiB device copy (torch copy_), whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the kernels' HBM traffic")
+    ap.add_argument("--profile", choices=PROFILE_LOOPS, default=None,
+                    help="run only this loop (warm-up, then one graph of --steps calls, "
+                         "replayed twice) and print its time: the command the counter "
+                         "summaries in profiles/ are taken with")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -423,23 +542,39 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
+    dev = g.device_info(0)
+    # bf16 dense matrix-core peak from the device's own compute units and peak clock
+    bf16_peak = dev["compute_units"] * BF16_FLOP_PER_CLK_CU * dev["clock_khz"] * 1e3 / 1e12
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     dc, pc = LLAMA_DECODE, LLAMA_PREFILL
-    dinp = for_config(dc)
-    q_d = upload(dinp["q"])
-    k0, v0 = upload(dinp["k"]), upload(dinp["v"])
-    kv_copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.kv_copies - 1)]
-    del dinp
-    ws = g.decode_workspace(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
-    plan = g.decode_plan(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
-    o_d = torch.empty((dc.B, dc.H_q, dc.d), dtype=torch.bfloat16, device="cuda")
-    lse_d = torch.empty((dc.B, dc.H_q), dtype=torch.float32, device="cuda")
-
-    pinp = for_config(pc)
-    q_p, k_p, v_p = upload(pinp["q"]), upload(pinp["k"]), upload(pinp["v"])
-    del pinp
-    o_p = torch.empty_like(q_p)
-    lse_p = torch.empty((pc.B, pc.H_q, pc.S), dtype=torch.float32, device="cuda")
+    K = args.steps
+    need_decode = args.profile in (None, "decode", "split", "merge", "ceiling")
+    need_prefill = args.profile in (None, "prefill", "prefill_bwd")
+    if need_decode:
+        dinp = for_config(dc)
+        q_d = upload(dinp["q"])
+        k0, v0 = upload(dinp["k"]), upload(dinp["v"])
+        kv_copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.kv_copies - 1)]
+        del dinp
+        ws = g.decode_workspace(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
+        plan = g.decode_plan(dc.B, dc.H_q, dc.H_kv, dc.d, dc.S_kv, dc.num_splits)
+        o_d = torch.empty((dc.B, dc.H_q, dc.d), dtype=torch.bfloat16, device="cuda")
+        lse_d = torch.empty((dc.B, dc.H_q), dtype=torch.float32, device="cuda")
+        sink = g.stream_read(kv_copies[0][0])
+    if need_prefill:
+        pinp = for_config(pc)
+        q_p, k_p, v_p = upload(pinp["q"]), upload(pinp["k"]), upload(pinp["v"])
+        del pinp
+        o_p = torch.empty_like(q_p)
+        lse_p = torch.empty((pc.B, pc.H_q, pc.S), dtype=torch.float32, device="cuda")
 
     def decode_call(i):
         k, v = kv_copies[i % len(kv_copies)]
@@ -455,21 +590,35 @@ def main():
         g.decode_combine(ws, o_d, lse_d, H_kv=dc.H_kv, S_max=dc.S_kv,
                          num_splits=dc.num_splits)
 
+    def ceiling_call(i):
+        # the same 128 MiB of K and V the decode reads in one call, read by a plain
+        # streaming kernel (one launch for K, one for V: 2 x 64 MiB)
+        k, v = kv_copies[i % len(kv_copies)]
+        g.stream_read(k, sink)
+        g.stream_read(v, sink)
+
     def prefill_call(i):
         g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
 
-    if args.copy_calibration:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    if args.profile is not None:
+        if args.profile in ("prefill_long", "prefill_bwd"):
+            res = profile_extra(args.profile, K, locals().get("q_p"), locals().get("k_p"),
+                                locals().get("v_p"))
+        else:
+            fn = {"decode": decode_call, "split": split_call, "merge": merge_call,
+                  "prefill": prefill_call, "ceiling": ceiling_call}[args.profile]
+            for i in range(args.warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            res = {"ms_per_call": graph_stats(fn, K, replays=2)}
+        print(json.dumps({"profile": args.profile, "steps": K, **res}), flush=True)
+        return
 
     # warm-up: eager calls of every kernel
     for i in range(args.warmup):
         decode_call(i)
         prefill_call(i)
+        ceiling_call(i)
     torch.cuda.synchronize()
 
     def capture(fn, n):
@@ -482,13 +631,12 @@ def main():
         torch.cuda.synchronize()
         return graph
 
-    K = args.steps
     graphs = {name: capture(fn, K) for name, fn in
               (("decode", decode_call), ("prefill", prefill_call), ("split", split_call),
-               ("merge", merge_call))}
+               ("merge", merge_call), ("ceiling", ceiling_call))}
 
     def replay_ms(name):
-        """Mean time per call of one replay, from events on the launch stream."""
+        """Time per call of one replay, from events on the launch stream."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         graphs[name].replay()
@@ -503,15 +651,33 @@ def main():
     prefill_ms = replay_ms("prefill")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations for the roofline figures (same launch stream, back to back)
-    split_ms = replay_ms("split")
-    merge_ms = replay_ms("merge")
+    # more replays of each loop (same launch stream, back to back): median and min per call,
+    # and the per-kernel durations of the roofline figures
+    reps = {name: [] for name in graphs}
+    reps["decode"].append(decode_ms)
+    reps["prefill"].append(prefill_ms)
+    for _ in range(REPLAYS - 1):
+        for name in graphs:
+            reps[name].append(replay_ms(name))
+    for name in ("split", "merge", "ceiling"):
+        reps[name].append(replay_ms(name))
+
+    def stat(name):
+        ts = reps[name]
+        return {"mean_ms": float(np.mean(ts)), "median_ms": float(np.median(ts)),
+                "min_ms": float(min(ts)), "replays": len(ts)}
+
+    split_ms = float(np.mean(reps["split"]))
+    merge_ms = float(np.mean(reps["merge"]))
+    ceiling_ms = float(np.mean(reps["ceiling"]))
 
     kv_bytes = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
     flop = acc.prefill_causal_flop(pc.B, pc.S, pc.H_q, pc.d)
     decode_gbs = kv_bytes / (decode_ms * 1e-3) / 1e9
     split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+    ceiling_gbs = kv_bytes / (ceiling_ms * 1e-3) / 1e9
     prefill_tflops = flop / (prefill_ms * 1e-3) / 1e12
+    ds, ps = stat("decode"), stat("prefill")
 
     out = {
         "metric": METRIC,
@@ -540,29 +706,48 @@ def main():
             "gbs": round(decode_gbs, 1),
             "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(dc.B / (decode_ms * 1e-3), 1),
+            "us_per_call": {"timed": round(decode_ms * 1e3, 2),
+                            "median": round(ds["median_ms"] * 1e3, 2),
+                            "min": round(ds["min_ms"] * 1e3, 2), "replays": ds["replays"]},
             "split_us": round(split_ms * 1e3, 2),
             "merge_us": round(merge_ms * 1e3, 2),
             "merge_traffic": measured_traffic("lse_merge"),
+            "ceiling_gbs": round(ceiling_gbs, 1),
+            "frac_of_ceiling": round(decode_gbs / ceiling_gbs, 4),
         },
+        "ceiling_gbs": round(ceiling_gbs, 1),
+        "ceiling": {"kernel": "hbm_read (gqa_stream_read)", "bytes": kv_bytes,
+                    "us": round(ceiling_ms * 1e3, 2),
+                    "frac_hbm_peak": round(ceiling_gbs / HBM_PEAK_GBS, 4),
+                    "what": "the same 128 MiB of K and V per call read by a plain streaming "
+                            "kernel (two launches of 64 MiB, 256 workgroups x 512 threads)"},
         "prefill": {
             "flop": flop,
             "tflops": round(prefill_tflops, 1),
-            "frac_bf16_peak": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
+            "frac_bf16_peak": round(prefill_tflops / bf16_peak, 4),
             "ms": round(prefill_ms, 4),
+            "ms_per_call": {"timed": round(prefill_ms, 4), "median": round(ps["median_ms"], 4),
+                            "min": round(ps["min_ms"], 4), "replays": ps["replays"]},
         },
+        "peaks": {"hbm_gbs": HBM_PEAK_GBS, "hbm_source": "MI355X published HBM3E bandwidth",
+                  "bf16_tflops": round(bf16_peak, 1),
+                  "bf16_source": f"{dev['compute_units']} CUs x {BF16_FLOP_PER_CLK_CU} FLOP/clk "
+                                 f"x {dev['clock_khz'] / 1e3:.0f} MHz (peak engine clock)"},
         "roofline": {"kernel": "decode_split", "bound": "hbm", "achieved": round(split_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("decode_split")},
+                     "traffic": measured_traffic("decode_split"),
+                     "traffic_source": TRAFFIC_SOURCE},
         "roofline_prefill": {"kernel": "prefill_causal", "bound": "mfma",
-                             "achieved": round(prefill_tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
-                             "traffic": measured_traffic("prefill_causal")},
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", "")},
+                             "achieved": round(prefill_tflops, 1), "peak": round(bf16_peak, 1),
+                             "unit": "TFLOP/s", "frac": round(prefill_tflops / bf16_peak, 4),
+                             "traffic": measured_traffic("prefill_causal"),
+                             "traffic_source": TRAFFIC_SOURCE},
+        "device": {"name": props.name, "cus": dev["compute_units"],
+                   "clock_mhz": dev["clock_khz"] / 1e3, "gcn_arch": dev["arch"]},
     }
     if not args.no_extra:
-        out.update(extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies))
+        out.update(extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies, bf16_peak))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -93,6 +93,12 @@ def load_library(path=LIBRARY):
     L.gqa_attn_prefill_causal_bwd.argtypes = [vp, vp, vp, vp, f32p, vp, vp, vp, vp, ci, ci, ci, ci,
                                               ci, cf, vp, cs, vp]
     L.gqa_attn_prefill_causal_bwd.restype = ci
+    L.gqa_device_info.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.c_char_p, cs]
+    L.gqa_device_info.restype = ci
+    L.gqa_stream_read_sink_bytes.argtypes = []
+    L.gqa_stream_read_sink_bytes.restype = cs
+    L.gqa_stream_read.argtypes = [vp, cs, vp, vp]
+    L.gqa_stream_read.restype = ci
     if path == LIBRARY:
         _lib = L
     return L
@@ -133,6 +139,28 @@ def _need(t, name, dtype, ndim):
 
 def _scale(d, softmax_scale):
     return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def device_info(device=0):
+    """Compute units, peak engine clock (kHz) and architecture name of a HIP device."""
+    L = load_library()
+    cus, khz = ctypes.c_int(), ctypes.c_int()
+    arch = ctypes.create_string_buffer(64)
+    _check(L.gqa_device_info(device, ctypes.byref(cus), ctypes.byref(khz), arch, 64))
+    return {"compute_units": cus.value, "clock_khz": khz.value, "arch": arch.value.decode()}
+
+
+def stream_read(buf, sink=None):
+    """One launch of the library's plain streaming-read kernel over the bytes of a GPU
+    tensor (the decode's bandwidth calibration); returns the sink tensor it may write."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    L = load_library()
+    if sink is None:
+        sink = torch.empty(L.gqa_stream_read_sink_bytes(), dtype=torch.uint8, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(L.gqa_stream_read(_ptr(buf), nbytes - nbytes % 16, _ptr(sink), _stream(buf.device)))
+    return sink
 
 
 def decode_plan(B, H_q, H_kv, d, S_max, num_splits=0):

@@ -312,7 +312,46 @@ const char *gqa_status_string(int status) {
 
 const char *gqa_last_error(void) { return g_err; }
 
-const char *gqa_version(void) { return "gqa_attn 0.1.0 (gfx950)"; }
+const char *gqa_version(void) { return "gqa_attn 0.2.0 (gfx950)"; }
+
+int gqa_device_info(int device, int *compute_units, int *clock_khz, char *arch, size_t arch_len) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDeviceCount: %s", hipGetErrorString(e));
+    if (device < 0 || device >= n)
+        return fail(GQA_ERR_BAD_SHAPE, "device %d outside [0, %d)", device, n);
+    if (compute_units &&
+        (e = hipDeviceGetAttribute(compute_units, hipDeviceAttributeMultiprocessorCount,
+                                   device)) != hipSuccess)
+        return fail(GQA_ERR_HIP, "compute-unit count: %s", hipGetErrorString(e));
+    if (clock_khz &&
+        (e = hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, device)) != hipSuccess)
+        return fail(GQA_ERR_HIP, "clock rate: %s", hipGetErrorString(e));
+    if (arch && arch_len > 0) {
+        hipDeviceProp_t prop;
+        if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess)
+            return fail(GQA_ERR_HIP, "device properties: %s", hipGetErrorString(e));
+        std::snprintf(arch, arch_len, "%s", prop.gcnArchName);
+    }
+    return ok();
+}
+
+size_t gqa_stream_read_sink_bytes(void) { return (size_t)gqa::hbm_read_blocks() * sizeof(uint32_t); }
+
+int gqa_stream_read(const void *buf, size_t bytes, void *sink, void *stream) {
+    if (!buf) return fail(GQA_ERR_NULL_POINTER, "buf is NULL");
+    if (!sink) return fail(GQA_ERR_NULL_POINTER, "sink is NULL");
+    if (!aligned(buf, 16)) return fail(GQA_ERR_ALIGNMENT, "buf is not 16-byte aligned");
+    if (!aligned(sink, 4)) return fail(GQA_ERR_ALIGNMENT, "sink is not 4-byte aligned");
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(GQA_ERR_BAD_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
+    int rc;
+    if ((rc = hip_status(gqa::launch_hbm_read(buf, bytes, static_cast<uint32_t *>(sink),
+                                              static_cast<hipStream_t>(stream)),
+                         "hbm_read")))
+        return rc;
+    return ok();
+}
 
 int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
                     int *partitions_out, int *states_out, size_t *workspace_bytes_out) {

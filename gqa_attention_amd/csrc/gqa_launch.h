@@ -130,6 +130,12 @@ struct BwdArgs {
 size_t prefill_bwd_workspace_bytes(int B, int S, int H_q);
 hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream);
 
+// Plain streaming read of `bytes` bytes (a multiple of 16) of device memory; sink holds
+// hbm_read_blocks() words and is written only in the (data-dependent, unlikely) case that
+// a workgroup's checksum equals the launch's magic value.
+int hbm_read_blocks();
+hipError_t launch_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 hipError_t launch_decode_split(const DecodeSplitArgs &a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream);

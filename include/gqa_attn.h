@@ -66,6 +66,33 @@ const char *gqa_last_error(void);
 const char *gqa_version(void);
 
 /*
+ * gqa_device_info -- what the roofline figures are computed from: the number of
+ * compute units, the peak engine clock (kHz) and the architecture name of HIP
+ * device `device` (the bf16 dense matrix-core peak of a CDNA4 part is
+ * compute_units * 4096 FLOP per clock).  Any output pointer may be NULL; `arch`
+ * receives at most arch_len bytes, NUL-terminated.  Returns GQA_ERR_BAD_SHAPE for
+ * a device index out of range, GQA_ERR_HIP if the runtime fails.
+ */
+int gqa_device_info(int device, int *compute_units, int *clock_khz, char *arch,
+                    size_t arch_len);
+
+/*
+ * gqa_stream_read -- the decode's bandwidth ceiling on this device: one launch of
+ * a plain streaming-read kernel (one workgroup of 512 threads per compute unit,
+ * eight 16-byte loads in flight per thread) over `bytes` bytes of device memory,
+ * read once each, as the decode sweep reads each cached K/V byte once (V07,
+ * section 14: decode is bound by the K/V bytes read).  Nothing is computed from
+ * the data; it is a calibration, timed by the caller.
+ *
+ *   buf    device memory, 16-byte aligned, read-only; bytes a positive multiple of 16
+ *   sink   gqa_stream_read_sink_bytes() bytes of device memory, 4-byte aligned; a
+ *          word of it is written only if a workgroup's checksum of the data
+ *          happens to equal a fixed constant (which keeps the loads)
+ */
+size_t gqa_stream_read_sink_bytes(void);
+int gqa_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
+
+/*
  * Split-KV plan of a decode launch (V07, section 17, split-K decode: the key
  * axis is cut into partitions whose partial states a second stage merges;
  * ADR-0060, section 4: the partial states are combined in two levels).

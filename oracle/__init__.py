@@ -94,7 +94,11 @@ def load(path=None):
 
 
 def default_threads():
-    return len(os.sched_getaffinity(0))
+    """Host threads the oracle uses: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when the environment sets it (a machine's share of its cores)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() and int(cap) > 0 else n
 
 
 def _u16(a):

@@ -75,36 +75,67 @@ def check_sampled(inp, o, lse, rows, what):
     return check(to_f64(o_all), to_f64(l_all), o_ref, lse_ref, what)
 
 
-def test_prefill_llama_s8192_sampled(gpu_available):
+def test_prefill_llama_s8192_full(gpu_available):
+    """The Llama S = 8192 causal prefill, every O and LSE element of all 64 heads against
+    the oracle (about 1.1e12 fp64 operations on the host)."""
     cfg = LLAMA_PREFILL
     inp = for_config(cfg)
-    say(f"prefill {cfg.name}")
+    say(f"prefill {cfg.name}: GPU, then the oracle on every row")
     q, k, v, o, lse = run_prefill(inp)
-    rows = sample_rows(cfg.S, cfg.H_q, cfg.B, np.random.default_rng(41), 256)
-    stats = check_sampled(inp, o, lse, rows, cfg.name)
-    say(f"  {len(rows)} rows: {stats}")
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o_ref, lse_ref = oracle.prefill_causal(inp["q"], inp["k"], inp["v"])
+    stats = check(to_f64(o), to_f64(lse), o_ref, lse_ref, cfg.name)
+    say(f"  every row of {cfg.H_q} heads: {stats}")
     # deterministic: a second run is bitwise identical
     o2, lse2 = g.prefill_causal(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
-def test_prefill_long_outliers_sampled(gpu_available):
+@pytest.fixture(scope="module")
+def long_prefill_run(gpu_available):
+    """The S = 65536 outlier prefill, run once on the GPU for the sampled checks below."""
     cfg = LLAMA_LONG_PREFILL
     inp = for_config(cfg)
     say(f"prefill {cfg.name}")
     q, k, v, o, lse = run_prefill(inp)
-    # rows right at and after outlier keys stress the online rescale
-    mask = inp["outlier_mask"][0, :, 0]
-    outlier_rows = np.flatnonzero(mask)
-    rng = np.random.default_rng(42)
-    pick = rng.choice(outlier_rows, size=24, replace=False)
-    extra = np.concatenate([pick, np.minimum(pick + 1, cfg.S - 1)])
-    rows = sample_rows(cfg.S, cfg.H_q, cfg.B, rng, 128, extra_rows=extra)
-    stats = check_sampled(inp, o, lse, rows, cfg.name)
+    yield cfg, inp, q, k, v, o, lse
+    del q, k, v, o, lse
+
+
+def long_positions(cfg, inp, part, parts):
+    """Query positions of the S = 65536 check, about 2048 in all, dealt round-robin into
+    `parts` shares: the first and last 64 rows, the rows either side of every 8th q-block
+    (256-row) boundary, the rows at and just after 256 outlier keys, and uniform rows."""
+    S = cfg.S
+    rng = np.random.default_rng(4242)
+    pos = set(range(64)) | set(range(S - 64, S))
+    for blk in range(256, S, 8 * 256):
+        pos |= {blk - 1, blk}
+    outl = np.flatnonzero(inp["outlier_mask"][0].any(axis=-1))
+    for i in rng.choice(outl, size=min(256, outl.size), replace=False):
+        pos |= {int(i), min(int(i) + 1, S - 1)}
+    while len(pos) < 2048:
+        pos.add(int(rng.integers(0, S)))
+    return np.array(sorted(pos))[part::parts]
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_prefill_long_outliers_all_heads(long_prefill_run, part):
+    """A quarter of about 2048 query positions of the S = 65536 prefill with outlier keys,
+    every one of the 64 heads, against the oracle row by row."""
+    cfg, inp, q, k, v, o, lse = long_prefill_run
+    pos = long_positions(cfg, inp, part, 4)
+    b, h, i = np.meshgrid([0], np.arange(cfg.H_q), pos, indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1).astype(np.int32)
+    say(f"  long prefill share {part}: {pos.size} positions x {cfg.H_q} heads")
+    stats = check_sampled(inp, o, lse, rows, f"{cfg.name} share {part}")
     say(f"  {len(rows)} rows: {stats}")
-    # properties at full size: finite, and LSE_i >= s_ii (the diagonal term is one of the sum's)
+
+
+def test_prefill_long_outliers_properties(long_prefill_run):
+    """Properties at full size: finite, and LSE_i >= s_ii (the diagonal term is one of the
+    sum's terms)."""
+    cfg, inp, q, k, v, o, lse = long_prefill_run
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     G = cfg.H_q // cfg.H_kv
     for h in (0, 17, 63):
