@@ -93,6 +93,11 @@ def load_library(path=LIBRARY):
     L.gqa_attn_prefill_causal_bwd.argtypes = [vp, vp, vp, vp, f32p, vp, vp, vp, vp, ci, ci, ci, ci,
                                               ci, cf, vp, cs, vp]
     L.gqa_attn_prefill_causal_bwd.restype = ci
+    L.gqa_attn_decode_noalloc.argtypes = [vp, vp, vp, i32p, vp, f32p, ci, ci, ci, ci, ci, cf, ci,
+                                          vp]
+    L.gqa_attn_decode_noalloc.restype = ci
+    L.gqa_decode_noalloc_max_workspace.argtypes = []
+    L.gqa_decode_noalloc_max_workspace.restype = cs
     L.gqa_device_info.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.c_char_p, cs]
     L.gqa_device_info.restype = ci
     L.gqa_stream_read_sink_bytes.argtypes = []
@@ -209,6 +214,19 @@ def decode(q, k_cache, v_cache, seqlens=None, softmax_scale=None, num_splits=0, 
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(l), B, H_q, H_kv, d,
         S_max, _scale(d, softmax_scale), num_splits, _ptr(workspace), workspace.numel(),
         _stream(q.device)))
+    return o, l
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens=None, softmax_scale=None, num_splits=0, out=None,
+                   lse=None):
+    """decode() with the library's own device workspace (gqa_attn_decode_noalloc): no
+    workspace argument; calls that overlap on one GPU race (see the header)."""
+    B, H_q, H_kv, d, S_max = _decode_shapes(q, k_cache, v_cache, seqlens)
+    o = torch.empty((B, H_q, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, H_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(load_library().gqa_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(l), B, H_q, H_kv, d,
+        S_max, _scale(d, softmax_scale), num_splits, _stream(q.device)))
     return o, l
 
 

@@ -414,6 +414,34 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
     return ok();
 }
 
+int gqa_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seqlens, void *o, float *lse, int B, int H_q, int H_kv,
+                            int d, int S_max, float softmax_scale, int num_splits, void *stream) {
+    Plan pl;
+    int rc;
+    if ((rc = make_plan(B, 1, H_q, H_kv, d, S_max, num_splits, &pl))) return rc;
+    if ((rc = decode_common_checks(q, k_cache, v_cache, seqlens, softmax_scale))) return rc;
+    if ((rc = check_bf16(o, "o")) || (rc = check_f32(lse, "lse"))) return rc;
+    if (pl.bytes > gqa::noalloc_scratch_bytes())
+        return fail(GQA_ERR_WORKSPACE,
+                    "this decode needs %zu bytes of workspace; the library's own holds %zu "
+                    "(use gqa_attn_decode with a caller workspace)",
+                    pl.bytes, gqa::noalloc_scratch_bytes());
+    void *ws = nullptr;
+    hipError_t e = gqa::noalloc_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(GQA_ERR_HIP, "device workspace lookup failed: %s", hipGetErrorString(e));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
+                        ws);
+    if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split"))) return rc;
+    auto m = combine_args(o, lse, B, H_q, d, pl, ws);
+    if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
+    return ok();
+}
+
+size_t gqa_decode_noalloc_max_workspace(void) { return gqa::noalloc_scratch_bytes(); }
+
 int gqa_attn_decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           const int32_t *block_table, const int32_t *seqlens, void *o, float *lse,
                           int B, int T_q, int H_q, int H_kv, int d, int page_size, int num_pages,

@@ -136,6 +136,11 @@ hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream);
 int hbm_read_blocks();
 hipError_t launch_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+// The library's own decode workspace on the current device (decode_noalloc.hip): its
+// size, and its device address (looked up once per device, on first use).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_decode_split(const DecodeSplitArgs &a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_causal(const PrefillArgs &a, hipStream_t stream);

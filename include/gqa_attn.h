@@ -161,6 +161,26 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gqa_attn_decode_noalloc -- gqa_attn_decode for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation): the same split plan, kernels and results,
+ * with the workspace taken from a device array of the library itself instead of
+ * a caller buffer.  Nothing is allocated or freed by this call.
+ *
+ * Every GPU the library runs on holds one such array of
+ * gqa_decode_noalloc_max_workspace() bytes (16 MiB) until the process ends; the
+ * first call on a device looks its address up.  A decode whose plan
+ * (gqa_decode_plan) needs more workspace is rejected with GQA_ERR_WORKSPACE.
+ * All calls on one GPU share its array, so calls that overlap on one GPU (on
+ * different streams, or from different threads) race; calls ordered on one
+ * stream do not.  Arguments and outputs as gqa_attn_decode.
+ */
+int gqa_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seqlens, void *o, float *lse, int B, int H_q, int H_kv,
+                            int d, int S_max, float softmax_scale, int num_splits, void *stream);
+size_t gqa_decode_noalloc_max_workspace(void);
+
+/*
  * The two stages of gqa_attn_decode as separate calls, with the same
  * arguments and workspace layout (V07, section 17: stage 1 writes the partial
  * (m, l, O) of every partition, stage 2 merges them).  gqa_decode_partials
