@@ -326,7 +326,8 @@ def decode_combine(workspace, out, lse, H_kv, S_max, num_splits=0):
 
 def workspace_views(workspace, B, H_q, H_kv, d, S_max, num_splits=0):
     """Views of a decode workspace: (seg [B, 2] int32 -- first state slot and slot count of
-    each sequence --, m2 [N, H_q], l [N, H_q], o [N, H_q, d] float32), N state slots."""
+    each sequence --, m2 [N, H_q], l [N, H_q] float32, o [N, H_q, d] bfloat16), N state
+    slots."""
     N = decode_plan(B, H_q, H_kv, d, S_max, num_splits)["states"]
     a256 = lambda n: (n + 255) // 256 * 256
     off_m2 = a256(B * 2 * 4)
@@ -336,7 +337,7 @@ def workspace_views(workspace, B, H_q, H_kv, d, S_max, num_splits=0):
     seg = f[:B * 2 * 4].view(torch.int32).view(B, 2)
     m2 = f[off_m2:off_m2 + N * H_q * 4].view(torch.float32).view(N, H_q)
     l = f[off_l:off_l + N * H_q * 4].view(torch.float32).view(N, H_q)
-    o = f[off_o:off_o + N * H_q * d * 4].view(torch.float32).view(N, H_q, d)
+    o = f[off_o:off_o + N * H_q * d * 2].view(torch.bfloat16).view(N, H_q, d)
     return seg, m2, l, o
 
 

@@ -606,10 +606,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
             for (int bk = 0; bk < CB; ++bk) {
                 if (row16 < nhb[bk]) {
                     const size_t row = srow + h0 + bk * 16 + row16;
-                    float *orow = a.part_o + row * D + grp * 4;
+                    uint16_t *orow = a.part_o + row * D + grp * 4;
 #pragma unroll
                     for (int dt = 0; dt < T::NDT; ++dt)
-                        *reinterpret_cast<f32x4 *>(orow + dt * 16) = st.o[bk][dt];
+                        *reinterpret_cast<u32x2 *>(orow + dt * 16) =
+                            u32x2{pack_bf16x2(st.o[bk][dt][0], st.o[bk][dt][1]),
+                                  pack_bf16x2(st.o[bk][dt][2], st.o[bk][dt][3])};
                     if (grp == 0) {
                         a.part_m2[row] = st.m[bk];
                         a.part_l[row] = st.l[bk];
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
                     O += al * rw[d];
                 }
                 const size_t row = srow + (hgrp * a.hpw + hw2) * GT + hg * CW + bk * 16 + h;
-                a.part_o[row * D + d] = O;
+                a.part_o[row * D + d] = __builtin_bit_cast(uint16_t, (__bf16)O);
                 if (d == 0) {
                     a.part_m2[row] = L > 0.f ? M : neg_inf();
                     a.part_l[row] = L;

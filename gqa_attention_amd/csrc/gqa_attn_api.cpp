@@ -101,7 +101,7 @@ int make_plan(int B, int T, int H_q, int H_kv, int d, int S_max, int num_splits,
     pl->off_m2 = align256((size_t)B * 2 * sizeof(int32_t));
     pl->off_l = pl->off_m2 + align256(states * sizeof(float));
     pl->off_o = pl->off_l + align256(states * sizeof(float));
-    pl->bytes = pl->off_o + align256(states * (size_t)d * sizeof(float));
+    pl->bytes = pl->off_o + align256(states * (size_t)d * sizeof(uint16_t));   // O in bf16
     return GQA_OK;
 }
 
@@ -159,7 +159,7 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     a.seg = reinterpret_cast<int32_t *>(base);
     a.part_m2 = reinterpret_cast<float *>(base + pl.off_m2);
     a.part_l = reinterpret_cast<float *>(base + pl.off_l);
-    a.part_o = reinterpret_cast<float *>(base + pl.off_o);
+    a.part_o = reinterpret_cast<uint16_t *>(base + pl.off_o);
     a.B = B;
     a.H_q = H_q;
     a.H_kv = H_kv;
@@ -179,13 +179,19 @@ gqa::DecodeSplitArgs split_args(const void *q, const void *k, const void *v,
     return a;
 }
 
+// uniform_tiles: the 16-key tiles of every sequence when all have the same length (seqlens
+// NULL: S_max), which lets the merge find each sequence's states from the plan alone; 0
+// when the lengths live on the device (the merge then reads the split kernel's slot table).
 gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Plan &pl,
-                            const void *ws, int T = 1) {
+                            const void *ws, int T = 1, int uniform_tiles = 0) {
     const char *base = static_cast<const char *>(ws);
     gqa::MergeArgs m;
     m.part_m2 = reinterpret_cast<const float *>(base + pl.off_m2);
     m.part_l = reinterpret_cast<const float *>(base + pl.off_l);
-    m.part_o = reinterpret_cast<const float *>(base + pl.off_o);
+    m.part_o = base + pl.off_o;
+    m.o_bf16 = 1;
+    m.uniform_tiles = uniform_tiles;
+    m.units = pl.units;
     m.seg = reinterpret_cast<const int32_t *>(base);
     m.counts = nullptr;
     m.P = pl.slots;
@@ -199,6 +205,11 @@ gqa::MergeArgs combine_args(void *o, float *lse, int B, int H_q, int d, const Pl
     m.d = d;
     m.T = T;
     return m;
+}
+
+// Tiles of every sequence when seqlens is NULL (all of length S_max), else 0.
+int uniform_tiles(const int32_t *seqlens, int S_max) {
+    return seqlens ? 0 : (S_max + kDecodeTile - 1) / kDecodeTile;
 }
 
 // A paged cache for prefill (block_table null: contiguous).
@@ -286,7 +297,7 @@ int decode_paged(const void *q, const void *k_pool, const void *v_pool, const in
     a.fp8 = fp8;
     a.page_bytes = fp8 ? (size_t)page_size * H_kv * d + 4u * (size_t)page_size : 0;
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (paged)"))) return rc;
-    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q, uniform_tiles(seqlens, S_max));
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -409,7 +420,7 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache,
     auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
                         workspace);
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split"))) return rc;
-    auto m = combine_args(o, lse, B, H_q, d, pl, workspace);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, 1, uniform_tiles(seqlens, S_max));
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -435,7 +446,7 @@ int gqa_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_ca
     auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
                         ws);
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split"))) return rc;
-    auto m = combine_args(o, lse, B, H_q, d, pl, ws);
+    auto m = combine_args(o, lse, B, H_q, d, pl, ws, 1, uniform_tiles(seqlens, S_max));
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -574,7 +585,7 @@ int gqa_attn_decode_tokens(const void *q, const void *k_cache, const void *v_cac
     auto a = split_args(q, k_cache, v_cache, seqlens, B, H_q, H_kv, d, S_max, softmax_scale, pl,
                         workspace, T_q);
     if ((rc = hip_status(gqa::launch_decode_split(a, s), "decode_split (tokens)"))) return rc;
-    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q);
+    auto m = combine_args(o, lse, B, H_q, d, pl, workspace, T_q, uniform_tiles(seqlens, S_max));
     if ((rc = hip_status(gqa::launch_lse_merge(m, s), "lse_merge"))) return rc;
     return ok();
 }
@@ -600,6 +611,9 @@ int gqa_lse_merge(const float *part_m2, const float *part_l, const float *part_o
     m.part_m2 = part_m2;
     m.part_l = part_l;
     m.part_o = part_o;
+    m.o_bf16 = 0;
+    m.uniform_tiles = 0;
+    m.units = 0;
     m.counts = split_counts;
     m.seg = nullptr;
     m.T = 1;
@@ -692,12 +706,11 @@ int gqa_attn_prefill_causal_bwd(const void *q, const void *k, const void *v, con
     if (S <= 0) return fail(GQA_ERR_BAD_SHAPE, "S=%d must be positive", S);
     if (d != 128)
         return fail(GQA_ERR_UNSUPPORTED, "prefill backward head size d=%d (supported: 128)", d);
-    const long n_kb = (S + 255) / 256;
-    if (n_kb * (long)B * H_q > 0x7FFFFFFFL)
+    const long n_qb = (S + 255) / 256;
+    if (n_qb * (long)B * H_q > 0x7FFFFFFFL)
         return fail(GQA_ERR_BAD_SHAPE, "B*H_q*ceil(S/256) exceeds the grid limit");
-    if ((long)B * S * H_kv * (d / 4) / 256 > 0x7FFFFFFFL ||
-        (long)B * H_q * ((S + 63) / 64) * 4 > 0x7FFFFFFFL)
-        return fail(GQA_ERR_BAD_SHAPE, "B*S*H exceeds the grid limit");
+    if ((long)B * H_q * ((S + 63) / 64) * 4 > 0x7FFFFFFFL)
+        return fail(GQA_ERR_BAD_SHAPE, "B*H_q*S exceeds the grid limit");
     if ((rc = check_bf16(q, "q")) || (rc = check_bf16(k, "k")) || (rc = check_bf16(v, "v")) ||
         (rc = check_bf16(o, "o")) || (rc = check_bf16(d_o, "d_o")) || (rc = check_f32(lse, "lse")) ||
         (rc = check_bf16(dq, "dq")) || (rc = check_bf16(dk, "dk")) || (rc = check_bf16(dv, "dv")))
@@ -718,7 +731,7 @@ int gqa_attn_prefill_causal_bwd(const void *q, const void *k, const void *v, con
     a.dq = static_cast<uint16_t *>(dq);
     a.dk = static_cast<uint16_t *>(dk);
     a.dv = static_cast<uint16_t *>(dv);
-    a.stats = a.part_dk = a.part_dv = nullptr;
+    a.stats = nullptr;
     a.B = B;
     a.S = S;
     a.H_q = H_q;

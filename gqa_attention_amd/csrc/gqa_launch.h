@@ -21,11 +21,12 @@ constexpr int kMaxDecodeBatch = 8192;
 // i is the sequence's position len - T + i and sees keys up to it.  Partition x writes its
 // partial state of sequence b (m2, l, O of every row of its KV heads) in state slot x + b;
 // states are stored slot-major, [slot][H_q * T] (O: [..][d]), and seg[b] = {first slot,
-// count} of b.
+// count} of b.  A state's O is stored in bf16 (its m2 and l in fp32).
 struct DecodeSplitArgs {
     const uint16_t *q, *k, *v;  // bf16 bit patterns; q [B][T][H_q][d]
     const int32_t *seqlens;     // [B] or nullptr
-    float *part_m2, *part_l, *part_o;
+    float *part_m2, *part_l;
+    uint16_t *part_o;           // bf16 bits
     int32_t *seg;               // [B][2], written by workgroup (0, 0)
     int B, H_q, H_kv, d, S_max;
     int T;                      // query tokens per sequence
@@ -73,13 +74,21 @@ struct KvDequantArgs {
 hipError_t launch_kv_dequantize_fp8(const KvDequantArgs &a, hipStream_t stream);
 
 // Partial states to merge for (b, r), r = h * T + i the row of query head h, token i:
+//   uniform_tiles > 0 (decode workspace, every sequence of uniform_tiles 16-key tiles):
+//     the slots of sequence b follow from the split plan itself -- the partitions x of
+//     the B * uniform_tiles tiles cut into W = min(units, B * uniform_tiles) ranges that
+//     hold a tile of b, in slot x + b -- at index slot * state_stride + r * head_stride;
 //   seg != nullptr (decode workspace): states p < seg[2b+1], at index
 //     (seg[2b] + p) * state_stride + r * head_stride;
 //   otherwise (caller's partials, T = 1): states p < (counts ? clamp(counts[b], 0, P) : P),
 //     at index b * batch_stride + r * head_stride + p * state_stride.
-// The O array holds d values per index.  Outputs: o [B][T][H_q][d], lse [B][H_q][T].
+// The O array holds d values per index, bf16 (o_bf16: the decode workspace) or fp32 (the
+// caller's partials).  Outputs: o [B][T][H_q][d], lse [B][H_q][T].
 struct MergeArgs {
-    const float *part_m2, *part_l, *part_o;
+    const float *part_m2, *part_l;
+    const void *part_o;
+    int o_bf16;
+    int uniform_tiles, units;
     const int32_t *seg;         // [B][2] or nullptr
     const int32_t *counts;      // [B] or nullptr
     int P;
@@ -114,14 +123,13 @@ struct PrefillArgs {
 constexpr int kPrefillMaxPages = 8192;
 
 // Backward of whole-prompt causal prefill: q, o, dout, dq [B][S][H_q][d]; k, v, dk, dv
-// [B][S][H_kv][d] (bf16); lse [B][H_q][S] (natural log, the forward's).  The launcher lays
-// its workspace out as per-row statistics (lse in log2 units and D = dO . O per 64-row
-// block) and the fp32 per-query-head shares of dK and dV.
+// [B][S][H_kv][d] (bf16); lse [B][H_q][S] (natural log, the forward's).  The workspace holds
+// the per-row statistics (lse in log2 units and D = dO . O per 64-row block).
 struct BwdArgs {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
     uint16_t *dq, *dk, *dv;
-    float *stats, *part_dk, *part_dv;   // set by the launcher inside the workspace
+    float *stats;                       // set by the launcher: the workspace
     int B, S, H_q, H_kv, d;
     float scale;                        // softmax_scale (tau)
     float scale_log2;                   // tau * log2(e)

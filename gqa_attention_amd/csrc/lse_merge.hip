@@ -12,6 +12,11 @@
 // m2 = -inf is empty (a_p = 0); a row with no non-empty partial gets O = 0 and
 // LSE = -inf (the identity state of the merge, V07 section 3).
 //
+// The decode's own states hold O in bf16 (m2 and l in fp32); caller-provided partials are
+// fp32 throughout.  When every sequence of the decode has the same length, the merge finds
+// a sequence's states from the split plan itself instead of reading the split kernel's
+// slot table (one dependent memory round trip less).
+//
 // A row's columns are cut into 32-wide slices, one workgroup of 4 waves per (row, slice),
 // so a row's partials are read by D/32 compute units at once.  Each workgroup folds every
 // partial's (m2, l) (the few bytes every slice needs) and its slice of O.  Lane l of a wave
@@ -45,7 +50,19 @@ __device__ __forceinline__ void merge_into(MState &x, const MState &y) {
     x.m = mn;
 }
 
-template <int D>
+// Four consecutive O values of a partial state: fp32, or bf16 (the decode workspace).
+template <bool OB>
+__device__ __forceinline__ f32x4 load_o4(const void *base, size_t idx) {
+    if constexpr (OB) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(base) + idx);
+        return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xFFFF0000u),
+                     __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
+    } else {
+        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
+    }
+}
+
+template <int D, bool OB>
 __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a) {
     constexpr int NS = D / kSlice;
     __shared__ float red[kMergeWaves][8][6];
@@ -56,7 +73,16 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
 
     int n;
     size_t row0;
-    if (a.seg) {
+    if (a.uniform_tiles > 0) {
+        // the split plan restated: tile t of the B * uniform_tiles went to partition
+        // floor(t * W / tot), and partition x holds its state of sequence b in slot x + b
+        const long tot = (long)a.B * a.uniform_tiles;
+        const long W = min((long)a.units, tot);
+        const long lo = (long)b * a.uniform_tiles, hi = lo + a.uniform_tiles;
+        const long x0 = lo * W / tot, x1 = (hi - 1) * W / tot;
+        n = (int)(x1 - x0 + 1);
+        row0 = (size_t)(x0 + b) * a.state_stride + (size_t)r * a.head_stride;
+    } else if (a.seg) {
         n = a.seg[2 * b + 1];
         row0 = (size_t)a.seg[2 * b] * a.state_stride + (size_t)r * a.head_stride;
     } else {
@@ -66,7 +92,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
     const size_t ss = a.state_stride;
     const float *m2 = a.part_m2 + row0;
     const float *lp = a.part_l + row0;
-    const float *op = a.part_o + row0 * D + q * kSlice + 4 * c;
+    const size_t oi = row0 * D + q * kSlice + 4 * c;   // element index of partial 0
 
     MState st{neg_inf(), 0.f, {0.f, 0.f, 0.f, 0.f}};
     for (int base = 64 * w; base < n; base += kPerRound) {
@@ -78,7 +104,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
             if (p < n) {
                 mv[j] = m2[p * ss];
                 lv[j] = lp[p * ss];
-                ov[j] = *reinterpret_cast<const f32x4 *>(op + (size_t)p * ss * D);
+                ov[j] = load_o4<OB>(a.part_o, oi + (size_t)p * ss * D);
             } else {
                 mv[j] = neg_inf();
                 lv[j] = 0.f;
@@ -130,8 +156,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
 
 template <int D>
 hipError_t launch(const MergeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(lse_merge_kernel<D>, dim3(a.H_q * a.T * (D / kSlice), a.B),
-                       dim3(kMergeWaves * 64), 0, stream, a);
+    const dim3 grid(a.H_q * a.T * (D / kSlice), a.B);
+    if (a.o_bf16)
+        hipLaunchKernelGGL((lse_merge_kernel<D, true>), grid, dim3(kMergeWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((lse_merge_kernel<D, false>), grid, dim3(kMergeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -8,16 +8,16 @@
 // and a KV head's dK and dV add up the contributions of its G query heads (section 14).
 // P is never stored: each kernel forms it again from the row's LSE (section 6.3, recompute).
 //
-// Four launches:
+// Three launches:
 //   bwd_prep   D_i as the row-wise dot of O and dO (section 6.2) and LSE in log2 units, kept
 //              per 64-row block as [lse2 x 64 | D x 64] so one DMA fetches a block's pair;
 //   bwd_dq     query-block outer, key tiles inner, dQ accumulated in registers: no atomics
 //              (section 8: Q outer removes the dQ atomics of the section 6.4 loop);
 //   bwd_dkdv   key-block outer, query tiles inner (the loop of section 6.4 without its dQ
-//              update), one workgroup per (key block, query head): each query head's share
-//              of dK and dV goes to an fp32 workspace slot of its own;
-//   bwd_reduce adds the G slots of each KV head in a fixed order (the split then two-stage
-//              reduce of section 6.5), so results are deterministic.
+//              update), one workgroup per (pair of key blocks, KV head), looping over the
+//              KV head's G query heads with dK and dV in registers: the reduction over the
+//              heads happens on chip (section 6.5), in a fixed order, so results are
+//              deterministic and no partial sums go through memory.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 32 keys x 32 query rows per wave step):
 //   dq kernel   S^T = K.Q^T and dP^T = V.dO^T (K, V rows from LDS; Q, dO fragments in
@@ -303,36 +303,72 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_dkdv: workgroup = 256 keys of one KV head against the rows of one query head (8 waves
-// x 32 keys).  LDS: the V block (64 KiB), then a ring of two slots of a 64-row query tile
-// (Q 16 KiB, dO 16 KiB, statistics 1 KiB), then 1 KiB that the other waves' statistics DMA
-// fills with zeros (every wave issues the same DMA count per tile).
+// bwd_dkdv: workgroup = one block of 128 keys of one KV head against the rows of all G query
+// heads of that KV head, with dK and dV accumulated in registers over the heads: the
+// reduction over a KV head's query heads happens on chip (V07 section 6.5), nothing but the
+// row statistics goes through memory, and the order of the additions is fixed.  Wave w takes
+// the 32 keys of key group w % 4 and, of each 64-row query tile, the 32 rows of row half
+// w / 4; the two waves of a SIMD (waves are dealt to SIMDs round-robin) thus share their keys
+// and split the rows of every tile, and at the end the second half's dK and dV are added to
+// the first's through LDS.  Blocks with the longest prefix of rows run first.
+// LDS: the block's V rows (32 KiB), then a ring of two slots of a 64-row query tile of one
+// head (Q 16 KiB, dO 16 KiB, statistics 1 KiB), then 1 KiB that the other waves' statistics
+// DMA fills with zeros (every wave issues the same DMA count per item).  A work item is a
+// (query tile, head) pair, heads inner.
 
-constexpr int kKBlk = 256;
-constexpr int kVBlock = kKBlk * kRowBytes;           // 64 KiB
-constexpr int kQTile = kStatRows * kRowBytes;        // 16 KiB
-constexpr int kSlot = 2 * kQTile + 1024;
+constexpr int kKBlk = 128;                           // keys per workgroup
+constexpr int kVBlock = kKBlk * kRowBytes;           // 32 KiB
+constexpr int kQTile = kStatRows * kRowBytes;        // 16 KiB: 64 rows
+constexpr int kSlot = 2 * kQTile + 1024;             // Q, dO, statistics
 constexpr int kRing = kVBlock;
 constexpr int kSink = kRing + 2 * kSlot;
-constexpr int kKvLds = kSink + 1024;                 // 131 KiB: one workgroup per CU
+constexpr int kKvLds = kSink + 1024;                 // 99 KiB: one workgroup per CU
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kb, int n_t,
-                                                               int S_pad) {
+// Row half 1 stores its accumulators x at xch (element 4 j .. 4 j + 3 at xch[64 j]); row
+// half 0 adds them to its own (half 0 + half 1, a fixed order).  Both halves call it.
+__device__ __forceinline__ void hand_over(f32x16 (&x)[4], f32x4 *xch, int rh) {
+    if (rh == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xch[(dt * 4 + q) * 64] =
+                    f32x4{x[dt][4 * q], x[dt][4 * q + 1], x[dt][4 * q + 2], x[dt][4 * q + 3]};
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 y = xch[(dt * 4 + q) * 64];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[dt][4 * q + e] += y[e];
+            }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kb, int n_t) {
     __shared__ __attribute__((aligned(256))) uint8_t smem[kKvLds];
     const int G = a.H_q / a.H_kv;
+    // workgroup -> (block, b, KV head g); consecutive workgroups (dealt round-robin over the
+    // XCDs) take consecutive KV heads, so the blocks of one KV head share an XCD's L2 for
+    // the Q and dO tiles of its query heads when H_kv is a multiple of 8
     int u = blockIdx.x;
-    const int h = u % a.H_q;
-    u /= a.H_q;
+    const int g = u % a.H_kv;
+    u /= a.H_kv;
     const int b = u % a.B;
-    const int kb = u / a.B;                // block 0 (every row sees it) first
-    const int g = h / G;
+    const int kb = u / a.B;                          // block 0 (every row sees it) first
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r32 = lane & 31, hf = lane >> 5;
+    const int rh = w / 4, kg = w % 4;                // row half, key group
     const int k0 = kb * kKBlk;
-    const int key = k0 + 32 * w + r32;     // the lane's key
-    const int t0 = k0 / kStatRows;         // first query tile (rows k0 ..)
+    const int kw0 = k0 + 32 * kg;                    // the wave's first key
+    const int key = kw0 + r32;                       // the lane's key
+    const int t0 = k0 / kStatRows;                   // first query tile: rows k0 ..
     const Addr ad = make_addr(lane);
     const int lr = 4 * w + lane / 16;
 
@@ -340,9 +376,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     const uint32_t kv_row_bytes = (uint32_t)a.H_kv * kRowBytes;
     const uint32_t qvoff = (uint32_t)lr * q_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
     const uint32_t kvvoff = (uint32_t)lr * kv_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
-    const uint16_t *qbase = a.q + ((size_t)b * a.S * a.H_q + h) * D;
-    const uint16_t *gbase = a.dout + ((size_t)b * a.S * a.H_q + h) * D;
-    const float *stbase = a.stats + ((size_t)b * a.H_q + h) * n_t * kStatFloats;
 
     // K fragments (B operand of S = Q.K^T): column = the lane's key, slots d = 16 ks + 8 hf ..
     bf16x8 kf[8];
@@ -355,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
             kf[ks] = as_bf16x8(live ? x : u32x4{0u, 0u, 0u, 0u});
         }
     }
-    // the V block: rows k0 .. k0 + 255 of KV head g
+    // the block's V rows: each wave copies 4 rows of every 32-row group
     {
         const uint16_t *vb = a.v + (((size_t)b * a.S + k0) * a.H_kv + g) * D;
 #pragma unroll
@@ -363,22 +396,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
             dma_rows32(smem, 32 * i * kRowBytes, vb + (size_t)32 * i * a.H_kv * D, kv_row_bytes,
                        a.S - k0 - 32 * i, kvvoff, w);
     }
-    auto issue = [&](int t, int slot) {
+    const int vrow = 32 * kg;                        // the wave's V rows in the block
+
+    const int n_items = (n_t - t0) * G;
+    auto issue = [&](int it, int slot) {
+        const bool real = it < n_items;
+        const int t = real ? t0 + it / G : 0;
+        const int h = g * G + (real ? it % G : 0);
         const int base = kRing + slot * kSlot;
         const int r = t * kStatRows;
+        const int rows = real ? a.S - r : 0;          // past the last item: zero-fill only
+        const uint16_t *qbase = a.q + (((size_t)b * a.S + r) * a.H_q + h) * D;
+        const uint16_t *gbase = a.dout + (((size_t)b * a.S + r) * a.H_q + h) * D;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            dma_rows32(smem, base + 32 * i * kRowBytes, qbase + (size_t)(r + 32 * i) * a.H_q * D,
-                       q_row_bytes, a.S - r - 32 * i, qvoff, w);
+            dma_rows32(smem, base + 32 * i * kRowBytes, qbase + (size_t)32 * i * a.H_q * D,
+                       q_row_bytes, rows - 32 * i, qvoff, w);
             dma_rows32(smem, base + kQTile + 32 * i * kRowBytes,
-                       gbase + (size_t)(r + 32 * i) * a.H_q * D, q_row_bytes, a.S - r - 32 * i,
-                       qvoff, w);
+                       gbase + (size_t)32 * i * a.H_q * D, q_row_bytes, rows - 32 * i, qvoff, w);
         }
-        // statistics block t (512 bytes) by wave 0; the other waves zero-fill the sink
-        const bool mine = w == 0 && t < n_t;
-        dma_bytes1k(smem, mine ? base + 2 * kQTile : kSink,
-                    stbase + (size_t)min(t, n_t - 1) * kStatFloats, mine ? 512u : 0u,
-                    16u * (uint32_t)lane);
+        // statistics block (h, t) (512 bytes) by wave 0; the other waves zero-fill the sink
+        const bool mine = w == 0 && real;
+        const float *stp = a.stats + (((size_t)b * a.H_q + h) * n_t + t) * kStatFloats;
+        dma_bytes1k(smem, mine ? base + 2 * kQTile : kSink, stp,
+                    mine ? (uint32_t)(kStatFloats * sizeof(float)) : 0u, 16u * (uint32_t)lane);
     };
 
     f32x16 dv[4], dk[4];
@@ -388,18 +429,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
         for (int r = 0; r < 16; ++r) dv[dt][r] = dk[dt][r] = 0.f;
     const float c = a.scale_log2;
 
-    issue(t0, 0);
+    issue(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = t0; t < n_t; ++t) {
-        const int slot = (t - t0) & 1;
-        issue(t + 1, slot ^ 1);
-        const uint32_t base = kRing + slot * kSlot;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int us = 2 * (t - t0) + hh;   // 32-row step relative to the key block
-            if (us < w) continue;               // rows all before the wave's keys
-            const uint32_t qh = base + hh * 32 * kRowBytes;
+    for (int it = 0; it < n_items; ++it) {
+        const int slot = it & 1;
+        issue(it + 1, slot ^ 1);
+        const int r0 = (t0 + it / G) * kStatRows + 32 * rh;   // the wave's first row
+        if (r0 >= kw0) {                                      // (rows all before the keys: skip)
+            const uint32_t qh = kRing + slot * kSlot + rh * 32 * kRowBytes;
             const uint32_t gh = qh + kQTile;
             f32x16 s, dp;
 #pragma unroll
@@ -407,23 +445,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 s = mfma32(read_row(smem, qh, ad, ks), kf[ks], s);
-                dp = mfma32(read_row(smem, gh, ad, ks),
-                            read_row(smem, 32 * w * kRowBytes, ad, ks), dp);
+                dp = mfma32(read_row(smem, gh, ad, ks), read_row(smem, vrow * kRowBytes, ad, ks),
+                            dp);
             }
-            // lse2 and D of the lane's 16 rows 32 hh + 8 q + 4 hf + (0..3)
-            const uint8_t *stp = smem + base + 2 * kQTile;
+            // lse2 and D of the lane's 16 rows 32 rh + 8 q + 4 hf + (0..3)
+            const uint8_t *stp = smem + kRing + slot * kSlot + 2 * kQTile;
             float p[16], ds[16];
-            const bool diag = us == w;
+            const bool diag = r0 == kw0;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int rr = 32 * hh + 8 * q4 + 4 * hf;
+                const int rr = 32 * rh + 8 * q4 + 4 * hf;
                 const f32x4 l4 = *reinterpret_cast<const f32x4 *>(stp + 4 * rr);
                 const f32x4 d4 = *reinterpret_cast<const f32x4 *>(stp + 4 * (kStatRows + rr));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * q4 + j;
                     float pv = exp2_fast(fmaf(s[r], c, -l4[j]));
-                    // diagonal step: rows k0 + 32 w + (8 q4 + 4 hf + j), keys k0 + 32 w + r32
+                    // diagonal step: rows r0 + (8 q4 + 4 hf + j), keys r0 + r32
                     if (diag && r32 > 8 * q4 + 4 * hf + j) pv = 0.f;
                     p[r] = pv;
                     ds[r] = pv * (dp[r] - d4[j]);
@@ -439,83 +477,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
                 dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 1), d1, dk[dt]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);   // the next tile's DMA
+        __builtin_amdgcn_s_waitcnt(0);   // the next item's DMA
         __syncthreads();
     }
 
-    // this query head's share: rows of the fp32 slot [b][h][key][d] (keys past S are padding)
+    // row half 1 hands its sums to row half 0 through LDS (the query-tile ring, free now),
+    // dK then dV: element 4 j .. 4 j + 3 of lane l of key group k at ((k * 16 + j) * 64 + l)
+    // * 16 bytes, so each store and load of a wave is 1 KiB contiguous
+    f32x4 *xch = reinterpret_cast<f32x4 *>(smem + kRing) + kg * 16 * 64 + lane;
+    hand_over(dk, xch, rh);
+    hand_over(dv, xch, rh);
+    if (rh == 1 || key >= a.S) return;
+
+    // dK (times tau) and dV of the lane's key, summed over the G heads, rounded to bf16
     const float tau = a.scale;
-    const size_t off = (((size_t)b * a.H_q + h) * S_pad + key) * D;
+    const size_t off = (((size_t)b * a.S + key) * a.H_kv + g) * D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
             const int dd = dt * 32 + rq * 8 + hf * 4;
             const int r = rq * 4;
-            *reinterpret_cast<f32x4 *>(a.part_dk + off + dd) =
-                f32x4{dk[dt][r] * tau, dk[dt][r + 1] * tau, dk[dt][r + 2] * tau, dk[dt][r + 3] * tau};
-            *reinterpret_cast<f32x4 *>(a.part_dv + off + dd) =
-                f32x4{dv[dt][r], dv[dt][r + 1], dv[dt][r + 2], dv[dt][r + 3]};
+            *reinterpret_cast<u32x2 *>(a.dk + off + dd) =
+                u32x2{pack_bf16x2(dk[dt][r] * tau, dk[dt][r + 1] * tau),
+                      pack_bf16x2(dk[dt][r + 2] * tau, dk[dt][r + 3] * tau)};
+            *reinterpret_cast<u32x2 *>(a.dv + off + dd) =
+                u32x2{pack_bf16x2(dv[dt][r], dv[dt][r + 1]), pack_bf16x2(dv[dt][r + 2], dv[dt][r + 3])};
         }
-}
-
-// ---------------------------------------------------------------------------------------
-// bwd_reduce: dK, dV of (b, j, g) = the sum of the G query heads' slots, in head order.
-
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int S_pad) {
-    const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    const long total = (long)a.B * a.S * a.H_kv * (D / 4);
-    if (t >= total) return;
-    const int c4 = (int)(t % (D / 4));
-    long x = t / (D / 4);
-    const int g = (int)(x % a.H_kv);
-    x /= a.H_kv;
-    const int j = (int)(x % a.S);
-    const int b = (int)(x / a.S);
-    const int G = a.H_q / a.H_kv;
-    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-    for (int e = 0; e < G; ++e) {
-        const size_t off = (((size_t)b * a.H_q + g * G + e) * S_pad + j) * D + 4 * c4;
-        sk += *reinterpret_cast<const f32x4 *>(a.part_dk + off);
-        sv += *reinterpret_cast<const f32x4 *>(a.part_dv + off);
-    }
-    const size_t o = (((size_t)b * a.S + j) * a.H_kv + g) * D + 4 * c4;
-    *reinterpret_cast<u32x2 *>(a.dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
-    *reinterpret_cast<u32x2 *>(a.dv + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
 }
 
 }  // namespace
 
 size_t prefill_bwd_workspace_bytes(int B, int S, int H_q) {
     const size_t n_t = (size_t)(S + kStatRows - 1) / kStatRows;
-    const size_t S_pad = (size_t)(S + kKBlk - 1) / kKBlk * kKBlk;
-    const size_t stats = (size_t)B * H_q * n_t * kStatFloats * sizeof(float);
-    const size_t part = (size_t)B * H_q * S_pad * D * sizeof(float);
-    return ((stats + 255) & ~size_t(255)) + 2 * part;
+    return (size_t)B * H_q * n_t * kStatFloats * sizeof(float);
 }
 
 hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream) {
     if (a.d != D) return hipErrorInvalidValue;
     const int n_t = (a.S + kStatRows - 1) / kStatRows;
     const int n_qb = (a.S + kQBr - 1) / kQBr;
-    const int n_kb = (a.S + kKBlk - 1) / kKBlk;
-    const int S_pad = n_kb * kKBlk;
-    char *base = static_cast<char *>(ws);
-    const size_t stats = (size_t)a.B * a.H_q * n_t * kStatFloats * sizeof(float);
-    a.stats = reinterpret_cast<float *>(base);
-    a.part_dk = reinterpret_cast<float *>(base + ((stats + 255) & ~size_t(255)));
-    a.part_dv = a.part_dk + (size_t)a.B * a.H_q * S_pad * D;
+    a.stats = static_cast<float *>(ws);
 
     const long prep_rows = (long)a.B * a.H_q * n_t * kStatRows;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((prep_rows + 15) / 16)), dim3(256), 0,
                        stream, a, n_t);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((long)n_qb * a.B * a.H_q)), dim3(kThreads),
                        0, stream, a, n_qb, n_t);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((long)n_kb * a.B * a.H_q)),
-                       dim3(kThreads), 0, stream, a, n_kb, n_t, S_pad);
-    const long red = (long)a.B * a.S * a.H_kv * (D / 4);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((red + 255) / 256)), dim3(256), 0,
-                       stream, a, S_pad);
+    const int n_kb = (a.S + kKBlk - 1) / kKBlk;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((long)n_kb * a.B * a.H_kv)),
+                       dim3(kThreads), 0, stream, a, n_kb, n_t);
     return hipGetLastError();
 }
 

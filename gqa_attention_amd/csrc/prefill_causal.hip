@@ -25,12 +25,17 @@
 // d column) come from the row-major V tile through the LDS transpose read.
 //
 // Software pipeline inside each wave (32-key steps): the matrix cores form the
-// scores of step u+1 while the vector units run the softmax of step u, and the
-// row maximum of step u+1 is taken while step u's P.V runs (V07 section 10
-// overlaps the same two phases across warpgroups).  K/V tiles travel from HBM
+// scores of step u+1 while the vector units run the softmax of step u (V07 section
+// 10 overlaps the same two phases across warpgroups).  A step first issues all of its
+// LDS fragment reads -- the K rows of step u+1 and the V^T fragments of step u -- so
+// that no product waits for LDS in the middle of the step.  The softmax runs against
+// the running max as it stands; only when a step's P passes a bound (a score above the
+// running max by about 8 in log2 units, and always on the first step) is the max
+// raised to the row's maximum and the step formed again, so the common step takes no
+// row maximum at all (V07 section 3: any common shift cancels in O / l).  K/V tiles travel from HBM
 // straight into LDS (buffer loads with an LDS destination: no staging
 // registers; rows past the sequence end read as zeros) through rings of four K
-// and three V tile buffers, issued a tile ahead of the tile that waits for them.
+// and four V tile buffers, each tile issued three tiles ahead of its use.
 // Rows are stored with their 16-byte chunks XOR-permuted so that the fragment
 // reads of both products are bank-conflict free without padding.
 //
@@ -63,13 +68,13 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRowBytes = D * 2;                  // one key row of one head: 256 B
 constexpr int kTileBytes = kBc * kRowBytes;       // 16 KiB
 constexpr int kNK = 4;                            // LDS: a ring of four K tile buffers
-constexpr int kNV = 3;                            // and a ring of three V tile buffers
+constexpr int kNV = 4;                            // and a ring of four V tile buffers
 constexpr int kKBuf = 0;
 constexpr int kVBuf = kNK * kTileBytes;
-constexpr int kLdsBytes = (kNK + kNV) * kTileBytes;   // 112 KiB: one workgroup per CU
+constexpr int kLdsBytes = (kNK + kNV) * kTileBytes;   // 128 KiB: one workgroup per CU
 constexpr int kDmaPerTile = 2;                    // DMA instructions per wave, tile and tensor
 constexpr int kXcds = 8;
-constexpr float kSlack = 8.f;     // lazy-rescale slack, log2 units: P <= 2^8 between rescales
+constexpr float kPBound = 256.f;   // a lane's step sum of P above this moves the running max
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -154,16 +159,27 @@ struct FragAddr {
     uint32_t v[4];   // V: transpose-read start for d tile dt (add 16 rows per k-step)
 };
 
-// S^T = K . Q^T for 32 keys whose K rows start at LDS byte offset kh.
-__device__ __forceinline__ void qk_half(f32x16 &s, const uint8_t *kh, const FragAddr &fa,
-                                        const bf16x8 (&qf)[8]) {
+// K fragments of 32 keys whose K rows start at LDS byte offset kh.
+__device__ __forceinline__ void load_k(bf16x8 (&kf)[8], const uint8_t *kh, const FragAddr &fa) {
+#pragma unroll
+    for (int k8 = 0; k8 < 8; ++k8)
+        kf[k8] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kh + fa.k[k8]));
+}
+
+// S^T = K . Q^T for 32 keys.
+__device__ __forceinline__ void qk_half(f32x16 &s, const bf16x8 (&kf)[8], const bf16x8 (&qf)[8]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int k8 = 0; k8 < 8; ++k8) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(kh + fa.k[k8]));
-        s = mfma32(kf, qf[k8], s);
-    }
+    for (int k8 = 0; k8 < 8; ++k8) s = mfma32(kf[k8], qf[k8], s);
+}
+
+// S^T = K . Q^T for 32 keys whose K rows start at LDS byte offset kh.
+__device__ __forceinline__ void qk_half(f32x16 &s, const uint8_t *kh, const FragAddr &fa,
+                                        const bf16x8 (&qf)[8]) {
+    bf16x8 kf[8];
+    load_k(kf, kh, fa);
+    qk_half(s, kf, qf);
 }
 
 // Element r of a lane's 16 scores of a half is key k0 + 8*(r/4) + 4*hf + r%4.
@@ -171,42 +187,10 @@ __device__ __forceinline__ int score_key(int k0, int r, int hf) {
     return k0 + (r >> 2) * 8 + hf * 4 + (r & 3);
 }
 
-// Row maximum of a lane's 16 raw scores (masked keys hold -inf).
-__device__ __forceinline__ float half_max(const f32x16 &s) {
-    float mx = neg_inf();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    return mx;
-}
-
-// Lazy rescale: the running max m (shared by the row's two lanes) moves only when a
-// score passes it by more than kSlack (log2 units); otherwise p = 2^(s2 - m) <= 2^kSlack,
-// O and l keep their scale, and no cross-lane step is needed.  A common shift cancels in
-// O / l (V07 section 3, shift insertion), so the result is the same; the slack only
-// bounds P and spares the O rescale in almost every step.  The first step always moves m
-// (m = -inf).  mx is the step's raw row max from this lane's half of the row.
-__device__ __forceinline__ void update_max(float mx, float c, float &m, float &l, float &lw,
-                                           f32x16 (&o)[4]) {
-    if (__any(mx * c > m + kSlack)) {
-        mx = wave_max_xor(mx, 32);
-        const float m_new = fmaxf(m, mx * c);
-        const float alpha = exp2_fast(m - m_new);     // 0 on the first step
-        l *= alpha;
-        lw *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        m = m_new;
-    }
-}
-
-// P = 2^(s * c - m) as the B operand of P.V (a masked score, -inf, gives 0).  k-step kk
-// (16 keys): slot j <-> element r = 8*kk + j, i.e. key 16*kk + 8*(j/4) + 4*hf + j%4.  Two
-// row sums: l of the fp32 P gives the LSE; lw of the bf16-rounded P (the weights the
-// matrix product uses) normalises O, so O is an exact convex combination of them.
+// P = 2^(s * c - m) as the B operand of P.V (a masked score, -inf, gives 0), with the
+// step's two row sums of this lane's half: rs of the fp32 P, rw of the bf16-rounded P.
 __device__ __forceinline__ void softmax_half(const f32x16 &s, float m, float c,
-                                             bf16x8 (&pf)[2], float &l, float &lw) {
+                                             bf16x8 (&pf)[2], float &rs_out, float &rw_out) {
     const float neg_m = -m;
     float rs = 0.f, rw = 0.f;
 #pragma unroll
@@ -223,15 +207,37 @@ __device__ __forceinline__ void softmax_half(const f32x16 &s, float m, float c,
         for (int i = 0; i < 4; ++i) rw = add_bf16_pair(w[i], rw);
         pf[kk] = as_bf16x8(w);
     }
-    l += rs;       // this lane's half of the row; the halves are added at the end
-    lw += rw;
+    rs_out = rs;
+    rw_out = rw;
 }
 
-// O^T += V^T . P^T over 32 keys whose V rows start at LDS byte offset vh.  Each transpose
-// read hands lane l the 4 keys of its slot run at column 32*dt + l%32; two of them make
-// one 8-key operand.
-__device__ __forceinline__ void pv_half(f32x16 (&o)[4], const uint8_t *vh, const uint32_t (&va)[4],
-                                        const bf16x8 (&pf)[2]) {
+// New running max after a step whose P overflowed the bound (or the first step, m = -inf):
+// m = the row's max of m and its scores (both lanes of the row agree), and O, l rescaled.
+__device__ __forceinline__ void raise_max(const f32x16 &s, float c, float &m, float &l, float &lw,
+                                          f32x16 (&o)[4]) {
+    float mx = neg_inf();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m, mx * c);
+    const float alpha = exp2_fast(m - m_new);     // 0 on the first step
+    l *= alpha;
+    lw *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    m = m_new;
+}
+
+// V^T fragments of 32 keys whose V rows start at LDS byte offset vh: for d tile dt and
+// k-step kk, the two transpose reads that make one 8-key operand.  Read all at once, ahead
+// of the softmax, so that the P.V products never wait for LDS.
+struct VtFrags {
+    u32x4 f[4][2];
+};
+
+__device__ __forceinline__ void load_vt(VtFrags &vt, const uint8_t *vh, const uint32_t (&va)[4]) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -239,10 +245,17 @@ __device__ __forceinline__ void pv_half(f32x16 (&o)[4], const uint8_t *vh, const
             const uint8_t *vp = vh + va[dt] + kk * 16 * kRowBytes;
             const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp));
             const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp + 8 * kRowBytes));
-            const u32x4 wv = {lo[0], lo[1], hi[0], hi[1]};
-            o[dt] = mfma32(as_bf16x8(wv), pf[kk], o[dt]);
+            vt.f[dt][kk] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
     }
+}
+
+// O^T += V^T . P^T over 32 keys.
+__device__ __forceinline__ void pv_half(f32x16 (&o)[4], const VtFrags &vt, const bf16x8 (&pf)[2]) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) o[dt] = mfma32(as_bf16x8(vt.f[dt][kk]), pf[kk], o[dt]);
 }
 
 struct WaveCtx {
@@ -273,7 +286,7 @@ __device__ __forceinline__ void dma(const WaveCtx &x, int dst, const uint16_t *b
 
 struct RowState {
     f32x16 o[4];
-    float m, l, lw, mx;   // mx: raw row max of the next step's scores
+    float m, l, lw;
 };
 
 // Scores of keys past the lane's query position become -inf (their P is then exactly 0).
@@ -293,39 +306,51 @@ __device__ __forceinline__ void half_step(const WaveCtx &x, int u, const f32x16 
                                           const uint32_t (&va)[4], const bf16x8 (&qf)[8],
                                           RowState &st) {
     if (u >= x.n_sub) return;
-    update_max(st.mx, x.c, st.m, st.l, st.lw, st.o);
+    bf16x8 kf[8];
+    load_k(kf, kn, x.fa);
+    VtFrags vt;
+    load_vt(vt, vh, va);
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[2];
-    softmax_half(s, st.m, x.c, pf, st.l, st.lw);
-    qk_half(sn, kn, x.fa, qf);
-    pv_half(st.o, vh, va, pf);
+    float rs, rw;
+    softmax_half(s, st.m, x.c, pf, rs, rw);
+    qk_half(sn, kf, qf);
+    // the running max is moved only when a P of this step passes the bound (or is NaN, as on
+    // the first step, where m = -inf): then the step is formed again against the new max
+    if (__any(!(rs <= kPBound))) {
+        raise_max(s, x.c, st.m, st.l, st.lw, st.o);
+        softmax_half(s, st.m, x.c, pf, rs, rw);
+    }
+    st.l += rs;
+    st.lw += rw;
+    pv_half(st.o, vt, pf);
     // (masking the scores of step n_sub, which no step uses, is harmless)
     if (u + 1 >= x.mask_from) mask_half(sn, (u + 1) * kHalf, x.row, x.hf);
-    st.mx = half_max(sn);
 }
 
-// One LDS tile kb (KI = kb % 4 names its K buffer; V buffers rotate mod 3 at run time).
-// Start the DMA of K(kb+3) into the K buffer that K(kb-1) has left, run the first
-// pipeline step of tile kb, start the DMA of V(kb+2) into the V buffer V(kb-1) has left
-// (issuing the two apart measured slightly faster than back to back), run the second
-// step (which forms the scores of tile kb+1's first half); then wait for the DMA issued
-// one tile earlier (the data of tile kb+1 and of K(kb+2)) and meet the other waves.
-// Every buffer written here is read two barriers later, and every buffer read here is
-// refilled only after the next barrier.  The DMA is issued on every tile (past the end
-// it only zero-fills a free buffer), so each wave has exactly 2 * kDmaPerTile of them
-// per tile.
+// One LDS tile kb (KI = kb % 4 names its K and V buffers).  Start the DMA of K(kb+3) into
+// the K buffer that K(kb-1) has left, run the first pipeline step of tile kb, start the DMA
+// of V(kb+3) into the V buffer V(kb-1) has left (issuing the two apart measured slightly
+// faster than back to back), run the second step (which forms the scores of tile kb+1's
+// first half); then wait for the DMA issued one tile earlier (K(kb+2) and V(kb+2)) and meet
+// the other waves.  Every buffer written here is read at least two barriers later, and
+// every buffer read here is refilled only after the next barrier.  The DMA is issued on
+// every tile (past the end it only zero-fills a free buffer), so each wave has exactly
+// 2 * kDmaPerTile of them per tile.
 template <int KI, bool Paged>
 __device__ __forceinline__ void tile_step(const WaveCtx &x, int kb, f32x16 &sa, f32x16 &sb,
                                           const bf16x8 (&qf)[8], RowState &st) {
     constexpr int kCur = kKBuf + KI * kTileBytes;
     constexpr int kNext = kKBuf + ((KI + 1) % kNK) * kTileBytes;
     constexpr int kFree = kKBuf + ((KI + 3) % kNK) * kTileBytes;
-    const int vcur = kVBuf + (kb % kNV) * kTileBytes;
+    constexpr int vcur = kVBuf + KI * kTileBytes;
+    constexpr int vfree = kVBuf + ((KI + 3) % kNV) * kTileBytes;
     dma<Paged>(x, kFree, x.kbase, (kb + 3) * kBc, x.koff);
     uint32_t va[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) va[dt] = x.fa.v[dt] + (uint32_t)vcur;
     half_step(x, 2 * kb, sa, sb, x.lds + kCur + kHalf * kRowBytes, x.lds, va, qf, st);
-    dma<Paged>(x, kVBuf + ((kb + 2) % kNV) * kTileBytes, x.vbase, (kb + 2) * kBc, x.voff);
+    dma<Paged>(x, vfree, x.vbase, (kb + 3) * kBc, x.voff);
     half_step(x, 2 * kb + 1, sb, sa, x.lds + kNext, x.lds + kHalf * kRowBytes, va, qf, st);
     // vmcnt(2 * kDmaPerTile): only this tile's DMA may still be in flight
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerTile));
@@ -426,7 +451,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     st.m = neg_inf();
     st.l = 0.f;
     st.lw = 0.f;
-    st.mx = neg_inf();
     f32x16 sa, sb;
 
     if constexpr (Paged) {
@@ -436,15 +460,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
         for (int i = threadIdx.x; i < n; i += kThreads) tbl[i] = row[i];
         __syncthreads();
     }
-    // prologue: K(0..2) and V(0..1) into LDS, then the scores of the first step
+    // prologue: K(0..2) and V(0..2) into LDS, then the scores of the first step
     for (int t = 0; t < 3; ++t) dma<Paged>(x, kKBuf + t * kTileBytes, x.kbase, t * kBc, x.koff);
-    for (int t = 0; t < 2; ++t) dma<Paged>(x, kVBuf + t * kTileBytes, x.vbase, t * kBc, x.voff);
+    for (int t = 0; t < 3; ++t) dma<Paged>(x, kVBuf + t * kTileBytes, x.vbase, t * kBc, x.voff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (x.n_sub > 0) {
         qk_half(sa, smem + kKBuf, x.fa, qf);
         if (x.mask_from == 0) mask_half(sa, 0, x.row, hf);
-        st.mx = half_max(sa);
     }
 
     int kb = 0;

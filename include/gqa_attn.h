@@ -460,8 +460,8 @@ int gqa_attn_decode_paged_fp8(const void *q, const void *k_pool, const void *v_p
 /*
  * gqa_prefill_bwd_workspace_bytes -- device workspace (bytes, 256-byte aligned
  * start required) of gqa_attn_prefill_causal_bwd for these sizes, or 0 if the
- * sizes are invalid.  It holds each row's statistics and the fp32 shares of dK
- * and dV of every query head: about 2 * B * H_q * S * d * 4 bytes.
+ * sizes are invalid.  It holds each row's statistics (its LSE in log2 units and
+ * D_i = dO_i . O_i): 8 bytes per query row and head, B * H_q * ceil(S/64) * 512.
  */
 size_t gqa_prefill_bwd_workspace_bytes(int B, int S, int H_q, int H_kv, int d);
 
@@ -475,8 +475,8 @@ size_t gqa_prefill_bwd_workspace_bytes(int B, int S, int H_q, int H_kv, int d);
  * with dK and dV of a KV head summed over its G query heads (section 14).  P is
  * formed again from LSE, never stored (section 6.3).  dQ is accumulated with the
  * query block outer and dK, dV with the key block outer, so no atomics are used
- * (section 8; section 6.5); dK and dV add the query heads' fp32 shares in a fixed
- * order, so results are bitwise reproducible.
+ * (section 8; section 6.5); dK and dV of a KV head are summed over its query heads
+ * on chip, in a fixed order, so results are bitwise reproducible.
  *
  *   q, o, d_o  [B, S, H_q, d]  bf16, device, read-only (o: the forward's output)
  *   k, v       [B, S, H_kv, d] bf16, device, read-only

@@ -64,13 +64,14 @@ def test_decode_plan(args, expect):
     assert plan["states"] == expect + B - 1
     a256 = lambda n: (n + 255) // 256 * 256
     n = plan["states"] * H_q
-    assert plan["workspace_bytes"] == a256(B * 8) + 2 * a256(n * 4) + a256(n * d * 4)
+    assert plan["workspace_bytes"] == a256(B * 8) + 2 * a256(n * 4) + a256(n * d * 2)
 
 
 def test_decode_plan_workspace_size_at_llama_shape():
-    # 256 partitions x 64 heads x (m, l, 128-wide O) fp32 partial states, plus the slot table
+    # 256 partitions x 64 heads x (m, l fp32; 128-wide O bf16) partial states, plus the
+    # slot table
     plan = g.decode_plan(1, 64, 8, 128, 32768, 32)
-    assert plan["workspace_bytes"] == 256 + 256 * 64 * (128 + 2) * 4
+    assert plan["workspace_bytes"] == 256 + 256 * 64 * (2 * 4 + 128 * 2)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -153,7 +154,7 @@ def test_decode_tokens_plan_folds_rows():
     assert p8["partitions"] == 128
     a256 = lambda n: (n + 255) // 256 * 256
     n = 256 * 64 * 4
-    assert p4["workspace_bytes"] == 256 + 2 * a256(n * 4) + a256(n * 128 * 4)
+    assert p4["workspace_bytes"] == 256 + 2 * a256(n * 4) + a256(n * 128 * 2)
     assert g.decode_tokens_plan(2, 1, 64, 8, 128, 1000, 0) == g.decode_plan(2, 64, 8, 128, 1000, 0)
 
 
@@ -217,13 +218,10 @@ def test_prefill_chunk_paged_rejects_before_launch(lib, kw, code):
 
 
 def test_prefill_bwd_workspace_size(lib):
-    """Statistics [B, H_q, ceil(S/64), 128] fp32 (256-byte aligned), then two fp32 shares
-    [B, H_q, S rounded up to 256, d]; 0 for invalid sizes."""
+    """Statistics only, [B, H_q, ceil(S/64), 128] fp32 (dK and dV are summed over the query
+    heads on chip); 0 for invalid sizes."""
     B, S, H_q, H_kv, d = 2, 300, 8, 2, 128
-    stats = B * H_q * 5 * 128 * 4
-    part = B * H_q * 512 * d * 4
-    assert lib.gqa_prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d) == \
-        ((stats + 255) // 256) * 256 + 2 * part
+    assert lib.gqa_prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d) == B * H_q * 5 * 128 * 4
     for bad in ((0, S, H_q, H_kv, d), (B, 0, H_q, H_kv, d), (B, S, H_q, 3, d), (B, S, H_q, H_kv, 64)):
         assert lib.gqa_prefill_bwd_workspace_bytes(*bad) == 0
 
