@@ -388,7 +388,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     const int last_row = min(i0 + kBr, a.T) - 1;
     // query row i is token qs + i (per sequence when given, clamped so that every key the
     // chunk sees lies in the cache)
-    const int qs = a.q_starts ? min(max(a.q_starts[b], 0), a.q_start_max) : a.q_start;
+    const int qs_raw = a.q_starts ? a.q_starts[b] : a.q_start;
+    const int qs = a.q_starts ? min(max(qs_raw, 0), a.q_start_max) : a.q_start;
+    // a start outside the table's capacity is clamped (no read past the table), and the
+    // sequence's LSE is written as NaN so that the caller can tell
+    const bool clamped = qs != qs_raw;
 
     WaveCtx x;
     x.lds = smem;
@@ -498,7 +502,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
                 u32x2{pack_bf16x2(st.o[dt][r] * inv, st.o[dt][r + 1] * inv),
                       pack_bf16x2(st.o[dt][r + 2] * inv, st.o[dt][r + 3] * inv)};
         }
-    if (hf == 0) a.lse[((size_t)b * a.H_q + h) * a.T + row] = kLn2 * (st.m + __builtin_log2f(l));
+    if (hf == 0)
+        a.lse[((size_t)b * a.H_q + h) * a.T + row] =
+            clamped ? __builtin_nanf("") : kLn2 * (st.m + __builtin_log2f(l));
 }
 
 }  // namespace

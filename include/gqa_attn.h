@@ -364,9 +364,11 @@ int gqa_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cac
  *               [0, num_pages) is not dereferenced: its keys read as zeros.  Pool
  *               rows of those blocks at or past q_start + T_q are never read.
  *   q_starts    [B] int32, device, or NULL (= q_start for every sequence): sequence b's
- *               chunk starts at q_starts[b], each sequence at its own position; values
- *               are clamped on the device to [0, min(max_blocks, 8192) * page_size - T_q]
- *               (the host checks below then apply to q_start only).
+ *               chunk starts at q_starts[b], each sequence at its own position.  A
+ *               value outside [0, min(max_blocks, 8192) * page_size - T_q] is clamped
+ *               on the device to that range (so no table entry past the row is read),
+ *               and that sequence's LSE rows are written as NaN to flag it; its O is
+ *               the clamped window's.  (The host checks below apply to q_start only.)
  *   o, lse      [B, T_q, H_q, d] bf16, [B, H_q, T_q] fp32, device, written
  *
  * Requires T_q >= 1, q_start >= 0, ceil((q_start + T_q) / page_size) <= max_blocks

@@ -223,9 +223,9 @@ def test_lse_merge_fuzz_against_oracle_merge(gpu_available):
 
 def test_decode_kv_reads_independent_of_group_size(gpu_available):
     """The same 32768-token cache (8 KV heads) read by 64 query heads (G = 8) and by 8
-    (G = 1): both match the oracle, and under a FETCH_SIZE counter pass both launches read
-    the cache's bytes once -- the M-fold reuses each K/V tile for all G heads of its group
-    (ADR-0060 section 11 item 2)."""
+    (G = 1): both match the oracle (the M-fold serves all G heads of a group from each K/V
+    tile, ADR-0060 section 11 item 2; the bytes it reads are measured by the FETCH_SIZE
+    counter runs summarised in profiles/, not here)."""
     inp = decode_inputs(1, 64, 8, 128, S_max=32768, seed=12)
     q64 = inp["q"]
     rng = np.random.default_rng(13)

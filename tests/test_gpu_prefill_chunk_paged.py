@@ -123,8 +123,9 @@ def test_paged_chunk_llama(gpu_available):
 
 def test_paged_chunk_per_sequence_starts(gpu_available):
     """Each sequence's chunk at its own position (a device array of starts): every sequence
-    of the batched call equals the call for that sequence alone, bit for bit; starts outside
-    [0, table capacity - T_q] are clamped on the device."""
+    of the batched call equals the call for that sequence alone, bit for bit; a start outside
+    [0, table capacity - T_q] is clamped on the device, O is the clamped window's and the
+    sequence's LSE is NaN."""
     B, T, page, keys = 3, 150, 16, 1150
     inp = chunk_inputs(B, T, keys, 16, 2, 128, seed=840)
     kp, vp, table = paged_case(inp, keys - T, T, page, seed=841)
@@ -134,11 +135,14 @@ def test_paged_chunk_per_sequence_starts(gpu_available):
     for starts in ([0, 333, 1000], [-5, 17, 5000]):
         say(f"paged prefill chunk, per-sequence starts {starts}")
         ob, lb = g.prefill_chunk_paged(q, kpg, vpg, tbl, to_gpu_i32(np.array(starts, np.int32)))
-        for b, s in enumerate(starts):
-            s = min(max(s, 0), cap - T)
+        for b, s_raw in enumerate(starts):
+            s = min(max(s_raw, 0), cap - T)
             o1, l1 = g.prefill_chunk_paged(q[b:b + 1].contiguous(), kpg, vpg,
                                            tbl[b:b + 1].contiguous(), s)
             torch.cuda.synchronize()
             # bit patterns: a clamped chunk may reach the pool's NaN rows, in both calls alike
             assert torch.equal(ob[b:b + 1].view(torch.int16), o1.view(torch.int16)), (starts, b)
-            assert torch.equal(lb[b:b + 1].view(torch.int32), l1.view(torch.int32)), (starts, b)
+            if s == s_raw:
+                assert torch.equal(lb[b:b + 1].view(torch.int32), l1.view(torch.int32)), (starts, b)
+            else:      # clamped: flagged by a NaN LSE on every row of the sequence
+                assert torch.isnan(lb[b]).all(), (starts, b)
