@@ -68,17 +68,21 @@ BF16_FLOP_PER_CLK_CU = 4096    # CDNA4 dense bf16 matrix-core FLOP per clock per
 COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many bytes
 REPLAYS = 5                    # timed replays of each graph loop (median and min reported)
 
-# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE at this workload
-# (fetch counter x 2.00, write x 1.00, both factors from the plain-copy calibration),
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE at this workload,
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
-# taken reports traffic null.  Figures and commands: profiles/hbm_traffic_*.md.
-TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00 per dispatch at this "
-                  "workload (profiles/hbm_traffic_*.md), valid while the kernel's source "
-                  "digest matches; null otherwise")
+# taken reports traffic null.  FETCH_SIZE counts a 128-byte read request as 64 bytes: the
+# plain-copy calibration (16-byte loads per lane, like decode_split and prefill_causal)
+# reads back half its bytes, so those kernels take fetch x 2.00; lse_merge reads its bf16
+# states with 8-byte loads (64-byte requests), counted in full (x 1.00).  Writes x 1.00.
+# Figures and commands: profiles/hbm_traffic_*.md.
+TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x request-size factor (2.00 for 128-byte requests, "
+                  "from a plain copy) + WRITE_SIZE x 1.00 per dispatch at this workload "
+                  "(profiles/hbm_traffic_*.md), valid while the kernel's source digest "
+                  "matches; null otherwise")
 MEASURED_TRAFFIC = {
-    "decode_split": ("31147fdf07f0e57b", 143_011_422),
-    "lse_merge": ("95db331d632c5be2", 9_527_225),
-    "prefill_causal": ("0acd9c8b9f9c37a4", 422_062_707),
+    "decode_split": ("39280f20da99d6d6", 138_838_824),
+    "lse_merge": ("ffa76bcde8b8768c", 4_790_067),
+    "prefill_causal": ("fd10e9bdd7b581e4", 423_056_960),
 }
 
 
@@ -572,6 +576,8 @@ def main():
         # the ceiling's buffers: each copy's K and V bytes in one contiguous 128 MiB buffer
         kv_flat = [torch.cat([k.view(-1), v.view(-1)]) for k, v in kv_copies]
         sink = g.stream_read(kv_flat[0])
+        # the launch floor: the same streaming kernel (same grid) over 16 bytes
+        tiny = torch.zeros(16, dtype=torch.uint8, device="cuda")
     if need_prefill:
         pinp = for_config(pc)
         q_p, k_p, v_p = upload(pinp["q"]), upload(pinp["k"]), upload(pinp["v"])
@@ -595,6 +601,9 @@ def main():
         # the 128 MiB of K and V the decode reads in one call, in one launch of a plain
         # streaming kernel (over a contiguous copy of the same bytes)
         g.stream_read(kv_flat[i % len(kv_flat)], sink)
+
+    def floor_call(i):
+        g.stream_read(tiny, sink)
 
     def prefill_call(i):
         g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
@@ -632,7 +641,7 @@ def main():
 
     graphs = {name: capture(fn, K) for name, fn in
               (("decode", decode_call), ("prefill", prefill_call), ("split", split_call),
-               ("merge", merge_call), ("ceiling", ceiling_call))}
+               ("merge", merge_call), ("ceiling", ceiling_call), ("floor", floor_call))}
 
     def replay_ms(name):
         """Time per call of one replay, from events on the launch stream."""
@@ -658,7 +667,7 @@ def main():
     for _ in range(REPLAYS - 1):
         for name in graphs:
             reps[name].append(replay_ms(name))
-    for name in ("split", "merge", "ceiling"):
+    for name in ("split", "merge", "ceiling", "floor"):
         reps[name].append(replay_ms(name))
 
     def stat(name):
@@ -669,6 +678,7 @@ def main():
     split_ms = float(np.mean(reps["split"]))
     merge_ms = float(np.mean(reps["merge"]))
     ceiling_ms = float(np.mean(reps["ceiling"]))
+    floor_ms = float(np.mean(reps["floor"]))
 
     kv_bytes = acc.decode_kv_bytes([dc.S_kv], dc.H_kv, dc.d)
     flop = acc.prefill_causal_flop(pc.B, pc.S, pc.H_q, pc.d)
@@ -716,6 +726,14 @@ def main():
             "merge_traffic": measured_traffic("lse_merge"),
             "ceiling_gbs": round(ceiling_gbs, 1),
             "frac_of_ceiling": round(decode_gbs / ceiling_gbs, 4),
+            # where the time per call goes, against one streaming launch over the same bytes
+            "gap_us": {"call": round(decode_ms * 1e3, 2),
+                       "ceiling_one_launch": round(ceiling_ms * 1e3, 2),
+                       "split_over_ceiling": round((split_ms - ceiling_ms) * 1e3, 2),
+                       "merge_launch": round(merge_ms * 1e3, 2),
+                       "launch_floor": round(floor_ms * 1e3, 2),
+                       "note": "launch_floor: the streaming kernel's grid over 16 bytes in the "
+                               "same kind of graph, the least any second launch adds"},
         },
         "ceiling_gbs": round(ceiling_gbs, 1),
         "ceiling": {"kernel": "hbm_read (gqa_stream_read)", "bytes": kv_bytes,
