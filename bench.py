@@ -495,7 +495,7 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies, bf16_peak):
         "frac_bf16_peak": round(tf_pg / bf16_peak, 4), "vs_contiguous": round(ms / ms_pg, 3)}
     del kpool, vpool
     # backward of the causal prefill at the Llama workload (S = 8192): the forward's O and
-    # LSE, a random output gradient, the four launches of one backward call per step
+    # LSE, a random output gradient, the three launches of one backward call per step
     o_f, lse_f, do_p, ws_b, grads = bwd_inputs(q_p, k_p, v_p)
 
     def bwd_call(i):

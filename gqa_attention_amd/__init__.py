@@ -430,8 +430,8 @@ def prefill_chunk_paged(q, k_pool, v_pool, block_table, q_start, softmax_scale=N
 
 
 def prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d):
-    """Workspace bytes of ``prefill_causal_bwd`` (per-row statistics and the fp32 shares
-    of dK, dV of every query head)."""
+    """Workspace bytes of ``prefill_causal_bwd``: the per-row statistics (LSE in log2 units
+    and D, 8 bytes per query row and head)."""
     n = load_library().gqa_prefill_bwd_workspace_bytes(B, S, H_q, H_kv, d)
     if n == 0:
         raise ValueError(f"invalid backward sizes B={B} S={S} H_q={H_q} H_kv={H_kv} d={d}")

@@ -147,7 +147,8 @@ int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
  *            Layout, with N = `states` slots per query head, each region starting
  *            at a 256-byte boundary: seg [B][2] int32 (first slot and number of
  *            slots of each sequence's states), then m2 [N][H_q] fp32 (running max,
- *            log2 units), l [N][H_q] fp32, O [N][H_q][d] fp32 (unnormalised).
+ *            log2 units), l [N][H_q] fp32, O [N][H_q][d] bf16 (unnormalised,
+ *            rounded to nearest even when stored).
  *            Sequence b's states are slots seg[b][0] .. seg[b][0] + seg[b][1] - 1;
  *            other slots are not written.  A state is defined up to a common
  *            shift of its (m2, l, O).
