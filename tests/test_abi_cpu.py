@@ -300,3 +300,45 @@ def test_binding_raises_with_detail():
     with pytest.raises(g.GQAError) as ei:
         g.decode_plan(1, 64, 7, 128, 1024, 0)
     assert ei.value.name == "GQA_ERR_BAD_SHAPE" and "divide" in ei.value.detail
+
+
+def test_stream_read_rejects_before_launch(lib):
+    """The streaming-read calibration checks its buffer, sink and size on the host."""
+    assert lib.gqa_stream_read(None, 1024, A, None) == NULLP
+    assert lib.gqa_stream_read(A, 1024, None, None) == NULLP
+    assert lib.gqa_stream_read(ctypes.c_void_p(0x10008), 1024, A, None) == ALIGN
+    assert lib.gqa_stream_read(A, 1024, ctypes.c_void_p(0x10002), None) == ALIGN
+    assert lib.gqa_stream_read(A, 0, A, None) == SHAPE
+    assert lib.gqa_stream_read(A, 1000, A, None) == SHAPE      # not a multiple of 16
+    sink = lib.gqa_stream_read_sink_bytes()
+    assert sink > 0 and sink % 4 == 0
+
+
+def _noalloc(lib, q=A, k=A, v=A, seqlens=None, o=A, lse=A, B=1, H_q=64, H_kv=8, d=128, S=64,
+             scale=0.088, splits=32):
+    return lib.gqa_attn_decode_noalloc(q, k, v, seqlens, o, lse, B, H_q, H_kv, d, S, scale,
+                                       splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(o=None), NULLP), (dict(lse=None), NULLP),
+    (dict(q=MIS), ALIGN), (dict(H_kv=3), SHAPE), (dict(d=16), UNSUP), (dict(splits=-1), SPLITS),
+    (dict(scale=float("nan")), SCALE),
+    # the most partitions the plan allows: 65535 + B - 1 slots x 64 heads x (256 + 8) bytes of
+    # states, beyond the library's own 16 MiB
+    (dict(splits=65535), WS),
+])
+def test_noalloc_decode_rejects_before_launch(lib, kw, code):
+    """The no-allocation decode validates like gqa_attn_decode and refuses a plan whose
+    workspace exceeds its own array, all before touching the GPU."""
+    assert _noalloc(lib, **kw) == code
+    assert lib.gqa_last_error().decode() != ""
+
+
+def test_noalloc_limit_holds_the_llama_decodes(lib):
+    """The 16 MiB array holds the workspace of the Llama decode and of the B = 8 batch."""
+    limit = lib.gqa_decode_noalloc_max_workspace()
+    assert limit == 16 << 20
+    for B, S, splits in ((1, 32768, 32), (8, 92610, 64)):
+        plan = g.decode_plan(B, 64, 8, 128, S, splits)
+        assert plan["workspace_bytes"] <= limit, (B, S, plan)
