@@ -14,9 +14,9 @@
 //   bwd_dq     query-block outer, key tiles inner, dQ accumulated in registers: no atomics
 //              (section 8: Q outer removes the dQ atomics of the section 6.4 loop);
 //   bwd_dkdv   key-block outer, query tiles inner (the loop of section 6.4 without its dQ
-//              update), one workgroup per (pair of key blocks, KV head), looping over the
-//              KV head's G query heads with dK and dV in registers: the reduction over the
-//              heads happens on chip (section 6.5), in a fixed order, so results are
+//              update), one workgroup per (key block, KV head), looping over the KV head's
+//              G query heads with dK and dV in registers: the reduction over the heads
+//              happens on chip (section 6.5), in a fixed order, so results are
 //              deterministic and no partial sums go through memory.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 32 keys x 32 query rows per wave step):
@@ -24,8 +24,8 @@
 //               registers); a lane owns one query row, so LSE and D are per-lane scalars;
 //               dQ^T += K^T.dS^T takes dS^T straight from the score registers (B operand)
 //               and K^T through the LDS transpose read.
-//   dkdv kernel S = Q.K^T and dP = dO.V^T (Q, dO rows from LDS; K fragments in registers,
-//               V rows from the workgroup's V block in LDS); a lane owns one key;
+//   dkdv kernel S = Q.K^T and dP = dO.V^T (Q, dO rows from LDS; K and V rows from the
+//               workgroup's K and V blocks in LDS); a lane owns one key;
 //               dV^T += dO^T.P and dK^T += Q^T.dS take P and dS straight from the score
 //               registers and dO^T, Q^T through the LDS transpose read.
 // Tiles that are read both by rows and transposed store 16-byte chunk c of row r at chunk
@@ -310,19 +310,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
 // the 32 keys of key group w % 4 and, of each 64-row query tile, the 32 rows of row half
 // w / 4; the two waves of a SIMD (waves are dealt to SIMDs round-robin) thus share their keys
 // and split the rows of every tile, and at the end the second half's dK and dV are added to
-// the first's through LDS.  Blocks with the longest prefix of rows run first.
-// LDS: the block's V rows (32 KiB), then a ring of two slots of a 64-row query tile of one
-// head (Q 16 KiB, dO 16 KiB, statistics 1 KiB), then 1 KiB that the other waves' statistics
-// DMA fills with zeros (every wave issues the same DMA count per item).  A work item is a
-// (query tile, head) pair, heads inner.
+// the first's through LDS.  Blocks with the longest prefix of rows run first.  A work item is
+// a (query tile, head) pair, heads inner.
+// The two halves run an item out of phase: row half 1 forms the dV / dK products of an item
+// one item late, at the start of the next, so that while row half 0 runs an item's softmax
+// arithmetic the other wave of its SIMD keeps the matrix core busy (with the items in step,
+// both waves of a SIMD would reach their softmax together, and the matrix core would idle).
+// Each half therefore DMAs only its own 32 rows of a tile, into a ring of its own: two slots
+// for half 0, three for half 1, whose late products still read an item's slot while the next
+// item's DMA goes out.  LDS: the block's V rows (32 KiB) and K rows (32 KiB), then the two
+// rings of slots of a half tile of one head (Q 8 KiB, dO 8 KiB, the tile's statistics block
+// 1 KiB), then 1 KiB that the other waves' statistics DMA fills with zeros.
 
 constexpr int kKBlk = 128;                           // keys per workgroup
 constexpr int kVBlock = kKBlk * kRowBytes;           // 32 KiB
-constexpr int kQTile = kStatRows * kRowBytes;        // 16 KiB: 64 rows
-constexpr int kSlot = 2 * kQTile + 1024;             // Q, dO, statistics
-constexpr int kRing = kVBlock;
-constexpr int kSink = kRing + 2 * kSlot;
-constexpr int kKvLds = kSink + 1024;                 // 99 KiB: one workgroup per CU
+constexpr int kKBlock = kVBlock;                     // the block's K rows after its V rows
+constexpr int kHalfTile = 32 * kRowBytes;           // 8 KiB: one row half of a query tile
+constexpr int kSlot = 2 * kHalfTile + 1024;          // Q, dO half tiles, statistics block
+constexpr int kRing = kVBlock + kKBlock;             // row half 0: slots 0, 1
+constexpr int kRing1 = kRing + 2 * kSlot;            // row half 1: slots 0, 1, 2
+constexpr int kSink = kRing1 + 3 * kSlot;
+constexpr int kKvLds = kSink + 1024;                 // 150 KiB: one workgroup per CU
 
 // Row half 1 stores its accumulators x at xch (element 4 j .. 4 j + 3 at xch[64 j]); row
 // half 0 adds them to its own (half 0 + half 1, a fixed order).  Both halves call it.
@@ -352,9 +360,6 @@ __device__ __forceinline__ void hand_over(f32x16 (&x)[4], f32x4 *xch, int rh) {
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kb, int n_t) {
     __shared__ __attribute__((aligned(256))) uint8_t smem[kKvLds];
     const int G = a.H_q / a.H_kv;
-    // workgroup -> (block, b, KV head g); consecutive workgroups (dealt round-robin over the
-    // XCDs) take consecutive KV heads, so the blocks of one KV head share an XCD's L2 for
-    // the Q and dO tiles of its query heads when H_kv is a multiple of 8
     int u = blockIdx.x;
     const int g = u % a.H_kv;
     u /= a.H_kv;
@@ -374,51 +379,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
 
     const uint32_t q_row_bytes = (uint32_t)a.H_q * kRowBytes;
     const uint32_t kv_row_bytes = (uint32_t)a.H_kv * kRowBytes;
-    const uint32_t qvoff = (uint32_t)lr * q_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
     const uint32_t kvvoff = (uint32_t)lr * kv_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lr));
+    // a row half's own rows: wave kg copies row quads kg and kg + 4 of its 32-row half (the
+    // swizzle of a row depends on its row % 16 only, so both quads share the lane's chunk)
+    const int lq = 4 * kg + lane / 16;
+    const uint32_t qvoff = (uint32_t)lq * q_row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(lq));
 
-    // K fragments (B operand of S = Q.K^T): column = the lane's key, slots d = 16 ks + 8 hf ..
-    bf16x8 kf[8];
+    // the block's V and K rows: each wave copies 4 rows of every 32-row group
     {
-        const size_t off = (((size_t)b * a.S + min(key, a.S - 1)) * a.H_kv + g) * D + hf * 8;
-        const bool live = key < a.S;
+        const size_t off = (((size_t)b * a.S + k0) * a.H_kv + g) * D;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const u32x4 x = load16(a.k + off + 16 * ks);
-            kf[ks] = as_bf16x8(live ? x : u32x4{0u, 0u, 0u, 0u});
+        for (int i = 0; i < kKBlk / 32; ++i) {
+            dma_rows32(smem, 32 * i * kRowBytes, a.v + off + (size_t)32 * i * a.H_kv * D,
+                       kv_row_bytes, a.S - k0 - 32 * i, kvvoff, w);
+            dma_rows32(smem, kVBlock + 32 * i * kRowBytes, a.k + off + (size_t)32 * i * a.H_kv * D,
+                       kv_row_bytes, a.S - k0 - 32 * i, kvvoff, w);
         }
     }
-    // the block's V rows: each wave copies 4 rows of every 32-row group
-    {
-        const uint16_t *vb = a.v + (((size_t)b * a.S + k0) * a.H_kv + g) * D;
-#pragma unroll
-        for (int i = 0; i < kKBlk / 32; ++i)
-            dma_rows32(smem, 32 * i * kRowBytes, vb + (size_t)32 * i * a.H_kv * D, kv_row_bytes,
-                       a.S - k0 - 32 * i, kvvoff, w);
-    }
-    const int vrow = 32 * kg;                        // the wave's V rows in the block
+    const uint32_t vrow = 32u * kg * kRowBytes;              // the wave's V rows in the block
+    const uint32_t krow = kVBlock + vrow;                    // and its K rows
 
     const int n_items = (n_t - t0) * G;
-    auto issue = [&](int it, int slot) {
+    // this wave's share of item it's DMA into its half's slot for the item: two row quads of
+    // its half of the Q and dO tiles; the first wave of each half also the statistics
+    // block, the other waves zero-fill the sink
+    auto slot_base = [&](int it) {
+        return rh == 0 ? kRing + (it & 1) * kSlot : kRing1 + (it % 3) * kSlot;
+    };
+    auto issue = [&](int it) {
         const bool real = it < n_items;
         const int t = real ? t0 + it / G : 0;
         const int h = g * G + (real ? it % G : 0);
-        const int base = kRing + slot * kSlot;
-        const int r = t * kStatRows;
+        const int base = slot_base(it);
+        const int r = t * kStatRows + 32 * rh;
         const int rows = real ? a.S - r : 0;          // past the last item: zero-fill only
         const uint16_t *qbase = a.q + (((size_t)b * a.S + r) * a.H_q + h) * D;
         const uint16_t *gbase = a.dout + (((size_t)b * a.S + r) * a.H_q + h) * D;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            dma_rows32(smem, base + 32 * i * kRowBytes, qbase + (size_t)32 * i * a.H_q * D,
-                       q_row_bytes, rows - 32 * i, qvoff, w);
-            dma_rows32(smem, base + kQTile + 32 * i * kRowBytes,
-                       gbase + (size_t)32 * i * a.H_q * D, q_row_bytes, rows - 32 * i, qvoff, w);
+            dma_rows32(smem, base, qbase, q_row_bytes, rows, qvoff + 16u * i * q_row_bytes,
+                       kg + 4 * i);
+            dma_rows32(smem, base + kHalfTile, gbase, q_row_bytes, rows,
+                       qvoff + 16u * i * q_row_bytes, kg + 4 * i);
         }
-        // statistics block (h, t) (512 bytes) by wave 0; the other waves zero-fill the sink
-        const bool mine = w == 0 && real;
+        // the statistics block (both halves' rows) by the first wave of each half
+        const bool mine = kg == 0 && real;
         const float *stp = a.stats + (((size_t)b * a.H_q + h) * n_t + t) * kStatFloats;
-        dma_bytes1k(smem, mine ? base + 2 * kQTile : kSink, stp,
+        dma_bytes1k(smem, mine ? base + 2 * kHalfTile : kSink, stp,
                     mine ? (uint32_t)(kStatFloats * sizeof(float)) : 0u, 16u * (uint32_t)lane);
     };
 
@@ -429,27 +436,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
         for (int r = 0; r < 16; ++r) dv[dt][r] = dk[dt][r] = 0.f;
     const float c = a.scale_log2;
 
-    issue(0, 0);
+    bf16x8 p0 = {}, p1 = {}, d0 = {}, d1 = {};
+    bool pend = false;                  // row half 1: an item's dV / dK products are owed
+    uint32_t pqh = 0;
+    auto dvdk = [&](uint32_t qh) {
+        const uint32_t gh = qh + kHalfTile;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            dv[dt] = mfma32(read_tr(smem, gh, ad, dt, 0), p0, dv[dt]);
+            dv[dt] = mfma32(read_tr(smem, gh, ad, dt, 1), p1, dv[dt]);
+            dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 0), d0, dk[dt]);
+            dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 1), d1, dk[dt]);
+        }
+    };
+
+    issue(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int it = 0; it < n_items; ++it) {
-        const int slot = it & 1;
-        issue(it + 1, slot ^ 1);
+        // row half 1: item it - 1's products first (its slot is not refilled until item
+        // it + 2's DMA, after the barrier that ends item it)
+        if (rh == 1 && pend) dvdk(pqh);
+        issue(it + 1);
         const int r0 = (t0 + it / G) * kStatRows + 32 * rh;   // the wave's first row
-        if (r0 >= kw0) {                                      // (rows all before the keys: skip)
-            const uint32_t qh = kRing + slot * kSlot + rh * 32 * kRowBytes;
-            const uint32_t gh = qh + kQTile;
+        pend = r0 >= kw0;                                     // (rows all before the keys: skip)
+        if (pend) {
+            const uint32_t qh = slot_base(it);
+            const uint32_t gh = qh + kHalfTile;
             f32x16 s, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                s = mfma32(read_row(smem, qh, ad, ks), kf[ks], s);
-                dp = mfma32(read_row(smem, gh, ad, ks), read_row(smem, vrow * kRowBytes, ad, ks),
-                            dp);
+                s = mfma32(read_row(smem, qh, ad, ks), read_row(smem, krow, ad, ks), s);
+                dp = mfma32(read_row(smem, gh, ad, ks), read_row(smem, vrow, ad, ks), dp);
             }
             // lse2 and D of the lane's 16 rows 32 rh + 8 q + 4 hf + (0..3)
-            const uint8_t *stp = smem + kRing + slot * kSlot + 2 * kQTile;
+            const uint8_t *stp = smem + slot_base(it) + 2 * kHalfTile;
             float p[16], ds[16];
             const bool diag = r0 == kw0;
 #pragma unroll
@@ -467,21 +490,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
                     ds[r] = pv * (dp[r] - d4[j]);
                 }
             }
-            const bf16x8 p0 = pack8(p, 0), p1 = pack8(p, 1);
-            const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 1);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                dv[dt] = mfma32(read_tr(smem, gh, ad, dt, 0), p0, dv[dt]);
-                dv[dt] = mfma32(read_tr(smem, gh, ad, dt, 1), p1, dv[dt]);
-                dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 0), d0, dk[dt]);
-                dk[dt] = mfma32(read_tr(smem, qh, ad, dt, 1), d1, dk[dt]);
-            }
+            p0 = pack8(p, 0);
+            p1 = pack8(p, 1);
+            d0 = pack8(ds, 0);
+            d1 = pack8(ds, 1);
+            pqh = qh;
+            if (rh == 0) dvdk(qh);
         }
         __builtin_amdgcn_s_waitcnt(0);   // the next item's DMA
         __syncthreads();
     }
+    if (rh == 1 && pend) dvdk(pqh);      // the last item's
+    __syncthreads();
 
-    // row half 1 hands its sums to row half 0 through LDS (the query-tile ring, free now),
+    // row half 1 hands its sums to row half 0 through LDS (the query-tile rings, free now),
     // dK then dV: element 4 j .. 4 j + 3 of lane l of key group k at ((k * 16 + j) * 64 + l)
     // * 16 bytes, so each store and load of a wave is 1 KiB contiguous
     f32x4 *xch = reinterpret_cast<f32x4 *>(smem + kRing) + kg * 16 * 64 + lane;
