@@ -43,9 +43,10 @@
 // folded into the exponent's FMA; V07 section 2, exp2 trick).
 //
 // Paged cache (the Paged instantiation; V07 sections 16-17, block table and pool): the
-// sequence's block-table row is staged in LDS when the workgroup starts, and each DMA
-// instruction of a tile, which covers four consecutive rows of one page, takes its page from
-// it; the tiles land in LDS exactly as from a contiguous cache, so the arithmetic is the same.
+// sequence's block-table row is staged in LDS when the workgroup starts; each DMA instruction
+// of a tile covers four consecutive rows of one page, whose pool row a wave looks up once per
+// tile and uses for both the K and the V DMA of that tile (K and V pools share the table);
+// the tiles land in LDS exactly as from a contiguous cache, so the arithmetic is the same.
 //
 // Grid: one workgroup per (q-block, sequence, query head), heaviest q-blocks
 // first (V07 section 12, causal-aware scheduling).  Consecutive workgroups are
@@ -284,6 +285,51 @@ __device__ __forceinline__ void dma(const WaveCtx &x, int dst, const uint16_t *b
         dma_tile(x.lds, dst, base, x.kv_row, k0, x.S, off, x.w);
 }
 
+// Paged: the pool rows of one tile's DMA for this wave (its rows 32 i + 4 w .. + 3 of the
+// tile lie in one page), looked up once and used for both the K and the V DMA of the tile.
+struct PageRows {
+    size_t row[kDmaPerTile];       // first pool row, in elements (0 when nothing is read)
+    uint32_t bytes[kDmaPerTile];   // bytes to read (0: zeros)
+};
+
+__device__ __forceinline__ PageRows page_rows(const WaveCtx &x, int k0) {
+    PageRows p;
+    const uint32_t row_bytes = (uint32_t)x.kv_row * 2u;
+#pragma unroll
+    for (int i = 0; i < kDmaPerTile; ++i) {
+        const int r = k0 + 32 * i + 4 * x.w;
+        uint32_t bytes = 0;
+        size_t row = 0;
+        if (r < x.S) {
+            const int pg = __builtin_amdgcn_readfirstlane(x.tbl[r / x.page]);
+            if ((unsigned)pg < (unsigned)x.num_pages) {
+                bytes = (uint32_t)min(4, x.S - r) * row_bytes;
+                row = ((size_t)pg * x.page + r % x.page) * x.kv_row;
+            }
+        }
+        p.row[i] = row;
+        p.bytes[i] = __builtin_amdgcn_readfirstlane(bytes);
+    }
+    return p;
+}
+
+// The paged DMA of one tile from precomputed pool rows (the same loads as dma_tile_paged).
+__device__ __forceinline__ void dma_rows_paged(const WaveCtx &x, int dst, const uint16_t *pool,
+                                               const PageRows &p, uint32_t voff) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerTile; ++i) {
+        const uint64_t base = (uint64_t)(pool + p.row[i]);
+        const u32x4 rsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) & 0xFFFFu,
+                            p.bytes[i], 0x00020000u};
+        const uint32_t lds_dst = (uint32_t)(uintptr_t)(x.lds + dst + (32 * i + 4 * x.w) * kRowBytes);
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_dst))
+                     : "memory");
+    }
+}
+
 struct RowState {
     f32x16 o[4];
     float m, l, lw;
@@ -345,12 +391,21 @@ __device__ __forceinline__ void tile_step(const WaveCtx &x, int kb, f32x16 &sa, 
     constexpr int kFree = kKBuf + ((KI + 3) % kNK) * kTileBytes;
     constexpr int vcur = kVBuf + KI * kTileBytes;
     constexpr int vfree = kVBuf + ((KI + 3) % kNV) * kTileBytes;
-    dma<Paged>(x, kFree, x.kbase, (kb + 3) * kBc, x.koff);
+    PageRows pr;
+    if constexpr (Paged) {
+        pr = page_rows(x, (kb + 3) * kBc);
+        dma_rows_paged(x, kFree, x.kbase, pr, x.koff);
+    } else {
+        dma<Paged>(x, kFree, x.kbase, (kb + 3) * kBc, x.koff);
+    }
     uint32_t va[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) va[dt] = x.fa.v[dt] + (uint32_t)vcur;
     half_step(x, 2 * kb, sa, sb, x.lds + kCur + kHalf * kRowBytes, x.lds, va, qf, st);
-    dma<Paged>(x, vfree, x.vbase, (kb + 3) * kBc, x.voff);
+    if constexpr (Paged)
+        dma_rows_paged(x, vfree, x.vbase, pr, x.voff);
+    else
+        dma<Paged>(x, vfree, x.vbase, (kb + 3) * kBc, x.voff);
     half_step(x, 2 * kb + 1, sb, sa, x.lds + kNext, x.lds + kHalf * kRowBytes, va, qf, st);
     // vmcnt(2 * kDmaPerTile): only this tile's DMA may still be in flight
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerTile));
