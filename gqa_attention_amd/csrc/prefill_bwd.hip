@@ -267,15 +267,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
                 s = mfma32(read_row(smem, kh, ad, ks), qf[ks], s);
                 dp = mfma32(read_row(smem, vh, ad, ks), gf[ks], dp);
             }
-            float ds[16];
-            const bool diag = us >= mask_from;
+            float p[16], ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * us + 8 * (r >> 2) + 4 * hf + (r & 3);
-                float p = exp2_fast(fmaf(s[r], c, -lse2));
-                if (diag && key > row) p = 0.f;
-                ds[r] = p * (dp[r] - Drow);
+            for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(s[r], c, -lse2));
+            if (us >= mask_from) {
+                // a step holding the wave's diagonal: keys past the lane's row get no weight
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * us + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (key > row) p[r] = 0.f;
+                }
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - Drow);
             const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 1);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
@@ -474,22 +478,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
             // lse2 and D of the lane's 16 rows 32 rh + 8 q + 4 hf + (0..3)
             const uint8_t *stp = smem + slot_base(it) + 2 * kHalfTile;
             float p[16], ds[16];
-            const bool diag = r0 == kw0;
+            f32x4 d4[4];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int rr = 32 * rh + 8 * q4 + 4 * hf;
                 const f32x4 l4 = *reinterpret_cast<const f32x4 *>(stp + 4 * rr);
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(stp + 4 * (kStatRows + rr));
+                d4[q4] = *reinterpret_cast<const f32x4 *>(stp + 4 * (kStatRows + rr));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * q4 + j;
-                    float pv = exp2_fast(fmaf(s[r], c, -l4[j]));
-                    // diagonal step: rows r0 + (8 q4 + 4 hf + j), keys r0 + r32
-                    if (diag && r32 > 8 * q4 + 4 * hf + j) pv = 0.f;
-                    p[r] = pv;
-                    ds[r] = pv * (dp[r] - d4[j]);
-                }
+                for (int j = 0; j < 4; ++j) p[4 * q4 + j] = exp2_fast(fmaf(s[4 * q4 + j], c, -l4[j]));
             }
+            if (r0 == kw0) {
+                // the diagonal step: rows r0 + (8 q4 + 4 hf + j), keys r0 + r32
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (r32 > 8 * q4 + 4 * hf + j) p[4 * q4 + j] = 0.f;
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ds[4 * q4 + j] = p[4 * q4 + j] * (dp[4 * q4 + j] - d4[q4][j]);
             p0 = pack8(p, 0);
             p1 = pack8(p, 1);
             d0 = pack8(ds, 0);
