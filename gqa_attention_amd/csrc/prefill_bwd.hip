@@ -32,6 +32,8 @@
 // position c ^ (4 (r % 4) + (r / 4) % 4): sixteen consecutive rows then fall on sixteen
 // distinct positions (row reads), and so do four consecutive rows of one 64-byte column
 // group (transpose reads).
+#include <type_traits>
+
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -174,7 +176,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int n_t) {
 
 // ---------------------------------------------------------------------------------------
 // bwd_dq: workgroup = 256 query rows of one query head (8 waves x 32 rows), key tiles of 64
-// through a ring of two LDS slots (K 16 KiB, V 16 KiB each).
+// through a ring of two LDS slots (K 16 KiB, V 16 KiB each); the tile loop is unrolled by two
+// so that each slot's fragment offsets are compile-time immediates.
 
 constexpr int kQBr = 256;
 constexpr int kKT = 64;
@@ -247,11 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
         }
     };
 
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < n_kt; ++t) {
-        const int slot = t & 1;
+    // one key tile t in ring slot SLOT = t % 2, a compile-time constant so that every LDS
+    // fragment address is a fixed per-lane register plus an immediate offset
+    auto tile = [&](int t, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
         issue(t + 1, slot ^ 1);   // (past the last tile it only zero-fills the free slot)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -289,7 +291,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
         }
         __builtin_amdgcn_s_waitcnt(0);   // the next tile's DMA
         __syncthreads();
+    };
+
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < n_kt; t += 2) {
+        tile(t, std::integral_constant<int, 0>{});
+        tile(t + 1, std::integral_constant<int, 1>{});
     }
+    if (t < n_kt) tile(t, std::integral_constant<int, 0>{});
 
     if (row >= a.S) return;
     const float tau = a.scale;
