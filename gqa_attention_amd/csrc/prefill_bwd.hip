@@ -416,21 +416,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     const uint32_t krow = kVBlock + vrow;                    // and its K rows
 
     const int n_items = (n_t - t0) * G;
-    // this wave's share of item it's DMA into its half's slot for the item: two row quads of
+    // items are (query tile, head) pairs, heads inner; the DMA side runs one item ahead of the
+    // compute side, and both step through the items by increments (no division per item)
+    auto slot_base = [&](int par, int m3) {
+        return rh == 0 ? kRing + par * kSlot : kRing1 + m3 * kSlot;
+    };
+    // the next item to issue: its tile, head index, position mod 3, and the element offsets
+    // of its rows in Q / dO and of its statistics block
+    int is_t = t0, is_j = 0, is_m3 = 0;
+    const size_t q_tile_step = (size_t)kStatRows * a.H_q * D;
+    const size_t st_head_step = (size_t)n_t * kStatFloats;
+    size_t is_q = (((size_t)b * a.S + (size_t)t0 * kStatRows + 32 * rh) * a.H_q + (size_t)g * G) * D;
+    size_t is_st = (((size_t)b * a.H_q + (size_t)g * G) * n_t + t0) * kStatFloats;
+    // this wave's share of an item's DMA into its half's slot for the item: two row quads of
     // its half of the Q and dO tiles; the first wave of each half also the statistics
     // block, the other waves zero-fill the sink
-    auto slot_base = [&](int it) {
-        return rh == 0 ? kRing + (it & 1) * kSlot : kRing1 + (it % 3) * kSlot;
-    };
     auto issue = [&](int it) {
         const bool real = it < n_items;
-        const int t = real ? t0 + it / G : 0;
-        const int h = g * G + (real ? it % G : 0);
-        const int base = slot_base(it);
-        const int r = t * kStatRows + 32 * rh;
+        const int base = slot_base(it & 1, is_m3);
+        const int r = is_t * kStatRows + 32 * rh;
         const int rows = real ? a.S - r : 0;          // past the last item: zero-fill only
-        const uint16_t *qbase = a.q + (((size_t)b * a.S + r) * a.H_q + h) * D;
-        const uint16_t *gbase = a.dout + (((size_t)b * a.S + r) * a.H_q + h) * D;
+        const uint16_t *qbase = a.q + is_q;
+        const uint16_t *gbase = a.dout + is_q;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             dma_rows32(smem, base, qbase, q_row_bytes, rows, qvoff + 16u * i * q_row_bytes,
@@ -440,9 +447,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
         }
         // the statistics block (both halves' rows) by the first wave of each half
         const bool mine = kg == 0 && real;
-        const float *stp = a.stats + (((size_t)b * a.H_q + h) * n_t + t) * kStatFloats;
-        dma_bytes1k(smem, mine ? base + 2 * kHalfTile : kSink, stp,
+        dma_bytes1k(smem, mine ? base + 2 * kHalfTile : kSink, a.stats + is_st,
                     mine ? (uint32_t)(kStatFloats * sizeof(float)) : 0u, 16u * (uint32_t)lane);
+        if (++is_j == G) {
+            is_j = 0;
+            ++is_t;
+            is_q += q_tile_step - (size_t)(G - 1) * D;
+            is_st += kStatFloats - (size_t)(G - 1) * st_head_step;
+        } else {
+            is_q += D;
+            is_st += st_head_step;
+        }
+        if (++is_m3 == 3) is_m3 = 0;
     };
 
     f32x16 dv[4], dk[4];
@@ -469,15 +485,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     issue(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    int cu_t = t0, cu_j = 0, cu_m3 = 0;   // the compute side's item: tile, head index, it % 3
     for (int it = 0; it < n_items; ++it) {
         // row half 1: item it - 1's products first (its slot is not refilled until item
         // it + 2's DMA, after the barrier that ends item it)
         if (rh == 1 && pend) dvdk(pqh);
         issue(it + 1);
-        const int r0 = (t0 + it / G) * kStatRows + 32 * rh;   // the wave's first row
+        const int r0 = cu_t * kStatRows + 32 * rh;            // the wave's first row
         pend = r0 >= kw0;                                     // (rows all before the keys: skip)
         if (pend) {
-            const uint32_t qh = slot_base(it);
+            const uint32_t qh = slot_base(it & 1, cu_m3);
             const uint32_t gh = qh + kHalfTile;
             f32x16 s, dp;
 #pragma unroll
@@ -488,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
                 dp = mfma32(read_row(smem, gh, ad, ks), read_row(smem, vrow, ad, ks), dp);
             }
             // lse2 and D of the lane's 16 rows 32 rh + 8 q + 4 hf + (0..3)
-            const uint8_t *stp = smem + slot_base(it) + 2 * kHalfTile;
+            const uint8_t *stp = smem + qh + 2 * kHalfTile;
             float p[16], ds[16];
             f32x4 d4[4];
 #pragma unroll
@@ -518,6 +535,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
             pqh = qh;
             if (rh == 0) dvdk(qh);
         }
+        if (++cu_j == G) {
+            cu_j = 0;
+            ++cu_t;
+        }
+        if (++cu_m3 == 3) cu_m3 = 0;
         __builtin_amdgcn_s_waitcnt(0);   // the next item's DMA
         __syncthreads();
     }
