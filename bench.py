@@ -27,6 +27,10 @@ Reported (one JSON line):
   roofline     decode_split, HBM-bound: K/V bytes / its mean duration vs 8 TB/s;
   roofline_prefill  prefill_causal, MFMA-bound: 4*S^2*d*H_q/2 FLOP / its mean
                duration vs the 2.5 PFLOP/s bf16 dense peak;
+  prefill.mfma_ceiling  the matrix cores' own rate on operands drawn like the prefill's
+               inputs (bf16 N(0,1)) and on zeros, from a kernel of independent 32x32x16
+               products and nothing else (gqa_mfma_rate): the clock the chip holds under
+               sustained matrix-core load depends on the operand bits;
   cpu_baseline the fp64 CPU oracle on the same decode workload (rank 0 only).
 
 Measured after the timed region, each in its own graph loop (not part of a step):
@@ -67,6 +71,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_FLOP_PER_CLK_CU = 4096    # CDNA4 dense bf16 matrix-core FLOP per clock per compute unit
 COPY_BYTES = 512 << 20         # calibration copy: reads and writes this many bytes
 REPLAYS = 5                    # timed replays of each graph loop (median and min reported)
+MFMA_ITERS = 1024              # rounds per wave of the matrix-core calibration (~0.6 ms)
+MFMA_OPS = 16 << 20            # bf16 operand elements (32 MiB: every thread its own)
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE at this workload,
 # keyed by a digest of the kernel's sources: a kernel edited since its counters were
@@ -584,6 +590,12 @@ def main():
         del pinp
         o_p = torch.empty_like(q_p)
         lse_p = torch.empty((pc.B, pc.H_q, pc.S), dtype=torch.float32, device="cuda")
+        # the matrix-core calibration's operands: bf16 N(0,1) like the prefill's inputs, and
+        # zeros
+        gen = torch.Generator(device="cuda").manual_seed(20260104)
+        mfma_ops = {"randn": torch.randn(MFMA_OPS, device="cuda", generator=gen).to(torch.bfloat16),
+                    "zeros": torch.zeros(MFMA_OPS, dtype=torch.bfloat16, device="cuda")}
+        mfma_sink = g.mfma_rate(mfma_ops["zeros"], 1)[0]
 
     def decode_call(i):
         k, v = kv_copies[i % len(kv_copies)]
@@ -608,6 +620,12 @@ def main():
     def prefill_call(i):
         g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
 
+    def mfma_randn_call(i):
+        g.mfma_rate(mfma_ops["randn"], MFMA_ITERS, mfma_sink)
+
+    def mfma_zeros_call(i):
+        g.mfma_rate(mfma_ops["zeros"], MFMA_ITERS, mfma_sink)
+
     if args.profile is not None:
         if args.profile in ("prefill_long", "prefill_bwd"):
             res = profile_extra(args.profile, K, locals().get("q_p"), locals().get("k_p"),
@@ -627,6 +645,7 @@ def main():
         decode_call(i)
         prefill_call(i)
         ceiling_call(i)
+        mfma_randn_call(i)
     torch.cuda.synchronize()
 
     def capture(fn, n):
@@ -641,7 +660,8 @@ def main():
 
     graphs = {name: capture(fn, K) for name, fn in
               (("decode", decode_call), ("prefill", prefill_call), ("split", split_call),
-               ("merge", merge_call), ("ceiling", ceiling_call), ("floor", floor_call))}
+               ("merge", merge_call), ("ceiling", ceiling_call), ("floor", floor_call),
+               ("mfma_randn", mfma_randn_call), ("mfma_zeros", mfma_zeros_call))}
 
     def replay_ms(name):
         """Time per call of one replay, from events on the launch stream."""
@@ -667,7 +687,7 @@ def main():
     for _ in range(REPLAYS - 1):
         for name in graphs:
             reps[name].append(replay_ms(name))
-    for name in ("split", "merge", "ceiling", "floor"):
+    for name in ("split", "merge", "ceiling", "floor", "mfma_randn", "mfma_zeros"):
         reps[name].append(replay_ms(name))
 
     def stat(name):
@@ -686,6 +706,9 @@ def main():
     split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
     ceiling_gbs = kv_bytes / (ceiling_ms * 1e-3) / 1e9
     prefill_tflops = flop / (prefill_ms * 1e-3) / 1e12
+    mfma_flop = g.mfma_rate(mfma_ops["zeros"], MFMA_ITERS, mfma_sink)[1]
+    mfma_tflops = {k: mfma_flop / (float(np.mean(reps["mfma_" + k])) * 1e-3) / 1e12
+                   for k in ("randn", "zeros")}
     ds, ps = stat("decode"), stat("prefill")
 
     out = {
@@ -749,6 +772,16 @@ def main():
             "ms": round(prefill_ms, 4),
             "ms_per_call": {"timed": round(prefill_ms, 4), "median": round(ps["median_ms"], 4),
                             "min": round(ps["min_ms"], 4), "replays": ps["replays"]},
+            "mfma_ceiling": {
+                "kernel": "mfma_rate (gqa_mfma_rate)",
+                "tflops_randn": round(mfma_tflops["randn"], 1),
+                "tflops_zeros": round(mfma_tflops["zeros"], 1),
+                "frac_bf16_peak_randn": round(mfma_tflops["randn"] / bf16_peak, 4),
+                "frac_of_ceiling": round(prefill_tflops / mfma_tflops["randn"], 4),
+                "what": f"{MFMA_ITERS} rounds of 16 independent bf16 32x32x16 products per wave, "
+                        "256 workgroups x 512 threads, operands loaded once: bf16 N(0,1) "
+                        "(the prefill's input distribution) or zeros; the chip's clock under "
+                        "matrix-core load falls with the operands' switching activity"},
         },
         "peaks": {"hbm_gbs": HBM_PEAK_GBS, "hbm_source": "MI355X published HBM3E bandwidth",
                   "bf16_tflops": round(bf16_peak, 1),

@@ -104,6 +104,10 @@ def load_library(path=LIBRARY):
     L.gqa_stream_read_sink_bytes.restype = cs
     L.gqa_stream_read.argtypes = [vp, cs, vp, vp]
     L.gqa_stream_read.restype = ci
+    L.gqa_mfma_rate_sink_bytes.argtypes = []
+    L.gqa_mfma_rate_sink_bytes.restype = cs
+    L.gqa_mfma_rate.argtypes = [vp, cs, ci, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.gqa_mfma_rate.restype = ci
     if path == LIBRARY:
         _lib = L
     return L
@@ -166,6 +170,23 @@ def stream_read(buf, sink=None):
     nbytes = buf.numel() * buf.element_size()
     _check(L.gqa_stream_read(_ptr(buf), nbytes - nbytes % 16, _ptr(sink), _stream(buf.device)))
     return sink
+
+
+def mfma_rate(ops, iters, sink=None):
+    """One launch of the library's matrix-core rate kernel on the operand bits of a GPU
+    tensor (the prefill's calibration: rounds of independent bf16 32x32x16 products, nothing
+    else); returns (sink tensor, FLOP count of the launch)."""
+    if not isinstance(ops, torch.Tensor) or not ops.is_cuda or not ops.is_contiguous():
+        raise ValueError("ops must be a contiguous GPU tensor")
+    L = load_library()
+    if sink is None:
+        sink = torch.empty(L.gqa_mfma_rate_sink_bytes() // 4, dtype=torch.float32,
+                           device=ops.device)
+    nbytes = ops.numel() * ops.element_size()
+    flop = ctypes.c_double()
+    _check(L.gqa_mfma_rate(_ptr(ops), nbytes - nbytes % 16, int(iters), _ptr(sink),
+                           ctypes.byref(flop), _stream(ops.device)))
+    return sink, flop.value
 
 
 def decode_plan(B, H_q, H_kv, d, S_max, num_splits=0):

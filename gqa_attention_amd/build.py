@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["gqa_attn_api.cpp", "decode_split.hip", "lse_merge.hip", "prefill_causal.hip",
-           "prefill_bwd.hip", "kv_fp8.hip", "hbm_read.hip",
+           "prefill_bwd.hip", "kv_fp8.hip", "hbm_read.hip", "mfma_rate.hip",
            "decode_noalloc.hip"]
 
 # Packed fp32 VALU instructions are switched off for every kernel; the host pass

@@ -364,6 +364,27 @@ int gqa_stream_read(const void *buf, size_t bytes, void *sink, void *stream) {
     return ok();
 }
 
+size_t gqa_mfma_rate_sink_bytes(void) { return (size_t)gqa::mfma_rate_threads() * sizeof(float); }
+
+int gqa_mfma_rate(const void *ops, size_t bytes, int iters, void *sink, double *flop_out,
+                  void *stream) {
+    if (!ops) return fail(GQA_ERR_NULL_POINTER, "ops is NULL");
+    if (!sink) return fail(GQA_ERR_NULL_POINTER, "sink is NULL");
+    if (!aligned(ops, 16)) return fail(GQA_ERR_ALIGNMENT, "ops is not 16-byte aligned");
+    if (!aligned(sink, 4)) return fail(GQA_ERR_ALIGNMENT, "sink is not 4-byte aligned");
+    if (bytes < 256 || bytes % 16 != 0)
+        return fail(GQA_ERR_BAD_SHAPE, "bytes=%zu must be a multiple of 16 and at least 256", bytes);
+    if (iters < 1 || iters > (1 << 20))
+        return fail(GQA_ERR_BAD_SHAPE, "iters=%d outside [1, 1048576]", iters);
+    int rc;
+    if ((rc = hip_status(gqa::launch_mfma_rate(ops, bytes, iters, static_cast<float *>(sink),
+                                               static_cast<hipStream_t>(stream)),
+                         "mfma_rate")))
+        return rc;
+    if (flop_out) *flop_out = gqa::mfma_rate_flop(iters);
+    return ok();
+}
+
 int gqa_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int num_splits,
                     int *partitions_out, int *states_out, size_t *workspace_bytes_out) {
     Plan pl;

@@ -144,6 +144,14 @@ hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream);
 int hbm_read_blocks();
 hipError_t launch_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+// Rounds of independent bf16 32x32x16 matrix products on operands loaded from `ops`
+// (`bytes`, a multiple of 16, at least 256 B); sink holds mfma_rate_threads() floats, one
+// written per thread.  mfma_rate_flop(iters) is the FLOP count of one launch.
+int mfma_rate_threads();
+double mfma_rate_flop(int iters);
+hipError_t launch_mfma_rate(const void *ops, size_t bytes, int iters, float *sink,
+                            hipStream_t stream);
+
 // The library's own decode workspace on the current device (decode_noalloc.hip): its
 // size, and its device address (looked up once per device, on first use).
 size_t noalloc_scratch_bytes();

@@ -93,6 +93,27 @@ size_t gqa_stream_read_sink_bytes(void);
 int gqa_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
 
 /*
+ * gqa_mfma_rate -- the prefill's matrix-core ceiling on this device for given operand
+ * data (V07, section 19: prefill is bound by its matrix products): one launch of a
+ * kernel (one workgroup of 512 threads per compute unit) in which every wave runs
+ * `iters` rounds of 16 independent bf16 32x32x16 matrix products on 16 operand
+ * fragments it loads once from `ops` -- thread t takes the 16-byte words
+ * (16 t + i) mod (bytes / 16), i = 0..15 -- and does nothing else.  The rate depends on
+ * the operand bits as well as on the instructions (under sustained load the engine
+ * clock falls with the switching of random mantissas), so the caller passes data drawn
+ * like the prefill's inputs and times the launch.  *flop_out, if flop_out is not NULL,
+ * receives the launch's FLOP count.
+ *
+ *   ops    device memory, 16-byte aligned, read-only; bytes a multiple of 16, >= 256
+ *   iters  rounds per wave, 1 .. 1048576
+ *   sink   gqa_mfma_rate_sink_bytes() bytes of device memory, 4-byte aligned: thread t
+ *          writes the sum of its accumulators (a float) at word t
+ */
+size_t gqa_mfma_rate_sink_bytes(void);
+int gqa_mfma_rate(const void *ops, size_t bytes, int iters, void *sink, double *flop_out,
+                  void *stream);
+
+/*
  * Split-KV plan of a decode launch (V07, section 17, split-K decode: the key
  * axis is cut into partitions whose partial states a second stage merges;
  * ADR-0060, section 4: the partial states are combined in two levels).

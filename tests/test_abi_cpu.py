@@ -314,6 +314,25 @@ def test_stream_read_rejects_before_launch(lib):
     assert sink > 0 and sink % 4 == 0
 
 
+def test_mfma_rate_rejects_before_launch(lib):
+    """The matrix-core calibration checks its operands, sink, size and round count on the
+    host, and leaves the FLOP count untouched when it refuses."""
+    flop = ctypes.c_double(-1.0)
+    fp = ctypes.byref(flop)
+    assert lib.gqa_mfma_rate(None, 1024, 4, A, fp, None) == NULLP
+    assert lib.gqa_mfma_rate(A, 1024, 4, None, fp, None) == NULLP
+    assert lib.gqa_mfma_rate(ctypes.c_void_p(0x10008), 1024, 4, A, fp, None) == ALIGN
+    assert lib.gqa_mfma_rate(A, 1024, 4, ctypes.c_void_p(0x10002), fp, None) == ALIGN
+    assert lib.gqa_mfma_rate(A, 240, 4, A, fp, None) == SHAPE        # under 256 bytes
+    assert lib.gqa_mfma_rate(A, 1000, 4, A, fp, None) == SHAPE       # not a multiple of 16
+    assert lib.gqa_mfma_rate(A, 1024, 0, A, fp, None) == SHAPE
+    assert lib.gqa_mfma_rate(A, 1024, (1 << 20) + 1, A, fp, None) == SHAPE
+    assert flop.value == -1.0
+    sink = lib.gqa_mfma_rate_sink_bytes()
+    # one float per thread of 256 workgroups of 512 threads
+    assert sink == 256 * 512 * 4
+
+
 def _noalloc(lib, q=A, k=A, v=A, seqlens=None, o=A, lse=A, B=1, H_q=64, H_kv=8, d=128, S=64,
              scale=0.088, splits=32):
     return lib.gqa_attn_decode_noalloc(q, k, v, seqlens, o, lse, B, H_q, H_kv, d, S, scale,

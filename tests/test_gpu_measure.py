@@ -1,5 +1,6 @@
-"""The two calls the roofline figures are computed from, on the GPU: the device's compute
-units and clock (the bf16 dense peak), and one launch of the streaming-read calibration."""
+"""The calls the roofline figures are computed from, on the GPU: the device's compute
+units and clock (the bf16 dense peak), one launch of the streaming-read calibration, and the
+matrix-core rate calibration."""
 import pytest
 import torch
 
@@ -26,3 +27,18 @@ def test_stream_read_runs_and_leaves_the_sink(gpu_available):
     torch.cuda.synchronize()
     assert bool((sink == 7).all())
     assert int(buf.count_nonzero()) == 0
+
+
+def test_mfma_rate_sums_its_products(gpu_available):
+    """Operands of bf16 ones: each product adds 16 to every element of its accumulator and
+    each of a thread's 4 accumulators (16 elements) takes 4 products a round, so after 8
+    rounds every thread's sum is 64 * 64 * 8 exactly; zeros give zero."""
+    ones = torch.ones(1 << 16, dtype=torch.bfloat16, device="cuda")
+    sink, flop = g.mfma_rate(ones, 8)
+    torch.cuda.synchronize()
+    assert flop == 256 * 8 * 8 * 16 * 2 * 32 * 32 * 16
+    assert sink.numel() == 256 * 512
+    assert bool((sink == 64 * 64 * 8).all())
+    sink, _ = g.mfma_rate(torch.zeros_like(ones), 8, sink)
+    torch.cuda.synchronize()
+    assert bool((sink == 0).all())
