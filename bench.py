@@ -523,7 +523,8 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies, bf16_peak):
     return res
 
 
-PROFILE_LOOPS = ("decode", "split", "merge", "prefill", "prefill_long", "prefill_bwd", "ceiling")
+PROFILE_LOOPS = ("decode", "split", "merge", "prefill", "prefill_long", "prefill_bwd", "ceiling",
+                 "mfma_randn", "mfma_zeros")
 
 
 def main():
@@ -568,7 +569,7 @@ def main():
     dc, pc = LLAMA_DECODE, LLAMA_PREFILL
     K = args.steps
     need_decode = args.profile in (None, "decode", "split", "merge", "ceiling")
-    need_prefill = args.profile in (None, "prefill", "prefill_bwd")
+    need_prefill = args.profile in (None, "prefill", "prefill_bwd", "mfma_randn", "mfma_zeros")
     if need_decode:
         dinp = for_config(dc)
         q_d = upload(dinp["q"])
@@ -632,11 +633,16 @@ def main():
                                 locals().get("v_p"))
         else:
             fn = {"decode": decode_call, "split": split_call, "merge": merge_call,
-                  "prefill": prefill_call, "ceiling": ceiling_call}[args.profile]
+                  "prefill": prefill_call, "ceiling": ceiling_call,
+                  "mfma_randn": mfma_randn_call, "mfma_zeros": mfma_zeros_call}[args.profile]
             for i in range(args.warmup):
                 fn(i)
             torch.cuda.synchronize()
             res = {"ms_per_call": graph_stats(fn, K, replays=2)}
+            if args.profile.startswith("mfma_"):
+                mflop = g.mfma_rate(mfma_ops["zeros"], MFMA_ITERS, mfma_sink)[1]
+                res["tflops"] = {k: round(mflop / (v * 1e-3) / 1e12, 1)
+                                 for k, v in res["ms_per_call"].items()}
         print(json.dumps({"profile": args.profile, "steps": K, **res}), flush=True)
         return
 
