@@ -523,8 +523,8 @@ def extra_measurements(K, q_p, k_p, v_p, decode_ms, kv_copies, bf16_peak):
     return res
 
 
-PROFILE_LOOPS = ("decode", "split", "merge", "prefill", "prefill_long", "prefill_bwd", "ceiling",
-                 "mfma_randn", "mfma_zeros")
+PROFILE_LOOPS = ("decode", "split", "merge", "prefill", "prefill_zeros", "prefill_long",
+                 "prefill_bwd", "ceiling", "mfma_randn", "mfma_zeros")
 
 
 def main():
@@ -569,7 +569,8 @@ def main():
     dc, pc = LLAMA_DECODE, LLAMA_PREFILL
     K = args.steps
     need_decode = args.profile in (None, "decode", "split", "merge", "ceiling")
-    need_prefill = args.profile in (None, "prefill", "prefill_bwd", "mfma_randn", "mfma_zeros")
+    need_prefill = args.profile in (None, "prefill", "prefill_zeros", "prefill_bwd", "mfma_randn",
+                                    "mfma_zeros")
     if need_decode:
         dinp = for_config(dc)
         q_d = upload(dinp["q"])
@@ -597,6 +598,8 @@ def main():
         mfma_ops = {"randn": torch.randn(MFMA_OPS, device="cuda", generator=gen).to(torch.bfloat16),
                     "zeros": torch.zeros(MFMA_OPS, dtype=torch.bfloat16, device="cuda")}
         mfma_sink = g.mfma_rate(mfma_ops["zeros"], 1)[0]
+        if args.profile == "prefill_zeros":
+            zq_p, zk_p, zv_p = (torch.zeros_like(t) for t in (q_p, k_p, v_p))
 
     def decode_call(i):
         k, v = kv_copies[i % len(kv_copies)]
@@ -621,6 +624,11 @@ def main():
     def prefill_call(i):
         g.prefill_causal(q_p, k_p, v_p, out=o_p, lse=lse_p)
 
+    def prefill_zeros_call(i):
+        # the same launch on all-zero Q, K and V: the instruction stream is the same, the
+        # operands switch nothing (the matrix cores' clock depends on the operand bits)
+        g.prefill_causal(zq_p, zk_p, zv_p, out=o_p, lse=lse_p)
+
     def mfma_randn_call(i):
         g.mfma_rate(mfma_ops["randn"], MFMA_ITERS, mfma_sink)
 
@@ -633,15 +641,18 @@ def main():
                                 locals().get("v_p"))
         else:
             fn = {"decode": decode_call, "split": split_call, "merge": merge_call,
-                  "prefill": prefill_call, "ceiling": ceiling_call,
+                  "prefill": prefill_call, "prefill_zeros": prefill_zeros_call,
+                  "ceiling": ceiling_call,
                   "mfma_randn": mfma_randn_call, "mfma_zeros": mfma_zeros_call}[args.profile]
             for i in range(args.warmup):
                 fn(i)
             torch.cuda.synchronize()
             res = {"ms_per_call": graph_stats(fn, K, replays=2)}
-            if args.profile.startswith("mfma_"):
-                mflop = g.mfma_rate(mfma_ops["zeros"], MFMA_ITERS, mfma_sink)[1]
-                res["tflops"] = {k: round(mflop / (v * 1e-3) / 1e12, 1)
+            if args.profile.startswith("mfma_") or args.profile.startswith("prefill"):
+                fl = (g.mfma_rate(mfma_ops["zeros"], MFMA_ITERS, mfma_sink)[1]
+                      if args.profile.startswith("mfma_")
+                      else acc.prefill_causal_flop(pc.B, pc.S, pc.H_q, pc.d))
+                res["tflops"] = {k: round(fl / (v * 1e-3) / 1e12, 1)
                                  for k, v in res["ms_per_call"].items()}
         print(json.dumps({"profile": args.profile, "steps": K, **res}), flush=True)
         return
