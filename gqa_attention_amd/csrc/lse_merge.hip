@@ -50,15 +50,42 @@ __device__ __forceinline__ void merge_into(MState &x, const MState &y) {
     x.m = mn;
 }
 
-// Four consecutive O values of a partial state: fp32, or bf16 (the decode workspace).
+// Four consecutive O values of a partial state as loaded: fp32, or bf16 (the decode
+// workspace: two words of two values each, widened by o4_value after every load of a round
+// has been issued -- widening inside the load's own branch would make each load wait).
 template <bool OB>
-__device__ __forceinline__ f32x4 load_o4(const void *base, size_t idx) {
+struct ORaw {
+    f32x4 v;
+};
+template <>
+struct ORaw<true> {
+    u32x2 v;
+};
+
+template <bool OB>
+__device__ __forceinline__ ORaw<OB> load_o4(const void *base, size_t idx) {
+    if constexpr (OB)
+        return {*reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(base) + idx)};
+    else
+        return {*reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx)};
+}
+
+template <bool OB>
+__device__ __forceinline__ ORaw<OB> zero_o4() {
+    if constexpr (OB)
+        return {u32x2{0u, 0u}};
+    else
+        return {f32x4{0.f, 0.f, 0.f, 0.f}};
+}
+
+template <bool OB>
+__device__ __forceinline__ f32x4 o4_value(const ORaw<OB> &r) {
     if constexpr (OB) {
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(base) + idx);
+        const u32x2 w = r.v;
         return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xFFFF0000u),
                      __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
     } else {
-        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
+        return r.v;
     }
 }
 
@@ -97,7 +124,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
     MState st{neg_inf(), 0.f, {0.f, 0.f, 0.f, 0.f}};
     for (int base = 64 * w; base < n; base += kPerRound) {
         float mv[8], lv[8];
-        f32x4 ov[8];
+        ORaw<OB> ov[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int p = base + 8 * j + s8;
@@ -108,13 +135,14 @@ __global__ __launch_bounds__(kMergeWaves * 64) void lse_merge_kernel(MergeArgs a
             } else {
                 mv[j] = neg_inf();
                 lv[j] = 0.f;
-                ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                ov[j] = zero_o4<OB>();
             }
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             // past the end, or an empty partial: m = -inf adds nothing
-            const MState y{mv[j], lv[j], {ov[j][0], ov[j][1], ov[j][2], ov[j][3]}};
+            const f32x4 o4 = o4_value<OB>(ov[j]);
+            const MState y{mv[j], lv[j], {o4[0], o4[1], o4[2], o4[3]}};
             merge_into(st, y);
         }
     }
