@@ -86,9 +86,9 @@ TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x request-size factor (2.00 for 128-byte
                   "(profiles/hbm_traffic_*.md), valid while the kernel's source digest "
                   "matches; null otherwise")
 MEASURED_TRAFFIC = {
-    "decode_split": ("39280f20da99d6d6", 138_838_834),
-    "lse_merge": ("ffa76bcde8b8768c", 4_790_067),
-    "prefill_causal": ("34c00fb6ea33ac3b", 422_964_804),
+    "decode_split": ("5e0faea18705afd1", 138_838_800),
+    "lse_merge": ("08c06f1324a0f153", 4_789_043),
+    "prefill_causal": ("6067cf10c63d565e", 423_036_980),
 }
 
 
