@@ -601,21 +601,40 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DecodeSplitAr
         const size_t srow = (size_t)(x + cb) * a.H_q * a.T;   // states: [slot][H_q * T]
 
         if (wph == 1) {
-            // one wave per head: its registers hold the whole state
+            // one wave per head: its registers hold the whole state.  Lane (row16, grp) holds
+            // elements 16 dt + 4 grp .. + 3 of state row row16, so stores from registers would
+            // write 32-byte pieces of 8 rows each; the block's rows go through the wave's own
+            // V staging area instead (free once its last tile is done; 32-byte segment s of
+            // row r at segment s ^ (r mod NDT)) and leave 1 KiB of consecutive rows per store.
+            uint8_t *stg = reinterpret_cast<uint8_t *>(vs);
 #pragma unroll
             for (int bk = 0; bk < CB; ++bk) {
-                if (row16 < nhb[bk]) {
-                    const size_t row = srow + h0 + bk * 16 + row16;
-                    uint16_t *orow = a.part_o + row * D + grp * 4;
+                const int nh = nhb[bk];
 #pragma unroll
-                    for (int dt = 0; dt < T::NDT; ++dt)
-                        *reinterpret_cast<u32x2 *>(orow + dt * 16) =
-                            u32x2{pack_bf16x2(st.o[bk][dt][0], st.o[bk][dt][1]),
-                                  pack_bf16x2(st.o[bk][dt][2], st.o[bk][dt][3])};
-                    if (grp == 0) {
-                        a.part_m2[row] = st.m[bk];
-                        a.part_l[row] = st.l[bk];
-                    }
+                for (int dt = 0; dt < T::NDT; ++dt)
+                    *reinterpret_cast<u32x2 *>(stg + row16 * (2 * D) +
+                                               32 * (dt ^ (row16 & (T::NDT - 1))) + 8 * grp) =
+                        u32x2{pack_bf16x2(st.o[bk][dt][0], st.o[bk][dt][1]),
+                              pack_bf16x2(st.o[bk][dt][2], st.o[bk][dt][3])};
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const size_t row0 = srow + h0 + bk * 16;
+                uint8_t *dst = reinterpret_cast<uint8_t *>(a.part_o + row0 * D);
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) {   // 16 rows of 2 D bytes, 1 KiB at a time
+                    const int byte = i * 1024 + lane * 16;
+                    const int r = byte / (2 * D), seg = (byte % (2 * D)) / 32;
+                    if (r < nh)
+                        *reinterpret_cast<u32x4 *>(dst + byte) = *reinterpret_cast<const u32x4 *>(
+                            stg + r * (2 * D) + 32 * (seg ^ (r & (T::NDT - 1))) + byte % 32);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (grp == 0 && row16 < nh) {
+                    a.part_m2[row0 + row16] = st.m[bk];
+                    a.part_l[row0 + row16] = st.l[bk];
                 }
             }
         } else {
