@@ -174,6 +174,39 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int n_t) {
     }
 }
 
+// Store 32 rows of a wave's accumulators x (times f, rounded to bf16) to rows r0 .. r0 + 31
+// of out (row_elems elements apart; rows at or past n_rows are not stored).  A lane holds
+// elements 32 dt + 8 rq + 4 hf .. + 3 of row r0 + lane % 32, so stores from registers would
+// touch 32 rows per instruction; the rows go through the wave's own 8 KiB of LDS (stage;
+// 16-byte chunks XOR-permuted by row, no bank conflicts either way) and leave as whole
+// 256-byte rows.
+__device__ __forceinline__ void store_rows(const f32x16 (&x)[4], float f, uint8_t *stage,
+                                           uint16_t *out, size_t row_elems, int r0, int n_rows,
+                                           int lane) {
+    const int r32 = lane & 31, hf = lane >> 5, cr = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int r = rq * 4;
+            const int c = (dt * 4 + rq) ^ (r32 & 15);
+            *reinterpret_cast<u32x2 *>(stage + r32 * kRowBytes + 16 * c + 8 * hf) =
+                u32x2{pack_bf16x2(x[dt][r] * f, x[dt][r + 1] * f),
+                      pack_bf16x2(x[dt][r + 2] * f, x[dt][r + 3] * f)};
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const u32x4 val =
+            *reinterpret_cast<const u32x4 *>(stage + rr * kRowBytes + 16 * (cr ^ (rr & 15)));
+        if (r0 + rr < n_rows)
+            *reinterpret_cast<u32x4 *>(out + (size_t)(r0 + rr) * row_elems + 8 * cr) = val;
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // bwd_dq: workgroup = 256 query rows of one query head (8 waves x 32 rows), key tiles of 64
 // through a ring of two LDS slots (K 16 KiB, V 16 KiB each); the tile loop is unrolled by two
@@ -303,19 +336,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
     }
     if (t < n_kt) tile(t, std::integral_constant<int, 0>{});
 
-    if (row >= a.S) return;
-    const float tau = a.scale;
-    uint16_t *out = a.dq + (((size_t)b * a.S + row) * a.H_q + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const int dd = dt * 32 + rq * 8 + hf * 4;
-            const int r = rq * 4;
-            *reinterpret_cast<u32x2 *>(out + dd) =
-                u32x2{pack_bf16x2(acc[dt][r] * tau, acc[dt][r + 1] * tau),
-                      pack_bf16x2(acc[dt][r + 2] * tau, acc[dt][r + 3] * tau)};
-        }
+    // dQ times tau; every tile ended with a barrier after its DMA landed, so the rings are
+    // free for the staging
+    store_rows(acc, a.scale, smem + w * (32 * kRowBytes), a.dq + ((size_t)b * a.S * a.H_q + h) * D,
+               (size_t)a.H_q * D, r0, a.S, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -552,23 +576,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     f32x4 *xch = reinterpret_cast<f32x4 *>(smem + kRing) + kg * 16 * 64 + lane;
     hand_over(dk, xch, rh);
     hand_over(dv, xch, rh);
-    if (rh == 1 || key >= a.S) return;
+    if (rh == 1) return;
 
-    // dK (times tau) and dV of the lane's key, summed over the G heads, rounded to bf16
-    const float tau = a.scale;
-    const size_t off = (((size_t)b * a.S + key) * a.H_kv + g) * D;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const int dd = dt * 32 + rq * 8 + hf * 4;
-            const int r = rq * 4;
-            *reinterpret_cast<u32x2 *>(a.dk + off + dd) =
-                u32x2{pack_bf16x2(dk[dt][r] * tau, dk[dt][r + 1] * tau),
-                      pack_bf16x2(dk[dt][r + 2] * tau, dk[dt][r + 3] * tau)};
-            *reinterpret_cast<u32x2 *>(a.dv + off + dd) =
-                u32x2{pack_bf16x2(dv[dt][r], dv[dt][r + 1]), pack_bf16x2(dv[dt][r + 2], dv[dt][r + 3])};
-        }
+    // dK (times tau) and dV of the wave's keys, summed over the G heads, rounded to bf16, staged
+    // in the block's K/V buffers (free since the hand-over's barriers), 16 KiB per key group
+    const size_t kvo = ((size_t)b * a.S * a.H_kv + g) * D;
+    uint8_t *stage = smem + kg * (64 * kRowBytes);
+    store_rows(dk, a.scale, stage, a.dk + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
+    store_rows(dv, 1.f, stage + 32 * kRowBytes, a.dv + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
 }
 
 }  // namespace
