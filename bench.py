@@ -86,9 +86,9 @@ TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x request-size factor (2.00 for 128-byte
                   "(profiles/hbm_traffic_*.md), valid while the kernel's source digest "
                   "matches; null otherwise")
 MEASURED_TRAFFIC = {
-    "decode_split": ("5e0faea18705afd1", 138_838_800),
+    "decode_split": ("370fd40da10d3571", 138_841_102),
     "lse_merge": ("08c06f1324a0f153", 4_789_043),
-    "prefill_causal": ("6067cf10c63d565e", 423_036_980),
+    "prefill_causal": ("858e3d785e9c5ad1", 421_837_952),
 }
 
 
