@@ -338,6 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
 
     // dQ times tau; every tile ended with a barrier after its DMA landed, so the rings are
     // free for the staging
+    static_assert(kWaves * 32 * kRowBytes <= kDqLds, "each wave stages its 32 rows");
     store_rows(acc, a.scale, smem + w * (32 * kRowBytes), a.dq + ((size_t)b * a.S * a.H_q + h) * D,
                (size_t)a.H_q * D, r0, a.S, lane);
 }
@@ -581,6 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     // dK (times tau) and dV of the wave's keys, summed over the G heads, rounded to bf16, staged
     // in the block's K/V buffers (free since the hand-over's barriers), 16 KiB per key group
     const size_t kvo = ((size_t)b * a.S * a.H_kv + g) * D;
+    static_assert(4 * 64 * kRowBytes <= kRing, "the four key groups stage in the K/V block");
     uint8_t *stage = smem + kg * (64 * kRowBytes);
     store_rows(dk, a.scale, stage, a.dk + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
     store_rows(dv, 1.f, stage + 32 * kRowBytes, a.dv + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
