@@ -30,6 +30,9 @@ SMALL = [
     (1, 520, 16, 2),      # G = 8 with the XCD remap active, ragged tail
     (2, 700, 16, 2),      # three 256-row q-blocks per head, ragged, B = 2 (remap active)
     (1, 1000, 8, 8),      # MHA at four q-blocks with a ragged last key tile
+    (1, 333, 4, 2),       # G = 2
+    (1, 300, 6, 2),       # G = 3 (no remap: 2 q-blocks x 2 KV heads is not a multiple of 8)
+    (1, 200, 32, 2),      # G = 16
 ]
 
 
