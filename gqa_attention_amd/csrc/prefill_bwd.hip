@@ -398,7 +398,7 @@ __device__ __forceinline__ void hand_over(f32x16 (&x)[4], f32x4 *xch, int rh) {
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_kb, int n_t) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_t) {
     __shared__ __attribute__((aligned(256))) uint8_t smem[kKvLds];
     const int G = a.H_q / a.H_kv;
     int u = blockIdx.x;
@@ -412,8 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     const int r32 = lane & 31, hf = lane >> 5;
     const int rh = w / 4, kg = w % 4;                // row half, key group
     const int k0 = kb * kKBlk;
-    const int kw0 = k0 + 32 * kg;                    // the wave's first key
-    const int key = kw0 + r32;                       // the lane's key
+    const int kw0 = k0 + 32 * kg;                    // the wave's first key (lane: kw0 + r32)
     const int t0 = k0 / kStatRows;                   // first query tile: rows k0 ..
     const Addr ad = make_addr(lane);
     const int lr = 4 * w + lane / 16;
@@ -608,7 +607,7 @@ hipError_t launch_prefill_bwd(BwdArgs a, void *ws, hipStream_t stream) {
                        0, stream, a, n_qb, n_t);
     const int n_kb = (a.S + kKBlk - 1) / kKBlk;
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((long)n_kb * a.B * a.H_kv)),
-                       dim3(kThreads), 0, stream, a, n_kb, n_t);
+                       dim3(kThreads), 0, stream, a, n_t);
     return hipGetLastError();
 }
 
