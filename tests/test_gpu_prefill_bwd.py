@@ -55,6 +55,8 @@ CASES = [
     (1, 1, 8, 2),       # a single token: dQ = dK = 0, dV = the group's dO
     (1, 1000, 16, 8),   # G = 2, four key blocks
     (1, 768, 64, 8),    # Llama3-70B heads, whole blocks
+    (1, 200, 6, 2),     # G = 3: the dK/dV items step through 3 heads a query tile
+    (1, 130, 32, 2),    # G = 16, a partial last key block
 ]
 
 
