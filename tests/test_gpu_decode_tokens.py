@@ -46,6 +46,7 @@ CASES = [
     (2, 16, 8, 1, 32, (20, 300), 4),       # MQA, 128 rows per KV head: 8 row groups
     (5, 5, 16, 2, 128, (1000, 3000), 0),   # 40 rows per KV head, 4 waves per head
     (4, 4, 4, 4, 128, (200, 900), 2),      # MHA, 4 rows per KV head
+    (2, 3, 6, 2, 128, (100, 900), 0),      # G = 3: 9 rows per KV head
 ]
 
 

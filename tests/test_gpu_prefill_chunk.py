@@ -41,6 +41,7 @@ SMALL = [
     (1, 17, 0, 17, 4, 4),           # q_start = 0, T = S_kv: plain causal prefill (MHA)
     (1, 513, 2047, 2600, 8, 8),     # three q-blocks, ragged, odd start, NaN tail
     (3, 40, 5, 45, 16, 2),          # short chunk near the start, B = 3
+    (1, 150, 70, 250, 6, 2),        # G = 3, start not on a 32-key step, NaN tail
 ]
 
 
