@@ -88,7 +88,7 @@ TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x request-size factor (2.00 for 128-byte
 MEASURED_TRAFFIC = {
     "decode_split": ("370fd40da10d3571", 138_841_102),
     "lse_merge": ("08c06f1324a0f153", 4_789_043),
-    "prefill_causal": ("858e3d785e9c5ad1", 421_837_952),
+    "prefill_causal": ("bd508c5a68e10f1d", 421_839_498),
 }
 
 

@@ -178,8 +178,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int n_t) {
 // of out (row_elems elements apart; rows at or past n_rows are not stored).  A lane holds
 // elements 32 dt + 8 rq + 4 hf .. + 3 of row r0 + lane % 32, so stores from registers would
 // touch 32 rows per instruction; the rows go through the wave's own 8 KiB of LDS (stage;
-// 16-byte chunks XOR-permuted by row, no bank conflicts either way) and leave as whole
-// 256-byte rows.
+// 16-byte chunks XOR-permuted by row, which keeps the 16-byte reads free of bank conflicts)
+// and leave as whole 256-byte rows.
 __device__ __forceinline__ void store_rows(const f32x16 (&x)[4], float f, uint8_t *stage,
                                            uint16_t *out, size_t row_elems, int r0, int n_rows,
                                            int lane) {

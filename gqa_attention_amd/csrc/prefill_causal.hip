@@ -545,7 +545,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     // A lane holds 4-element pieces of its row's O, and its row lies H_q * d elements from
     // the next lane's: stored from registers, every store instruction would touch 32 rows.
     // The wave's 32 rows go through LDS instead (8 KiB a wave, 16-byte chunks XOR-permuted
-    // by row so that neither side has bank conflicts) and leave as whole 256-byte rows.
+    // by row, which keeps the 16-byte reads free of bank conflicts) and leave as whole
+    // 256-byte rows.
     // After this barrier every wave's DMA has landed and no wave reads a tile buffer.
     __syncthreads();
     const float l = st.l + __shfl_xor(st.l, 32);
