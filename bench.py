@@ -86,9 +86,9 @@ TRAFFIC_SOURCE = ("rocprofv3 FETCH_SIZE x request-size factor (2.00 for 128-byte
                   "(profiles/hbm_traffic_*.md), valid while the kernel's source digest "
                   "matches; null otherwise")
 MEASURED_TRAFFIC = {
-    "decode_split": ("370fd40da10d3571", 138_841_102),
-    "lse_merge": ("08c06f1324a0f153", 4_789_043),
-    "prefill_causal": ("bd508c5a68e10f1d", 421_839_498),
+    "decode_split": ("5889bc87a4d2e4d6", 138_841_078),
+    "lse_merge": ("c740c74f663b283e", 4_789_096),
+    "prefill_causal": ("6a5c283ec7c706ef", 421_773_415),
 }
 
 

@@ -96,4 +96,37 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Store the 32 rows of a wave's four 32x32 accumulator tiles x (d = 128; times f, rounded
+// to bf16) to rows r0 .. r0 + 31 of out (row_elems elements apart; rows at or past n_rows are
+// not stored).  A lane holds elements 32 dt + 8 rq + 4 hf .. + 3 of row r0 + lane % 32, so
+// stores from registers would touch 32 rows per instruction; the rows go through the wave's
+// own 8 KiB of LDS (stage; 16-byte chunks XOR-permuted by row, which keeps the 16-byte reads
+// free of bank conflicts) and leave as whole 256-byte rows.
+__device__ __forceinline__ void store_rows128(const f32x16 (&x)[4], float f, uint8_t *stage,
+                                              uint16_t *out, size_t row_elems, int r0,
+                                              int n_rows, int lane) {
+    const int r32 = lane & 31, hf = lane >> 5, cr = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int r = rq * 4;
+            const int c = (dt * 4 + rq) ^ (r32 & 15);
+            *reinterpret_cast<u32x2 *>(stage + r32 * 256 + 16 * c + 8 * hf) =
+                u32x2{pack_bf16x2(x[dt][r] * f, x[dt][r + 1] * f),
+                      pack_bf16x2(x[dt][r + 2] * f, x[dt][r + 3] * f)};
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const u32x4 val =
+            *reinterpret_cast<const u32x4 *>(stage + rr * 256 + 16 * (cr ^ (rr & 15)));
+        if (r0 + rr < n_rows)
+            *reinterpret_cast<u32x4 *>(out + (size_t)(r0 + rr) * row_elems + 8 * cr) = val;
+    }
+}
+
 }  // namespace gqa

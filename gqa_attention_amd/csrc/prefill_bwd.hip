@@ -174,39 +174,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int n_t) {
     }
 }
 
-// Store 32 rows of a wave's accumulators x (times f, rounded to bf16) to rows r0 .. r0 + 31
-// of out (row_elems elements apart; rows at or past n_rows are not stored).  A lane holds
-// elements 32 dt + 8 rq + 4 hf .. + 3 of row r0 + lane % 32, so stores from registers would
-// touch 32 rows per instruction; the rows go through the wave's own 8 KiB of LDS (stage;
-// 16-byte chunks XOR-permuted by row, which keeps the 16-byte reads free of bank conflicts)
-// and leave as whole 256-byte rows.
-__device__ __forceinline__ void store_rows(const f32x16 (&x)[4], float f, uint8_t *stage,
-                                           uint16_t *out, size_t row_elems, int r0, int n_rows,
-                                           int lane) {
-    const int r32 = lane & 31, hf = lane >> 5, cr = lane & 15;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const int r = rq * 4;
-            const int c = (dt * 4 + rq) ^ (r32 & 15);
-            *reinterpret_cast<u32x2 *>(stage + r32 * kRowBytes + 16 * c + 8 * hf) =
-                u32x2{pack_bf16x2(x[dt][r] * f, x[dt][r + 1] * f),
-                      pack_bf16x2(x[dt][r + 2] * f, x[dt][r + 3] * f)};
-        }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int rr = 4 * i + (lane >> 4);
-        const u32x4 val =
-            *reinterpret_cast<const u32x4 *>(stage + rr * kRowBytes + 16 * (cr ^ (rr & 15)));
-        if (r0 + rr < n_rows)
-            *reinterpret_cast<u32x4 *>(out + (size_t)(r0 + rr) * row_elems + 8 * cr) = val;
-    }
-}
-
 // ---------------------------------------------------------------------------------------
 // bwd_dq: workgroup = 256 query rows of one query head (8 waves x 32 rows), key tiles of 64
 // through a ring of two LDS slots (K 16 KiB, V 16 KiB each); the tile loop is unrolled by two
@@ -339,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qb
     // dQ times tau; every tile ended with a barrier after its DMA landed, so the rings are
     // free for the staging
     static_assert(kWaves * 32 * kRowBytes <= kDqLds, "each wave stages its 32 rows");
-    store_rows(acc, a.scale, smem + w * (32 * kRowBytes), a.dq + ((size_t)b * a.S * a.H_q + h) * D,
+    store_rows128(acc, a.scale, smem + w * (32 * kRowBytes), a.dq + ((size_t)b * a.S * a.H_q + h) * D,
                (size_t)a.H_q * D, r0, a.S, lane);
 }
 
@@ -583,8 +550,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     const size_t kvo = ((size_t)b * a.S * a.H_kv + g) * D;
     static_assert(4 * 64 * kRowBytes <= kRing, "the four key groups stage in the K/V block");
     uint8_t *stage = smem + kg * (64 * kRowBytes);
-    store_rows(dk, a.scale, stage, a.dk + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
-    store_rows(dv, 1.f, stage + 32 * kRowBytes, a.dv + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
+    store_rows128(dk, a.scale, stage, a.dk + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
+    store_rows128(dv, 1.f, stage + 32 * kRowBytes, a.dv + kvo, (size_t)a.H_kv * D, kw0, a.S, lane);
 }
 
 }  // namespace

@@ -542,38 +542,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_causal_kernel(PrefillArgs
     __builtin_amdgcn_s_waitcnt(0);   // no DMA left in flight at exit
 
     // ---- epilogue: O = O^T / lw -> bf16, LSE = ln2 * (m + log2 l) ----
-    // A lane holds 4-element pieces of its row's O, and its row lies H_q * d elements from
-    // the next lane's: stored from registers, every store instruction would touch 32 rows.
-    // The wave's 32 rows go through LDS instead (8 KiB a wave, 16-byte chunks XOR-permuted
-    // by row, which keeps the 16-byte reads free of bank conflicts) and leave as whole
-    // 256-byte rows.
-    // After this barrier every wave's DMA has landed and no wave reads a tile buffer.
+    // (O leaves through the wave's own 8 KiB of the rings as whole rows; after this barrier
+    // every wave's DMA has landed and no wave reads a tile buffer)
     __syncthreads();
     const float l = st.l + __shfl_xor(st.l, 32);
     const float lw = st.lw + __shfl_xor(st.lw, 32);
-    const float inv = 1.f / lw;
-    uint8_t *stage = smem + w * (32 * kRowBytes);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const int r = rq * 4;   // elements d = 32 dt + 8 rq + 4 hf + 0..3
-            const int c = (dt * 4 + rq) ^ (r32 & 15);
-            *reinterpret_cast<u32x2 *>(stage + r32 * kRowBytes + 16 * c + 8 * hf) =
-                u32x2{pack_bf16x2(st.o[dt][r] * inv, st.o[dt][r + 1] * inv),
-                      pack_bf16x2(st.o[dt][r + 2] * inv, st.o[dt][r + 3] * inv)};
-        }
-    __syncthreads();
-    const int cr = lane & 15;   // 16-byte chunk of the row, d = 8 cr ... 8 cr + 7
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int rr = 4 * i + (lane >> 4);   // row of the wave's 32
-        const u32x4 val =
-            *reinterpret_cast<const u32x4 *>(stage + rr * kRowBytes + 16 * (cr ^ (rr & 15)));
-        if (r0 + rr < a.T)
-            *reinterpret_cast<u32x4 *>(a.o + (((size_t)b * a.T + r0 + rr) * a.H_q + h) * D +
-                                       8 * cr) = val;
-    }
+    static_assert(kWaves * 32 * kRowBytes <= kLdsBytes, "each wave stages its 32 rows");
+    store_rows128(st.o, 1.f / lw, smem + w * (32 * kRowBytes),
+                  a.o + ((size_t)b * a.T * a.H_q + h) * D, (size_t)a.H_q * D, r0, a.T, lane);
     if (hf == 0 && row < a.T)
         a.lse[((size_t)b * a.H_q + h) * a.T + row] =
             clamped ? __builtin_nanf("") : kLn2 * (st.m + __builtin_log2f(l));
